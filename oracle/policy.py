@@ -1,0 +1,123 @@
+"""Miss-path policy: q* split, miss ordering and the LRU slot pool — oracle (test only).
+
+Sources.  The bandwidth-adaptive split sends q* = m * Bp / Bh of a token's m missed experts
+over PCIe into GPU slots and computes the rest on host cores in host RAM at the same time,
+Bp being the measured PCIe transfer bandwidth and Bh the measured effective host memory
+bandwidth (smzdm explainer a825qpgl, section 二, formula and table).  The source-reading
+article (lowalt.boxinlu2.cn, section 二) states the same rule as pull : compute =
+pcie_bw : (cpu_bw - pcie_bw), because the DMA itself consumes Bp of host memory bandwidth;
+solving q / (m - q) = Bp / (Bh - Bp) gives q = m * Bp / Bh.  Experts enter VRAM through a
+global LRU slot pool: recently used experts are brought in, cold ones evicted (smzdm
+explainer aomxznrn, "FreeToken干的事", item 2).
+
+Readings where the pages are silent:
+  * q is the nearest integer to q*, halves rounded up, clamped to [0, m]; Bh <= Bp gives m.
+  * misses are ordered by descending routing weight summed over the call's tokens, ties to
+    the lower expert id; the first q are streamed, the rest computed on the host.
+  * streamed misses are admitted to the pool; host-computed misses are not; hits refresh
+    their slot's last-use step.  Admission takes the lowest-index empty slot, else evicts
+    the occupied slot with the smallest last-use step among slots not used in this step,
+    ties to the lower slot index.  When no slot can be taken the expert is computed on the
+    host instead (so at most the number of takeable slots are streamed).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def qstar_split(m: int, Bp: float, Bh: float):
+    """(q, q*) for m misses at PCIe bandwidth Bp and host bandwidth Bh."""
+    if m < 0 or not (Bp > 0) or not (Bh > 0):
+        raise ValueError("need m >= 0, Bp > 0, Bh > 0")
+    qstar = m * Bp / Bh
+    q = int(math.floor(qstar + 0.5))
+    return max(0, min(m, q)), qstar
+
+
+def qstar_makespan(m: int, Bp: float, Bh: float) -> int:
+    """Variant (reported, not the contract): the integer q minimising the finishing time
+    max(q / Bp, (m - q) / (Bh - Bp)) of the two concurrent sides; lowest q on ties."""
+    if m < 0 or not (Bp > 0) or not (Bh > 0):
+        raise ValueError("need m >= 0, Bp > 0, Bh > 0")
+    if Bh <= Bp:
+        return m
+    cost = [max(q / Bp, (m - q) / (Bh - Bp)) for q in range(m + 1)]
+    return int(np.argmin(cost))
+
+
+def order_misses(misses, weight):
+    """Misses sorted by descending total routing weight, ties to the lower expert id."""
+    return sorted(misses, key=lambda e: (-weight[e], e))
+
+
+@dataclass
+class StepResult:
+    step: int
+    selected: list
+    hits: list
+    misses: list
+    q: int               # q from the split rule
+    streamed: list       # experts copied into slots this step (admitted), in order
+    host: list           # experts computed on the host this step
+    evicted: list        # (slot, expert) pairs evicted this step
+    e2s: np.ndarray = field(repr=False, default=None)
+    s2e: np.ndarray = field(repr=False, default=None)
+
+
+class LruPool:
+    """Expert-slot pool with E experts and S slots (the pool starts empty)."""
+
+    def __init__(self, E: int, S: int):
+        self.E, self.S = E, S
+        self.e2s = np.full(E, -1, dtype=np.int64)
+        self.s2e = np.full(S, -1, dtype=np.int64)
+        self.last_use = np.full(S, -1, dtype=np.int64)
+        self.step_no = 0
+
+    def _take_slot(self, step: int):
+        empty = np.nonzero(self.s2e < 0)[0]
+        if empty.size:
+            return int(empty[0]), None
+        cand = [s for s in range(self.S) if self.last_use[s] < step]
+        if not cand:
+            return None, None
+        s = min(cand, key=lambda s: (self.last_use[s], s))
+        return s, int(self.s2e[s])
+
+    def step(self, idx: np.ndarray, w: np.ndarray, Bp: float, Bh: float, q_override=None):
+        """One decode call: idx/w [T][k] routing of its tokens."""
+        step = self.step_no
+        weight = {}
+        for t in range(idx.shape[0]):
+            for j in range(idx.shape[1]):
+                e = int(idx[t, j])
+                weight[e] = weight.get(e, 0.0) + float(w[t, j])
+        selected = sorted(weight)
+        hits = [e for e in selected if self.e2s[e] >= 0]
+        for e in hits:
+            self.last_use[self.e2s[e]] = step
+        misses = order_misses([e for e in selected if self.e2s[e] < 0], weight)
+        m = len(misses)
+        q = qstar_split(m, Bp, Bh)[0] if q_override is None else max(0, min(m, q_override))
+        streamed, host, evicted = [], [], []
+        for n, e in enumerate(misses):
+            if n >= q:
+                host.append(e)
+                continue
+            s, old = self._take_slot(step)
+            if s is None:
+                host.append(e)
+                continue
+            if old is not None:
+                self.e2s[old] = -1
+                evicted.append((s, old))
+            self.s2e[s] = e
+            self.e2s[e] = s
+            self.last_use[s] = step
+            streamed.append(e)
+        self.step_no += 1
+        return StepResult(step, selected, hits, misses, q, streamed, host, evicted,
+                          self.e2s.copy(), self.s2e.copy())

@@ -1,0 +1,129 @@
+"""Pins for the oracle's q* split, miss ordering, LRU pool and prefill permutation (CPU)."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import perm, policy
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "qstar_table.txt")
+
+
+def _qstar_rows():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, bp, bh, pct = line.split()
+        rows.append((name, float(bp), float(bh), float(pct)))
+    return rows
+
+
+def test_qstar_reproduces_the_pages_table():
+    rows = _qstar_rows()
+    assert len(rows) == 4
+    for name, bp, bh, pct in rows:
+        m = 1000
+        _, qstar = policy.qstar_split(m, bp, bh)
+        assert round(100.0 * qstar / m, 1) == pct, name
+
+
+def test_qstar_matches_pull_to_compute_ratio_form():
+    """pull : compute = Bp : (Bh - Bp) is the same rule as q* = m Bp / Bh."""
+    for _, bp, bh, _ in _qstar_rows():
+        for m in (1, 2, 3, 6, 7, 12):
+            _, q = policy.qstar_split(m, bp, bh)
+            assert q / (m - q) == pytest.approx(bp / (bh - bp), rel=1e-12)
+
+
+def test_qstar_integer_rule():
+    assert policy.qstar_split(0, 50.0, 60.0) == (0, 0.0)
+    assert policy.qstar_split(1, 1.0, 2.0)[0] == 1          # 0.5 rounds up
+    assert policy.qstar_split(3, 1.0, 2.0)[0] == 2          # 1.5 rounds up
+    assert policy.qstar_split(6, 49.0, 53.8)[0] == 5        # 5.465
+    assert policy.qstar_split(6, 60.0, 50.0)[0] == 6        # Bh <= Bp: everything streams
+    assert policy.qstar_split(6, 1.0, 1e9)[0] == 0
+    for bad in ((-1, 1.0, 1.0), (1, 0.0, 1.0), (1, 1.0, 0.0), (1, float("nan"), 1.0)):
+        with pytest.raises(ValueError):
+            policy.qstar_split(*bad)
+
+
+def test_makespan_variant_differs_where_expected():
+    # the finishing-time variant of the split picks 6 on the 5090 desktop at m = 6
+    assert policy.qstar_makespan(6, 49.0, 53.8) == 6
+    assert policy.qstar_split(6, 49.0, 53.8)[0] == 5
+    assert policy.qstar_makespan(2, 52.7, 77.3) == 2
+    assert policy.qstar_makespan(3, 11.8, 47.5) == 0
+    assert policy.qstar_split(3, 11.8, 47.5)[0] == 1
+
+
+def test_miss_order():
+    w = {4: 0.2, 1: 0.5, 9: 0.2, 2: 0.1}
+    assert policy.order_misses([4, 1, 9, 2], w) == [1, 4, 9, 2]
+
+
+def test_lru_scripted_sequence():
+    P = policy.LruPool(E=8, S=2)
+    r = P.step(np.array([[3, 5]]), np.array([[0.6, 0.4]]), 1.0, 1.0)
+    assert r.streamed == [3, 5] and list(r.s2e) == [3, 5] and r.evicted == []
+    r = P.step(np.array([[5, 1]]), np.array([[0.7, 0.3]]), 1.0, 1.0)
+    assert r.hits == [5] and r.streamed == [1] and r.evicted == [(0, 3)]
+    assert list(r.s2e) == [1, 5] and r.e2s[3] == -1
+    r = P.step(np.array([[2, 4]]), np.array([[0.5, 0.5]]), 1.0, 1.0)
+    assert r.misses == [2, 4] and r.evicted == [(0, 1), (1, 5)] and list(r.s2e) == [2, 4]
+    r = P.step(np.array([[6, 2]]), np.array([[0.9, 0.1]]), 1.0, 10.0)
+    assert r.hits == [2] and r.q == 0 and r.host == [6] and list(r.s2e) == [2, 4]
+    r = P.step(np.array([[7, 6]]), np.array([[0.55, 0.45]]), 1.0, 2.5)
+    assert r.q == 1 and r.streamed == [7] and r.host == [6] and r.evicted == [(1, 4)]
+    assert list(r.s2e) == [2, 7]
+
+
+def test_lru_no_takeable_slot_goes_to_host():
+    P = policy.LruPool(E=4, S=1)
+    r = P.step(np.array([[0, 1]]), np.array([[0.6, 0.4]]), 1.0, 1.0)
+    assert r.streamed == [0] and r.host == [1] and r.q == 2
+
+
+def test_lru_invariants_random():
+    rng = np.random.default_rng(3)
+    E, S, k = 32, 6, 4
+    P = policy.LruPool(E, S)
+    for step in range(300):
+        T = int(rng.integers(1, 4))
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+        w = rng.random((T, k))
+        w /= w.sum(1, keepdims=True)
+        bh = float(rng.uniform(0.5, 4.0))
+        r = P.step(idx, w, 1.0, bh)
+        res = np.nonzero(r.e2s >= 0)[0]
+        assert len(res) <= S
+        for e in res:
+            assert r.s2e[r.e2s[e]] == e
+        for s in range(S):
+            if r.s2e[s] >= 0:
+                assert r.e2s[r.s2e[s]] == s
+        sel = set(int(e) for e in idx.ravel())
+        parts = [set(r.hits), set(r.streamed), set(r.host)]
+        assert set().union(*parts) == sel
+        assert sum(len(p) for p in parts) == len(sel)
+        for e in r.streamed + r.hits:
+            assert r.e2s[e] >= 0
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (7, 2, 5), (64, 8, 16), (200, 6, 256)])
+def test_permutation_matches_stable_sort(T, k, E):
+    rng = np.random.default_rng(T * 31 + k)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    counts, offsets, pos, rows = perm.permutation(idx, E)
+    assert counts.sum() == T * k and offsets[-1] == T * k
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    order = np.argsort(idx.ravel(), kind="stable")       # library stable sort
+    assert np.array_equal(rows[:, 0] * k + rows[:, 1], order)
+    flat = pos.ravel()
+    assert np.array_equal(np.sort(flat), np.arange(T * k))
+    for p in range(T * k):
+        t, j = rows[p]
+        assert pos[t, j] == p
+        e = idx[t, j]
+        assert offsets[e] <= p < offsets[e + 1]
