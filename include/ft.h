@@ -1,0 +1,210 @@
+/*
+ * ft.h — C ABI of libft, an MI355X (gfx950) sparse MoE expert layer with block-scaled FP4
+ * expert weights.
+ *
+ * What the layer computes (FreeToken pages: mubeitech explainer, MoE paragraph — a gate
+ * picks a few experts per token; smzdm explainer a825qpgl, section 二 — 6 of 256 experts
+ * active, three classes of selected expert, merged by routing weight):
+ *
+ *   logits_t = x_t . W_r^T + b                       (fp32)
+ *   S_t      = the k largest logits (ties: lower index), in rank order
+ *   w_tj     = softmax over the k kept logits         (== full softmax renormalised)
+ *   y_e(x)   = W_d,e . bf16(silu(W_g,e x) * (W_u,e x))   (SwiGLU; h rounded to bf16)
+ *   y_t      = sum_j w_tj y_{S_tj}(x_t) + sum_s y_shared_s(x_t)
+ *
+ * Experts whose weights are not in the GPU slot pool (misses) are split by the rule
+ * q* = m * Bp / Bh (same page, section 二): q of the m misses are copied from pinned host
+ * memory into pool slots with hipMemcpyAsync and computed on the GPU, the other m - q are
+ * computed on host cores at the same time.  The pool is an LRU over expert slots (smzdm
+ * explainer aomxznrn, "FreeToken干的事", item 2).
+ *
+ * Conventions
+ *   - Every function returns FT_OK (0) or a negative FT_E* code; ft_last_error() then gives
+ *     a message (thread-local).  No function aborts or throws across the ABI.
+ *   - "device" pointers are HIP device memory on the context's device; "host" pointers are
+ *     ordinary host memory unless "pinned" is said (allocated with hipHostMalloc or
+ *     torch's pin_memory).  The caller owns every buffer it passes; the library borrows
+ *     layer buffers for the layer's lifetime and owns only its internal state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is enqueued on it
+ *     asynchronously unless stated otherwise; outputs are valid after the stream syncs.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Calls on one layer must be serialised by the caller.
+ */
+#ifndef FT_H
+#define FT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FT_API __attribute__((visibility("default")))
+
+enum {
+  FT_OK = 0,
+  FT_EINVAL = -1,        /* bad argument (null pointer, size out of range, bad layout) */
+  FT_ENOMEM = -2,        /* host or device allocation failed */
+  FT_EHIP = -3,          /* a HIP runtime call failed; the message names it */
+  FT_EUNSUPPORTED = -4,  /* valid request this build does not implement */
+  FT_ESTATE = -5         /* call not valid in the object's current state */
+};
+
+enum { FT_MXFP4 = 0, FT_NVFP4 = 1 };
+enum { FT_PREFILL_EXACT = 0, FT_PREFILL_MXFP4 = 1 };
+
+/* Largest token count of one ft_route / ft_moe_decode call. */
+#define FT_MAX_DECODE_TOKENS 16
+/* Largest k. */
+#define FT_MAX_TOPK 16
+
+typedef struct ft_ctx ft_ctx;
+typedef struct ft_layer ft_layer;
+
+/*
+ * Expert blob: one expert's gate [I][H], up [I][H] and down [H][I] matrices in the
+ * library's tiled FP4 layout, each sub-tensor starting on a 4096-byte boundary so that one
+ * copy moves a whole expert (the FTW rule that every tensor is 4096-aligned:
+ * lowalt.boxinlu2.cn article, section 三).  A 4096-byte header holds the format, sizes and
+ * the three NVFP4 tensor scales.  Blobs are produced by ft_pack_expert.
+ */
+
+/* Bytes of one blob (a multiple of 4096).  H and I must be positive multiples of 128. */
+FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes);
+
+/*
+ * Pack one expert into `blob` (host memory, ft_blob_bytes() bytes).  Logical inputs,
+ * row-major: codes uint8 [rows][K/2] with element 2i in the low nibble; scales uint8
+ * [rows][K/B] (MXFP4: E8M0, B = 32; NVFP4: E4M3, B = 16) along the contraction axis K.
+ * gate/up: rows = I, K = H; down: rows = H, K = I.  tensor_scales: 3 fp32 (gate, up,
+ * down), used by NVFP4, may be NULL for MXFP4.  Pure host function.
+ */
+FT_API int ft_pack_expert(int format, int H, int I,
+                          const uint8_t* gate_codes, const uint8_t* gate_scales,
+                          const uint8_t* up_codes, const uint8_t* up_scales,
+                          const uint8_t* down_codes, const uint8_t* down_scales,
+                          const float* tensor_scales, void* blob);
+
+/* Context: device, internal copy stream, host thread pool for host-computed experts. */
+FT_API int ft_ctx_create(int device, ft_ctx** out);
+FT_API int ft_ctx_destroy(ft_ctx* ctx);
+
+typedef struct ft_layer_desc {
+  int32_t H, I, E, k, n_shared;
+  int32_t format;             /* FT_MXFP4 or FT_NVFP4 */
+  int32_t n_slots;            /* slots in the device pool (1 .. E) */
+  int32_t max_tokens;         /* largest decode T (1 .. FT_MAX_DECODE_TOKENS) */
+  const float* router_w;      /* device fp32 [E][H] */
+  const float* router_b;      /* device fp32 [E], or NULL for no bias */
+  void* pool;                 /* device, n_slots * blob_stride bytes */
+  const void* shared_blobs;   /* device, n_shared blobs at blob_stride, or NULL if none */
+  const void* host_blobs;     /* pinned host, E blobs at blob_stride (needed when not all
+                                 experts are resident), or NULL */
+  uint64_t blob_stride;       /* >= ft_blob_bytes(), multiple of 4096 */
+  int32_t resident;           /* 1: slot e already holds expert e for every e (needs
+                                 n_slots == E); 0: the pool starts empty */
+  int32_t reserved;
+} ft_layer_desc;
+
+/* Create a layer over caller-owned buffers; allocates the library's device workspace. */
+FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** out);
+FT_API int ft_layer_destroy(ft_layer* layer);
+
+/*
+ * Routing (top-k softmax).  x: device bf16 [T][H]; idx: device int32 [T][k] (rank order);
+ * w: device fp32 [T][k].  1 <= T <= max_tokens.  Asynchronous on `stream`.
+ */
+FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_t* x, int T,
+                    int32_t* idx, float* w, void* stream);
+
+typedef struct ft_decode_stats {
+  int32_t n_selected;   /* distinct routed experts of the call */
+  int32_t n_hits;       /* of those, resident in the pool */
+  int32_t n_miss;       /* m */
+  int32_t q;            /* the split rule's q for m */
+  int32_t n_streamed;   /* misses copied into slots this call */
+  int32_t n_host;       /* misses computed on host cores */
+  int32_t n_evicted;
+  int32_t step;         /* decode-call counter of this layer (the LRU clock) */
+  double qstar;         /* m * Bp / Bh */
+  double bp, bh;        /* bandwidths used (bytes/s) */
+  double host_us;       /* wall time of the host experts */
+  double wait_us;       /* wall time blocked on the routing read-back */
+} ft_decode_stats;
+
+/*
+ * Decode T tokens (1 <= T <= max_tokens).  x: device bf16 [T][H]; y: device fp32 [T][H].
+ * All-resident layers run fully asynchronously.  Otherwise the call blocks until the
+ * routing of these tokens is read back, classifies hits and misses, streams q misses into
+ * slots on the internal copy stream, enqueues the GPU experts on `stream`, computes the
+ * other misses on host cores, enqueues their results and the combine, and returns; y is
+ * valid after `stream` syncs.  stats may be NULL (asynchronous path: counts are filled
+ * only where known on the host, i.e. in the miss path).
+ */
+FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T, float* y,
+                         ft_decode_stats* stats, void* stream);
+
+/*
+ * Prefill (large T, all experts resident).  mode FT_PREFILL_EXACT: bf16 activations,
+ * exact FP4 weights, bf16 MFMA; FT_PREFILL_MXFP4: activations and h quantised to MXFP4
+ * per 32 along K and weights transcoded to MXFP4, scaled-FP4 MFMA.  ws: device workspace of
+ * at least ft_moe_prefill_workspace_size() bytes (caller-owned).
+ */
+FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T, int mode, size_t* bytes);
+FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T, float* y,
+                          int mode, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The split rule (smzdm explainer a825qpgl, section 二; lowalt.boxinlu2.cn article,
+ * section 二): qstar = m * Bp / Bh; q = floor(qstar + 1/2) clamped to [0, m] (Bh <= Bp
+ * gives m).  FT_EINVAL if m < 0, Bp <= 0 or Bh <= 0.  Pure host function.
+ */
+FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
+
+/*
+ * Startup probes: Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
+ * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.
+ * Needs host_blobs.  Blocks.  The values are stored in the layer and used by decode.
+ */
+FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh);
+/* Override Bp and Bh (bytes/s, both > 0). */
+FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh);
+/* Force q for every later decode call (q >= 0, clamped to m), or restore the rule (q < 0). */
+FT_API int ft_force_q(ft_layer* layer, int q);
+
+FT_API const char* ft_last_error(void);
+
+/*
+ * Kernel timing.  After ft_profile_begin(layer, n) the next n eager decode (or prefill) calls
+ * launch their two expert kernels, gate/up (+SwiGLU) and down, with start/stop HIP events
+ * that the dispatches record on the call's stream (so host-side gaps are not counted).
+ * ft_profile_end synchronises those events and returns the mean kernel durations in
+ * microseconds and the number of calls recorded.  Not for calls under graph capture.
+ */
+FT_API int ft_profile_begin(ft_layer* layer, int n);
+FT_API int ft_profile_end(ft_layer* layer, double* gateup_us, double* down_us, int* n_recorded);
+
+/* ---- test hooks ---------------------------------------------------------------------- */
+
+/* Dequantise one matrix (0 gate, 1 up, 2 down) of pool slot `slot` (or, when slot < 0, of
+ * shared expert -1 - slot) to device fp32 [rows][K] in logical order. */
+FT_API int ft_debug_dequant(const ft_layer* layer, int slot, int matrix, float* out,
+                            void* stream);
+/* Host copies of the expert->slot table [E] and slot->expert table [n_slots] (-1 = none),
+ * read back from the device tables the kernels use.  Blocks. */
+FT_API int ft_debug_tables(const ft_layer* layer, int32_t* e2s, int32_t* s2e);
+/* The library's host expert FFN on one blob (host memory): x host bf16 [T][H] -> y host
+ * fp32 [T][H].  Runs on the calling thread plus the context's pool when ctx != NULL. */
+FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, const void* blob,
+                              const uint16_t* x, int T, float* y);
+/* Prefill permutation of the last ft_moe_prefill call: counts [E], offsets [E+1],
+ * pos [T][k] (device int32), copied from the workspace `ws` of that call. */
+FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
+                                 int32_t* counts, int32_t* offsets, int32_t* pos,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FT_H */

@@ -1,0 +1,699 @@
+// C ABI of libft: contexts, layers, decode (resident and miss paths), probes, test hooks.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ft_host.h"
+
+using namespace ft;
+
+// kernel launchers (ft_kernels.hip)
+extern "C" int ftk_route_decode(const uint16_t* x, const float* wr, const float* b, int T, int H,
+                                int E, int k, int n_shared, float* logits, int* ticket,
+                                int32_t* idx_out, float* w_out, const int32_t* e2s,
+                                WorkItem* items, int* n_items, hipStream_t st);
+extern "C" int ftk_ffn_decode(const uint16_t* x, int H, int I, const WorkItem* items,
+                              const int* n_items, int max_items, const uint8_t* pool,
+                              const uint8_t* shared, uint64_t stride, const BlobLayout* L,
+                              uint16_t* h, float* P, hipStream_t st, const hipEvent_t* ev);
+extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
+                           float* y, hipStream_t st);
+extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
+                           float* out, hipStream_t st);
+
+namespace {
+
+using clk = std::chrono::steady_clock;
+double us_since(clk::time_point t0) {
+  return std::chrono::duration<double, std::micro>(clk::now() - t0).count();
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(FT_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));           \
+  } while (0)
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+}  // namespace
+
+struct ft_ctx {
+  int device = 0;
+  hipStream_t copy_stream = nullptr;
+  std::unique_ptr<ThreadPool> pool;
+};
+
+struct ft_layer {
+  ft_ctx* ctx = nullptr;
+  ft_layer_desc d{};
+  BlobLayout L{};
+  int kk = 0;            // k + n_shared
+  int max_items = 0;     // work-list entries per call
+  bool all_resident = false;
+  // device workspace (one allocation)
+  void* dev = nullptr;
+  float* logits = nullptr;
+  int* ticket = nullptr;
+  int32_t* idx = nullptr;
+  float* w = nullptr;
+  WorkItem* items = nullptr;     // [2][max_items] (second list: streamed misses)
+  int* n_items = nullptr;        // [2]
+  uint16_t* h = nullptr;
+  float* P = nullptr;
+  int32_t* e2s_dev = nullptr;
+  int32_t* s2e_dev = nullptr;
+  // pinned host staging
+  void* pin = nullptr;
+  int32_t* idx_h = nullptr;
+  float* w_h = nullptr;
+  uint16_t* x_h = nullptr;
+  WorkItem* items_h = nullptr;   // [2][max_items] followed by int counts[2]
+  int* n_items_h = nullptr;
+  float* P_h = nullptr;          // host expert outputs [T * kk][H]
+  int32_t* e2s_h = nullptr;
+  int32_t* s2e_h = nullptr;
+  hipEvent_t ev_copy = nullptr;
+  // policy state
+  LruState lru;
+  double bp = 0.0, bh = 0.0;
+  int force_q = -1;
+  // kernel timing events: [n][4] = gate/up start, stop, down start, stop
+  std::vector<hipEvent_t> prof;
+  int prof_n = 0, prof_i = 0;
+};
+
+// the four timing events of the next profiled call, or null
+static const hipEvent_t* prof_events(ft_layer* l) {
+  if (l->prof_i >= l->prof_n) return nullptr;
+  return &l->prof[(size_t)4 * l->prof_i++];
+}
+
+// ---- blobs ------------------------------------------------------------------------------------
+static bool dims_ok(int format, int H, int I) {
+  return (format == FT_MXFP4 || format == FT_NVFP4) && H > 0 && I > 0 && H % kTileK == 0 &&
+         I % kTileK == 0;
+}
+
+extern "C" FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes) {
+  if (!bytes || !dims_ok(format, H, I))
+    return fail(FT_EINVAL, "ft_blob_bytes: format must be FT_MXFP4/FT_NVFP4 and H, I positive "
+                           "multiples of 128");
+  *bytes = blob_layout(format, H, I).bytes;
+  return FT_OK;
+}
+
+static void pack_matrix(int fmt, int R, int K, const uint8_t* codes, const uint8_t* scales,
+                        uint8_t* dst_codes, uint8_t* dst_scales) {
+  const int KC = K / kTileK, RT = R / kTileRows;
+  const int B = fmt == FT_MXFP4 ? 32 : 16;
+  const int sbytes = scale_tile_bytes(fmt);
+  for (int rt = 0; rt < RT; ++rt)
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint64_t tile = (uint64_t)rt * KC + kc;
+      uint8_t* tc = dst_codes + tile * kTileCodeBytes;
+      uint8_t* ts = dst_scales + tile * sbytes;
+      for (int l = 0; l < 64; ++l) {
+        const int row = rt * kTileRows + (l & 15);
+        const int k0 = kc * kTileK + 32 * (l >> 4);
+        std::memcpy(tc + 16 * l, codes + (uint64_t)row * (K / 2) + k0 / 2, 16);
+        if (fmt == FT_MXFP4) {
+          ts[l] = scales[(uint64_t)row * (K / B) + k0 / B];
+        } else {
+          ts[2 * l] = scales[(uint64_t)row * (K / B) + k0 / B];
+          ts[2 * l + 1] = scales[(uint64_t)row * (K / B) + k0 / B + 1];
+        }
+      }
+    }
+}
+
+extern "C" FT_API int ft_pack_expert(int format, int H, int I, const uint8_t* gc,
+                                     const uint8_t* gs, const uint8_t* uc, const uint8_t* us,
+                                     const uint8_t* dc, const uint8_t* ds,
+                                     const float* tensor_scales, void* blob) {
+  if (!dims_ok(format, H, I)) return fail(FT_EINVAL, "ft_pack_expert: bad format or sizes");
+  if (!gc || !gs || !uc || !us || !dc || !ds || !blob)
+    return fail(FT_EINVAL, "ft_pack_expert: null pointer");
+  const BlobLayout L = blob_layout(format, H, I);
+  uint8_t* b = (uint8_t*)blob;
+  std::memset(b, 0, kAlign);
+  BlobHeader hdr{};
+  hdr.magic = kBlobMagic;
+  hdr.fmt = format;
+  hdr.H = H;
+  hdr.I = I;
+  for (int i = 0; i < 3; ++i) hdr.tensor_scale[i] = tensor_scales ? tensor_scales[i] : 1.0f;
+  std::memcpy(b, &hdr, sizeof(hdr));
+  // zero the alignment padding so blobs are byte-deterministic
+  for (int i = 0; i < 6; ++i) {
+    const uint64_t end = (i + 1 < 6) ? L.off[i + 1] : L.bytes;
+    std::memset(b + L.off[i], 0, end - L.off[i]);
+  }
+  pack_matrix(format, I, H, gc, gs, b + L.off[0], b + L.off[1]);
+  pack_matrix(format, I, H, uc, us, b + L.off[2], b + L.off[3]);
+  pack_matrix(format, H, I, dc, ds, b + L.off[4], b + L.off[5]);
+  return FT_OK;
+}
+
+// ---- context ----------------------------------------------------------------------------------
+extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) {
+  if (!out) return fail(FT_EINVAL, "ft_ctx_create: out is null");
+  int n = 0;
+  HIP_TRY(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return fail(FT_EINVAL, "ft_ctx_create: no such device");
+  HIP_TRY(hipSetDevice(device));
+  std::unique_ptr<ft_ctx> c(new (std::nothrow) ft_ctx);
+  if (!c) return fail(FT_ENOMEM, "ft_ctx_create: out of host memory");
+  c->device = device;
+  HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
+  const int hw = (int)std::thread::hardware_concurrency();
+  const int nt = env_int("FT_HOST_THREADS", std::max(1, std::min(16, hw)));
+  c->pool.reset(new ThreadPool(std::max(1, nt)));
+  *out = c.release();
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
+  if (!ctx) return FT_OK;
+  if (ctx->copy_stream) {
+    hipSetDevice(ctx->device);
+    hipStreamSynchronize(ctx->copy_stream);
+    hipStreamDestroy(ctx->copy_stream);
+  }
+  delete ctx;
+  return FT_OK;
+}
+
+// ---- layer ------------------------------------------------------------------------------------
+template <class T>
+static T* carve(uint8_t*& p, size_t n) {
+  T* r = (T*)p;
+  p += align_up(n * sizeof(T), 256);
+  return r;
+}
+
+static void free_layer(ft_layer* l) {
+  if (!l) return;
+  for (hipEvent_t e : l->prof) hipEventDestroy(e);
+  if (l->ev_copy) hipEventDestroy(l->ev_copy);
+  if (l->dev) hipFree(l->dev);
+  if (l->pin) hipHostFree(l->pin);
+  delete l;
+}
+
+extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** out) {
+  if (!ctx || !desc || !out) return fail(FT_EINVAL, "ft_layer_create: null argument");
+  const ft_layer_desc& d = *desc;
+  if (!dims_ok(d.format, d.H, d.I)) return fail(FT_EINVAL, "ft_layer_create: bad format or H/I");
+  if (d.E < 1 || d.E > 1024 || d.k < 1 || d.k > FT_MAX_TOPK || d.k > d.E)
+    return fail(FT_EINVAL, "ft_layer_create: need 1 <= k <= min(E, 16) and E <= 1024");
+  if (d.n_shared < 0 || d.n_shared > 4) return fail(FT_EINVAL, "ft_layer_create: n_shared 0..4");
+  if (d.n_slots < 1 || d.n_slots > d.E) return fail(FT_EINVAL, "ft_layer_create: n_slots 1..E");
+  if (d.max_tokens < 1 || d.max_tokens > FT_MAX_DECODE_TOKENS)
+    return fail(FT_EINVAL, "ft_layer_create: max_tokens 1..16");
+  if (!d.router_w || !d.pool) return fail(FT_EINVAL, "ft_layer_create: router_w/pool null");
+  if (d.n_shared > 0 && !d.shared_blobs)
+    return fail(FT_EINVAL, "ft_layer_create: shared_blobs null with n_shared > 0");
+  const BlobLayout L = blob_layout(d.format, d.H, d.I);
+  if (d.blob_stride < L.bytes || d.blob_stride % kAlign)
+    return fail(FT_EINVAL, "ft_layer_create: blob_stride below ft_blob_bytes() or not a "
+                           "multiple of 4096");
+  if (d.resident && d.n_slots != d.E)
+    return fail(FT_EINVAL, "ft_layer_create: resident layers need n_slots == E");
+  if (!d.resident && !d.host_blobs)
+    return fail(FT_EINVAL, "ft_layer_create: a non-resident layer needs host_blobs");
+  HIP_TRY(hipSetDevice(ctx->device));
+
+  std::unique_ptr<ft_layer, void (*)(ft_layer*)> l(new (std::nothrow) ft_layer, free_layer);
+  if (!l) return fail(FT_ENOMEM, "ft_layer_create: out of host memory");
+  l->ctx = ctx;
+  l->d = d;
+  l->L = L;
+  l->kk = d.k + d.n_shared;
+  l->max_items = d.max_tokens * d.k + d.n_shared;
+  l->all_resident = d.resident != 0;
+  const int T = d.max_tokens;
+
+  size_t need = 0;
+  auto add = [&](size_t bytes) { need += align_up(bytes, 256); };
+  add((size_t)T * d.E * 4);                        // logits
+  add(4);                                          // ticket
+  add((size_t)T * d.k * 4);                        // idx
+  add((size_t)T * d.k * 4);                        // w
+  add((size_t)2 * l->max_items * sizeof(WorkItem));
+  add(2 * sizeof(int));
+  add((size_t)l->max_items * kMaxCols * d.I * 2);  // h
+  add((size_t)T * l->kk * d.H * 4);                // P
+  add((size_t)d.E * 4);
+  add((size_t)d.n_slots * 4);
+  if (hipMalloc(&l->dev, need) != hipSuccess)
+    return fail(FT_ENOMEM, "ft_layer_create: device workspace allocation failed");
+  HIP_TRY(hipMemset(l->dev, 0, need));
+  uint8_t* p = (uint8_t*)l->dev;
+  l->logits = carve<float>(p, (size_t)T * d.E);
+  l->ticket = carve<int>(p, 1);
+  l->idx = carve<int32_t>(p, (size_t)T * d.k);
+  l->w = carve<float>(p, (size_t)T * d.k);
+  l->items = carve<WorkItem>(p, (size_t)2 * l->max_items);
+  l->n_items = carve<int>(p, 2);
+  l->h = carve<uint16_t>(p, (size_t)l->max_items * kMaxCols * d.I);
+  l->P = carve<float>(p, (size_t)T * l->kk * d.H);
+  l->e2s_dev = carve<int32_t>(p, d.E);
+  l->s2e_dev = carve<int32_t>(p, d.n_slots);
+
+  size_t pneed = 0;
+  auto padd = [&](size_t bytes) { pneed += align_up(bytes, 256); };
+  padd((size_t)T * d.k * 4);
+  padd((size_t)T * d.k * 4);
+  padd((size_t)T * d.H * 2);
+  padd((size_t)2 * l->max_items * sizeof(WorkItem) + 2 * sizeof(int));
+  padd((size_t)T * l->kk * d.H * 4);
+  padd((size_t)d.E * 4);
+  padd((size_t)d.n_slots * 4);
+  if (hipHostMalloc(&l->pin, pneed, hipHostMallocDefault) != hipSuccess)
+    return fail(FT_ENOMEM, "ft_layer_create: pinned staging allocation failed");
+  uint8_t* q = (uint8_t*)l->pin;
+  l->idx_h = carve<int32_t>(q, (size_t)T * d.k);
+  l->w_h = carve<float>(q, (size_t)T * d.k);
+  l->x_h = carve<uint16_t>(q, (size_t)T * d.H);
+  l->items_h = (WorkItem*)q;
+  l->n_items_h = (int*)(q + (size_t)2 * l->max_items * sizeof(WorkItem));
+  q += align_up((size_t)2 * l->max_items * sizeof(WorkItem) + 2 * sizeof(int), 256);
+  l->P_h = carve<float>(q, (size_t)T * l->kk * d.H);
+  l->e2s_h = carve<int32_t>(q, d.E);
+  l->s2e_h = carve<int32_t>(q, d.n_slots);
+
+  l->lru.init(d.E, d.n_slots, l->all_resident);
+  std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
+  std::copy(l->lru.s2e.begin(), l->lru.s2e.end(), l->s2e_h);
+  HIP_TRY(hipMemcpy(l->e2s_dev, l->e2s_h, (size_t)d.E * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipEventCreateWithFlags(&l->ev_copy, hipEventDisableTiming));
+  *out = l.release();
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_layer_destroy(ft_layer* layer) {
+  if (!layer) return FT_OK;
+  hipSetDevice(layer->ctx->device);
+  hipDeviceSynchronize();
+  free_layer(layer);
+  return FT_OK;
+}
+
+// ---- routing / decode ---------------------------------------------------------------------
+static int check_call(const ft_ctx* ctx, const ft_layer* layer, const void* x, int T,
+                      const char* who) {
+  if (!ctx || !layer || !x) return fail(FT_EINVAL, std::string(who) + ": null argument");
+  if (layer->ctx != ctx) return fail(FT_EINVAL, std::string(who) + ": layer of another context");
+  if (T < 1 || T > layer->d.max_tokens)
+    return fail(FT_EINVAL, std::string(who) + ": T must be in 1..max_tokens");
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_t* x, int T,
+                               int32_t* idx, float* w, void* stream) {
+  int rc = check_call(ctx, layer, x, T, "ft_route");
+  if (rc) return rc;
+  if (!idx || !w) return fail(FT_EINVAL, "ft_route: idx/w null");
+  const ft_layer_desc& d = layer->d;
+  HIP_TRY(hipSetDevice(ctx->device));
+  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, d.E, d.k, d.n_shared,
+                                       layer->logits, layer->ticket, idx, w, nullptr, nullptr,
+                                       nullptr, (hipStream_t)stream));
+  return FT_OK;
+}
+
+static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipStream_t st) {
+  const ft_layer_desc& d = l->d;
+  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, d.E, d.k, d.n_shared,
+                                       l->logits, l->ticket, l->idx, l->w, l->e2s_dev,
+                                       l->items, l->n_items, st));
+  const int items_max = T * d.k + d.n_shared;
+  HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items, l->n_items, items_max,
+                                     (const uint8_t*)d.pool, (const uint8_t*)d.shared_blobs,
+                                     d.blob_stride, &l->L, l->h, l->P, st, prof_events(l)));
+  HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
+  return FT_OK;
+}
+
+static void add_item(WorkItem* list, int* n, int expert, int slot) {
+  WorkItem& it = list[(*n)++];
+  std::memset(&it, 0, sizeof(it));
+  it.expert = expert;
+  it.slot = slot;
+}
+
+static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, float* y,
+                            ft_decode_stats* stats, hipStream_t st) {
+  const ft_layer_desc& d = l->d;
+  const int k = d.k, kk = l->kk, E = d.E;
+  ft_decode_stats S{};
+  auto t0 = clk::now();
+  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, E, k, d.n_shared,
+                                       l->logits, l->ticket, l->idx, l->w, nullptr, nullptr,
+                                       nullptr, st));
+  HIP_TRY(hipMemcpyAsync(l->idx_h, l->idx, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(l->w_h, l->w, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(l->x_h, x, (size_t)T * d.H * 2, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  S.wait_us = us_since(t0);
+
+  // classify: selected experts with their summed routing weight
+  const int64_t now = l->lru.step;
+  std::vector<double> wsum(E, 0.0);
+  std::vector<char> sel(E, 0);
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      const int e = l->idx_h[t * k + j];
+      if (e < 0 || e >= E) return fail(FT_ESTATE, "ft_moe_decode: routing produced a bad index");
+      sel[e] = 1;
+      wsum[e] += l->w_h[t * k + j];
+    }
+  std::vector<int> hits, misses;
+  for (int e = 0; e < E; ++e) {
+    if (!sel[e]) continue;
+    ++S.n_selected;
+    if (l->lru.e2s[e] >= 0) {
+      hits.push_back(e);
+      l->lru.last_use[l->lru.e2s[e]] = now;
+    } else {
+      misses.push_back(e);
+    }
+  }
+  std::stable_sort(misses.begin(), misses.end(), [&](int a, int b) {
+    return wsum[a] > wsum[b] || (wsum[a] == wsum[b] && a < b);
+  });
+  const int m = (int)misses.size();
+  int q = 0;
+  double qstar = 0.0;
+  if (l->bp <= 0.0 || l->bh <= 0.0)
+    return fail(FT_ESTATE, "ft_moe_decode: Bp/Bh unknown; call ft_measure_bandwidth or "
+                           "ft_set_bandwidth first");
+  int rc = qstar_split(m, l->bp, l->bh, &q, &qstar);
+  if (rc) return rc;
+  if (l->force_q >= 0) q = std::min(m, l->force_q);
+  std::vector<int> streamed, host;
+  for (int n = 0; n < m; ++n) {
+    const int e = misses[n];
+    if (n >= q) { host.push_back(e); continue; }
+    int32_t old = -1;
+    const int s = l->lru.take_slot(now, &old);
+    if (s < 0) { host.push_back(e); continue; }
+    if (old >= 0) { l->lru.e2s[old] = -1; ++S.n_evicted; }
+    l->lru.s2e[s] = e;
+    l->lru.e2s[e] = s;
+    l->lru.last_use[s] = now;
+    streamed.push_back(e);
+  }
+  l->lru.step++;
+  S.n_hits = (int)hits.size();
+  S.n_miss = m;
+  S.q = q;
+  S.qstar = qstar;
+  S.n_streamed = (int)streamed.size();
+  S.n_host = (int)host.size();
+  S.bp = l->bp;
+  S.bh = l->bh;
+  S.step = (int)now;
+
+  // work lists: list 0 = hits + shared experts, list 1 = streamed misses
+  WorkItem* L0 = l->items_h;
+  WorkItem* L1 = l->items_h + l->max_items;
+  int n0 = 0, n1 = 0;
+  auto fill_cols = [&](WorkItem& it, int e) {
+    int c = 0;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (l->idx_h[t * k + j] == e) { it.tok[c] = t; it.pair[c] = t * kk + j; ++c; }
+    it.ntok = c;
+  };
+  for (int e : hits) { add_item(L0, &n0, e, l->lru.e2s[e]); fill_cols(L0[n0 - 1], e); }
+  for (int s = 0; s < d.n_shared; ++s) {
+    add_item(L0, &n0, -1 - s, -1 - s);
+    WorkItem& it = L0[n0 - 1];
+    it.ntok = T;
+    for (int t = 0; t < T; ++t) { it.tok[t] = t; it.pair[t] = t * kk + k + s; }
+  }
+  for (int e : streamed) { add_item(L1, &n1, e, l->lru.e2s[e]); fill_cols(L1[n1 - 1], e); }
+  l->n_items_h[0] = n0;
+  l->n_items_h[1] = n1;
+  std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
+  std::copy(l->lru.s2e.begin(), l->lru.s2e.end(), l->s2e_h);
+
+  // copies of streamed experts into their slots, on the copy stream
+  for (int e : streamed) {
+    const int s = l->lru.e2s[e];
+    HIP_TRY(hipMemcpyAsync((uint8_t*)d.pool + (uint64_t)s * d.blob_stride,
+                           (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride,
+                           l->L.bytes, hipMemcpyHostToDevice, ctx->copy_stream));
+  }
+  HIP_TRY(hipEventRecord(l->ev_copy, ctx->copy_stream));
+  // work lists and tables to the device (compute stream, before the kernels)
+  HIP_TRY(hipMemcpyAsync(l->items, l->items_h, (size_t)2 * l->max_items * sizeof(WorkItem),
+                         hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(l->n_items, l->n_items_h, 2 * sizeof(int), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(l->e2s_dev, l->e2s_h, (size_t)E * 4, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice, st));
+  const uint8_t* pool = (const uint8_t*)d.pool;
+  const uint8_t* shared = (const uint8_t*)d.shared_blobs;
+  if (n0 > 0)
+    HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items, l->n_items, n0, pool, shared,
+                                       d.blob_stride, &l->L, l->h, l->P, st, nullptr));
+  HIP_TRY(hipStreamWaitEvent(st, l->ev_copy, 0));
+  if (n1 > 0)
+    HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items + l->max_items, l->n_items + 1, n1,
+                                       pool, shared, d.blob_stride, &l->L,
+                                       l->h, l->P, st, nullptr));
+
+  // host experts, concurrently with the GPU work enqueued above
+  auto th = clk::now();
+  std::vector<float> yt((size_t)T * d.H);
+  std::vector<uint16_t> xt((size_t)T * d.H);
+  for (int e : host) {
+    // the tokens routed to e, packed
+    int cols[FT_MAX_DECODE_TOKENS], js[FT_MAX_DECODE_TOKENS], c = 0;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (l->idx_h[t * k + j] == e) { cols[c] = t; js[c] = j; ++c; }
+    for (int i = 0; i < c; ++i)
+      std::memcpy(&xt[(size_t)i * d.H], l->x_h + (size_t)cols[i] * d.H, (size_t)d.H * 2);
+    rc = host_expert_ffn(ctx->pool.get(), l->L,
+                         (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride, xt.data(), c,
+                         yt.data());
+    if (rc) return rc;
+    for (int i = 0; i < c; ++i) {
+      const int pair = cols[i] * kk + js[i];
+      std::memcpy(l->P_h + (size_t)pair * d.H, &yt[(size_t)i * d.H], (size_t)d.H * 4);
+      HIP_TRY(hipMemcpyAsync(l->P + (size_t)pair * d.H, l->P_h + (size_t)pair * d.H,
+                             (size_t)d.H * 4, hipMemcpyHostToDevice, st));
+    }
+  }
+  S.host_us = us_since(th);
+  HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, k, d.n_shared, y, st));
+  if (stats) *stats = S;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
+                                    float* y, ft_decode_stats* stats, void* stream) {
+  int rc = check_call(ctx, layer, x, T, "ft_moe_decode");
+  if (rc) return rc;
+  if (!y) return fail(FT_EINVAL, "ft_moe_decode: y null");
+  HIP_TRY(hipSetDevice(ctx->device));
+  hipStream_t st = (hipStream_t)stream;
+  if (layer->all_resident) {
+    if (stats) {
+      std::memset(stats, 0, sizeof(*stats));
+      stats->bp = layer->bp;
+      stats->bh = layer->bh;
+      stats->step = (int)layer->lru.step;
+    }
+    layer->lru.step++;
+    return decode_resident(layer, x, T, y, st);
+  }
+  return decode_miss_path(ctx, layer, x, T, y, stats, st);
+}
+
+// ---- split rule and probes ----------------------------------------------------------------
+extern "C" FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar) {
+  return qstar_split(m, Bp, Bh, q, qstar);
+}
+
+extern "C" FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh) {
+  if (!layer || !(Bp > 0.0) || !(Bh > 0.0))
+    return fail(FT_EINVAL, "ft_set_bandwidth: need a layer and Bp, Bh > 0");
+  layer->bp = Bp;
+  layer->bh = Bh;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_force_q(ft_layer* layer, int q) {
+  if (!layer) return fail(FT_EINVAL, "ft_force_q: null layer");
+  layer->force_q = q < 0 ? -1 : q;
+  return FT_OK;
+}
+
+static double median(std::vector<double> v) {
+  std::sort(v.begin(), v.end());
+  return v.empty() ? 0.0 : v[v.size() / 2];
+}
+
+extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh) {
+  if (!ctx || !layer) return fail(FT_EINVAL, "ft_measure_bandwidth: null argument");
+  const ft_layer_desc& d = layer->d;
+  if (!d.host_blobs) return fail(FT_ESTATE, "ft_measure_bandwidth: the layer has no host_blobs");
+  HIP_TRY(hipSetDevice(ctx->device));
+  const uint64_t bytes = layer->L.bytes;
+  void* tmp = nullptr;
+  if (hipMalloc(&tmp, bytes) != hipSuccess)
+    return fail(FT_ENOMEM, "ft_measure_bandwidth: probe buffer allocation failed");
+  hipEvent_t a, b;
+  HIP_TRY(hipEventCreate(&a));
+  HIP_TRY(hipEventCreate(&b));
+  std::vector<double> bps;
+  const int reps = env_int("FT_PROBE_REPS", 7);
+  for (int r = 0; r < reps + 1; ++r) {
+    const uint8_t* src = (const uint8_t*)d.host_blobs + (uint64_t)(r % d.E) * d.blob_stride;
+    hipEventRecord(a, ctx->copy_stream);
+    hipMemcpyAsync(tmp, src, bytes, hipMemcpyHostToDevice, ctx->copy_stream);
+    hipEventRecord(b, ctx->copy_stream);
+    hipEventSynchronize(b);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, a, b);
+    if (r > 0 && ms > 0.f) bps.push_back((double)bytes / (ms * 1e-3));
+  }
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  hipFree(tmp);
+  std::vector<double> bhs;
+  std::vector<uint16_t> x(d.H, 0x3f80);  // ones
+  std::vector<float> y(d.H);
+  for (int r = 0; r < reps + 1; ++r) {
+    const uint8_t* src = (const uint8_t*)d.host_blobs + (uint64_t)((r + 1) % d.E) * d.blob_stride;
+    auto t0 = clk::now();
+    int rc = host_expert_ffn(ctx->pool.get(), layer->L, src, x.data(), 1, y.data());
+    if (rc) return rc;
+    const double s = us_since(t0) * 1e-6;
+    if (r > 0 && s > 0) bhs.push_back((double)bytes / s);
+  }
+  layer->bp = median(bps);
+  layer->bh = median(bhs);
+  if (Bp) *Bp = layer->bp;
+  if (Bh) *Bh = layer->bh;
+  return FT_OK;
+}
+
+// ---- kernel timing ------------------------------------------------------------------------
+extern "C" FT_API int ft_profile_begin(ft_layer* layer, int n) {
+  if (!layer || n < 0 || n > 1000000) return fail(FT_EINVAL, "ft_profile_begin: bad argument");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  const size_t need = (size_t)n * 4;
+  while (layer->prof.size() < need) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    layer->prof.push_back(e);
+  }
+  layer->prof_n = n;
+  layer->prof_i = 0;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_profile_end(ft_layer* layer, double* gateup_us, double* down_us,
+                                     int* n_recorded) {
+  if (!layer) return fail(FT_EINVAL, "ft_profile_end: null layer");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  double a = 0.0, b = 0.0;
+  const int n = layer->prof_i;
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t* e = &layer->prof[(size_t)i * 4];
+    HIP_TRY(hipEventSynchronize(e[3]));
+    float m0 = 0.f, m1 = 0.f;
+    HIP_TRY(hipEventElapsedTime(&m0, e[0], e[1]));
+    HIP_TRY(hipEventElapsedTime(&m1, e[2], e[3]));
+    a += m0 * 1e3;
+    b += m1 * 1e3;
+  }
+  if (gateup_us) *gateup_us = n ? a / n : 0.0;
+  if (down_us) *down_us = n ? b / n : 0.0;
+  if (n_recorded) *n_recorded = n;
+  layer->prof_n = layer->prof_i = 0;
+  return FT_OK;
+}
+
+// ---- test hooks ---------------------------------------------------------------------------
+extern "C" FT_API int ft_debug_dequant(const ft_layer* layer, int slot, int matrix, float* out,
+                                       void* stream) {
+  if (!layer || !out || matrix < 0 || matrix > 2)
+    return fail(FT_EINVAL, "ft_debug_dequant: bad argument");
+  const ft_layer_desc& d = layer->d;
+  const uint8_t* blob;
+  if (slot >= 0) {
+    if (slot >= d.n_slots) return fail(FT_EINVAL, "ft_debug_dequant: slot out of range");
+    blob = (const uint8_t*)d.pool + (uint64_t)slot * d.blob_stride;
+  } else {
+    const int s = -1 - slot;
+    if (s >= d.n_shared) return fail(FT_EINVAL, "ft_debug_dequant: no such shared expert");
+    blob = (const uint8_t*)d.shared_blobs + (uint64_t)s * d.blob_stride;
+  }
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  float ts = 1.0f;
+  if (d.format == FT_NVFP4) {
+    BlobHeader hdr;
+    HIP_TRY(hipMemcpy(&hdr, blob, sizeof(hdr), hipMemcpyDeviceToHost));
+    ts = hdr.tensor_scale[matrix];
+  }
+  HIP_TRY((hipError_t)ftk_dequant(blob, &layer->L, matrix, ts, out, (hipStream_t)stream));
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_debug_tables(const ft_layer* layer, int32_t* e2s, int32_t* s2e) {
+  if (!layer || !e2s || !s2e) return fail(FT_EINVAL, "ft_debug_tables: null argument");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(e2s, layer->e2s_dev, (size_t)layer->d.E * 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(s2e, layer->s2e_dev, (size_t)layer->d.n_slots * 4, hipMemcpyDeviceToHost));
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, const void* blob,
+                                         const uint16_t* x, int T, float* y) {
+  if (!dims_ok(format, H, I) || !blob || !x || !y || T < 1)
+    return fail(FT_EINVAL, "ft_host_expert_ffn: bad argument");
+  return host_expert_ffn(ctx ? ctx->pool.get() : nullptr, blob_layout(format, H, I),
+                         (const uint8_t*)blob, x, T, y);
+}
+
+// ---- prefill ------------------------------------------------------------------------------
+extern "C" FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T, int mode,
+                                                    size_t* bytes) {
+  (void)layer; (void)T; (void)mode; (void)bytes;
+  return fail(FT_EUNSUPPORTED, "ft_moe_prefill_workspace_size: prefill not built yet");
+}
+
+extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
+                                     float* y, int mode, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  (void)ctx; (void)layer; (void)x; (void)T; (void)y; (void)mode; (void)ws; (void)ws_bytes;
+  (void)stream;
+  return fail(FT_EUNSUPPORTED, "ft_moe_prefill: prefill not built yet");
+}
+
+extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
+                                            int32_t* counts, int32_t* offsets, int32_t* pos,
+                                            void* stream) {
+  (void)layer; (void)ws; (void)T; (void)counts; (void)offsets; (void)pos; (void)stream;
+  return fail(FT_EUNSUPPORTED, "ft_debug_prefill_perm: prefill not built yet");
+}

@@ -1,0 +1,226 @@
+// Host-side pieces of libft: errors, thread pool, host expert FFN, split rule, LRU.
+#include "ft_host.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+namespace ft {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+}  // namespace ft
+
+extern "C" FT_API const char* ft_last_error(void) { return ft::g_last_error.c_str(); }
+
+namespace ft {
+
+// ---- thread pool ------------------------------------------------------------------------
+ThreadPool::ThreadPool(int n_threads) : n_(std::max(1, n_threads)) {
+  for (int i = 0; i < n_ - 1; ++i) threads_.emplace_back([this, i] { worker(i); });
+}
+
+ThreadPool::~ThreadPool() {
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    stop_ = true;
+  }
+  cv_.notify_all();
+  for (auto& t : threads_) t.join();
+}
+
+void ThreadPool::worker(int id) {
+  uint64_t seen = 0;
+  for (;;) {
+    const std::function<void(int, int)>* job;
+    {
+      std::unique_lock<std::mutex> lk(mu_);
+      cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+      if (stop_) return;
+      seen = gen_;
+      job = job_;
+    }
+    (*job)(id, n_);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      if (--pending_ == 0) done_cv_.notify_one();
+    }
+  }
+}
+
+void ThreadPool::run(const std::function<void(int, int)>& fn) {
+  if (n_ == 1) {
+    fn(0, 1);
+    return;
+  }
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    job_ = &fn;
+    pending_ = n_ - 1;
+    ++gen_;
+  }
+  cv_.notify_all();
+  fn(n_ - 1, n_);
+  std::unique_lock<std::mutex> lk(mu_);
+  done_cv_.wait(lk, [&] { return pending_ == 0; });
+}
+
+// ---- host expert FFN ------------------------------------------------------------------------
+// E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} with the sign bit (OCP MX v1.0 FP4 table).
+static const float kE2M1[16] = {0.f,  0.5f,  1.f,  1.5f,  2.f,  3.f,  4.f,  6.f,
+                                -0.f, -0.5f, -1.f, -1.5f, -2.f, -3.f, -4.f, -6.f};
+
+static inline float e8m0_value(uint8_t e) {
+  if (e == 255) return NAN;
+  if (e == 0) return std::ldexp(1.0f, -127);
+  return std::ldexp(1.0f, (int)e - 127);
+}
+
+static inline float e4m3_value(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  float v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = std::ldexp((float)m / 8.f, -6);
+  else v = std::ldexp(1.f + (float)m / 8.f, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+static inline float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+static inline float round_to_bf16(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return f;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  b &= 0xffff0000u;
+  std::memcpy(&f, &b, 4);
+  return f;
+}
+
+// acc[t][r] += sum over K of W[r][K] * xs[t][K] for rows [rt0*16, rt1*16) of a tiled matrix.
+// Block sums are formed on unscaled E2M1 values and scaled once per 32 (MXFP4) or 16 (NVFP4)
+// elements; with power-of-two MX scales this is exact reassociation.
+static void gemv_tiles(const BlobLayout& L, const uint8_t* codes, const uint8_t* scales, int K,
+                       int rt0, int rt1, const float* xs, int T, float tensor_scale,
+                       float* acc /* [T][R] */, int R) {
+  const int KC = K / kTileK;
+  const bool mx = L.fmt == FT_MXFP4;
+  for (int rt = rt0; rt < rt1; ++rt) {
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint64_t tile = (uint64_t)rt * KC + kc;
+      const uint8_t* c = codes + tile * kTileCodeBytes;
+      const uint8_t* s = scales + tile * (mx ? 64 : 128);
+      for (int l = 0; l < 64; ++l) {
+        const int row = rt * kTileRows + (l & 15);
+        const int k0 = kc * kTileK + 32 * (l >> 4);
+        float w[32];
+        const uint8_t* cb = c + 16 * l;
+        for (int b = 0; b < 16; ++b) {
+          w[2 * b] = kE2M1[cb[b] & 15];
+          w[2 * b + 1] = kE2M1[cb[b] >> 4];
+        }
+        float s0, s1;
+        if (mx) {
+          s0 = s1 = e8m0_value(s[l]);
+        } else {
+          s0 = e4m3_value(s[2 * l]) * tensor_scale;
+          s1 = e4m3_value(s[2 * l + 1]) * tensor_scale;
+        }
+        for (int t = 0; t < T; ++t) {
+          const float* xv = xs + (uint64_t)t * K + k0;
+          float p0 = 0.f, p1 = 0.f;
+          for (int q = 0; q < 16; ++q) p0 += w[q] * xv[q];
+          for (int q = 16; q < 32; ++q) p1 += w[q] * xv[q];
+          acc[(uint64_t)t * R + row] += p0 * s0 + p1 * s1;
+        }
+      }
+    }
+  }
+}
+
+int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
+                    const uint16_t* x, int T, float* y) {
+  const int H = L.H, I = L.I;
+  BlobHeader hdr;
+  std::memcpy(&hdr, blob, sizeof(hdr));
+  if (hdr.magic != kBlobMagic || hdr.fmt != L.fmt || hdr.H != H || hdr.I != I)
+    return fail(FT_EINVAL, "host_expert_ffn: blob header does not match the layer");
+  std::vector<float> xs((size_t)T * H), g((size_t)T * I, 0.f), u((size_t)T * I, 0.f),
+      h((size_t)T * I);
+  for (size_t i = 0; i < xs.size(); ++i) xs[i] = bf16_to_f32(x[i]);
+  std::fill(y, y + (size_t)T * H, 0.f);
+  const int RTg = I / kTileRows, RTd = H / kTileRows;
+  auto part = [&](int n, int i, int total, int* a, int* b) {
+    *a = (int)((int64_t)total * i / n);
+    *b = (int)((int64_t)total * (i + 1) / n);
+  };
+  auto job = [&](int i, int n) {
+    int a, b;
+    part(n, i, RTg, &a, &b);
+    gemv_tiles(L, blob + L.off[0], blob + L.off[1], H, a, b, xs.data(), T, hdr.tensor_scale[0],
+               g.data(), I);
+    gemv_tiles(L, blob + L.off[2], blob + L.off[3], H, a, b, xs.data(), T, hdr.tensor_scale[1],
+               u.data(), I);
+  };
+  auto job2 = [&](int i, int n) {
+    int a, b;
+    part(n, i, RTd, &a, &b);
+    gemv_tiles(L, blob + L.off[4], blob + L.off[5], I, a, b, h.data(), T, hdr.tensor_scale[2],
+               y, H);
+  };
+  if (pool) pool->run(job); else job(0, 1);
+  for (size_t i = 0; i < h.size(); ++i) {
+    const float z = g[i];
+    h[i] = round_to_bf16(z / (1.0f + std::exp(-z)) * u[i]);
+  }
+  if (pool) pool->run(job2); else job2(0, 1);
+  return FT_OK;
+}
+
+// ---- split rule ----------------------------------------------------------------------------
+int qstar_split(int m, double Bp, double Bh, int* q, double* qstar) {
+  if (m < 0 || !(Bp > 0.0) || !(Bh > 0.0))
+    return fail(FT_EINVAL, "ft_qstar_split: need m >= 0, Bp > 0 and Bh > 0");
+  const double qs = (double)m * Bp / Bh;
+  double r = std::floor(qs + 0.5);
+  if (r < 0) r = 0;
+  if (r > m) r = m;
+  if (qstar) *qstar = qs;
+  if (q) *q = (int)r;
+  return FT_OK;
+}
+
+// ---- LRU ------------------------------------------------------------------------------------
+void LruState::init(int E, int S, bool resident) {
+  e2s.assign(E, -1);
+  s2e.assign(S, -1);
+  last_use.assign(S, -1);
+  step = 0;
+  if (resident)
+    for (int e = 0; e < E && e < S; ++e) { e2s[e] = e; s2e[e] = e; }
+}
+
+int LruState::take_slot(int64_t now, int32_t* evicted) const {
+  *evicted = -1;
+  const int S = (int)s2e.size();
+  for (int s = 0; s < S; ++s)
+    if (s2e[s] < 0) return s;
+  int best = -1;
+  for (int s = 0; s < S; ++s)
+    if (last_use[s] < now && (best < 0 || last_use[s] < last_use[best])) best = s;
+  if (best >= 0) *evicted = s2e[best];
+  return best;
+}
+
+}  // namespace ft

@@ -1,0 +1,60 @@
+// Host-side pieces of libft: error reporting, thread pool, host expert FFN, LRU policy.
+#pragma once
+
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "ft_internal.h"
+
+namespace ft {
+
+// thread-local last error
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+
+// Fixed set of worker threads; run(fn) calls fn(i, n) for i in [0, n) on the workers and the
+// calling thread (i = n - 1) and returns when all have finished.
+class ThreadPool {
+ public:
+  explicit ThreadPool(int n_threads);
+  ~ThreadPool();
+  int size() const { return n_; }
+  void run(const std::function<void(int, int)>& fn);
+
+ private:
+  void worker(int id);
+  int n_;
+  std::vector<std::thread> threads_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(int, int)>* job_ = nullptr;
+  uint64_t gen_ = 0;
+  int pending_ = 0;
+  bool stop_ = false;
+};
+
+// SwiGLU FFN of one expert blob on host cores: y[t] = W_d bf16(silu(W_g x_t) * (W_u x_t)),
+// fp32 accumulation, x as bf16 bits [T][H], y fp32 [T][H].  pool may be null.
+int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
+                    const uint16_t* x, int T, float* y);
+
+// The split rule: q = floor(m Bp / Bh + 1/2) clamped to [0, m].
+int qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
+
+// Expert-slot LRU: streamed misses are admitted into the lowest empty slot, else into the
+// slot with the oldest last use among slots not used in this step (ties: lower slot).
+struct LruState {
+  std::vector<int32_t> e2s, s2e;
+  std::vector<int64_t> last_use;
+  int64_t step = 0;
+  void init(int E, int S, bool resident);
+  // returns the slot to admit into and the evicted expert (-1 if none), or slot -1 when no
+  // slot can be taken in this step
+  int take_slot(int64_t now, int32_t* evicted) const;
+};
+
+}  // namespace ft

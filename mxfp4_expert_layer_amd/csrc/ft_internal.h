@@ -1,0 +1,78 @@
+// Internal declarations of libft shared by the host runtime (g++) and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/ft.h"
+
+#if defined(__HIPCC__)
+#define FT_HD __host__ __device__
+#else
+#define FT_HD
+#endif
+
+namespace ft {
+
+// ---- tiled blob layout ------------------------------------------------------------------
+// A matrix [R][K] (K = contraction axis) is stored in tiles of 16 rows x 128 K.  Tile
+// (rt, kc) holds 1024 code bytes; lane l (0..63) of a wave owns bytes [16 l, 16 l + 16):
+// row rt*16 + l%16, K elements kc*128 + 32*(l/16) .. +31, two codes per byte, low nibble
+// first.  This is the operand layout of one 16-row x 32-K slab per lane group of the
+// 16x16x32 MFMA, so one 128-bit load per lane feeds four MFMAs with no shuffles.
+// Scales: MXFP4 one E8M0 byte per lane per tile (64 B per tile, lane l's byte = block
+// kc*4 + l/16 of row l%16); NVFP4 two E4M3 bytes per lane (128 B per tile, lane l's pair =
+// blocks kc*8 + 2*(l/16) + {0,1}).  Tiles are ordered row-tile major: tile index =
+// rt * (K/128) + kc, so a wave walking K for one row tile reads contiguous memory.
+
+constexpr int kTileRows = 16;
+constexpr int kTileK = 128;
+constexpr int kTileCodeBytes = 1024;
+constexpr uint64_t kAlign = 4096;
+constexpr uint32_t kBlobMagic = 0x31425446u;  // "FTB1"
+
+FT_HD inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+FT_HD inline int scale_tile_bytes(int fmt) { return fmt == FT_MXFP4 ? 64 : 128; }
+
+struct BlobLayout {
+  int fmt, H, I;
+  uint64_t off[6];   // gate codes, gate scales, up codes, up scales, down codes, down scales
+  uint64_t bytes;    // whole blob, multiple of 4096
+};
+
+struct BlobHeader {
+  uint32_t magic;
+  int32_t fmt, H, I;
+  float tensor_scale[3];
+  int32_t reserved[9];
+};
+
+FT_HD inline BlobLayout blob_layout(int fmt, int H, int I) {
+  BlobLayout L;
+  L.fmt = fmt; L.H = H; L.I = I;
+  const uint64_t gc = (uint64_t)I * H / 2, dc = (uint64_t)H * I / 2;
+  const uint64_t sb = (uint64_t)scale_tile_bytes(fmt);
+  const uint64_t gs = (uint64_t)(I / kTileRows) * (H / kTileK) * sb;
+  const uint64_t ds = (uint64_t)(H / kTileRows) * (I / kTileK) * sb;
+  uint64_t o = kAlign;  // header
+  const uint64_t sz[6] = {gc, gs, gc, gs, dc, ds};
+  for (int i = 0; i < 6; ++i) { L.off[i] = o; o = align_up(o + sz[i], kAlign); }
+  L.bytes = o;
+  return L;
+}
+
+// ---- decode work list ------------------------------------------------------------------
+// One entry per distinct expert of a decode call (plus one per shared expert): the blob to
+// read and up to 16 (token, pair) columns.  `pair` indexes the per-(token, choice) partial
+// buffer P[T * kk + j] with kk = k + n_shared (j = k + s for shared expert s).
+constexpr int kMaxCols = 16;
+struct WorkItem {
+  int32_t expert;    // routed expert id, or -1 - s for shared expert s
+  int32_t slot;      // pool slot, or -1 - s for shared expert s
+  int32_t ntok;      // columns in use (1..16)
+  int32_t pad;
+  int32_t tok[kMaxCols];
+  int32_t pair[kMaxCols];
+};
+
+}  // namespace ft

@@ -1,0 +1,251 @@
+"""GPU parity of the decode path (libft through its C ABI) against the float64 oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from mxfp4_expert_layer_amd import synth
+from oracle import fp4, moe, policy
+
+from gpu_util import check_output, check_routing, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ft = pytest.importorskip("mxfp4_expert_layer_amd.ft")
+from mxfp4_expert_layer_amd.layer import GpuLayer, stream_ptr  # noqa: E402
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    c = ft.Context(0)
+    yield c
+    c.close()
+
+
+_layers = {}
+
+
+def layer_for(ctx, name, **kw):
+    """One GpuLayer per name for the whole module (building the big layers takes seconds)."""
+    if name not in _layers:
+        cfg = kw.pop("cfg") if "cfg" in kw else synth.CONFIGS[name]
+        log(f"[gpu] building layer {name} {cfg.H}x{cfg.I} E={cfg.E}")
+        _layers[name] = GpuLayer(ctx, cfg, **kw)
+    return _layers[name]
+
+
+def run_decode(ctx, L, x_bits, stats=None):
+    T = x_bits.shape[0]
+    xd = to_dev(x_bits)
+    y = torch.empty((T, L.cfg.H), dtype=torch.float32, device="cuda")
+    ft.moe_decode(ctx, L.handle, xd, T, y, stream_ptr(), stats)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def run_route(ctx, L, x_bits):
+    T = x_bits.shape[0]
+    xd = to_dev(x_bits)
+    idx = torch.empty((T, L.cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, L.cfg.k), dtype=torch.float32, device="cuda")
+    ft.route(ctx, L.handle, xd, T, idx, w, stream_ptr())
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+# ---- A3: dequantisation, bit-exact ----------------------------------------------------------
+
+def _dequant(L, slot, matrix):
+    cfg = L.cfg
+    R, K = (cfg.H, cfg.I) if matrix == 2 else (cfg.I, cfg.H)
+    out = torch.empty((R, K), dtype=torch.float32, device="cuda")
+    ft.debug_dequant(L.handle, slot, matrix, out, stream_ptr())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _expected(L, ex, matrix, fmt):
+    names = [("gate_codes", "gate_scales"), ("up_codes", "up_scales"), ("down_codes", "down_scales")]
+    c, s = names[matrix]
+    v = fp4.dequant(fmt, getattr(ex, c), getattr(ex, s), float(ex.tensor_scales[matrix]))
+    with np.errstate(over="ignore"):
+        return v.astype(np.float32)
+
+
+def _same(a, b):
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+def test_dequant_bit_exact_tiny_workload(ctx):
+    L = layer_for(ctx, "cfg1", max_tokens=16)
+    OL = L.oracle_layer()
+    for slot in range(L.cfg.E):
+        for m in range(3):
+            assert _same(_dequant(L, slot, m), _expected(L, OL.expert(slot), m, "mxfp4")), (slot, m)
+
+
+def _allcodes_layer(ctx):
+    cfg = synth.small_config("allcodes", seed=3, H=256, I=256, E=2, k=1)
+    ex = synth.gen_expert(cfg, 0)
+    rows, nb = cfg.I, cfg.H // 2
+    ex.gate_codes = ((np.arange(rows)[:, None] * nb + np.arange(nb)[None, :]) % 256).astype(np.uint8)
+    ex.gate_scales = (np.arange(rows * cfg.H // 32) % 256).astype(np.uint8).reshape(rows, -1)
+    return layer_for(ctx, "allcodes", cfg=cfg, max_tokens=1, experts={0: ex}), ex
+
+
+def test_dequant_every_code_normal_scales(ctx):
+    """Every byte of E2M1 code pairs under every E8M0 scale whose products are normal fp32
+    and bf16 numbers (codes 2..253)."""
+    L, ex = _allcodes_layer(ctx)
+    got = _dequant(L, 0, 0)
+    exp = _expected(L, ex, 0, "mxfp4")
+    sc = np.repeat(ex.gate_scales.astype(np.int64), 32, axis=1)
+    sel = (sc >= 2) & (sc <= 253)
+    assert _same(got[sel], exp[sel])
+
+
+def test_dequant_extreme_scales(ctx):
+    """E8M0 codes 0, 1, 254 and 255: subnormal, overflowing and NaN products."""
+    L, ex = _allcodes_layer(ctx)
+    got = _dequant(L, 0, 0)
+    exp = _expected(L, ex, 0, "mxfp4")
+    sc = np.repeat(ex.gate_scales.astype(np.int64), 32, axis=1)
+    for code in (0, 1, 254, 255):
+        sel = sc == code
+        g, e = got[sel], exp[sel]
+        bad = ~((g == e) | (np.isnan(g) & np.isnan(e)))
+        assert not bad.any(), (code, list(zip(g[bad][:6], e[bad][:6])))
+
+
+def test_dequant_nvfp4_bit_exact(ctx):
+    cfg = synth.small_config("nvsmall", seed=5, H=256, I=128, E=3, k=2, fmt=synth.NVFP4,
+                             code_dist="uniform", nv_tensor_scale=1 / 64)
+    L = layer_for(ctx, "nvsmall", cfg=cfg, max_tokens=2)
+    OL = L.oracle_layer()
+    for slot in range(3):
+        for m in range(3):
+            assert _same(_dequant(L, slot, m), _expected(L, OL.expert(slot), m, "nvfp4"))
+
+
+# ---- A1: routing ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8), ("cfg3", 1), ("cfg3", 16)])
+def test_route_matches_oracle(ctx, name, T):
+    L = layer_for(ctx, name, max_tokens=16)
+    OL = L.oracle_layer()
+    x = synth.gen_tokens(L.cfg, T, batch=7)
+    idx, w = run_route(ctx, L, x)
+    xr = fp4.bf16_bits_to_f64(x)
+    r_idx, r_w, logits, gap = moe.route(xr, OL.router_w, OL.router_b, L.cfg.k)
+    check_routing(idx, w, dict(idx=r_idx, w=r_w, logits=logits, gap=gap))
+    assert np.all(np.abs(w.sum(1) - 1) <= 1e-6)
+
+
+# ---- A4-A6: decode layer outputs ------------------------------------------------------------
+
+def _decode_and_check(ctx, L, T, batch):
+    x = synth.gen_tokens(L.cfg, T, batch=batch)
+    log(f"[gpu] decode {L.cfg.name} T={T} batch={batch}")
+    y = run_decode(ctx, L, x)
+    idx, w = run_route(ctx, L, x)
+    OL = L.oracle_layer()
+    ref = moe.moe_forward(OL, x)
+    ties = check_routing(idx, w, ref)
+    if ties:
+        ref = moe.moe_forward(OL, x, idx=idx)
+    return check_output(y, ref["y"], f"{L.cfg.name} T={T}")
+
+
+@pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8),
+                                    ("cfg3", 1), ("cfg3", 4), ("cfg3", 16)])
+def test_decode_matches_oracle(ctx, name, T):
+    L = layer_for(ctx, name, max_tokens=16)
+    err = _decode_and_check(ctx, L, T, batch=100 + T)
+    log(f"[gpu] {name} T={T} rel-L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("H,I,E,k,ns,T", [(128, 128, 4, 2, 0, 3), (384, 256, 5, 3, 1, 7),
+                                          (640, 384, 9, 4, 2, 16), (1152, 640, 17, 5, 1, 11),
+                                          (256, 1152, 6, 1, 0, 2), (512, 2176, 3, 3, 1, 5)])
+def test_decode_ragged_shapes(ctx, H, I, E, k, ns, T):
+    """K chunk counts that do not divide the wave split, odd row-tile counts, shared experts."""
+    cfg = synth.small_config(f"rag{H}_{I}", seed=H + I, H=H, I=I, E=E, k=k, n_shared=ns,
+                             code_dist="normal", router_sigma=1 / np.sqrt(H))
+    L = layer_for(ctx, cfg.name, cfg=cfg, max_tokens=16)
+    _decode_and_check(ctx, L, T, batch=1)
+
+
+def test_decode_is_deterministic(ctx):
+    L = layer_for(ctx, "cfg2", max_tokens=16)
+    x = synth.gen_tokens(L.cfg, 8, batch=3)
+    a = run_decode(ctx, L, x)
+    b = run_decode(ctx, L, x)
+    assert np.array_equal(a, b)
+
+
+def test_decode_rejects_bad_token_count(ctx):
+    L = layer_for(ctx, "cfg1_T4", cfg=synth.CONFIGS["cfg1"], max_tokens=4)
+    x = synth.gen_tokens(L.cfg, 5)
+    with pytest.raises(ft.FtError) as e:
+        run_decode(ctx, L, x)
+    assert e.value.code == ft.FT_EINVAL
+
+
+# ---- A2/A7: slot pool and miss path ---------------------------------------------------------
+
+def _miss_sequence(ctx, L, steps, bp, bh, check_every, T=1, q_force=None, batch0=0):
+    cfg = L.cfg
+    OL = L.oracle_layer()
+    pool = policy.LruPool(cfg.E, L.n_slots)
+    ft.set_bandwidth(L.handle, bp, bh)
+    ft.force_q(L.handle, -1 if q_force is None else q_force)
+    hits = total = 0
+    for s in range(steps):
+        x = synth.gen_tokens(cfg, T, batch=batch0 + s)
+        st = ft.DecodeStats()
+        y = run_decode(ctx, L, x, st)
+        xr = fp4.bf16_bits_to_f64(x)
+        r_idx, r_w, logits, gap = moe.route(xr, OL.router_w, OL.router_b, cfg.k)
+        assert np.all(gap >= 1e-6), "near-tie in a miss-path step; choose another seed"
+        res = pool.step(r_idx, r_w, bp, bh, q_override=q_force)
+        e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+        assert np.array_equal(e2s, res.e2s), f"step {s}: e2s differs"
+        assert np.array_equal(s2e, res.s2e), f"step {s}: s2e differs"
+        assert (st.n_hits, st.n_miss, st.q, st.n_streamed, st.n_host) == (
+            len(res.hits), len(res.misses), res.q, len(res.streamed), len(res.host)), s
+        hits += len(res.hits)
+        total += len(res.selected)
+        if s % check_every == 0 or s == steps - 1:
+            ref = moe.moe_forward(OL, x)
+            check_output(y, ref["y"], f"miss step {s}")
+    return hits / max(1, total)
+
+
+def test_miss_path_small_pool(ctx):
+    cfg = synth.small_config("misssmall", seed=77, H=256, I=128, E=16, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 16, zipf_c=0.7)
+    L = layer_for(ctx, "misssmall", cfg=cfg, resident=False, n_slots=5, max_tokens=4)
+    _miss_sequence(ctx, L, steps=30, bp=1.0, bh=2.5, check_every=3, T=2)
+
+
+@pytest.mark.parametrize("q_force", [0, 2, 99])
+def test_miss_path_forced_split_gives_same_outputs(ctx, q_force):
+    cfg = synth.small_config("missforce", seed=78, H=384, I=256, E=12, k=4, n_shared=0,
+                             code_dist="normal", router_sigma=1 / 20)
+    L = layer_for(ctx, f"missforce{q_force}", cfg=cfg, resident=False, n_slots=4, max_tokens=2)
+    _miss_sequence(ctx, L, steps=8, bp=1.0, bh=3.0, check_every=1, T=1, q_force=q_force)
+
+
+def test_miss_path_284b_layer(ctx):
+    """The 284B-class layer with a 48-slot pool: 64 warm-up and 64 timed single tokens with the
+    slot tables checked after every step and the outputs every 8th step."""
+    L = layer_for(ctx, "cfg4", resident=False, n_slots=48, max_tokens=1)
+    rate = _miss_sequence(ctx, L, steps=128, bp=50e9, bh=120e9, check_every=16, T=1)
+    log(f"[gpu] cfg4 hit rate over 128 steps: {rate:.3f}")
