@@ -15,15 +15,12 @@
 
 using namespace ft;
 
-// kernel launchers (ft_kernels.hip)
-extern "C" int ftk_route_decode(const uint16_t* x, const float* wr, const float* b, int T, int H,
-                                int E, int k, int n_shared, float* logits, int* ticket,
-                                int32_t* idx_out, float* w_out, const int32_t* e2s,
-                                WorkItem* items, int* n_items, hipStream_t st);
-extern "C" int ftk_ffn_decode(const uint16_t* x, int H, int I, const WorkItem* items,
-                              const int* n_items, int max_items, const uint8_t* pool,
-                              const uint8_t* shared, uint64_t stride, const BlobLayout* L,
-                              uint16_t* h, float* P, hipStream_t st, const hipEvent_t* ev);
+// kernel launchers (ft_decode.hip, ft_debug.hip)
+extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, int T, int H, int E,
+                          float* logits, hipStream_t st);
+extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_out, float* w_out,
+                        hipStream_t st);
+extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
                            float* y, hipStream_t st);
 extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
@@ -66,7 +63,6 @@ struct ft_layer {
   // device workspace (one allocation)
   void* dev = nullptr;
   float* logits = nullptr;
-  int* ticket = nullptr;
   int32_t* idx = nullptr;
   float* w = nullptr;
   WorkItem* items = nullptr;     // [2][max_items] (second list: streamed misses)
@@ -249,7 +245,6 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   size_t need = 0;
   auto add = [&](size_t bytes) { need += align_up(bytes, 256); };
   add((size_t)T * d.E * 4);                        // logits
-  add(4);                                          // ticket
   add((size_t)T * d.k * 4);                        // idx
   add((size_t)T * d.k * 4);                        // w
   add((size_t)2 * l->max_items * sizeof(WorkItem));
@@ -263,7 +258,6 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipMemset(l->dev, 0, need));
   uint8_t* p = (uint8_t*)l->dev;
   l->logits = carve<float>(p, (size_t)T * d.E);
-  l->ticket = carve<int>(p, 1);
   l->idx = carve<int32_t>(p, (size_t)T * d.k);
   l->w = carve<float>(p, (size_t)T * d.k);
   l->items = carve<WorkItem>(p, (size_t)2 * l->max_items);
@@ -330,21 +324,40 @@ extern "C" FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_
   if (!idx || !w) return fail(FT_EINVAL, "ft_route: idx/w null");
   const ft_layer_desc& d = layer->d;
   HIP_TRY(hipSetDevice(ctx->device));
-  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, d.E, d.k, d.n_shared,
-                                       layer->logits, layer->ticket, idx, w, nullptr, nullptr,
-                                       nullptr, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, d.E, layer->logits, st));
+  HIP_TRY((hipError_t)ftk_topk(layer->logits, T, d.E, d.k, idx, w, st));
   return FT_OK;
+}
+
+static DecodeLaunch launch_args(ft_layer* l, const uint16_t* x, int T, int route, WorkItem* items,
+                                int* n_items, int max_items) {
+  const ft_layer_desc& d = l->d;
+  DecodeLaunch a{};
+  a.x = x;
+  a.T = T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k; a.n_shared = d.n_shared;
+  a.route = route;
+  a.logits = l->logits;
+  a.e2s = l->e2s_dev;
+  a.idx_out = l->idx;
+  a.w_out = l->w;
+  a.items = items;
+  a.n_items = n_items;
+  a.max_items = max_items;
+  a.pool = (const uint8_t*)d.pool;
+  a.shared = (const uint8_t*)d.shared_blobs;
+  a.stride = d.blob_stride;
+  a.L = l->L;
+  a.h = l->h;
+  a.P = l->P;
+  return a;
 }
 
 static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipStream_t st) {
   const ft_layer_desc& d = l->d;
-  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, d.E, d.k, d.n_shared,
-                                       l->logits, l->ticket, l->idx, l->w, l->e2s_dev,
-                                       l->items, l->n_items, st));
-  const int items_max = T * d.k + d.n_shared;
-  HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items, l->n_items, items_max,
-                                     (const uint8_t*)d.pool, (const uint8_t*)d.shared_blobs,
-                                     d.blob_stride, &l->L, l->h, l->P, st, prof_events(l)));
+  HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, d.E, l->logits, st));
+  const DecodeLaunch a = launch_args(l, x, T, 1, l->items, l->n_items, T * d.k + d.n_shared);
+  HIP_TRY((hipError_t)ftk_decode_experts(&a, st, prof_events(l)));
   HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
   return FT_OK;
 }
@@ -362,9 +375,8 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   const int k = d.k, kk = l->kk, E = d.E;
   ft_decode_stats S{};
   auto t0 = clk::now();
-  HIP_TRY((hipError_t)ftk_route_decode(x, d.router_w, d.router_b, T, d.H, E, k, d.n_shared,
-                                       l->logits, l->ticket, l->idx, l->w, nullptr, nullptr,
-                                       nullptr, st));
+  HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, E, l->logits, st));
+  HIP_TRY((hipError_t)ftk_topk(l->logits, T, E, k, l->idx, l->w, st));
   HIP_TRY(hipMemcpyAsync(l->idx_h, l->idx, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipMemcpyAsync(l->w_h, l->w, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipMemcpyAsync(l->x_h, x, (size_t)T * d.H * 2, hipMemcpyDeviceToHost, st));
@@ -467,16 +479,15 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   HIP_TRY(hipMemcpyAsync(l->n_items, l->n_items_h, 2 * sizeof(int), hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(l->e2s_dev, l->e2s_h, (size_t)E * 4, hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice, st));
-  const uint8_t* pool = (const uint8_t*)d.pool;
-  const uint8_t* shared = (const uint8_t*)d.shared_blobs;
-  if (n0 > 0)
-    HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items, l->n_items, n0, pool, shared,
-                                       d.blob_stride, &l->L, l->h, l->P, st, nullptr));
+  if (n0 > 0) {
+    const DecodeLaunch a = launch_args(l, x, T, 0, l->items, l->n_items, n0);
+    HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
+  }
   HIP_TRY(hipStreamWaitEvent(st, l->ev_copy, 0));
-  if (n1 > 0)
-    HIP_TRY((hipError_t)ftk_ffn_decode(x, d.H, d.I, l->items + l->max_items, l->n_items + 1, n1,
-                                       pool, shared, d.blob_stride, &l->L,
-                                       l->h, l->P, st, nullptr));
+  if (n1 > 0) {
+    const DecodeLaunch a = launch_args(l, x, T, 0, l->items + l->max_items, l->n_items + 1, n1);
+    HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
+  }
 
   // host experts, concurrently with the GPU work enqueued above
   auto th = clk::now();

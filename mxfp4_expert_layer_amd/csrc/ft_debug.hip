@@ -1,0 +1,61 @@
+// Test-hook kernels of libft: dequantise one matrix of a blob to fp32 in logical order.
+#include <hip/hip_runtime.h>
+
+#include "ft_device.h"
+
+namespace ft {
+
+// One wave per tile; MXFP4 decodes with the same conversion the GEMVs use.
+__global__ __launch_bounds__(64) void k_dequant_mx(const uint8_t* codes, const uint8_t* scales,
+                                                   int R, int K, float* out) {
+  const int KC = K / kTileK;
+  const int tile = blockIdx.x, lane = threadIdx.x;
+  const int rt = tile / KC, kc = tile % KC;
+  const int row = rt * kTileRows + (lane & 15);
+  const int k0 = kc * kTileK + 32 * (lane >> 4);
+  const uint4 c = ((const uint4*)codes)[(uint64_t)tile * 64 + lane];
+  const float s = e8m0_f32(scales[(uint64_t)tile * 64 + lane]);
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 v = fp4x8_bf16(w[i], s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[(uint64_t)row * K + k0 + 8 * i + q] = (float)v[q];
+  }
+}
+
+// NVFP4: E2M1 value * E4M3 block scale * tensor scale in fp32.
+__global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* codes, const uint8_t* scales,
+                                                   int R, int K, float ts, float* out) {
+  const int KC = K / kTileK;
+  const int tile = blockIdx.x, lane = threadIdx.x;
+  const int rt = tile / KC, kc = tile % KC;
+  const int row = rt * kTileRows + (lane & 15);
+  const int k0 = kc * kTileK + 32 * (lane >> 4);
+  const uint4 c = ((const uint4*)codes)[(uint64_t)tile * 64 + lane];
+  const float s0 = e4m3_f32(scales[(uint64_t)tile * 128 + 2 * lane]);
+  const float s1 = e4m3_f32(scales[(uint64_t)tile * 128 + 2 * lane + 1]);
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  for (int q = 0; q < 32; ++q) {
+    const uint32_t code = (w[q >> 3] >> (4 * (q & 7))) & 15;
+    out[(uint64_t)row * K + k0 + q] = e2m1_f32(code) * (q < 16 ? s0 : s1) * ts;
+  }
+}
+
+}  // namespace ft
+
+using namespace ft;
+
+extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
+                           float* out, hipStream_t st) {
+  const int R = matrix == 2 ? L->H : L->I;
+  const int K = matrix == 2 ? L->I : L->H;
+  const uint8_t* codes = blob + L->off[2 * matrix];
+  const uint8_t* scales = blob + L->off[2 * matrix + 1];
+  const int tiles = (R / kTileRows) * (K / kTileK);
+  if (L->fmt == FT_MXFP4)
+    hipLaunchKernelGGL(k_dequant_mx, dim3(tiles), dim3(64), 0, st, codes, scales, R, K, out);
+  else
+    hipLaunchKernelGGL(k_dequant_nv, dim3(tiles), dim3(64), 0, st, codes, scales, R, K, ts, out);
+  return (int)hipGetLastError();
+}

@@ -1,0 +1,561 @@
+// Decode kernels of libft for gfx950 (CDNA4).
+//
+// One decode call of T <= 16 tokens (the MoE layer of the FreeToken pages: a gate picks k
+// experts per token and their outputs are merged by routing weight — smzdm explainer
+// a825qpgl, section 二) runs as four kernels on the caller's stream:
+//   k_logits   logits[t][e] = x_t . W_r[e] + b[e] in fp32; one workgroup per expert row.
+//   k_gateup   prologue: every workgroup takes the top-k of the logits (ties to the lower
+//              index), the softmax over the kept logits and the list of distinct experts
+//              with their token columns, in LDS (workgroup 0 also publishes them for the
+//              next kernel); then per (expert, 16-row tile): g = W_g x, u = W_u x on the
+//              16x16x32 bf16 MFMA with FP4 codes converted to bf16 in registers (exact),
+//              h = bf16(silu(g) * u).  Tokens are the MFMA's N columns, so every weight is
+//              read once per call however many tokens share the expert.
+//   k_down     per (expert, 16-row tile of W_d): y_e = W_d h into the partial buffer
+//              P[t * kk + j] (j = top-k rank, k + s for shared expert s).
+//   k_combine  y_t = sum_j w_tj P[t][j] + sum_s P[t][k + s], in that order.
+// Workgroups never wait on each other inside a kernel: on this chip a device-scope fence
+// writes back and invalidates the issuing XCD's L2, so data moves between workgroups only
+// at kernel boundaries.
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include "ft_device.h"
+
+namespace ft {
+
+constexpr int kMaxItems = FT_MAX_DECODE_TOKENS * FT_MAX_TOPK + 4;
+constexpr int kRouteMaxEPerLane = 16;  // E <= 1024
+
+// ---- router logits ----------------------------------------------------------------------
+// One workgroup per expert row.  Thread tid covers H positions tid*4 + i*1024.  TB is the
+// token count rounded up to a power of two; rows past T re-read row T-1 and are dropped,
+// and positions past H are clamped and masked at the FMA, so no load sits behind a branch
+// and a lane's weight and token loads are all in flight together.
+template <int TB>
+__global__ __launch_bounds__(256) void k_logits(const uint16_t* __restrict__ x,
+                                                const float* __restrict__ wr,
+                                                const float* __restrict__ b, int T, int H, int E,
+                                                float* __restrict__ logits) {
+  constexpr int NI = TB >= 8 ? 2 : (TB >= 4 ? 4 : 6);
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = 0.f;
+  const float* wrow = wr + (uint64_t)e * H;
+  for (int base = tid * 4; base < H; base += NI * 1024) {
+    float4 wv[NI];
+    uint2 xv[TB][NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wv[i] = *(const float4*)(wrow + min(base + i * 1024, H - 4));
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const uint16_t* xr = x + (uint64_t)min(t, T - 1) * H;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) xv[t][i] = *(const uint2*)(xr + min(base + i * 1024, H - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float m = base + i * 1024 < H ? 1.f : 0.f;
+      const float4 w4 = make_float4(wv[i].x * m, wv[i].y * m, wv[i].z * m, wv[i].w * m);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        acc[t] = fmaf(w4.x, bf16_lo(xv[t][i].x), acc[t]);
+        acc[t] = fmaf(w4.y, bf16_hi(xv[t][i].x), acc[t]);
+        acc[t] = fmaf(w4.z, bf16_lo(xv[t][i].y), acc[t]);
+        acc[t] = fmaf(w4.w, bf16_hi(xv[t][i].y), acc[t]);
+      }
+    }
+  }
+  __shared__ float red[4][TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const float sum = wave_sum(acc[t]);
+    if (lane == 0) red[wave][t] = sum;
+  }
+  __syncthreads();
+  if (tid < T)
+    logits[(uint64_t)tid * E + e] =
+        ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) + (b ? b[e] : 0.f);
+}
+
+// ---- top-k and the work list in LDS -------------------------------------------------------
+struct TopkLds {
+  int idx[kMaxCols][FT_MAX_TOPK];
+  float w[kMaxCols][FT_MAX_TOPK];
+};
+
+// Order-preserving key of a float: a > b  <=>  key(a) > key(b) (NaN is mapped to -inf first).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Per-token top-k by a radix select: one wave per token finds the k-th largest key with a
+// 32-step bitwise search whose counts are wave ballots (no cross-lane shuffles), keeps
+// every key above it plus the lowest-index keys equal to it, compacts the k winners into
+// LDS and ranks them (logit descending, ties to the lower index).  Weights are the softmax
+// over the k kept logits.  EPL = experts per lane (E <= 64 * EPL).  Called by all 256
+// threads; ends synchronised.
+template <int EPL>
+__device__ __forceinline__ void topk_tokens(const float* logits, int T, int E, int k, TopkLds& s,
+                                            float (*c_val)[FT_MAX_TOPK],
+                                            int (*c_idx)[FT_MAX_TOPK]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t = wave; t < T; t += 4) {
+    float v[EPL];
+    uint32_t key[EPL];
+    // loads are unconditional (clamped to a valid index) so all are in flight together
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = logits[(uint64_t)t * E + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (v[i] != v[i]) v[i] = -INFINITY;           // NaN logits never win
+      key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;  // padding ranks below -inf
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) c += __popcll(__ballot(key[i] >= cand));
+      if (c >= k) tau = cand;
+    }
+    int n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) n_gt += __popcll(__ballot(key[i] > tau));
+    const int need_eq = k - n_gt;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint64_t eqb = __ballot(key[i] == tau);
+      const bool sel = key[i] > tau ||
+                       (key[i] == tau && eq_before + __popcll(eqb & lt_mask) < need_eq);
+      const uint64_t selb = __ballot(sel);
+      if (sel) {
+        const int pos = sel_before + __popcll(selb & lt_mask);
+        c_val[t][pos] = v[i];
+        c_idx[t][pos] = lane + 64 * i;
+      }
+      eq_before += __popcll(eqb);
+      sel_before += __popcll(selb);
+    }
+  }
+  __syncthreads();
+  // rank the k winners of each token: thread (t, j) handles winner j of token t
+  const int tid = threadIdx.x;
+  if (tid < T * k) {
+    const int t = tid / k, j = tid % k;
+    const float vj = c_val[t][j];
+    const int ej = c_idx[t][j];
+    float vq[FT_MAX_TOPK];
+    int eq[FT_MAX_TOPK];
+#pragma unroll
+    for (int q = 0; q < FT_MAX_TOPK; ++q) {
+      vq[q] = c_val[t][min(q, k - 1)];
+      eq[q] = c_idx[t][min(q, k - 1)];
+    }
+    int rank = 0;
+    float vmax = vj;
+#pragma unroll
+    for (int q = 0; q < FT_MAX_TOPK; ++q) {
+      if (q < k) {
+        rank += (vq[q] > vj || (vq[q] == vj && eq[q] < ej));
+        vmax = fmaxf(vmax, vq[q]);
+      }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < FT_MAX_TOPK; ++q)
+      if (q < k) sum += expf(vq[q] - vmax);
+    s.idx[t][rank] = ej;
+    s.w[t][rank] = expf(vj - vmax) / sum;
+  }
+  __syncthreads();
+}
+
+struct ListLds {
+  int n_items;
+  int wave_tot[4];
+  int expert[kMaxItems];
+  int slot[kMaxItems];
+  int ntok[kMaxItems];
+  uint8_t tok[kMaxItems][kMaxCols];
+  uint8_t jj[kMaxItems][kMaxCols];
+  uint32_t tokmask[1024];   // per expert: bit t set when token t selected it
+  int pos[1024];            // per expert: its item index
+};
+
+// Distinct routed experts in ascending id with their tokens ascending, then the shared
+// experts (all tokens).  Per-expert token bitmasks make every step O(1) per thread: a
+// token's column within its expert is the number of lower tokens in that mask.  All
+// threads call; ends synchronised.
+__device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int k, int n_shared,
+                                           const int32_t* e2s, ListLds& L) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 256) L.tokmask[e] = 0u;
+  __syncthreads();
+  if (tid < T * k) atomicOr(&L.tokmask[tk.idx[tid / k][tid % k]], 1u << (tid / k));
+  __syncthreads();
+  int has[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ee = tid * 4 + i;
+    has[i] = ee < E ? (L.tokmask[ee] != 0u) : 0;
+  }
+  const int mine = has[0] + has[1] + has[2] + has[3];
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int nb = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += nb;
+  }
+  if (lane == 63) L.wave_tot[wave] = incl;
+  __syncthreads();
+  int base = incl - mine;
+  for (int w2 = 0; w2 < wave; ++w2) base += L.wave_tot[w2];
+  const int n_routed = L.wave_tot[0] + L.wave_tot[1] + L.wave_tot[2] + L.wave_tot[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ee = tid * 4 + i;
+    if (has[i]) {
+      L.pos[ee] = base;
+      L.expert[base] = ee;
+      L.slot[base] = e2s[ee];
+      L.ntok[base] = __popc(L.tokmask[ee]);
+      ++base;
+    }
+  }
+  __syncthreads();
+  if (tid < T * k) {
+    const int t = tid / k, j = tid % k;
+    const int ee = tk.idx[t][j];
+    const int it = L.pos[ee];
+    const int col = __popc(L.tokmask[ee] & ((1u << t) - 1u));
+    L.tok[it][col] = (uint8_t)t;
+    L.jj[it][col] = (uint8_t)j;
+  }
+  if (tid < n_shared * kMaxCols) {
+    const int sh = tid / kMaxCols, t = tid % kMaxCols;
+    const int it = n_routed + sh;
+    if (t == 0) { L.expert[it] = -1 - sh; L.slot[it] = -1 - sh; L.ntok[it] = T; }
+    if (t < T) { L.tok[it][t] = (uint8_t)t; L.jj[it][t] = (uint8_t)(k + sh); }
+  }
+  if (tid == 0) L.n_items = n_routed + n_shared;
+  __syncthreads();
+}
+
+// Publish the routing and the list for the next kernel (global memory).
+__device__ void store_route(const TopkLds& tk, const ListLds& L, int T, int k, int n_shared,
+                            int32_t* idx_out, float* w_out, WorkItem* items, int* n_items) {
+  const int tid = threadIdx.x, kk = k + n_shared;
+  if (tid < T * k) {
+    idx_out[tid] = tk.idx[tid / k][tid % k];
+    w_out[tid] = tk.w[tid / k][tid % k];
+  }
+  for (int i = tid; i < L.n_items; i += 256) {
+    WorkItem& it = items[i];
+    it.expert = L.expert[i];
+    it.slot = L.slot[i];
+    it.ntok = L.ntok[i];
+    it.pad = 0;
+    for (int n = 0; n < L.ntok[i]; ++n) {
+      it.tok[n] = L.tok[i][n];
+      it.pair[n] = L.tok[i][n] * kk + L.jj[i][n];
+    }
+  }
+  if (tid == 0) *n_items = L.n_items;
+}
+
+// Copy a host-built list (miss path) into LDS.  All threads call; ends synchronised.
+__device__ void load_list(const WorkItem* items, const int* n_items, ListLds& L) {
+  const int n = min(*n_items, kMaxItems);
+  for (int i = threadIdx.x; i < n; i += 256) {
+    L.expert[i] = items[i].expert;
+    L.slot[i] = items[i].slot;
+    L.ntok[i] = items[i].ntok;
+    for (int c = 0; c < items[i].ntok && c < kMaxCols; ++c) L.tok[i][c] = (uint8_t)items[i].tok[c];
+  }
+  if (threadIdx.x == 0) L.n_items = n;
+  __syncthreads();
+}
+
+// Single-workgroup top-k (ft_route and the miss path): idx/w to global.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float* logits, int T, int E, int k,
+                                              int32_t* idx_out, float* w_out) {
+  __shared__ TopkLds tk;
+  __shared__ float c_val[kMaxCols][FT_MAX_TOPK];
+  __shared__ int c_idx[kMaxCols][FT_MAX_TOPK];
+  topk_tokens<EPL>(logits, T, E, k, tk, c_val, c_idx);
+  const int tid = threadIdx.x;
+  if (tid < T * k) {
+    idx_out[tid] = tk.idx[tid / k][tid % k];
+    w_out[tid] = tk.w[tid / k][tid % k];
+  }
+}
+
+// ---- expert GEMVs -------------------------------------------------------------------------
+__device__ __forceinline__ const uint8_t* blob_of(int expert, int slot, const uint8_t* pool,
+                                                  const uint8_t* shared, uint64_t stride) {
+  return expert >= 0 ? pool + (uint64_t)slot * stride : shared + (uint64_t)(-1 - expert) * stride;
+}
+
+// acc[m] += W_m[tile rows][chunks ks, ks+kstep, ...] x B for NM matrices sharing the B
+// operand (gate and up share x).  Each lane owns 32 K values of one tile row per chunk: one
+// 128-bit code load, one scale byte and four MFMA k-steps.  The loads of UNR chunks are all
+// issued before any is consumed.  brow: this lane's B column (token row or h row) at K
+// offset 32*g; bcol false makes the column zero without loading it.
+template <int NM, int UNR>
+__device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uint8_t* const* scales,
+                                          uint64_t tile0, int KC, int ks, int kstep,
+                                          const uint16_t* brow, bool bcol, int lane, f32x4* acc) {
+  const int NC = (KC - ks + kstep - 1) / kstep;
+  for (int c0 = 0; c0 < NC; c0 += UNR) {
+    uint4 cw[UNR][NM];
+    uint32_t sc[UNR][NM];
+    uint4 xb[UNR][4];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const bool ok = c0 + u < NC;
+      const uint64_t tile = tile0 + (uint64_t)(ks + (c0 + u) * kstep);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        cw[u][m] = ok ? ((const uint4*)codes[m])[tile * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+        sc[u][m] = ok ? scales[m][tile * 64 + lane] : 127u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const bool ok = c0 + u < NC && bcol;
+      const uint4* xr = (const uint4*)(brow + (uint64_t)(ks + (c0 + u) * kstep) * kTileK);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xb[u][i] = ok ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const float s = e8m0_f32(sc[u][m]);
+        const uint32_t wv[4] = {cw[u][m].x, cw[u][m].y, cw[u][m].z, cw[u][m].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(wv[i], s),
+                                                           as_bf16x8(xb[u][i]), acc[m], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Workgroup = 4 waves.  KSPLIT waves share one 16-row tile and split its K chunks; the
+// workgroup covers 4 / KSPLIT row tiles.  A unit is (item, group of row tiles); workgroups
+// walk the units with a grid stride.
+template <int KSPLIT, int UNR, int EPL>
+__global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
+  constexpr int RPW = 4 / KSPLIT;
+  constexpr bool ROUTE = EPL > 0;
+  __shared__ TopkLds tk;
+  __shared__ ListLds ls;
+  __shared__ f32x4 red[4][2][64];
+  if (ROUTE) {
+    topk_tokens<(ROUTE ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk, (float (*)[FT_MAX_TOPK])&red[0][0][0],
+                                    (int (*)[FT_MAX_TOPK])&red[2][0][0]);
+    build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
+    if (blockIdx.x == 0)
+      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items);
+  } else {
+    load_list(a.items, a.n_items, ls);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rl = wave / KSPLIT, ks = wave % KSPLIT;
+  const int n = lane & 15, g = lane >> 4;
+  const int RT = a.I / kTileRows, KC = a.H / kTileK;
+  const int groups = (RT + RPW - 1) / RPW;
+  const int units = ls.n_items * groups;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int iti = u / groups;
+    const int rt = (u % groups) * RPW + rl;
+    const int expert = ls.expert[iti], slot = ls.slot[iti], ntok = ls.ntok[iti];
+    const bool active = rt < RT && (expert < 0 || slot >= 0);
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+      const uint8_t* blob = blob_of(expert, slot, a.pool, a.shared, a.stride);
+      const uint8_t* codes[2] = {blob + a.L.off[0], blob + a.L.off[2]};
+      const uint8_t* scales[2] = {blob + a.L.off[1], blob + a.L.off[3]};
+      const bool col = n < ntok;
+      const uint16_t* brow = a.x + (uint64_t)(col ? ls.tok[iti][n] : 0) * a.H + 32 * g;
+      tile_gemv<2, UNR>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane, acc);
+    }
+    if (KSPLIT > 1) {
+      red[wave][0][lane] = acc[0];
+      red[wave][1][lane] = acc[1];
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int s2 = 1; s2 < KSPLIT; ++s2) {
+          acc[0] += red[wave + s2][0][lane];
+          acc[1] += red[wave + s2][1][lane];
+        }
+      }
+    }
+    if (ks == 0 && active && n < ntok) {
+      uint16_t hv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = f32_to_bf16_rne(silu_f32(acc[0][r]) * acc[1][r]);
+      const uint2 pk = make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
+                                  (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+      *(uint2*)(a.h + ((uint64_t)iti * kMaxCols + n) * a.I + rt * kTileRows + 4 * g) = pk;
+    }
+    if (KSPLIT > 1) __syncthreads();
+  }
+}
+
+template <int KSPLIT, int UNR>
+__global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
+  constexpr int RPW = 4 / KSPLIT;
+  __shared__ f32x4 red[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rl = wave / KSPLIT, ks = wave % KSPLIT;
+  const int n = lane & 15, g = lane >> 4;
+  const int RT = a.H / kTileRows, KC = a.I / kTileK;
+  const int groups = (RT + RPW - 1) / RPW;
+  const int units = (*a.n_items) * groups;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int iti = u / groups;
+    const int rt = (u % groups) * RPW + rl;
+    const WorkItem& it = a.items[iti];
+    const bool active = rt < RT && (it.expert < 0 || it.slot >= 0);
+    const int ntok = it.ntok;
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+      const uint8_t* blob = blob_of(it.expert, it.slot, a.pool, a.shared, a.stride);
+      const uint8_t* codes[1] = {blob + a.L.off[4]};
+      const uint8_t* scales[1] = {blob + a.L.off[5]};
+      const bool col = n < ntok;
+      const uint16_t* brow = a.h + ((uint64_t)iti * kMaxCols + n) * a.I + 32 * g;
+      tile_gemv<1, UNR>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane, acc);
+    }
+    if (KSPLIT > 1) {
+      red[wave][lane] = acc[0];
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int s2 = 1; s2 < KSPLIT; ++s2) acc[0] += red[wave + s2][lane];
+      }
+    }
+    if (ks == 0 && active && n < ntok) {
+      float* dst = a.P + (uint64_t)it.pair[n] * a.H + rt * kTileRows + 4 * g;
+      *(float4*)dst = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+    }
+    if (KSPLIT > 1) __syncthreads();
+  }
+}
+
+// y[t][r] = sum_{j<k} w[t][j] P[t*kk + j][r] + sum_s P[t*kk + k + s][r]; all loads of an
+// output are issued together.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ P,
+                                                 const float* __restrict__ w, int T, int H,
+                                                 int k, int n_shared, float* __restrict__ y) {
+  constexpr int MAXKK = FT_MAX_TOPK + 4;
+  const int t = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= H || t >= T) return;
+  const int kk = k + n_shared;
+  const float* p = P + (uint64_t)t * kk * H + r;
+  float v[MAXKK];
+#pragma unroll
+  for (int j = 0; j < MAXKK; ++j) v[j] = j < kk ? p[(uint64_t)j * H] : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < FT_MAX_TOPK; ++j)
+    if (j < k) acc = fmaf(w[t * k + j], v[j], acc);
+#pragma unroll
+  for (int j = 0; j < MAXKK; ++j)
+    if (j >= k && j < kk) acc += v[j];
+  y[(uint64_t)t * H + r] = acc;
+}
+
+}  // namespace ft
+
+// ---- launchers (C linkage, called by the host runtime) -----------------------------------
+using namespace ft;
+
+static int grid_for(int units_max, int cap) {
+  const int g = units_max < cap ? units_max : cap;
+  return g < 1 ? 1 : g;
+}
+
+extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, int T, int H, int E,
+                          float* logits, hipStream_t st) {
+  if (T <= 1)
+    hipLaunchKernelGGL(k_logits<1>, dim3(E), dim3(256), 0, st, x, wr, b, T, H, E, logits);
+  else if (T <= 2)
+    hipLaunchKernelGGL(k_logits<2>, dim3(E), dim3(256), 0, st, x, wr, b, T, H, E, logits);
+  else if (T <= 4)
+    hipLaunchKernelGGL(k_logits<4>, dim3(E), dim3(256), 0, st, x, wr, b, T, H, E, logits);
+  else if (T <= 8)
+    hipLaunchKernelGGL(k_logits<8>, dim3(E), dim3(256), 0, st, x, wr, b, T, H, E, logits);
+  else
+    hipLaunchKernelGGL(k_logits<16>, dim3(E), dim3(256), 0, st, x, wr, b, T, H, E, logits);
+  return (int)hipGetLastError();
+}
+
+extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_out, float* w_out,
+                        hipStream_t st) {
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk<2>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+  else
+    hipLaunchKernelGGL(k_topk<16>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+  return (int)hipGetLastError();
+}
+
+// ev: null, or 4 events [gate/up start, stop, down start, stop] that the dispatches record
+// themselves (hipExtLaunchKernelGGL), so host-side gaps are not counted.
+#define FT_LAUNCH(kern, grid, evs, eve, arg)                                                \
+  do {                                                                                      \
+    auto* kfn_ = kern;                                                                      \
+    if (evs) hipExtLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, evs, eve, 0, arg);         \
+    else hipLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, arg);                             \
+  } while (0)
+
+// EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts
+template <int EPL>
+static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const int cap = 2048, KC = a.H / kTileK, RT = a.I / kTileRows;
+  if (KC >= 16)
+    FT_LAUNCH((k_gateup<4, 4, EPL>), dim3(grid_for(a.max_items * RT, cap)), e0, e1, a);
+  else if (KC >= 8)
+    FT_LAUNCH((k_gateup<2, 4, EPL>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e0, e1, a);
+  else
+    FT_LAUNCH((k_gateup<1, 4, EPL>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e0, e1, a);
+}
+
+extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
+  const DecodeLaunch& a = *ap;
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+  if (!a.route) launch_gateup<0>(a, st, e0, e1);
+  else if (a.E <= 64) launch_gateup<1>(a, st, e0, e1);
+  else if (a.E <= 128) launch_gateup<2>(a, st, e0, e1);
+  else if (a.E <= 256) launch_gateup<4>(a, st, e0, e1);
+  else launch_gateup<16>(a, st, e0, e1);
+  const int cap = 2048, KC = a.I / kTileK, RT = a.H / kTileRows;
+  if (KC >= 8)
+    FT_LAUNCH((k_down<2, 4>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e2, e3, a);
+  else
+    FT_LAUNCH((k_down<1, 4>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e2, e3, a);
+  return (int)hipGetLastError();
+}
+
+extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
+                           float* y, hipStream_t st) {
+  hipLaunchKernelGGL(k_combine, dim3((H + 255) / 256, T), dim3(256), 0, st, P, w, T, H, k,
+                     n_shared, y);
+  return (int)hipGetLastError();
+}

@@ -1,0 +1,70 @@
+// Device helpers shared by libft's HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ft_internal.h"
+
+namespace ft {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// E8M0 code -> fp32 scale 2^(e - 127): e = 0 is 2^-127 (an fp32 subnormal), e = 255 NaN.
+// The scaled FP4 converts below use only the exponent field of this value, which for every
+// code but 255 is exactly the E8M0 exponent (measured on gfx950: a scale of 0.75 acts as 2^-1,
+// and the subnormal 2^-127 acts as 2^-127).
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  uint32_t bits = (e == 0u) ? 0x00400000u : ((e == 255u) ? 0x7fc00000u : (e << 23));
+  return __uint_as_float(bits);
+}
+
+// Eight E2M1 codes (one dword, element 0 in the low nibble) times a power-of-two scale ->
+// eight bf16 (exact: an E2M1 value has at most 2 significant bits).
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// E2M1 value table and E4M3 decode in plain fp32 (NVFP4 paths and the debug dequant).
+__device__ __forceinline__ float e2m1_f32(uint32_t c) {
+  const float m = (c & 4) ? ((c & 2) ? ((c & 1) ? 6.f : 4.f) : ((c & 1) ? 3.f : 2.f))
+                          : ((c & 2) ? ((c & 1) ? 1.5f : 1.f) : ((c & 1) ? 0.5f : 0.f));
+  return (c & 8) ? -m : m;
+}
+__device__ __forceinline__ float e4m3_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15, m = c & 7;
+  float v;
+  if (e == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+  else if (e == 0) v = ldexpf((float)m * 0.125f, -6);
+  else v = ldexpf(1.f + (float)m * 0.125f, (int)e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+}  // namespace ft

@@ -75,4 +75,25 @@ struct WorkItem {
   int32_t pair[kMaxCols];
 };
 
+// Arguments of one decode expert pass (gate/up + SwiGLU, then down) as the host hands them
+// to the kernel launcher.
+struct DecodeLaunch {
+  const uint16_t* x;            // device bf16 tokens [T][H]
+  int T, H, I, E, k, n_shared;
+  int route;                    // 1: top-k + work list from `logits` (resident decode)
+  const float* logits;          // [T][E] (route)
+  const int32_t* e2s;           // [E] (route)
+  int32_t* idx_out;             // [T][k] (route: written by workgroup 0)
+  float* w_out;                 // [T][k] (route)
+  WorkItem* items;              // route: written; otherwise read
+  int* n_items;
+  int max_items;                // launch sizing bound on the item count
+  const uint8_t* pool;
+  const uint8_t* shared;
+  uint64_t stride;
+  BlobLayout L;
+  uint16_t* h;                  // [max_items][16][I]
+  float* P;                     // [T * (k + n_shared)][H]
+};
+
 }  // namespace ft

@@ -36,7 +36,7 @@ class GpuLayer:
 
     def __init__(self, ctx: ft.Context, cfg: synth.LayerConfig, *, resident=True,
                  n_slots=None, max_tokens=16, threads=8, copies=1, device="cuda",
-                 experts=None):
+                 experts=None, router=None):
         self.ctx, self.cfg = ctx, cfg
         self.device = device
         self.stride = ft.blob_bytes(cfg.fmt, cfg.H, cfg.I)
@@ -63,8 +63,9 @@ class GpuLayer:
         else:
             self.shared = None
         self.routers = []
+        self.router_override = router
         for c in range(max(1, copies)):
-            w, b = synth.gen_router(cfg, c)
+            w, b = router if router is not None else synth.gen_router(cfg, c)
             self.routers.append((torch.from_numpy(w).to(device),
                                  torch.from_numpy(b).to(device) if b is not None else None))
         self.handles = []
@@ -88,6 +89,8 @@ class GpuLayer:
         """The synth.Layer the oracle evaluates (experts drawn lazily on access)."""
         L = synth.gen_layer(self.cfg, experts=None, copy=copy)
         L.experts.update(self.override)
+        if self.router_override is not None:
+            L.router_w, L.router_b = self.router_override
         return L
 
     def close(self):

@@ -148,6 +148,24 @@ def test_route_matches_oracle(ctx, name, T):
     assert np.all(np.abs(w.sum(1) - 1) <= 1e-6)
 
 
+def test_route_exact_ties_go_to_lower_index(ctx):
+    """Duplicated router rows give bit-identical logits; the lower expert id must win."""
+    cfg = synth.small_config("ties", seed=31, H=256, I=128, E=64, k=6, router_sigma=1 / 16)
+    w, _ = synth.gen_router(cfg)
+    w = w.copy()
+    for a, b in [(3, 40), (7, 8), (21, 63), (50, 2), (11, 12), (12, 13)]:
+        w[b] = w[a]
+    L = layer_for(ctx, "ties", cfg=cfg, max_tokens=16, router=(w, None))
+    OL = L.oracle_layer()
+    x = synth.gen_tokens(cfg, 16, batch=4)
+    idx, wt = run_route(ctx, L, x)
+    r_idx, r_w, logits, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+    # ties inside the kept set are exact on both sides; only the kept/dropped boundary may
+    # legitimately differ under the near-tie rule
+    check_routing(idx, wt, dict(idx=r_idx, w=r_w, logits=logits, gap=gap))
+    assert (idx == r_idx).mean() > 0.9
+
+
 # ---- A4-A6: decode layer outputs ------------------------------------------------------------
 
 def _decode_and_check(ctx, L, T, batch):
