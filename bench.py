@@ -5,6 +5,8 @@ Workloads (seeded synthetic layers, no trained weights exist for these shapes):
   decode-35b-a3b   hidden 2048, 256 experts, top-8, intermediate 512, MXFP4   (default)
   decode-284b      hidden 4096, 256 experts + 1 shared, top-6, intermediate 2048, MXFP4
   miss-path-284b   the 284B-class layer with a 48-slot pool, q* split of misses
+  prefill-753b     4096 tokens through hidden 6144, 160 experts, top-8, intermediate 2048,
+                   NVFP4 (exact bf16-MFMA grouped GEMMs)
 A step is one ft_moe_decode call of T tokens (routing, gate/up + SwiGLU, down, combine).
 Decode steps are captured in a HIP graph and replayed; inputs are resident in HBM; the
 layer is replicated to several device copies (different addresses) so repeated steps are
@@ -35,7 +37,10 @@ WORKLOADS = {
     "decode-35b-a3b": dict(cfg="cfg2", T=1, copies=8, steps=2048, warmup=128),
     "decode-284b": dict(cfg="cfg3", T=1, copies=4, steps=2048, warmup=128),
     "miss-path-284b": dict(cfg="cfg4", T=1, copies=1, steps=64, warmup=64),
+    "prefill-753b": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3),
 }
+BF16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0
 
 
 def log(msg):
@@ -245,6 +250,101 @@ def bench_miss_path(args, wl):
     return res
 
 
+def cpu_baseline_prefill(cfg, x, seconds):
+    """The float64 oracle on a sample of the prefill tokens (experts drawn beforehand)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mxfp4_expert_layer_amd import synth
+    from oracle import fp4, moe
+
+    OL = synth.gen_layer(cfg, experts=None)
+    n_tok = 2
+    xs = x[:n_tok]
+    idx, _, _, _ = moe.route(fp4.bf16_bits_to_f64(xs), OL.router_w, OL.router_b, cfg.k)
+    for e in np.unique(idx):
+        OL.expert(int(e))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        moe.moe_forward(OL, xs)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds or reps >= 3:
+            break
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": reps * n_tok / dt, "unit": "tokens/s", "cores": max(blas) if blas else 1,
+            "kind": "oracle",
+            "sample": f"{reps} x {n_tok} of the 4096 prefill tokens (float64 numpy oracle, "
+                      f"{dt:.1f} s)"}
+
+
+def bench_prefill(args, wl):
+    import numpy as np
+    import torch
+
+    from mxfp4_expert_layer_amd import ft, synth
+    from mxfp4_expert_layer_amd.layer import GpuLayer
+
+    cfg = synth.CONFIGS[wl["cfg"]]
+    T = args.tokens or wl["T"]
+    K = args.steps if args.steps is not None else wl["steps"]
+    W = args.warmup if args.warmup is not None else wl["warmup"]
+    ctx = ft.Context(0)
+    log(f"[bench] building {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I}, {cfg.fmt})")
+    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16)
+    xh = [synth.gen_tokens(cfg, T, batch=b) for b in range(2)]
+    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xh]
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    mode = ft.FT_PREFILL_EXACT
+    nbytes = ft.moe_prefill_workspace_size(L.handle, T, mode)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(W):
+        ft.moe_prefill(ctx, L.handle, xs[i % 2], T, y, mode, ws, nbytes, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ft.moe_prefill(ctx, L.handle, xs[i % 2], T, y, mode, ws, nbytes, s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"[bench] timed {K} prefill steps in {dt * 1e3:.1f} ms")
+    ft.profile_begin(L.handle, K)
+    for i in range(K):
+        ft.moe_prefill(ctx, L.handle, xs[i % 2], T, y, mode, ws, nbytes, s)
+    torch.cuda.synchronize()
+    gu_us, dn_us, nrec = ft.profile_end(L.handle)
+    pairs = T * cfg.k
+    fl_gu = 2.0 * pairs * 2 * cfg.I * cfg.H
+    fl_dn = 2.0 * pairs * cfg.H * cfg.I
+    step_s = dt / K
+    gu_tf = fl_gu / (gu_us * 1e-6) / 1e12
+    res = {
+        "metric": METRIC, "value": T * K / dt, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k, "weights": cfg.fmt,
+                   "mode": "exact-bf16-mfma"},
+        "roofline": {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
+                     "flops_per_launch": fl_gu, "timing": "dispatch-events"},
+        "layer": {"flops_per_step": fl_gu + fl_dn,
+                  "TFLOPs_per_step": (fl_gu + fl_dn) / step_s / 1e12,
+                  "fp4_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / FP4_PEAK_TFLOPS,
+                  "bf16_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / BF16_PEAK_TFLOPS,
+                  "down_kernel_us": dn_us,
+                  "down_TFLOPs": fl_dn / (dn_us * 1e-6) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, xh[0], args.cpu_seconds)
+    L.close()
+    ctx.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +363,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.workload == "miss-path-284b":
         res = bench_miss_path(args, wl)
+    elif args.workload == "prefill-753b":
+        res = bench_prefill(args, wl)
     else:
         res = bench_decode(args, wl)
     print(json.dumps(res), flush=True)

@@ -203,6 +203,10 @@ FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, const void*
 FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
                                  int32_t* counts, int32_t* offsets, int32_t* pos,
                                  void* stream);
+/* Routing of the last ft_moe_prefill call: idx [T][k] (device int32) and w [T][k] (device
+ * fp32), copied from the workspace `ws` of that call. */
+FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* ws, int T, int32_t* idx,
+                                  float* w, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ OUT = os.path.join(HERE, "libft.so")
 BUILD = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["ft_decode.hip", "ft_debug.hip"]
+HIP_SOURCES = ["ft_decode.hip", "ft_prefill.hip", "ft_debug.hip"]
 CXX_SOURCES = ["ft_api.cpp", "ft_host.cpp"]
 
 HIPCC_FLAGS = [

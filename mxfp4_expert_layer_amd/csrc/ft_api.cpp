@@ -25,6 +25,8 @@ extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, 
                            float* y, hipStream_t st);
 extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
                            float* out, hipStream_t st);
+extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes, hipStream_t st);
+extern "C" int ftk_prefill(const PrefillLaunch* a, hipStream_t st, const hipEvent_t* ev);
 
 namespace {
 
@@ -71,6 +73,7 @@ struct ft_layer {
   float* P = nullptr;
   int32_t* e2s_dev = nullptr;
   int32_t* s2e_dev = nullptr;
+  uint16_t* wr_planes = nullptr;  // [3][E][H] bf16 split of router_w (prefill router)
   // pinned host staging
   void* pin = nullptr;
   int32_t* idx_h = nullptr;
@@ -253,6 +256,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   add((size_t)T * l->kk * d.H * 4);                // P
   add((size_t)d.E * 4);
   add((size_t)d.n_slots * 4);
+  add((size_t)3 * d.E * d.H * 2);                  // router planes
   if (hipMalloc(&l->dev, need) != hipSuccess)
     return fail(FT_ENOMEM, "ft_layer_create: device workspace allocation failed");
   HIP_TRY(hipMemset(l->dev, 0, need));
@@ -266,6 +270,9 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   l->P = carve<float>(p, (size_t)T * l->kk * d.H);
   l->e2s_dev = carve<int32_t>(p, d.E);
   l->s2e_dev = carve<int32_t>(p, d.n_slots);
+  l->wr_planes = carve<uint16_t>(p, (size_t)3 * d.E * d.H);
+  HIP_TRY((hipError_t)ftk_split_router(d.router_w, d.E, d.H, l->wr_planes, nullptr));
+  HIP_TRY(hipDeviceSynchronize());
 
   size_t pneed = 0;
   auto padd = [&](size_t bytes) { pneed += align_up(bytes, 256); };
@@ -688,23 +695,125 @@ extern "C" FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, 
 }
 
 // ---- prefill ------------------------------------------------------------------------------
+// Workspace layout of one prefill call (every region 256-byte aligned); returns the bytes.
+static size_t prefill_carve(const ft_layer* l, int T, uint8_t* base, PrefillLaunch* a) {
+  const ft_layer_desc& d = l->d;
+  const size_t nblk = (size_t)(T + kPermBlock - 1) / kPermBlock;
+  const size_t pairs = (size_t)T * d.k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* r = base ? base + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  uint8_t* logits = take((size_t)T * d.E * 4);
+  uint8_t* idx = take(pairs * 4);
+  uint8_t* w = take(pairs * 4);
+  uint8_t* masks = take(nblk * d.E * 8 * 4);
+  uint8_t* bcnt = take(nblk * d.E * 4);
+  uint8_t* counts = take((size_t)d.E * 4);
+  uint8_t* offsets = take((size_t)(d.E + 1) * 4);
+  uint8_t* bas = take(nblk * d.E * 4);
+  uint8_t* tb_off = take((size_t)(d.E + 1) * 4);
+  uint8_t* pos = take(pairs * 4);
+  uint8_t* perm_tok = take(pairs * 4);
+  uint8_t* hperm = take(pairs * d.I * 2);
+  uint8_t* yperm = take(pairs * d.H * 4);
+  if (a) {
+    a->logits = (float*)logits;
+    a->idx = (int32_t*)idx;
+    a->w = (float*)w;
+    a->masks = (uint32_t*)masks;
+    a->bcnt = (int32_t*)bcnt;
+    a->counts = (int32_t*)counts;
+    a->offsets = (int32_t*)offsets;
+    a->base = (int32_t*)bas;
+    a->tb_off = (int32_t*)tb_off;
+    a->pos = (int32_t*)pos;
+    a->perm_tok = (int32_t*)perm_tok;
+    a->hperm = (uint16_t*)hperm;
+    a->Yperm = (float*)yperm;
+  }
+  return off;
+}
+
+static int prefill_check(const ft_layer* layer, int T, int mode, const char* who) {
+  if (!layer) return fail(FT_EINVAL, std::string(who) + ": null layer");
+  if (T < 1 || (int64_t)T * layer->d.k > (int64_t)1 << 28)
+    return fail(FT_EINVAL, std::string(who) + ": T out of range");
+  if (mode != FT_PREFILL_EXACT && mode != FT_PREFILL_MXFP4)
+    return fail(FT_EINVAL, std::string(who) + ": unknown mode");
+  if (mode == FT_PREFILL_MXFP4)
+    return fail(FT_EUNSUPPORTED, std::string(who) + ": the MXFP4-activation mode is not built");
+  if (!layer->all_resident)
+    return fail(FT_ESTATE, std::string(who) + ": prefill needs an all-resident layer");
+  if (layer->d.n_shared > 0)
+    return fail(FT_EUNSUPPORTED, std::string(who) + ": prefill of layers with shared experts "
+                                                    "is not built");
+  return FT_OK;
+}
+
 extern "C" FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T, int mode,
                                                     size_t* bytes) {
-  (void)layer; (void)T; (void)mode; (void)bytes;
-  return fail(FT_EUNSUPPORTED, "ft_moe_prefill_workspace_size: prefill not built yet");
+  int rc = prefill_check(layer, T, mode, "ft_moe_prefill_workspace_size");
+  if (rc) return rc;
+  if (!bytes) return fail(FT_EINVAL, "ft_moe_prefill_workspace_size: bytes is null");
+  *bytes = prefill_carve(layer, T, nullptr, nullptr);
+  return FT_OK;
 }
 
 extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
                                      float* y, int mode, void* ws, size_t ws_bytes,
                                      void* stream) {
-  (void)ctx; (void)layer; (void)x; (void)T; (void)y; (void)mode; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return fail(FT_EUNSUPPORTED, "ft_moe_prefill: prefill not built yet");
+  int rc = prefill_check(layer, T, mode, "ft_moe_prefill");
+  if (rc) return rc;
+  if (!ctx || !x || !y || !ws) return fail(FT_EINVAL, "ft_moe_prefill: null argument");
+  if (layer->ctx != ctx) return fail(FT_EINVAL, "ft_moe_prefill: layer of another context");
+  if ((uintptr_t)ws % 256) return fail(FT_EINVAL, "ft_moe_prefill: ws must be 256-byte aligned");
+  const size_t need = prefill_carve(layer, T, nullptr, nullptr);
+  if (ws_bytes < need) return fail(FT_EINVAL, "ft_moe_prefill: workspace too small");
+  const ft_layer_desc& d = layer->d;
+  HIP_TRY(hipSetDevice(ctx->device));
+  PrefillLaunch a{};
+  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  a.x = x;
+  a.T = T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
+  a.wr_planes = layer->wr_planes;
+  a.router_b = d.router_b;
+  a.pool = (const uint8_t*)d.pool;
+  a.stride = d.blob_stride;
+  a.L = layer->L;
+  a.y = y;
+  HIP_TRY((hipError_t)ftk_prefill(&a, (hipStream_t)stream, prof_events(layer)));
+  return FT_OK;
 }
 
 extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
                                             int32_t* counts, int32_t* offsets, int32_t* pos,
                                             void* stream) {
-  (void)layer; (void)ws; (void)T; (void)counts; (void)offsets; (void)pos; (void)stream;
-  return fail(FT_EUNSUPPORTED, "ft_debug_prefill_perm: prefill not built yet");
+  if (!layer || !ws || !counts || !offsets || !pos || T < 1)
+    return fail(FT_EINVAL, "ft_debug_prefill_perm: bad argument");
+  PrefillLaunch a{};
+  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  const ft_layer_desc& d = layer->d;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  HIP_TRY(hipMemcpyAsync(counts, a.counts, (size_t)d.E * 4, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipMemcpyAsync(offsets, a.offsets, (size_t)(d.E + 1) * 4, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipMemcpyAsync(pos, a.pos, (size_t)T * d.k * 4, hipMemcpyDeviceToDevice, st));
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* ws, int T,
+                                             int32_t* idx, float* w, void* stream) {
+  if (!layer || !ws || !idx || !w || T < 1)
+    return fail(FT_EINVAL, "ft_debug_prefill_route: bad argument");
+  PrefillLaunch a{};
+  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t n = (size_t)T * layer->d.k * 4;
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  HIP_TRY(hipMemcpyAsync(idx, a.idx, n, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipMemcpyAsync(w, a.w, n, hipMemcpyDeviceToDevice, st));
+  return FT_OK;
 }

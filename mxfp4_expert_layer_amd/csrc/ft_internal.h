@@ -96,4 +96,34 @@ struct DecodeLaunch {
   float* P;                     // [T * (k + n_shared)][H]
 };
 
+// Prefill of T tokens through an all-resident layer (slot e = expert e).
+constexpr int kPermBlock = 256;   // tokens per permutation block (one mask word per 32)
+constexpr int kGemmM = 128;       // tokens per grouped-GEMM block
+constexpr int kGemmN = 128;       // weight rows per grouped-GEMM block
+
+struct PrefillLaunch {
+  const uint16_t* x;            // device bf16 [T][H]
+  int T, H, I, E, k;
+  const uint16_t* wr_planes;    // [3][E][H] bf16, exact split of the fp32 router weights
+  const float* router_b;        // [E] or null
+  const uint8_t* pool;          // slot e holds expert e
+  uint64_t stride;
+  BlobLayout L;
+  // workspace (caller-owned, carved by the host)
+  float* logits;                // [T][E]
+  int32_t* idx;                 // [T][k]
+  float* w;                     // [T][k]
+  uint32_t* masks;              // [T/256][E][8] token bitmasks per permutation block
+  int32_t* bcnt;                // [T/256][E]
+  int32_t* counts;              // [E]
+  int32_t* offsets;             // [E+1]
+  int32_t* base;                // [T/256][E]
+  int32_t* tb_off;              // [E+1] 128-row token blocks per expert, prefix
+  int32_t* pos;                 // [T][k]
+  int32_t* perm_tok;            // [T*k]
+  uint16_t* hperm;              // [T*k][I] bf16
+  float* Yperm;                 // [T*k][H]
+  float* y;                     // [T][H]
+};
+
 }  // namespace ft

@@ -73,6 +73,7 @@ _sig = {
     "ft_debug_tables": [_vp, _vp, _vp],
     "ft_host_expert_ffn": [_vp, _i, _i, _i, _vp, _vp, _i, _vp],
     "ft_debug_prefill_perm": [_vp, _vp, _i, _vp, _vp, _vp, _vp],
+    "ft_debug_prefill_route": [_vp, _vp, _i, _vp, _vp, _vp],
     "ft_profile_begin": [_vp, _i],
     "ft_profile_end": [_vp, C.POINTER(_d), C.POINTER(_d), C.POINTER(_i)],
 }
@@ -226,3 +227,7 @@ def profile_end(layer_h):
     a, b, n = C.c_double(), C.c_double(), C.c_int()
     check(lib.ft_profile_end(layer_h, C.byref(a), C.byref(b), C.byref(n)))
     return a.value, b.value, n.value
+
+
+def debug_prefill_route(layer_h, ws, T, idx, w, stream=None):
+    check(lib.ft_debug_prefill_route(layer_h, _ptr(ws), T, _ptr(idx), _ptr(w), stream))

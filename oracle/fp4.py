@@ -58,18 +58,32 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     return out
 
 
+def _element_values(codes: np.ndarray) -> np.ndarray:
+    """E2M1 values [R][K] of packed codes [R][K/2]: the closed form above evaluated once per
+    code (16 values) and indexed, low nibble = even element."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = e2m1_value(np.arange(16))
+    R, half = codes.shape
+    out = np.empty((R, 2 * half), dtype=np.float64)
+    out[:, 0::2] = table[codes & 0xF]
+    out[:, 1::2] = table[codes >> 4]
+    return out
+
+
 def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """MXFP4 matrix: value[r][k] = E2M1(code[r][k]) * E8M0(scale[r][k // 32])."""
-    v = e2m1_value(unpack_codes(codes))
-    s = e8m0_value(scales)
-    return v * np.repeat(s, 32, axis=1)
+    v = _element_values(codes)
+    R, K = v.shape
+    s = e8m0_value(np.asarray(scales, dtype=np.int64))
+    return (v.reshape(R, K // 32, 32) * s[:, :, None]).reshape(R, K)
 
 
 def dequant_nvfp4(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
     """NVFP4 matrix: value[r][k] = E2M1(code[r][k]) * E4M3(scale[r][k // 16]) * tensor_scale."""
-    v = e2m1_value(unpack_codes(codes))
-    s = e4m3_value(scales)
-    return v * np.repeat(s, 16, axis=1) * np.float64(tensor_scale)
+    v = _element_values(codes)
+    R, K = v.shape
+    s = e4m3_value(np.asarray(scales, dtype=np.int64))
+    return (v.reshape(R, K // 16, 16) * s[:, :, None]).reshape(R, K) * np.float64(tensor_scale)
 
 
 def dequant(fmt: str, codes, scales, tensor_scale=1.0) -> np.ndarray:
