@@ -363,7 +363,11 @@ static DecodeLaunch launch_args(ft_layer* l, const uint16_t* x, int T, int route
 static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipStream_t st) {
   const ft_layer_desc& d = l->d;
   HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, d.E, l->logits, st));
-  const DecodeLaunch a = launch_args(l, x, T, 1, l->items, l->n_items, T * d.k + d.n_shared);
+  // few tokens: the gate/up kernel takes the top-k itself (one launch less); more tokens:
+  // a top-k kernel with one wave per token first, so no workgroup routes tokens serially
+  const int route = T <= 2 ? 1 : 2;
+  if (route == 2) HIP_TRY((hipError_t)ftk_topk(l->logits, T, d.E, d.k, l->idx, l->w, st));
+  const DecodeLaunch a = launch_args(l, x, T, route, l->items, l->n_items, T * d.k + d.n_shared);
   HIP_TRY((hipError_t)ftk_decode_experts(&a, st, prof_events(l)));
   HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
   return FT_OK;

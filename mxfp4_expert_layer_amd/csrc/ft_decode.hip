@@ -247,11 +247,12 @@ __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int 
   __syncthreads();
 }
 
-// Publish the routing and the list for the next kernel (global memory).
+// Publish the routing (when write_route) and the list for the next kernel (global memory).
 __device__ void store_route(const TopkLds& tk, const ListLds& L, int T, int k, int n_shared,
-                            int32_t* idx_out, float* w_out, WorkItem* items, int* n_items) {
+                            int32_t* idx_out, float* w_out, WorkItem* items, int* n_items,
+                            bool write_route) {
   const int tid = threadIdx.x, kk = k + n_shared;
-  if (tid < T * k) {
+  if (write_route && tid < T * k) {
     idx_out[tid] = tk.idx[tid / k][tid % k];
     w_out[tid] = tk.w[tid / k][tid % k];
   }
@@ -282,18 +283,21 @@ __device__ void load_list(const WorkItem* items, const int* n_items, ListLds& L)
   __syncthreads();
 }
 
-// Single-workgroup top-k (ft_route and the miss path): idx/w to global.
+// Top-k kernel (batched decode, ft_route and the miss path): one wave per token, four
+// tokens per workgroup, idx/w to global.
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float* logits, int T, int E, int k,
                                               int32_t* idx_out, float* w_out) {
   __shared__ TopkLds tk;
   __shared__ float c_val[kMaxCols][FT_MAX_TOPK];
   __shared__ int c_idx[kMaxCols][FT_MAX_TOPK];
-  topk_tokens<EPL>(logits, T, E, k, tk, c_val, c_idx);
+  const int t0 = blockIdx.x * 4;
+  const int nt = min(4, T - t0);
+  topk_tokens<EPL>(logits + (uint64_t)t0 * E, nt, E, k, tk, c_val, c_idx);
   const int tid = threadIdx.x;
-  if (tid < T * k) {
-    idx_out[tid] = tk.idx[tid / k][tid % k];
-    w_out[tid] = tk.w[tid / k][tid % k];
+  if (tid < nt * k) {
+    idx_out[(uint64_t)t0 * k + tid] = tk.idx[tid / k][tid % k];
+    w_out[(uint64_t)t0 * k + tid] = tk.w[tid / k][tid % k];
   }
 }
 
@@ -352,19 +356,28 @@ __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uin
 // Workgroup = 4 waves.  KSPLIT waves share one 16-row tile and split its K chunks; the
 // workgroup covers 4 / KSPLIT row tiles.  A unit is (item, group of row tiles); workgroups
 // walk the units with a grid stride.
+// EPL > 0: the prologue takes the top-k of the logits (E <= 64 * EPL); EPL == 0: the
+// work list is read from memory (miss path); EPL < 0: the list is built from the routed
+// indices a previous k_topk wrote.  Workgroup 0 publishes the list for k_down.
 template <int KSPLIT, int UNR, int EPL>
 __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
   constexpr int RPW = 4 / KSPLIT;
-  constexpr bool ROUTE = EPL > 0;
   __shared__ TopkLds tk;
   __shared__ ListLds ls;
   __shared__ f32x4 red[4][2][64];
-  if (ROUTE) {
-    topk_tokens<(ROUTE ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk, (float (*)[FT_MAX_TOPK])&red[0][0][0],
-                                    (int (*)[FT_MAX_TOPK])&red[2][0][0]);
+  if (EPL > 0) {
+    topk_tokens<(EPL > 0 ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk,
+                                     (float (*)[FT_MAX_TOPK])&red[0][0][0],
+                                     (int (*)[FT_MAX_TOPK])&red[2][0][0]);
     build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
     if (blockIdx.x == 0)
-      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items);
+      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items, true);
+  } else if (EPL < 0) {
+    if (threadIdx.x < a.T * a.k) tk.idx[threadIdx.x / a.k][threadIdx.x % a.k] = a.idx_out[threadIdx.x];
+    __syncthreads();
+    build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
+    if (blockIdx.x == 0)
+      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items, false);
   } else {
     load_list(a.items, a.n_items, ls);
   }
@@ -504,14 +517,15 @@ extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, in
 
 extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_out, float* w_out,
                         hipStream_t st) {
+  const dim3 grid((T + 3) / 4);
   if (E <= 64)
-    hipLaunchKernelGGL(k_topk<1>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+    hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
   else if (E <= 128)
-    hipLaunchKernelGGL(k_topk<2>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+    hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
   else if (E <= 256)
-    hipLaunchKernelGGL(k_topk<4>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+    hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
   else
-    hipLaunchKernelGGL(k_topk<16>, dim3(1), dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+    hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
   return (int)hipGetLastError();
 }
 
@@ -524,7 +538,8 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
     else hipLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, arg);                             \
   } while (0)
 
-// EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts
+// EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts;
+// EPL < 0: list built from routed indices
 template <int EPL>
 static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const int cap = 2048, KC = a.H / kTileK, RT = a.I / kTileRows;
@@ -540,7 +555,8 @@ extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const 
   const DecodeLaunch& a = *ap;
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-  if (!a.route) launch_gateup<0>(a, st, e0, e1);
+  if (a.route == 0) launch_gateup<0>(a, st, e0, e1);
+  else if (a.route == 2) launch_gateup<-1>(a, st, e0, e1);
   else if (a.E <= 64) launch_gateup<1>(a, st, e0, e1);
   else if (a.E <= 128) launch_gateup<2>(a, st, e0, e1);
   else if (a.E <= 256) launch_gateup<4>(a, st, e0, e1);

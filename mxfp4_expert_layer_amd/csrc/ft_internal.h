@@ -80,7 +80,8 @@ struct WorkItem {
 struct DecodeLaunch {
   const uint16_t* x;            // device bf16 tokens [T][H]
   int T, H, I, E, k, n_shared;
-  int route;                    // 1: top-k + work list from `logits` (resident decode)
+  int route;                    // 0: work list from `items`; 1: top-k + list from `logits`;
+                                // 2: list from the routed indices in `idx_out`
   const float* logits;          // [T][E] (route)
   const int32_t* e2s;           // [E] (route)
   int32_t* idx_out;             // [T][k] (route: written by workgroup 0)

@@ -305,6 +305,24 @@ __device__ __forceinline__ void decode_tile_lane(int fmt, const uint8_t* codes, 
   }
 }
 
+__device__ __forceinline__ void decode_tile_regs(int fmt, uint4 c, uint32_t sc0, uint32_t sc1,
+                                                 uint4 out[4]) {
+  const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
+  if (fmt == FT_MXFP4) {
+    const float s = e8m0_f32(sc0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(uint4, fp4x8_bf16(wv[i], s));
+  } else {
+    const float s0 = e4m3_f32(sc0), s1 = e4m3_f32(sc1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = i < 2 ? s0 : s1;
+      out[i] = make_uint4(nv_pair(wv[i], s, 0), nv_pair(wv[i], s, 1), nv_pair(wv[i], s, 2),
+                          nv_pair(wv[i], s, 3));
+    }
+  }
+}
+
 __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
   return ((const BlobHeader*)blob)->tensor_scale[m];
 }
@@ -373,14 +391,32 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < KC; ++kc) {
-    // token tile: 8 x 16 B per thread
-    uint4 xv[8];
+  // software pipeline: the global loads of chunk kc + 1 (token tile rows and this wave's
+  // two weight tiles) are in flight while the MFMAs of chunk kc run
+  uint4 xv[8], cw[2];
+  uint32_t sc[2][2];
+  auto load_chunk = [&](int kc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) xv[i] = *(const uint4*)(src + kc * kTileK + sh * 64 + 8 * i);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint64_t tile = wrow[d] + kc;
+      cw[d] = ((const uint4*)wc[d])[tile * 64 + lane];
+      if (fmt == FT_MXFP4) {
+        sc[d][0] = wsc[d][tile * 64 + lane];
+        sc[d][1] = 0u;
+      } else {
+        sc[d][0] = wsc[d][tile * 128 + 2 * lane];
+        sc[d][1] = wsc[d][tile * 128 + 2 * lane + 1];
+      }
+    }
+  };
+  load_chunk(0);
+  for (int kc = 0; kc < KC; ++kc) {
     uint4 dq[2][4];
 #pragma unroll
-    for (int d = 0; d < 2; ++d) decode_tile_lane(fmt, wc[d], wsc[d], wrow[d] + kc, lane, dq[d]);
+    for (int d = 0; d < 2; ++d) decode_tile_regs(fmt, cw[d], sc[d][0], sc[d][1], dq[d]);
+    __syncthreads();  // the previous chunk's MFMAs are done with the LDS tiles
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *(uint4*)&xs[sr][sh * 64 + 8 * i] = srow ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
@@ -389,6 +425,7 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ws[2 * wave + d][i][lane] = dq[d][i];
     __syncthreads();
+    if (kc + 1 < KC) load_chunk(kc + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x8 A[4], B[4];
@@ -403,7 +440,6 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
         for (int t = 0; t < 4; ++t)
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], B[t], acc[j][t], 0, 0, 0);
     }
-    __syncthreads();
   }
 
   if (MODE == 0) {
