@@ -47,6 +47,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {
+    "decode": ["ft_internal.h", "ft_device.h", "ft_decode.hip"],
+    "prefill": ["ft_internal.h", "ft_device.h", "ft_prefill.hip"],
+}
+
+
+def kernel_sources_sha(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "mxfp4_expert_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key, kind):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy) from
+    profiles/hbm_traffic.json, or None when the kernel sources changed since the counters
+    were taken (or no counters were recorded)."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as fh:
+            rec = json.load(fh)["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha(kind):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def cpu_baseline(cfg, x_batches, seconds):
     """Time the float64 oracle (as it stands) on decode steps of the same workload."""
     import numpy as np
@@ -71,7 +100,7 @@ def cpu_baseline(cfg, x_batches, seconds):
         moe.moe_forward(OL, xb)
         tokens += xb.shape[0]
         n += 1
-        if time.perf_counter() - t0 >= seconds or n >= 4 * len(todo):
+        if time.perf_counter() - t0 >= seconds or n >= 4096:
             break
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -135,12 +164,12 @@ def bench_decode(args, wl):
 
     # dominant kernel: start/stop events recorded by the gate/up dispatches themselves, over
     # an eager pass of the same steps (events cannot be timed inside a captured graph).  The
-    # stream first runs a 20 ms spin kernel, so every step is queued before the GPU reaches
+    # stream first runs a 250 ms spin kernel, so every step is queued before the GPU reaches
     # it and the steps run back to back as in a replay, whatever the host's launch speed.
     for h in L.handles:
         ft.profile_begin(h, G // copies + 1)
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(2.4e9 * 0.02))
+        torch.cuda._sleep(int(2.4e9 * 0.25))
         for i in range(G):
             step(i, stream)
     torch.cuda.synchronize()
@@ -179,7 +208,8 @@ def bench_decode(args, wl):
                    "tokens_per_step": T, "weights": cfg.fmt, "layer_copies": copies,
                    "graph_replay": True},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"k_gateup@{args.workload}-T{T}", "decode"),
                      "kernel": "k_gateup", "kernel_us": gate_us, "timing": prof_mode,
                      "bytes_per_launch": n_exp * gu_bytes_expert},
         "layer": {"algorithmic_bytes_per_step": step_bytes,
@@ -189,7 +219,7 @@ def bench_decode(args, wl):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(cfg, xh[:4], args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, xh, args.cpu_seconds)
     L.close()
     ctx.close()
     return res
@@ -202,7 +232,10 @@ def bench_miss_path(args, wl):
     from mxfp4_expert_layer_amd import ft, synth
     from mxfp4_expert_layer_amd.layer import GpuLayer
 
+    import dataclasses
     cfg = synth.CONFIGS[wl["cfg"]]
+    if args.zipf_c is not None:
+        cfg = dataclasses.replace(cfg, zipf_c=args.zipf_c)
     K = args.steps if args.steps is not None else wl["steps"]
     W = args.warmup if args.warmup is not None else wl["warmup"]
     ctx = ft.Context(0)
@@ -330,7 +363,8 @@ def bench_prefill(args, wl):
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k, "weights": cfg.fmt,
                    "mode": "exact-bf16-mfma"},
         "roofline": {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(f"k_ggemm<0>@{args.workload}", "prefill"),
                      "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
                      "flops_per_launch": fl_gu, "timing": "dispatch-events"},
         "layer": {"flops_per_step": fl_gu + fl_dn,
@@ -377,6 +411,8 @@ def main():
     ap.add_argument("--copies", type=int, default=None, help="device copies of the layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--zipf-c", type=float, default=None,
+                    help="miss path: router bias strength c of b_e = -c ln(rank_e)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

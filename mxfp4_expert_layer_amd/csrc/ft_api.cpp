@@ -19,7 +19,8 @@ using namespace ft;
 extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, int T, int H, int E,
                           float* logits, hipStream_t st);
 extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_out, float* w_out,
-                        hipStream_t st);
+                        int32_t* idx_host, float* w_host, const uint16_t* x, uint16_t* x_host,
+                        int H, hipStream_t st);
 extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
                            float* y, hipStream_t st);
@@ -76,6 +77,7 @@ struct ft_layer {
   uint16_t* wr_planes = nullptr;  // [3][E][H] bf16 split of router_w (prefill router)
   // pinned host staging
   void* pin = nullptr;
+  uint8_t* pin_dev = nullptr;    // device address of the mapped pinned staging
   int32_t* idx_h = nullptr;
   float* w_h = nullptr;
   uint16_t* x_h = nullptr;
@@ -85,6 +87,7 @@ struct ft_layer {
   int32_t* e2s_h = nullptr;
   int32_t* s2e_h = nullptr;
   hipEvent_t ev_copy = nullptr;
+  hipEvent_t ev_route = nullptr;
   // policy state
   LruState lru;
   double bp = 0.0, bh = 0.0;
@@ -207,6 +210,7 @@ static void free_layer(ft_layer* l) {
   if (!l) return;
   for (hipEvent_t e : l->prof) hipEventDestroy(e);
   if (l->ev_copy) hipEventDestroy(l->ev_copy);
+  if (l->ev_route) hipEventDestroy(l->ev_route);
   if (l->dev) hipFree(l->dev);
   if (l->pin) hipHostFree(l->pin);
   delete l;
@@ -283,8 +287,13 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   padd((size_t)T * l->kk * d.H * 4);
   padd((size_t)d.E * 4);
   padd((size_t)d.n_slots * 4);
-  if (hipHostMalloc(&l->pin, pneed, hipHostMallocDefault) != hipSuccess)
+  if (hipHostMalloc(&l->pin, pneed, hipHostMallocMapped) != hipSuccess)
     return fail(FT_ENOMEM, "ft_layer_create: pinned staging allocation failed");
+  {
+    void* dp = nullptr;
+    HIP_TRY(hipHostGetDevicePointer(&dp, l->pin, 0));
+    l->pin_dev = (uint8_t*)dp;
+  }
   uint8_t* q = (uint8_t*)l->pin;
   l->idx_h = carve<int32_t>(q, (size_t)T * d.k);
   l->w_h = carve<float>(q, (size_t)T * d.k);
@@ -302,6 +311,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipMemcpy(l->e2s_dev, l->e2s_h, (size_t)d.E * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipMemcpy(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_copy, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&l->ev_route, hipEventDisableTiming));
   *out = l.release();
   return FT_OK;
 }
@@ -333,7 +343,8 @@ extern "C" FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_
   HIP_TRY(hipSetDevice(ctx->device));
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, d.E, layer->logits, st));
-  HIP_TRY((hipError_t)ftk_topk(layer->logits, T, d.E, d.k, idx, w, st));
+  HIP_TRY((hipError_t)ftk_topk(layer->logits, T, d.E, d.k, idx, w, nullptr, nullptr, nullptr,
+                               nullptr, d.H, st));
   return FT_OK;
 }
 
@@ -366,7 +377,9 @@ static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipS
   // few tokens: the gate/up kernel takes the top-k itself (one launch less); more tokens:
   // a top-k kernel with one wave per token first, so no workgroup routes tokens serially
   const int route = T <= 2 ? 1 : 2;
-  if (route == 2) HIP_TRY((hipError_t)ftk_topk(l->logits, T, d.E, d.k, l->idx, l->w, st));
+  if (route == 2)
+    HIP_TRY((hipError_t)ftk_topk(l->logits, T, d.E, d.k, l->idx, l->w, nullptr, nullptr, nullptr,
+                                 nullptr, d.H, st));
   const DecodeLaunch a = launch_args(l, x, T, route, l->items, l->n_items, T * d.k + d.n_shared);
   HIP_TRY((hipError_t)ftk_decode_experts(&a, st, prof_events(l)));
   HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
@@ -387,11 +400,12 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   ft_decode_stats S{};
   auto t0 = clk::now();
   HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, E, l->logits, st));
-  HIP_TRY((hipError_t)ftk_topk(l->logits, T, E, k, l->idx, l->w, st));
-  HIP_TRY(hipMemcpyAsync(l->idx_h, l->idx, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipMemcpyAsync(l->w_h, l->w, (size_t)T * k * 4, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipMemcpyAsync(l->x_h, x, (size_t)T * d.H * 2, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipStreamSynchronize(st));
+  // the top-k kernel writes idx, w and the token rows into the mapped pinned staging
+  auto dev_of = [&](const void* hp) { return l->pin_dev + ((const uint8_t*)hp - (const uint8_t*)l->pin); };
+  HIP_TRY((hipError_t)ftk_topk(l->logits, T, E, k, l->idx, l->w, (int32_t*)dev_of(l->idx_h),
+                               (float*)dev_of(l->w_h), x, (uint16_t*)dev_of(l->x_h), d.H, st));
+  HIP_TRY(hipEventRecord(l->ev_route, st));
+  HIP_TRY(hipEventSynchronize(l->ev_route));
   S.wait_us = us_since(t0);
 
   // classify: selected experts with their summed routing weight

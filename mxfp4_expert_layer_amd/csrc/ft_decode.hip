@@ -285,9 +285,14 @@ __device__ void load_list(const WorkItem* items, const int* n_items, ListLds& L)
 
 // Top-k kernel (batched decode, ft_route and the miss path): one wave per token, four
 // tokens per workgroup, idx/w to global.
+// With the host pointers set (mapped pinned memory, miss path), the routing and the
+// workgroup's token rows are also written straight to host memory, so the host reads them
+// after one event wait instead of separate device-to-host copies.
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float* logits, int T, int E, int k,
-                                              int32_t* idx_out, float* w_out) {
+                                              int32_t* idx_out, float* w_out, int32_t* idx_host,
+                                              float* w_host, const uint16_t* x, uint16_t* x_host,
+                                              int H) {
   __shared__ TopkLds tk;
   __shared__ float c_val[kMaxCols][FT_MAX_TOPK];
   __shared__ int c_idx[kMaxCols][FT_MAX_TOPK];
@@ -296,8 +301,19 @@ __global__ __launch_bounds__(256) void k_topk(const float* logits, int T, int E,
   topk_tokens<EPL>(logits + (uint64_t)t0 * E, nt, E, k, tk, c_val, c_idx);
   const int tid = threadIdx.x;
   if (tid < nt * k) {
-    idx_out[(uint64_t)t0 * k + tid] = tk.idx[tid / k][tid % k];
-    w_out[(uint64_t)t0 * k + tid] = tk.w[tid / k][tid % k];
+    const int32_t e = tk.idx[tid / k][tid % k];
+    const float wv = tk.w[tid / k][tid % k];
+    idx_out[(uint64_t)t0 * k + tid] = e;
+    w_out[(uint64_t)t0 * k + tid] = wv;
+    if (idx_host) {
+      idx_host[(uint64_t)t0 * k + tid] = e;
+      w_host[(uint64_t)t0 * k + tid] = wv;
+    }
+  }
+  if (x_host) {
+    const uint32_t* src = (const uint32_t*)(x + (uint64_t)t0 * H);
+    uint32_t* dst = (uint32_t*)(x_host + (uint64_t)t0 * H);
+    for (int i = tid; i < nt * H / 2; i += 256) dst[i] = src[i];
   }
 }
 
@@ -516,16 +532,17 @@ extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, in
 }
 
 extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_out, float* w_out,
-                        hipStream_t st) {
+                        int32_t* idx_host, float* w_host, const uint16_t* x, uint16_t* x_host,
+                        int H, hipStream_t st) {
   const dim3 grid((T + 3) / 4);
-  if (E <= 64)
-    hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
-  else if (E <= 128)
-    hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
-  else if (E <= 256)
-    hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
-  else
-    hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out);
+#define FT_TOPK(EPLV)                                                                     \
+  hipLaunchKernelGGL(k_topk<EPLV>, grid, dim3(256), 0, st, logits, T, E, k, idx_out, w_out, \
+                     idx_host, w_host, x, x_host, H)
+  if (E <= 64) FT_TOPK(1);
+  else if (E <= 128) FT_TOPK(2);
+  else if (E <= 256) FT_TOPK(4);
+  else FT_TOPK(16);
+#undef FT_TOPK
   return (int)hipGetLastError();
 }
 

@@ -1,8 +1,11 @@
 // Host-side pieces of libft: errors, thread pool, host expert FFN, split rule, LRU.
 #include "ft_host.h"
 
+#include <immintrin.h>
+
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 namespace ft {
@@ -149,6 +152,71 @@ static void gemv_tiles(const BlobLayout& L, const uint8_t* codes, const uint8_t*
   }
 }
 
+// AVX-512 (BF16) path for MXFP4 tiles.  Per 32-value lane block: the 16 code bytes expand
+// to 32 nibble indices in 16-bit lanes, which index a 16-entry bf16 table of E2M1 values
+// scaled by the block's E8M0 scale (the scale is added to the exponent field of the nonzero
+// entries, exact for normal results), and vdpbf16ps accumulates the products with the bf16
+// activations into 16 fp32 lanes per row.  acc[row] sums for rows rt*16 .. rt*16+15.
+__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl")))
+static void gemv_tiles_mx_avx512(const uint8_t* codes, const uint8_t* scales, int K, int rt0,
+                                 int rt1, const uint16_t* xb, int T, float* acc_out, int R) {
+  const int KC = K / kTileK;
+  // bf16 bits of E2M1 codes 0..15 (0, .5, 1, 1.5, 2, 3, 4, 6 and their negatives)
+  alignas(64) static const uint16_t kBase[32] = {
+      0x0000, 0x3F00, 0x3F80, 0x3FC0, 0x4000, 0x4040, 0x4080, 0x40C0,
+      0x8000, 0xBF00, 0xBF80, 0xBFC0, 0xC000, 0xC040, 0xC080, 0xC0C0,
+      0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const __m512i base = _mm512_load_si512((const void*)kBase);
+  const __mmask32 nonzero = 0x0000FEFEu;  // entries 1..7 and 9..15
+  const __m512i m15 = _mm512_set1_epi32(15);
+  for (int t = 0; t < T; ++t) {
+    const uint16_t* xt = xb + (uint64_t)t * K;
+    for (int rt = rt0; rt < rt1; ++rt) {
+      __m512 acc[16];
+      for (int r = 0; r < 16; ++r) acc[r] = _mm512_setzero_ps();
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint64_t tile = (uint64_t)rt * KC + kc;
+        const uint8_t* c = codes + tile * kTileCodeBytes;
+        const uint8_t* sc = scales + tile * 64;
+        __m512bh xv[4];
+        for (int g = 0; g < 4; ++g)
+          xv[g] = (__m512bh)_mm512_loadu_si512((const void*)(xt + kc * kTileK + 32 * g));
+        for (int l = 0; l < 64; ++l) {
+          const __m512i bytes = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)(c + 16 * l)));
+          const __m512i idx = _mm512_or_si512(_mm512_and_si512(bytes, m15),
+                                              _mm512_slli_epi32(_mm512_srli_epi32(bytes, 4), 16));
+          const __m512i shift = _mm512_set1_epi16((short)((int)sc[l] - 127) << 7);
+          const __m512i table = _mm512_mask_add_epi16(base, nonzero, base, shift);
+          const __m512bh w = (__m512bh)_mm512_permutexvar_epi16(idx, table);
+          acc[l & 15] = _mm512_dpbf16_ps(acc[l & 15], w, xv[l >> 4]);
+        }
+      }
+      for (int r = 0; r < 16; ++r)
+        acc_out[(uint64_t)t * R + rt * kTileRows + r] += _mm512_reduce_add_ps(acc[r]);
+    }
+  }
+}
+
+static bool have_avx512_bf16() {
+  static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                         __builtin_cpu_supports("avx512bf16");
+  return ok;
+}
+
+// The table trick is exact when every scaled E2M1 value is a normal bf16 number: scale codes
+// 2..253 (0.5 * 2^-125 .. 6 * 2^126).  Other codes (including the NaN code 255) take the
+// scalar path, which follows the format definition for every code.
+static bool mx_scales_in_fast_range(const BlobLayout& L, const uint8_t* blob) {
+  for (int m = 0; m < 3; ++m) {
+    const uint8_t* s = blob + L.off[2 * m + 1];
+    const int R = m == 2 ? L.H : L.I, K = m == 2 ? L.I : L.H;
+    const uint64_t n = (uint64_t)(R / kTileRows) * (K / kTileK) * 64;
+    for (uint64_t i = 0; i < n; ++i)
+      if (s[i] < 2 || s[i] > 253) return false;
+  }
+  return true;
+}
+
 int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
                     const uint16_t* x, int T, float* y) {
   const int H = L.H, I = L.I;
@@ -158,9 +226,40 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
     return fail(FT_EINVAL, "host_expert_ffn: blob header does not match the layer");
   std::vector<float> xs((size_t)T * H), g((size_t)T * I, 0.f), u((size_t)T * I, 0.f),
       h((size_t)T * I);
-  for (size_t i = 0; i < xs.size(); ++i) xs[i] = bf16_to_f32(x[i]);
+  std::vector<uint16_t> hb((size_t)T * I);
   std::fill(y, y + (size_t)T * H, 0.f);
   const int RTg = I / kTileRows, RTd = H / kTileRows;
+  const char* force_scalar = std::getenv("FT_HOST_SCALAR");
+  const bool fast = L.fmt == FT_MXFP4 && have_avx512_bf16() &&
+                    !(force_scalar && *force_scalar == '1') && mx_scales_in_fast_range(L, blob);
+  if (fast) {
+    auto part = [&](int n, int i, int total, int* a, int* b) {
+      *a = (int)((int64_t)total * i / n);
+      *b = (int)((int64_t)total * (i + 1) / n);
+    };
+    auto job = [&](int i, int n) {
+      int a, b;
+      part(n, i, RTg, &a, &b);
+      gemv_tiles_mx_avx512(blob + L.off[0], blob + L.off[1], H, a, b, x, T, g.data(), I);
+      gemv_tiles_mx_avx512(blob + L.off[2], blob + L.off[3], H, a, b, x, T, u.data(), I);
+    };
+    if (pool) pool->run(job); else job(0, 1);
+    for (size_t i = 0; i < hb.size(); ++i) {
+      const float z = g[i];
+      const float hv = round_to_bf16(z / (1.0f + std::exp(-z)) * u[i]);
+      uint32_t bits;
+      std::memcpy(&bits, &hv, 4);
+      hb[i] = (uint16_t)(bits >> 16);
+    }
+    auto job2 = [&](int i, int n) {
+      int a, b;
+      part(n, i, RTd, &a, &b);
+      gemv_tiles_mx_avx512(blob + L.off[4], blob + L.off[5], I, a, b, hb.data(), T, y, H);
+    };
+    if (pool) pool->run(job2); else job2(0, 1);
+    return FT_OK;
+  }
+  for (size_t i = 0; i < xs.size(); ++i) xs[i] = bf16_to_f32(x[i]);
   auto part = [&](int n, int i, int total, int* a, int* b) {
     *a = (int)((int64_t)total * i / n);
     *b = (int)((int64_t)total * (i + 1) / n);

@@ -90,8 +90,11 @@ def test_pack_roundtrip(fmt):
         assert np.array_equal(s, getattr(ex, sn))
 
 
+@pytest.mark.parametrize("scalar", [False, True])
 @pytest.mark.parametrize("fmt,T", [("mxfp4", 1), ("mxfp4", 3), ("nvfp4", 2)])
-def test_host_expert_ffn_matches_oracle(fmt, T):
+def test_host_expert_ffn_matches_oracle(fmt, T, scalar, monkeypatch):
+    """Both host paths (AVX-512 BF16 where the CPU has it, and the scalar one)."""
+    monkeypatch.setenv("FT_HOST_SCALAR", "1" if scalar else "0")
     cfg = synth.small_config(seed=8, H=256, I=128, fmt=fmt, code_dist="normal",
                              nv_tensor_scale=1 / 64)
     ex = synth.gen_expert(cfg, 1)
@@ -116,3 +119,23 @@ def test_bad_arguments_return_einval():
     with pytest.raises(ft.FtError) as e:
         ft.pack_expert("mxfp4", 250, 128, synth.gen_expert(synth.small_config(H=256, I=128), 0))
     assert e.value.code == ft.FT_EINVAL
+
+
+def test_host_expert_ffn_nan_scale_propagates():
+    """E8M0 code 255 is NaN: the outputs that depend on it are NaN (scalar path taken)."""
+    cfg = synth.small_config(seed=8, H=256, I=128, code_dist="normal")
+    ex = synth.gen_expert(cfg, 2)
+    ex.down_scales = ex.down_scales.copy()
+    ex.down_scales[5, 1] = 255
+    blob = ft.pack_expert("mxfp4", cfg.H, cfg.I, ex)
+    y = ft.host_expert_ffn("mxfp4", cfg.H, cfg.I, blob, synth.gen_tokens(cfg, 1))
+
+    class _L:
+        pass
+    L = _L()
+    L.cfg = cfg
+    wg, wu, wd = moe.expert_weights(L, ex)
+    ref = moe.swiglu_ffn(fp4.bf16_bits_to_f64(synth.gen_tokens(cfg, 1)), wg, wu, wd)
+    assert np.array_equal(np.isnan(y), np.isnan(ref)) and np.isnan(y[0, 5])
+    fin = ~np.isnan(ref)
+    assert moe.rel_l2(y[fin], ref[fin]) <= 1e-3
