@@ -38,7 +38,9 @@ WORKLOADS = {
     "decode-284b": dict(cfg="cfg3", T=1, copies=4, steps=2048, warmup=128),
     "miss-path-284b": dict(cfg="cfg4", T=1, copies=1, steps=64, warmup=64),
     "prefill-753b": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3),
+    "prefill-753b-mxfp4": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3, mode="mxfp4"),
 }
+HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0
 
@@ -286,8 +288,10 @@ def bench_miss_path(args, wl):
     return res
 
 
-def cpu_baseline_prefill(cfg, x, seconds):
-    """The float64 oracle on a sample of the prefill tokens (experts drawn beforehand)."""
+def cpu_baseline_prefill(cfg, x, seconds, mode="exact"):
+    """The float64 oracle on a sample of the prefill tokens (experts drawn beforehand).  The
+    "mxfp4" mode requantises every selected expert's weights, so its sample is one token with
+    the experts evaluated on 16 threads."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -295,7 +299,8 @@ def cpu_baseline_prefill(cfg, x, seconds):
     from oracle import fp4, moe
 
     OL = synth.gen_layer(cfg, experts=None)
-    n_tok = 2
+    n_tok = 2 if mode == "exact" else 1
+    threads = 1 if mode == "exact" else 16
     xs = x[:n_tok]
     idx, _, _, _ = moe.route(fp4.bf16_bits_to_f64(xs), OL.router_w, OL.router_b, cfg.k)
     for e in np.unique(idx):
@@ -303,16 +308,17 @@ def cpu_baseline_prefill(cfg, x, seconds):
     t0 = time.perf_counter()
     reps = 0
     while True:
-        moe.moe_forward(OL, xs)
+        moe.moe_forward(OL, xs, mode=mode, threads=threads)
         reps += 1
         if time.perf_counter() - t0 >= seconds or reps >= 3:
             break
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": reps * n_tok / dt, "unit": "tokens/s", "cores": max(blas) if blas else 1,
+    cores = max(blas) if blas else 1
+    return {"value": reps * n_tok / dt, "unit": "tokens/s", "cores": max(cores, threads),
             "kind": "oracle",
             "sample": f"{reps} x {n_tok} of the 4096 prefill tokens (float64 numpy oracle, "
-                      f"{dt:.1f} s)"}
+                      f"mode {mode}, {dt:.1f} s)"}
 
 
 def bench_prefill(args, wl):
@@ -327,12 +333,13 @@ def bench_prefill(args, wl):
     K = args.steps if args.steps is not None else wl["steps"]
     W = args.warmup if args.warmup is not None else wl["warmup"]
     ctx = ft.Context(0)
+    s1 = wl.get("mode") == "mxfp4"
     log(f"[bench] building {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I}, {cfg.fmt})")
-    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16)
+    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16, prefill_mxfp4=s1)
     xh = [synth.gen_tokens(cfg, T, batch=b) for b in range(2)]
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xh]
     y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
-    mode = ft.FT_PREFILL_EXACT
+    mode = ft.FT_PREFILL_MXFP4 if s1 else ft.FT_PREFILL_EXACT
     nbytes = ft.moe_prefill_workspace_size(L.handle, T, mode)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
@@ -355,18 +362,34 @@ def bench_prefill(args, wl):
     fl_dn = 2.0 * pairs * cfg.H * cfg.I
     step_s = dt / K
     gu_tf = fl_gu / (gu_us * 1e-6) / 1e12
+    if s1:
+        # algorithmic bytes of k_s1_gemm<0>: the gate and up MXFP4 weights of every expert
+        # (17/32 byte per weight: code nibble + E8M0 byte per 32), the quantised tokens once,
+        # the quantised h written once
+        mx = 17.0 / 32.0
+        by_gu = cfg.E * 2 * cfg.I * cfg.H * mx + T * cfg.H * mx + pairs * cfg.I * mx
+        gbs = by_gu / (gu_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS,
+                "traffic": measured_traffic(f"k_s1_gemm<0>@{args.workload}", "prefill"),
+                "kernel": "k_s1_gemm<0> (gate/up + SwiGLU + MXFP4 quantise of h)",
+                "kernel_us": gu_us, "bytes_per_launch": by_gu, "flops_per_launch": fl_gu,
+                "fp4_mfma_tflops": gu_tf, "fp4_mfma_frac": gu_tf / FP4_PEAK_TFLOPS,
+                "timing": "dispatch-events"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic(f"k_ggemm<0>@{args.workload}", "prefill"),
+                "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
+                "flops_per_launch": fl_gu, "timing": "dispatch-events"}
     res = {
         "metric": METRIC, "value": T * K / dt, "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "mxfp4" if s1 else "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k, "weights": cfg.fmt,
-                   "mode": "exact-bf16-mfma"},
-        "roofline": {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(f"k_ggemm<0>@{args.workload}", "prefill"),
-                     "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
-                     "flops_per_launch": fl_gu, "timing": "dispatch-events"},
+                   "mode": "mxfp4-scaled-fp4-mfma" if s1 else "exact-bf16-mfma"},
+        "roofline": roof,
         "layer": {"flops_per_step": fl_gu + fl_dn,
                   "TFLOPs_per_step": (fl_gu + fl_dn) / step_s / 1e12,
                   "fp4_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / FP4_PEAK_TFLOPS,
@@ -376,7 +399,8 @@ def bench_prefill(args, wl):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline_prefill(cfg, xh[0], args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, xh[0], args.cpu_seconds,
+                                                   "mxfp4" if s1 else "exact")
     L.close()
     ctx.close()
     return res
@@ -426,7 +450,7 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.workload == "miss-path-284b":
         res = bench_miss_path(args, wl)
-    elif args.workload == "prefill-753b":
+    elif args.workload.startswith("prefill-"):
         res = bench_prefill(args, wl)
     else:
         res = bench_decode(args, wl)

@@ -104,8 +104,19 @@ typedef struct ft_layer_desc {
   uint64_t blob_stride;       /* >= ft_blob_bytes(), multiple of 4096 */
   int32_t resident;           /* 1: slot e already holds expert e for every e (needs
                                  n_slots == E); 0: the pool starts empty */
-  int32_t reserved;
+  int32_t flags;              /* 0 or FT_LAYER_PREFILL_MXFP4 */
 } ft_layer_desc;
+
+/*
+ * FT_LAYER_PREFILL_MXFP4: prepare the layer for ft_moe_prefill(..., FT_PREFILL_MXFP4, ...).
+ * An NVFP4 layer (which must be resident) gets its experts transcoded once, here, to MXFP4
+ * blobs held by the library (E * ft_blob_bytes(FT_MXFP4, H, I) device bytes, freed by
+ * ft_layer_destroy): each weight's exact value E2M1 x E4M3 x tensor scale is requantised
+ * per 32 along K by the OCP MX rule (see ft_moe_prefill), so the tensor scale lives inside
+ * the new values.  Later writes to the pool are not seen by that copy.  MXFP4 layers need no
+ * copy (requantising an MXFP4 block reproduces its values) and ignore the flag.
+ */
+enum { FT_LAYER_PREFILL_MXFP4 = 1 };
 
 /* Create a layer over caller-owned buffers; allocates the library's device workspace. */
 FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** out);
@@ -146,10 +157,23 @@ FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
                          ft_decode_stats* stats, void* stream);
 
 /*
- * Prefill (large T, all experts resident).  mode FT_PREFILL_EXACT: bf16 activations,
- * exact FP4 weights, bf16 MFMA; FT_PREFILL_MXFP4: activations and h quantised to MXFP4
- * per 32 along K and weights transcoded to MXFP4, scaled-FP4 MFMA.  ws: device workspace of
- * at least ft_moe_prefill_workspace_size() bytes (caller-owned).
+ * Prefill (large T, all experts resident; smzdm explainer aomxznrn, "FreeToken干的事", item 4:
+ * prefill takes its own, compute-bound strategy).  Routing as ft_route; the (token, choice)
+ * pairs are sorted by expert (stable), every expert's rows go through one grouped SwiGLU
+ * FFN, and y[t] = sum_j w[t][j] * FFN_{idx[t][j]}(x[t]) in rank order.
+ *   FT_PREFILL_EXACT: bf16 activations, the exact FP4 weights, bf16 MFMA, fp32 accumulate,
+ *     h rounded to bf16 (as decode).
+ *   FT_PREFILL_MXFP4: both operands FP4 on the scaled-FP4 MFMA.  x and h are quantised per
+ *     32 along K by the OCP MX rule: scale 2^(floor(log2 max|v|) - 2), exponent clamped to
+ *     [-127, 127], an all-zero block gets scale code 0; each v / scale rounds to the nearest
+ *     E2M1 value, ties to the even code, saturating at 6, with v's sign bit.  The weights are
+ *     the layer's MXFP4 blobs, or for NVFP4 the copy made by FT_LAYER_PREFILL_MXFP4
+ *     (FT_ESTATE without it).  h is quantised from its fp32 value.
+ * x: device bf16 [T][H]; y: device fp32 [T][H].  ws: device workspace of at least
+ * ft_moe_prefill_workspace_size(layer, T, mode) bytes, 256-byte aligned, caller-owned; it
+ * holds the routing, permutation and intermediates of the call until the next call.
+ * Errors: FT_EINVAL (bad T, mode, pointers or workspace), FT_ESTATE (layer not resident, or
+ * no MXFP4 weights for FT_PREFILL_MXFP4), FT_EUNSUPPORTED (shared experts).  Asynchronous.
  */
 FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T, int mode, size_t* bytes);
 FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T, float* y,
@@ -207,6 +231,15 @@ FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
  * fp32), copied from the workspace `ws` of that call. */
 FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* ws, int T, int32_t* idx,
                                   float* w, void* stream);
+/* MXFP4 operands of the last FT_PREFILL_MXFP4 call, copied from its workspace: which = 0:
+ * the quantised tokens, codes [T][H/2] (two per byte, low nibble first) and E8M0 scales
+ * [T][H/32]; which = 1: the quantised h in permuted row order, codes [T*k][I/2] and scales
+ * [T*k][I/32].  codes and scales are device buffers. */
+FT_API int ft_debug_prefill_quant(const ft_layer* layer, const void* ws, int T, int which,
+                                  uint8_t* codes, uint8_t* scales, void* stream);
+/* The MXFP4 blob that FT_PREFILL_MXFP4 uses for expert e (ft_blob_bytes(FT_MXFP4, H, I)
+ * bytes), copied to the device buffer out.  FT_ESTATE if the layer has none. */
+FT_API int ft_debug_prefill_weights(const ft_layer* layer, int e, void* out, void* stream);
 
 #ifdef __cplusplus
 }

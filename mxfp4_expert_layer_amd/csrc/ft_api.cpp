@@ -28,6 +28,8 @@ extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix,
                            float* out, hipStream_t st);
 extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes, hipStream_t st);
 extern "C" int ftk_prefill(const PrefillLaunch* a, hipStream_t st, const hipEvent_t* ev);
+extern "C" int ftk_nv_to_mx(const uint8_t* src, uint8_t* dst, const BlobLayout* S,
+                            const BlobLayout* D, hipStream_t st);
 
 namespace {
 
@@ -75,6 +77,11 @@ struct ft_layer {
   int32_t* e2s_dev = nullptr;
   int32_t* s2e_dev = nullptr;
   uint16_t* wr_planes = nullptr;  // [3][E][H] bf16 split of router_w (prefill router)
+  // MXFP4 weights of the scaled-FP4 prefill: the pool itself (MXFP4 layers) or a transcoded
+  // copy owned here (NVFP4 layers created with FT_LAYER_PREFILL_MXFP4); null if neither
+  const uint8_t* mx_pool = nullptr;
+  uint64_t mx_stride = 0;
+  void* mx_owned = nullptr;
   // pinned host staging
   void* pin = nullptr;
   uint8_t* pin_dev = nullptr;    // device address of the mapped pinned staging
@@ -212,6 +219,7 @@ static void free_layer(ft_layer* l) {
   if (l->ev_copy) hipEventDestroy(l->ev_copy);
   if (l->ev_route) hipEventDestroy(l->ev_route);
   if (l->dev) hipFree(l->dev);
+  if (l->mx_owned) hipFree(l->mx_owned);
   if (l->pin) hipHostFree(l->pin);
   delete l;
 }
@@ -237,6 +245,10 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
     return fail(FT_EINVAL, "ft_layer_create: resident layers need n_slots == E");
   if (!d.resident && !d.host_blobs)
     return fail(FT_EINVAL, "ft_layer_create: a non-resident layer needs host_blobs");
+  if (d.flags & ~FT_LAYER_PREFILL_MXFP4)
+    return fail(FT_EINVAL, "ft_layer_create: unknown flags");
+  if ((d.flags & FT_LAYER_PREFILL_MXFP4) && d.format == FT_NVFP4 && !d.resident)
+    return fail(FT_EINVAL, "ft_layer_create: FT_LAYER_PREFILL_MXFP4 needs a resident layer");
   HIP_TRY(hipSetDevice(ctx->device));
 
   std::unique_ptr<ft_layer, void (*)(ft_layer*)> l(new (std::nothrow) ft_layer, free_layer);
@@ -276,6 +288,21 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   l->s2e_dev = carve<int32_t>(p, d.n_slots);
   l->wr_planes = carve<uint16_t>(p, (size_t)3 * d.E * d.H);
   HIP_TRY((hipError_t)ftk_split_router(d.router_w, d.E, d.H, l->wr_planes, nullptr));
+  if (d.format == FT_MXFP4 && d.resident) {
+    l->mx_pool = (const uint8_t*)d.pool;
+    l->mx_stride = d.blob_stride;
+  } else if (d.format == FT_NVFP4 && (d.flags & FT_LAYER_PREFILL_MXFP4)) {
+    const BlobLayout ML = blob_layout(FT_MXFP4, d.H, d.I);
+    if (hipMalloc(&l->mx_owned, (size_t)d.E * ML.bytes) != hipSuccess)
+      return fail(FT_ENOMEM, "ft_layer_create: MXFP4 weight copy allocation failed");
+    HIP_TRY(hipMemset(l->mx_owned, 0, (size_t)d.E * ML.bytes));
+    for (int e = 0; e < d.E; ++e)
+      HIP_TRY((hipError_t)ftk_nv_to_mx((const uint8_t*)d.pool + (uint64_t)e * d.blob_stride,
+                                       (uint8_t*)l->mx_owned + (uint64_t)e * ML.bytes, &L, &ML,
+                                       nullptr));
+    l->mx_pool = (const uint8_t*)l->mx_owned;
+    l->mx_stride = ML.bytes;
+  }
   HIP_TRY(hipDeviceSynchronize());
 
   size_t pneed = 0;
@@ -714,7 +741,8 @@ extern "C" FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, 
 
 // ---- prefill ------------------------------------------------------------------------------
 // Workspace layout of one prefill call (every region 256-byte aligned); returns the bytes.
-static size_t prefill_carve(const ft_layer* l, int T, uint8_t* base, PrefillLaunch* a) {
+static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
+                            PrefillLaunch* a) {
   const ft_layer_desc& d = l->d;
   const size_t nblk = (size_t)(T + kPermBlock - 1) / kPermBlock;
   const size_t pairs = (size_t)T * d.k;
@@ -735,7 +763,12 @@ static size_t prefill_carve(const ft_layer* l, int T, uint8_t* base, PrefillLaun
   uint8_t* tb_off = take((size_t)(d.E + 1) * 4);
   uint8_t* pos = take(pairs * 4);
   uint8_t* perm_tok = take(pairs * 4);
-  uint8_t* hperm = take(pairs * d.I * 2);
+  const bool mx = mode == FT_PREFILL_MXFP4;
+  uint8_t* hperm = mx ? nullptr : take(pairs * d.I * 2);
+  uint8_t* xq = mx ? take((size_t)T * d.H / 2) : nullptr;
+  uint8_t* xqs = mx ? take((size_t)T * d.H / 32) : nullptr;
+  uint8_t* hq = mx ? take(pairs * d.I / 2) : nullptr;
+  uint8_t* hqs = mx ? take(pairs * d.I / 32) : nullptr;
   uint8_t* yperm = take(pairs * d.H * 4);
   if (a) {
     a->logits = (float*)logits;
@@ -750,6 +783,10 @@ static size_t prefill_carve(const ft_layer* l, int T, uint8_t* base, PrefillLaun
     a->pos = (int32_t*)pos;
     a->perm_tok = (int32_t*)perm_tok;
     a->hperm = (uint16_t*)hperm;
+    a->xq = xq;
+    a->xqs = xqs;
+    a->hq = hq;
+    a->hqs = hqs;
     a->Yperm = (float*)yperm;
   }
   return off;
@@ -761,10 +798,11 @@ static int prefill_check(const ft_layer* layer, int T, int mode, const char* who
     return fail(FT_EINVAL, std::string(who) + ": T out of range");
   if (mode != FT_PREFILL_EXACT && mode != FT_PREFILL_MXFP4)
     return fail(FT_EINVAL, std::string(who) + ": unknown mode");
-  if (mode == FT_PREFILL_MXFP4)
-    return fail(FT_EUNSUPPORTED, std::string(who) + ": the MXFP4-activation mode is not built");
   if (!layer->all_resident)
     return fail(FT_ESTATE, std::string(who) + ": prefill needs an all-resident layer");
+  if (mode == FT_PREFILL_MXFP4 && !layer->mx_pool)
+    return fail(FT_ESTATE, std::string(who) + ": FT_PREFILL_MXFP4 on an NVFP4 layer needs "
+                                              "FT_LAYER_PREFILL_MXFP4 at ft_layer_create");
   if (layer->d.n_shared > 0)
     return fail(FT_EUNSUPPORTED, std::string(who) + ": prefill of layers with shared experts "
                                                     "is not built");
@@ -776,7 +814,7 @@ extern "C" FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T
   int rc = prefill_check(layer, T, mode, "ft_moe_prefill_workspace_size");
   if (rc) return rc;
   if (!bytes) return fail(FT_EINVAL, "ft_moe_prefill_workspace_size: bytes is null");
-  *bytes = prefill_carve(layer, T, nullptr, nullptr);
+  *bytes = prefill_carve(layer, T, mode, nullptr, nullptr);
   return FT_OK;
 }
 
@@ -788,12 +826,12 @@ extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_
   if (!ctx || !x || !y || !ws) return fail(FT_EINVAL, "ft_moe_prefill: null argument");
   if (layer->ctx != ctx) return fail(FT_EINVAL, "ft_moe_prefill: layer of another context");
   if ((uintptr_t)ws % 256) return fail(FT_EINVAL, "ft_moe_prefill: ws must be 256-byte aligned");
-  const size_t need = prefill_carve(layer, T, nullptr, nullptr);
+  const size_t need = prefill_carve(layer, T, mode, nullptr, nullptr);
   if (ws_bytes < need) return fail(FT_EINVAL, "ft_moe_prefill: workspace too small");
   const ft_layer_desc& d = layer->d;
   HIP_TRY(hipSetDevice(ctx->device));
   PrefillLaunch a{};
-  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  prefill_carve(layer, T, mode, (uint8_t*)ws, &a);
   a.x = x;
   a.T = T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
   a.wr_planes = layer->wr_planes;
@@ -801,6 +839,11 @@ extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_
   a.pool = (const uint8_t*)d.pool;
   a.stride = d.blob_stride;
   a.L = layer->L;
+  a.mode = mode;
+  a.mrows = mode == FT_PREFILL_MXFP4 ? kS1Rows : kGemmM;
+  a.mxpool = layer->mx_pool;
+  a.mxstride = layer->mx_stride;
+  a.ML = blob_layout(FT_MXFP4, d.H, d.I);
   a.y = y;
   HIP_TRY((hipError_t)ftk_prefill(&a, (hipStream_t)stream, prof_events(layer)));
   return FT_OK;
@@ -812,7 +855,7 @@ extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* w
   if (!layer || !ws || !counts || !offsets || !pos || T < 1)
     return fail(FT_EINVAL, "ft_debug_prefill_perm: bad argument");
   PrefillLaunch a{};
-  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  prefill_carve(layer, T, FT_PREFILL_EXACT, (uint8_t*)ws, &a);  // same offsets in both modes
   const ft_layer_desc& d = layer->d;
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY(hipSetDevice(layer->ctx->device));
@@ -827,11 +870,42 @@ extern "C" FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* 
   if (!layer || !ws || !idx || !w || T < 1)
     return fail(FT_EINVAL, "ft_debug_prefill_route: bad argument");
   PrefillLaunch a{};
-  prefill_carve(layer, T, (uint8_t*)ws, &a);
+  prefill_carve(layer, T, FT_PREFILL_EXACT, (uint8_t*)ws, &a);  // same offsets in both modes
   hipStream_t st = (hipStream_t)stream;
   const size_t n = (size_t)T * layer->d.k * 4;
   HIP_TRY(hipSetDevice(layer->ctx->device));
   HIP_TRY(hipMemcpyAsync(idx, a.idx, n, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(w, a.w, n, hipMemcpyDeviceToDevice, st));
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_debug_prefill_quant(const ft_layer* layer, const void* ws, int T,
+                                             int which, uint8_t* codes, uint8_t* scales,
+                                             void* stream) {
+  if (!layer || !ws || !codes || !scales || T < 1 || (which != 0 && which != 1))
+    return fail(FT_EINVAL, "ft_debug_prefill_quant: bad argument");
+  PrefillLaunch a{};
+  prefill_carve(layer, T, FT_PREFILL_MXFP4, (uint8_t*)ws, &a);
+  const ft_layer_desc& d = layer->d;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t rows = which == 0 ? (size_t)T : (size_t)T * d.k;
+  const size_t K = which == 0 ? (size_t)d.H : (size_t)d.I;
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  HIP_TRY(hipMemcpyAsync(codes, which == 0 ? a.xq : a.hq, rows * K / 2, hipMemcpyDeviceToDevice,
+                         st));
+  HIP_TRY(hipMemcpyAsync(scales, which == 0 ? a.xqs : a.hqs, rows * K / 32,
+                         hipMemcpyDeviceToDevice, st));
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_debug_prefill_weights(const ft_layer* layer, int e, void* out,
+                                               void* stream) {
+  if (!layer || !out || e < 0 || e >= layer->d.E)
+    return fail(FT_EINVAL, "ft_debug_prefill_weights: bad argument");
+  if (!layer->mx_pool) return fail(FT_ESTATE, "ft_debug_prefill_weights: no MXFP4 weights");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  HIP_TRY(hipMemcpyAsync(out, layer->mx_pool + (uint64_t)e * layer->mx_stride,
+                         blob_layout(FT_MXFP4, layer->d.H, layer->d.I).bytes,
+                         hipMemcpyDeviceToDevice, (hipStream_t)stream));
   return FT_OK;
 }

@@ -67,4 +67,27 @@ __device__ __forceinline__ float e4m3_f32(uint32_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+// ---- OCP MX quantiser (32-value blocks, E8M0 scale, E2M1 codes) -----------------------------
+// Block scale 2^(floor(log2 amax) - 2) (2 is E2M1's largest exponent) with the exponent
+// clamped to [-127, 127]: for a finite fp32 amax with biased exponent field f that is the E8M0
+// code max(f - 2, 0) (zero and subnormal blocks get 0).  A non-finite amax gives the NaN code.
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+  const uint32_t f = (__float_as_uint(amax) >> 23) & 0xffu;
+  return f == 0xffu ? 0xffu : (f > 2u ? f - 2u : 0u);
+}
+// 1 / scale = 2^(127 - code), a normal fp32 for codes 0..252 (NaN for 255).
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  return code == 0xffu ? __uint_as_float(0x7fc00000u) : __uint_as_float((254u - code) << 23);
+}
+// E2M1 code of v / scale: r = |v| / scale (exact, a power-of-two product) rounded to the
+// nearest of 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, saturating at 6; the code's
+// sign bit is v's sign bit.
+__device__ __forceinline__ uint32_t mx_code(float v, float inv) {
+  const float r = fabsf(v) * inv;
+  const uint32_t c = (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
+                     (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
+                     (uint32_t)(r > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
 }  // namespace ft

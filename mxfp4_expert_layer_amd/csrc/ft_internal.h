@@ -101,6 +101,7 @@ struct DecodeLaunch {
 constexpr int kPermBlock = 256;   // tokens per permutation block (one mask word per 32)
 constexpr int kGemmM = 128;       // tokens per grouped-GEMM block
 constexpr int kGemmN = 128;       // weight rows per grouped-GEMM block
+constexpr int kS1Rows = 256;      // token rows per scaled-FP4 grouped-GEMM block
 
 struct PrefillLaunch {
   const uint16_t* x;            // device bf16 [T][H]
@@ -110,6 +111,11 @@ struct PrefillLaunch {
   const uint8_t* pool;          // slot e holds expert e
   uint64_t stride;
   BlobLayout L;
+  int mode;                     // FT_PREFILL_EXACT or FT_PREFILL_MXFP4
+  int mrows;                    // token rows per grouped-GEMM block (kGemmM or kS1Rows)
+  const uint8_t* mxpool;        // FT_PREFILL_MXFP4: MXFP4 blob of expert e at e * mxstride
+  uint64_t mxstride;
+  BlobLayout ML;                // layout of those blobs
   // workspace (caller-owned, carved by the host)
   float* logits;                // [T][E]
   int32_t* idx;                 // [T][k]
@@ -119,10 +125,14 @@ struct PrefillLaunch {
   int32_t* counts;              // [E]
   int32_t* offsets;             // [E+1]
   int32_t* base;                // [T/256][E]
-  int32_t* tb_off;              // [E+1] 128-row token blocks per expert, prefix
+  int32_t* tb_off;              // [E+1] prefix of mrows-row token blocks per expert
   int32_t* pos;                 // [T][k]
   int32_t* perm_tok;            // [T*k]
-  uint16_t* hperm;              // [T*k][I] bf16
+  uint16_t* hperm;              // [T*k][I] bf16 (exact mode)
+  uint8_t* xq;                  // MXFP4 mode: quantised x, codes [T][H/2]
+  uint8_t* xqs;                 //   and E8M0 scales [T][H/32]
+  uint8_t* hq;                  // MXFP4 mode: quantised h (permuted rows), codes [T*k][I/2]
+  uint8_t* hqs;                 //   and scales [T*k][I/32]
   float* Yperm;                 // [T*k][H]
   float* y;                     // [T][H]
 };

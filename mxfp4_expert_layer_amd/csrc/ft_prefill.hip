@@ -18,6 +18,13 @@
 //                     is applied in the epilogue), h = bf16(silu(ts_g G) * (ts_u U)).
 //   k_ggemm<1>        per (expert, token block, 128 rows of W_d): Y_perm = ts_d (W_d h).
 //   k_unpermute       y[t] = sum_j w[t][j] Y_perm[pos[t][j]].
+// The scaled-FP4 mode replaces the two GEMMs (both operands FP4):
+//   k_quant_x         x -> MXFP4 per 32 along H (OCP MX rule), once per token.
+//   k_s1_gemm<0>      per (expert, 256-row block, 64 gate + 64 up features): G, U on the
+//                     16x16x128 scaled-FP4 MFMA; h = silu(G) * U quantised to MXFP4 per 32
+//                     features in the epilogue.
+//   k_s1_gemm<1>      per (expert, row block, 128 rows of W_d): Y_perm = W_d h.
+// and its NVFP4 weights come from k_nv_to_mx, run once when the layer is created.
 // Workgroups of one kernel never wait on each other.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(256) void k_perm_masks(PrefillLaunch a) {
   }
 }
 
-// One workgroup: counts, offsets, bases and the 128-row block map.
+// One workgroup: counts, offsets, bases and the map of mrows-row token blocks.
 __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
   __shared__ int s_wave[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
     if (e < a.E)
       for (int b = 0; b < NBk; ++b) c += a.bcnt[(uint64_t)b * a.E + e];
     cnt[i] = c;
-    blk[i] = (c + kGemmM - 1) / kGemmM;
+    blk[i] = (c + a.mrows - 1) / a.mrows;
   }
   // two exclusive scans over experts (pairs and 128-row blocks), four experts per thread
   for (int pass = 0; pass < 2; ++pass) {
@@ -479,6 +486,322 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
   }
 }
 
+// ---- scaled-FP4 mode (both MFMA operands FP4) ------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// D (16 weight rows x 16 tokens) += A (16 x 128 E2M1, E8M0 scale sa per lane) * B (128 x 16
+// E2M1, scale sb per lane).  Lane l holds row / column l % 16, K elements 32 (l / 16) .. +31:
+// exactly one 16-byte slice of the tile layout and one MX block, so each lane's scale is the
+// scale of its block.  The scale operands use their low byte.
+__device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, const uint4& b, f32x4 c, uint32_t sa,
+                                          uint32_t sb) {
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// x (bf16 [T][H]) -> codes [T][H/2] + scales [T][H/32]; one thread per 32-value block.
+__global__ __launch_bounds__(256) void k_quant_x(PrefillLaunch a) {
+  const uint64_t nblk = (uint64_t)a.T * (a.H / 32);
+  const uint64_t b = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblk) return;
+  const uint4* src = (const uint4*)(a.x + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  const uint32_t sc = mx_scale_code(amax);
+  const float inv = mx_inv_scale(sc);
+  uint32_t out[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wi = w[4 * q + i];
+      o |= mx_code(bf16_lo(wi), inv) << (8 * i);
+      o |= mx_code(bf16_hi(wi), inv) << (8 * i + 4);
+    }
+    out[q] = o;
+  }
+  *(uint4*)(a.xq + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  a.xqs[b] = (uint8_t)sc;
+}
+
+// NVFP4 blob -> MXFP4 blob of the same expert: every weight's exact value E2M1 x E4M3 x tensor
+// scale (fp64: at most 8 + 24 significant bits) requantised by the OCP MX rule per 32 along K.
+// A tile lane holds one 32-value K run of one row (two NVFP4 blocks), which is one MX block in
+// the same lane of the same tile.  One thread per (matrix, tile, lane).
+__device__ __forceinline__ double e2m1_f64(uint32_t c) {
+  const double m = (c & 4) ? ((c & 2) ? ((c & 1) ? 6.0 : 4.0) : ((c & 1) ? 3.0 : 2.0))
+                           : ((c & 2) ? ((c & 1) ? 1.5 : 1.0) : ((c & 1) ? 0.5 : 0.0));
+  return (c & 8) ? -m : m;
+}
+
+__global__ __launch_bounds__(256) void k_nv_to_mx(const uint8_t* __restrict__ src,
+                                                  uint8_t* __restrict__ dst, BlobLayout S,
+                                                  BlobLayout D, uint64_t lanes_per_matrix) {
+  const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid == 0) {
+    BlobHeader* h = (BlobHeader*)dst;
+    h->magic = kBlobMagic;
+    h->fmt = FT_MXFP4;
+    h->H = D.H;
+    h->I = D.I;
+    for (int i = 0; i < 3; ++i) h->tensor_scale[i] = 1.0f;
+    for (int i = 0; i < 9; ++i) h->reserved[i] = 0;
+  }
+  if (gid >= 3 * lanes_per_matrix) return;
+  const int m = (int)(gid / lanes_per_matrix);
+  const uint64_t tl = gid % lanes_per_matrix;     // tile * 64 + lane
+  const double ts = (double)((const BlobHeader*)src)->tensor_scale[m];
+  const uint4 c = *(const uint4*)(src + S.off[2 * m] + tl * 16);
+  const uint8_t* sp = src + S.off[2 * m + 1] + (tl >> 6) * 128 + 2 * (tl & 63);
+  const double s0 = (double)e4m3_f32(sp[0]) * ts, s1 = (double)e4m3_f32(sp[1]) * ts;
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  double v[32];
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = e2m1_f64((cw[i >> 3] >> (4 * (i & 7))) & 15u) * (i < 16 ? s0 : s1);
+    amax = fmax(amax, fabs(v[i]));
+  }
+  int sc = 0;
+  if (amax > 0.0) {
+    int ex;
+    frexp(amax, &ex);                                 // amax = f 2^ex, f in [0.5, 1)
+    sc = min(max(ex - 3, -127), 127) + 127;           // exponent floor(log2 amax) - 2
+  }
+  const double inv = ldexp(1.0, 127 - sc);
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double r = fabs(v[i]) * inv;
+    uint32_t q = (uint32_t)(r > 0.25) + (uint32_t)(r >= 0.75) + (uint32_t)(r > 1.25) +
+                 (uint32_t)(r >= 1.75) + (uint32_t)(r > 2.5) + (uint32_t)(r >= 3.5) +
+                 (uint32_t)(r > 5.0);
+    if (signbit(v[i])) q |= 8u;
+    out[i >> 3] |= q << (4 * (i & 7));
+  }
+  *(uint4*)(dst + D.off[2 * m] + tl * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[D.off[2 * m + 1] + tl] = (uint8_t)sc;
+}
+
+// Grouped GEMM on the scaled-FP4 MFMA.  MODE 0: gate/up + SwiGLU + MXFP4 quantise of h;
+// MODE 1: down -> Y_perm.  A workgroup owns 8 weight tiles (MODE 0: 4 gate + the same 4 up
+// row tiles, 64 features; MODE 1: 8 row tiles of W_d) and a block of up to 256 token rows of
+// one expert.  Weights stream from HBM once per block through a double-buffered LDS stage
+// (two chunks of 128 K in flight in registers); each wave takes the token tiles
+// wave, wave + 4, ... and loads their FP4 rows straight into MFMA operands, so tokens are
+// never staged.  Block (token block g, feature block fb) sits on XCD g % 8.
+template <int N>
+struct ic { static constexpr int value = N; };
+
+template <int MODE, int NS, bool TAIL>
+__global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
+  __shared__ uint4 wl[2][8][64];        // [buffer][weight tile][lane] codes, 16 KB
+  __shared__ uint32_t wsl[2][64][2];    // [buffer][lane]: scale byte of tile t at t / 4, t % 4
+  __shared__ int s_e;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int Lb = blockIdx.x, xcd = Lb & 7, jj = Lb >> 3;
+  const int gblk = xcd + 8 * (jj / NB), fb = jj % NB;
+  if (gblk >= a.tb_off[a.E]) return;
+  if (tid == 0) {  // expert of this token block: tb_off[e] <= gblk < tb_off[e + 1]
+    int lo = 0, hi = a.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tb_off[mid] <= gblk) lo = mid; else hi = mid - 1;
+    }
+    s_e = lo;
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_e);
+  const int row0 = a.offsets[e] + (gblk - a.tb_off[e]) * kS1Rows;
+  const int nrows = min(kS1Rows, a.offsets[e + 1] - row0);
+  const int ntile = (nrows + 15) >> 4;
+  const int nj = __builtin_amdgcn_readfirstlane(max(0, (ntile - wave + 3) >> 2));
+  const int KC = (MODE == 0 ? a.H : a.I) / kTileK;
+  const uint8_t* blob = a.mxpool + (uint64_t)e * a.mxstride;
+
+  // staging roles: 32 code bytes (lanes 2 sp, 2 sp + 1) of tile st; waves 0 and 1 also stage
+  // the scale bytes of lanes 4 sq .. 4 sq + 3 of tile sct
+  const int st = tid >> 5, sp = tid & 31;
+  const int sct = (tid >> 4) & 7, sq = tid & 15;
+  const bool stage_scales = wave < 2;
+  const int mc = MODE == 0 ? (st < 4 ? 0 : 1) : 2;
+  const int rc = MODE == 0 ? fb * 4 + (st & 3) : fb * 8 + st;
+  const int ms = MODE == 0 ? (sct < 4 ? 0 : 1) : 2;
+  const int rs = MODE == 0 ? fb * 4 + (sct & 3) : fb * 8 + sct;
+  const uint8_t* wsrc = blob + a.ML.off[2 * mc] + (uint64_t)rc * KC * kTileCodeBytes + sp * 32;
+  const uint8_t* ssrc = blob + a.ML.off[2 * ms + 1] + (uint64_t)rs * KC * 64 + sq * 4;
+
+  // token operand sources of the wave's tiles (rows past the block's end re-read its last
+  // row, which is valid, and are never stored)
+  const uint8_t* tsrc[4];
+  const uint8_t* tssrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = row0 + min(16 * (wave + 4 * j) + n, nrows - 1);
+    if (MODE == 0) {
+      const uint64_t t = (uint64_t)a.perm_tok[rr];
+      tsrc[j] = a.xq + t * (a.H / 2) + 16 * g;
+      tssrc[j] = a.xqs + t * (a.H / 32) + g;
+    } else {
+      tsrc[j] = a.hq + (uint64_t)rr * (a.I / 2) + 16 * g;
+      tssrc[j] = a.hqs + (uint64_t)rr * (a.I / 32) + g;
+    }
+  }
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // NS register sets of weight chunks in flight (chunk kc lives in set kc % NS) and two sets
+  // of token operands (chunk kc in set kc % 2), all in separately named registers.  Every load
+  // is unconditional, so the compiler's wait counts stay exact: chunk indices past the end
+  // re-read the last chunk (an L2 hit) and are never used.
+  static_assert(NS == 2 || NS == 4, "two or four weight chunks in flight");
+  uint4 w0a, w0b, w1a, w1b, w2a, w2b, w3a, w3b;
+  uint32_t s0, s1, s2, s3;
+  uint4 tA[4], tB[4];
+  uint32_t uA[4], uB[4];
+
+#define FT_S1_WLOAD(kc_, A_, B_, S_)                                                   \
+  do {                                                                                 \
+    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                  \
+    const uint4* p_ = (const uint4*)(wsrc + c_ * kTileCodeBytes);                      \
+    A_ = p_[0];                                                                        \
+    B_ = p_[1];                                                                        \
+    S_ = *(const uint32_t*)(ssrc + c_ * 64);                                           \
+  } while (0)
+#define FT_S1_TLOAD(kc_, T_, U_)                                                       \
+  do {                                                                                 \
+    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                  \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                 \
+      T_[j_] = *(const uint4*)(tsrc[j_] + c_ * 64);                                    \
+      U_[j_] = tssrc[j_][c_ * 4];                                                      \
+    }                                                                                  \
+  } while (0)
+  // chunk kc: stage its weights into LDS buffer kc & 1 (last read by chunk kc - 2, which every
+  // wave finished before the barrier of chunk kc - 1), load the tokens of chunk kc + 1, refill
+  // the register set with chunk kc + NS, then run chunk kc's MFMAs.  The token loads go out
+  // before the weight loads: waits retire loads in issue order, so waiting for the tokens
+  // of the next chunk leaves the weight chunks in flight.
+#define FT_S1_STEP(kc_, A_, B_, S_, T_, U_, TN_, UN_)                                    \
+  do {                                                                                   \
+    const int buf_ = (kc_) & 1;                                                          \
+    wl[buf_][st][2 * sp] = A_;                                                           \
+    wl[buf_][st][2 * sp + 1] = B_;                                                       \
+    if (stage_scales) {                                                                  \
+      uint8_t* sb_ = (uint8_t*)&wsl[buf_][0][0];                                         \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                   \
+        sb_[(4 * sq + i_) * 8 + sct] = (uint8_t)(S_ >> (8 * i_));                        \
+    }                                                                                    \
+    FT_S1_TLOAD((kc_) + 1, TN_, UN_);                                                    \
+    FT_S1_WLOAD((kc_) + NS, A_, B_, S_);                                                 \
+    __syncthreads();                                                                     \
+    const uint32_t slo_ = wsl[buf_][lane][0], shi_ = wsl[buf_][lane][1];                 \
+    uint4 Aop_[8];                                                                       \
+    _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_) Aop_[f_] = wl[buf_][f_][lane];      \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                   \
+      if (j_ < nj) {                                                                     \
+        _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_)                                 \
+          acc[f_][j_] = mfma_fp4(Aop_[f_], T_[j_], acc[f_][j_],                          \
+                                 (f_ < 4 ? slo_ : shi_) >> (8 * (f_ & 3)), U_[j_]);      \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
+
+  FT_S1_WLOAD(0, w0a, w0b, s0);
+  FT_S1_WLOAD(1, w1a, w1b, s1);
+  if (NS == 4) {
+    FT_S1_WLOAD(2, w2a, w2b, s2);
+    FT_S1_WLOAD(3, w3a, w3b, s3);
+  }
+  FT_S1_TLOAD(0, tA, uA);
+  // without TAIL, KC is a multiple of NS and the loop body has no branches
+  for (int kc = 0; kc < KC; kc += NS) {
+    FT_S1_STEP(kc, w0a, w0b, s0, tA, uA, tB, uB);
+    if (!TAIL || kc + 1 < KC) FT_S1_STEP(kc + 1, w1a, w1b, s1, tB, uB, tA, uA);
+    if (NS == 4) {
+      if (!TAIL || kc + 2 < KC) FT_S1_STEP(kc + 2, w2a, w2b, s2, tA, uA, tB, uB);
+      if (!TAIL || kc + 3 < KC) FT_S1_STEP(kc + 3, w3a, w3b, s3, tB, uB, tA, uA);
+    }
+  }
+#undef FT_S1_STEP
+#undef FT_S1_TLOAD
+#undef FT_S1_WLOAD
+
+  if (MODE == 0) {
+    // h = silu(G) * U per (feature, token); MX block b (32 features) of a token is spread over
+    // the four lanes n, n + 16, n + 32, n + 48 (tiles 2b, 2b + 1, four rows each)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= nj) continue;
+      const int row = 16 * (wave + 4 * j) + n;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float hv[2][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float h = silu_f32(acc[2 * b + t2][j][r]) * acc[4 + 2 * b + t2][j][r];
+            hv[t2][r] = h;
+            amax = fmaxf(amax, fabsf(h));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const uint32_t sc = mx_scale_code(amax);
+        const float inv = mx_inv_scale(sc);
+        // features 4g .. 4g + 3 of tile 2b + t2 are block bytes 8 t2 + 2g, 8 t2 + 2g + 1
+        uint32_t half[2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+          half[t2] = mx_code(hv[t2][0], inv) | (mx_code(hv[t2][1], inv) << 4) |
+                     (mx_code(hv[t2][2], inv) << 8) | (mx_code(hv[t2][3], inv) << 12);
+        const uint32_t mine = half[0] | (half[1] << 16);
+        // lane group g writes block bytes 4g .. 4g + 3: the halves t2 = g / 2 of groups
+        // 2 (g % 2) and 2 (g % 2) + 1
+        const int src0 = n + 32 * (g & 1);
+        const uint32_t v0 = (uint32_t)__shfl((int)mine, src0, 64);
+        const uint32_t v1 = (uint32_t)__shfl((int)mine, src0 + 16, 64);
+        const uint32_t word = g < 2 ? ((v0 & 0xffffu) | (v1 << 16))
+                                    : ((v0 >> 16) | (v1 & 0xffff0000u));
+        if (row < nrows) {
+          const uint64_t pr = (uint64_t)(row0 + row);
+          *(uint32_t*)(a.hq + pr * (a.I / 2) + (fb * 64 + 32 * b) / 2 + 4 * g) = word;
+          if (g == 0) a.hqs[pr * (a.I / 32) + fb * 2 + b] = (uint8_t)sc;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= nj) continue;
+      const int row = 16 * (wave + 4 * j) + n;
+      if (row < nrows) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const int col = fb * kGemmN + f * 16 + 4 * g;
+          *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + col) =
+              make_float4(acc[f][j][0], acc[f][j][1], acc[f][j][2], acc[f][j][3]);
+        }
+      }
+    }
+  }
+}
+
 // y[t][h] = sum_j w[t][j] Y_perm[pos[t][j]][h], j in rank order; four h per thread.
 __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
   const int t = blockIdx.y;
@@ -532,6 +855,10 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
                      dim3((a.T + kRouterTokens - 1) / kRouterTokens,
                           (a.E + kRouterExperts - 1) / kRouterExperts),
                      dim3(256), 0, st, a);
+  if (a.mode == FT_PREFILL_MXFP4) {
+    const uint64_t nq = (uint64_t)a.T * (a.H / 32);
+    hipLaunchKernelGGL(k_quant_x, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, a);
+  }
   const dim3 tg((a.T + 15) / 16);
   if (a.E <= 64) hipLaunchKernelGGL(k_topk_many<1>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
   else if (a.E <= 128) hipLaunchKernelGGL(k_topk_many<2>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
@@ -540,14 +867,35 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   hipLaunchKernelGGL(k_perm_masks, dim3(nblk), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_place, dim3(nblk), dim3(256), 0, st, a);
-  // upper bound on 128-row token blocks: sum_e ceil(c_e / 128) <= T*k/128 + E
-  const int gmax = (a.T * a.k + kGemmM - 1) / kGemmM + a.E;
+  // upper bound on mrows-row token blocks: sum_e ceil(c_e / mrows) <= T*k/mrows + E
+  const int gmax = (a.T * a.k + a.mrows - 1) / a.mrows + a.E;
   const int g8 = (gmax + 7) / 8 * 8;
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   const int nb0 = a.I / 64, nb1 = a.H / kGemmN;
-  FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
-  FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
+  if (a.mode == FT_PREFILL_MXFP4) {
+    // four weight chunks in flight when the chunk count allows a branch-free loop
+    const int kc0 = a.H / kTileK, kc1 = a.I / kTileK;
+    if (kc0 % 4 == 0) FT_PLAUNCH((k_s1_gemm<0, 4, false>), dim3(g8 * nb0), e0, e1, a, nb0);
+    else if (kc0 % 2 == 0) FT_PLAUNCH((k_s1_gemm<0, 2, false>), dim3(g8 * nb0), e0, e1, a, nb0);
+    else FT_PLAUNCH((k_s1_gemm<0, 2, true>), dim3(g8 * nb0), e0, e1, a, nb0);
+    if (kc1 % 4 == 0) FT_PLAUNCH((k_s1_gemm<1, 4, false>), dim3(g8 * nb1), e2, e3, a, nb1);
+    else if (kc1 % 2 == 0) FT_PLAUNCH((k_s1_gemm<1, 2, false>), dim3(g8 * nb1), e2, e3, a, nb1);
+    else FT_PLAUNCH((k_s1_gemm<1, 2, true>), dim3(g8 * nb1), e2, e3, a, nb1);
+  } else {
+    FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
+    FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
+  }
   hipLaunchKernelGGL(k_unpermute, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+// NVFP4 blob -> MXFP4 blob (layouts S and D of the same H, I).
+extern "C" int ftk_nv_to_mx(const uint8_t* src, uint8_t* dst, const BlobLayout* S,
+                            const BlobLayout* D, hipStream_t st) {
+  const uint64_t lanes = (uint64_t)(S->I / kTileRows) * (S->H / kTileK) * 64;  // per matrix
+  const uint64_t n = 3 * lanes;
+  hipLaunchKernelGGL(k_nv_to_mx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst,
+                     *S, *D, lanes);
   return (int)hipGetLastError();
 }

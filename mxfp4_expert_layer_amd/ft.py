@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("FT_LIB", os.path.join(_HERE, "libft.so"))
 FT_OK, FT_EINVAL, FT_ENOMEM, FT_EHIP, FT_EUNSUPPORTED, FT_ESTATE = 0, -1, -2, -3, -4, -5
 FT_MXFP4, FT_NVFP4 = 0, 1
 FT_PREFILL_EXACT, FT_PREFILL_MXFP4 = 0, 1
+FT_LAYER_PREFILL_MXFP4 = 1
 MAX_DECODE_TOKENS = 16
 FORMATS = {"mxfp4": FT_MXFP4, "nvfp4": FT_NVFP4}
 
@@ -39,7 +40,7 @@ class LayerDesc(C.Structure):
                 ("max_tokens", C.c_int32), ("router_w", C.c_void_p), ("router_b", C.c_void_p),
                 ("pool", C.c_void_p), ("shared_blobs", C.c_void_p),
                 ("host_blobs", C.c_void_p), ("blob_stride", C.c_uint64),
-                ("resident", C.c_int32), ("reserved", C.c_int32)]
+                ("resident", C.c_int32), ("flags", C.c_int32)]
 
 
 class DecodeStats(C.Structure):
@@ -74,6 +75,8 @@ _sig = {
     "ft_host_expert_ffn": [_vp, _i, _i, _i, _vp, _vp, _i, _vp],
     "ft_debug_prefill_perm": [_vp, _vp, _i, _vp, _vp, _vp, _vp],
     "ft_debug_prefill_route": [_vp, _vp, _i, _vp, _vp, _vp],
+    "ft_debug_prefill_quant": [_vp, _vp, _i, _i, _vp, _vp, _vp],
+    "ft_debug_prefill_weights": [_vp, _i, _vp, _vp],
     "ft_profile_begin": [_vp, _i],
     "ft_profile_end": [_vp, C.POINTER(_d), C.POINTER(_d), C.POINTER(_i)],
 }
@@ -231,3 +234,13 @@ def profile_end(layer_h):
 
 def debug_prefill_route(layer_h, ws, T, idx, w, stream=None):
     check(lib.ft_debug_prefill_route(layer_h, _ptr(ws), T, _ptr(idx), _ptr(w), stream))
+
+
+def debug_prefill_quant(layer_h, ws, T, which, codes, scales, stream=None):
+    """which 0: quantised tokens; 1: quantised h (permuted rows) of the last MXFP4 prefill."""
+    check(lib.ft_debug_prefill_quant(layer_h, _ptr(ws), T, which, _ptr(codes), _ptr(scales),
+                                     stream))
+
+
+def debug_prefill_weights(layer_h, e, out, stream=None):
+    check(lib.ft_debug_prefill_weights(layer_h, e, _ptr(out), stream))

@@ -36,7 +36,7 @@ class GpuLayer:
 
     def __init__(self, ctx: ft.Context, cfg: synth.LayerConfig, *, resident=True,
                  n_slots=None, max_tokens=16, threads=8, copies=1, device="cuda",
-                 experts=None, router=None):
+                 experts=None, router=None, prefill_mxfp4=False):
         self.ctx, self.cfg = ctx, cfg
         self.device = device
         self.stride = ft.blob_bytes(cfg.fmt, cfg.H, cfg.I)
@@ -78,7 +78,8 @@ class GpuLayer:
                 pool=self.pools[c].data_ptr(),
                 shared_blobs=self.shared.data_ptr() if self.shared is not None else None,
                 host_blobs=self.host_blobs.data_ptr() if self.host_blobs is not None else None,
-                blob_stride=self.stride, resident=1 if resident else 0, reserved=0)
+                blob_stride=self.stride, resident=1 if resident else 0,
+                flags=ft.FT_LAYER_PREFILL_MXFP4 if prefill_mxfp4 else 0)
             self.handles.append(ft.layer_create(ctx, desc))
         self.handle = self.handles[0]
 

@@ -69,31 +69,48 @@ def route(x: np.ndarray, router_w, router_b, k: int):
     return idx, w, logits, gap
 
 
+def swiglu_hidden(xs: np.ndarray, wg, wu) -> np.ndarray:
+    """silu(W_g x) * (W_u x) on float64 rows xs [n][H], before any rounding of h."""
+    g = xs @ wg.T
+    u = xs @ wu.T
+    return silu(g) * u
+
+
 def swiglu_ffn(xs: np.ndarray, wg, wu, wd, h_quant=None) -> np.ndarray:
     """SwiGLU expert FFN on float64 rows xs [n][H]; h is rounded to bf16 unless ``h_quant``
     (a function on [n][I] float64 arrays) replaces that rounding."""
-    g = xs @ wg.T
-    u = xs @ wu.T
-    a = silu(g) * u
+    a = swiglu_hidden(xs, wg, wu)
     h = fp4.round_bf16(a) if h_quant is None else h_quant(a)
     return h @ wd.T
 
 
-def expert_outputs(layer, x: np.ndarray, idx: np.ndarray, mode: str = "exact"):
+def expert_outputs(layer, x: np.ndarray, idx: np.ndarray, mode: str = "exact",
+                   threads: int = 1):
     """Per-(t, j) expert outputs y_{t,j} [T][k][H] and shared outputs [T][n_shared][H].
 
     Each selected (token, expert) pair is evaluated by the definition above; tokens sharing
     an expert are evaluated together with one matmul (a library primitive), which changes
-    nothing but the order of independent rows."""
+    nothing but the order of independent rows.  threads > 1 evaluates distinct experts
+    concurrently (each writes only its own rows)."""
     cfg = layer.cfg
     T, k = idx.shape
     ys = np.zeros((T, k, cfg.H))
-    x_in, hq, wq = _mode_ops(mode)
+    x_in, hq, wq = mode_ops(mode)
     xq = x_in(x)
-    for e in np.unique(idx):
+
+    def one(e):
         tt, jj = np.nonzero(idx == e)
         wg, wu, wd = wq(expert_weights(layer, layer.expert(int(e))))
         ys[tt, jj] = swiglu_ffn(xq[tt], wg, wu, wd, hq)
+
+    experts = [int(e) for e in np.unique(idx)]
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            list(pool.map(one, experts))
+    else:
+        for e in experts:
+            one(e)
     sh = np.zeros((T, cfg.n_shared, cfg.H))
     for s in range(cfg.n_shared):
         wg, wu, wd = wq(expert_weights(layer, layer.shared[s]))
@@ -106,7 +123,7 @@ def combine(w: np.ndarray, ys: np.ndarray, sh: np.ndarray) -> np.ndarray:
     return np.einsum("tj,tjh->th", w, ys) + sh.sum(axis=1)
 
 
-def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact"):
+def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact", threads: int = 1):
     """The whole layer on bf16 tokens x_bits (uint16 [T][H]).
 
     ``idx`` overrides the routing choice (its weights are then recomputed from the oracle's
@@ -122,7 +139,7 @@ def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact"):
         p = np.exp(sel - sel.max(axis=1, keepdims=True))
         r_w = p / p.sum(axis=1, keepdims=True)
         r_idx = idx
-    ys, sh = expert_outputs(layer, x, r_idx, mode)
+    ys, sh = expert_outputs(layer, x, r_idx, mode, threads)
     y = combine(r_w, ys, sh)
     return dict(y=y, idx=r_idx, w=r_w, logits=logits, gap=gap, ys=ys, shared=sh)
 
@@ -147,7 +164,10 @@ def dense_masked_forward(layer, x_bits: np.ndarray):
     return y
 
 
-def _mode_ops(mode):
+def mode_ops(mode):
+    """(token transform, h transform or None for bf16 rounding, weight transform) of a mode:
+    "exact" is the bf16-activation layer; "mxfp4" quantises x, h and the weights by the OCP
+    MX rule (``mxq``)."""
     ident = lambda a: a
     if mode == "exact":
         return ident, None, ident

@@ -32,11 +32,16 @@ def quantize(v: np.ndarray):
     sexp = np.clip(ex - 1 - 2, -127, 127)
     scale_code = np.where(nz, sexp + 127, 0)
     r = np.abs(b) / np.ldexp(1.0, sexp)[..., None]
-    d = np.abs(r[..., None] - _GRID)                  # distance to each grid point
-    best = np.argmin(d, axis=-1)                      # lowest index among the nearest
+    # nearest grid point, the lowest index among equally near ones (one pass per point)
+    best = np.zeros(r.shape, dtype=np.int64)
+    bestd = np.abs(r - _GRID[0])
+    for i in range(1, len(_GRID)):
+        di = np.abs(r - _GRID[i])
+        closer = di < bestd
+        best = np.where(closer, i, best)
+        bestd = np.where(closer, di, bestd)
     nxt = np.minimum(best + 1, 7)
-    tie = (np.take_along_axis(d, nxt[..., None], -1)[..., 0] ==
-           np.take_along_axis(d, best[..., None], -1)[..., 0]) & (nxt != best)
+    tie = (np.abs(r - _GRID[nxt]) == bestd) & (nxt != best)
     best = np.where(tie & (best % 2 == 1), nxt, best)  # ties go to the even mantissa
     codes = best | np.where(np.signbit(b), 8, 0)
     return codes.reshape(R, K).astype(np.int64), scale_code.astype(np.int64)

@@ -5,9 +5,10 @@ import numpy as np
 import pytest
 
 from mxfp4_expert_layer_amd import synth
-from oracle import fp4, moe, perm
+from oracle import fp4, moe, mxq, perm
 
-from gpu_util import check_output, check_routing, to_dev
+import tiled
+from gpu_util import check_mx_quant, check_output, check_routing, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +35,8 @@ _layers = {}
 def layer_for(ctx, name, cfg, **kw):
     if name not in _layers:
         log(f"[gpu] building layer {name} {cfg.H}x{cfg.I} E={cfg.E} {cfg.fmt}")
-        _layers[name] = GpuLayer(ctx, cfg, max_tokens=1, **kw)
+        # every prefill layer also carries the weights of the scaled-FP4 mode
+        _layers[name] = GpuLayer(ctx, cfg, max_tokens=1, prefill_mxfp4=True, **kw)
     return _layers[name]
 
 
@@ -61,6 +63,51 @@ def prefill_state(L, ws, T):
     torch.cuda.synchronize()
     return (idx.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(),
             pos.cpu().numpy())
+
+
+def prefill_quant(L, ws, T, which):
+    """The MXFP4 operands of the last scaled-FP4 call: which 0 tokens, 1 permuted h."""
+    rows = T if which == 0 else T * L.cfg.k
+    K = L.cfg.H if which == 0 else L.cfg.I
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+    ft.debug_prefill_quant(L.handle, ws, T, which, codes, scales, stream_ptr())
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def prefill_weights(L, e):
+    """(codes, scales) of gate, up, down in the MXFP4 blob the scaled-FP4 mode uses for e."""
+    cfg = L.cfg
+    nb = ft.blob_bytes("mxfp4", cfg.H, cfg.I)
+    out = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ft.debug_prefill_weights(L.handle, e, out, stream_ptr())
+    torch.cuda.synchronize()
+    blob = out.cpu().numpy()
+    hdr = blob[:16].view(np.int32)
+    assert hdr[0] == 0x31425446 and hdr[1] == ft.FT_MXFP4 and hdr[2] == cfg.H and hdr[3] == cfg.I
+    return tiled.matrices(blob, "mxfp4", cfg.H, cfg.I)
+
+
+def check_s1_weights(L, OL, e, threads=1):
+    """The expert's MXFP4 weights against the oracle's requantisation of its exact weights:
+    codes and scales bit-exact for a transcoded NVFP4 expert, values for an MXFP4 pool blob
+    (requantising keeps an MXFP4 block's values but may re-express its codes).  Returns the
+    oracle's requantised weights (gate, up, down) as float64."""
+    from concurrent.futures import ThreadPoolExecutor
+    ws = moe.expert_weights(OL, OL.expert(e))
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as pool:
+        qs = list(pool.map(mxq.quantize, ws))
+    got = prefill_weights(L, e)
+    out = []
+    for m, ((c, s), (gc, gs)) in enumerate(zip(qs, got)):
+        if L.cfg.fmt == synth.NVFP4:
+            assert np.array_equal(gs, s.astype(np.uint8)), f"expert {e} matrix {m}: scales"
+            assert np.array_equal(gc, mxq.pack_codes(c)), f"expert {e} matrix {m}: codes"
+        deq = mxq.dequantize(c, s)
+        assert np.array_equal(fp4.dequant_mxfp4(gc, gs), deq), f"expert {e} matrix {m}: values"
+        out.append(deq)
+    return out
 
 
 def _check_perm(idx, counts, offsets, pos, E):
@@ -124,6 +171,20 @@ def test_prefill_rejects_bad_calls(ctx):
     with pytest.raises(ft.FtError) as e:
         ft.moe_prefill(ctx, L.handle, x, 8, y, ft.FT_PREFILL_EXACT, ws, nbytes - 256, stream_ptr())
     assert e.value.code == ft.FT_EINVAL
+    with pytest.raises(ft.FtError) as e:
+        ft.moe_prefill_workspace_size(L.handle, 8, 7)
+    assert e.value.code == ft.FT_EINVAL
+    # an NVFP4 layer created without FT_LAYER_PREFILL_MXFP4 has no MXFP4 weights
+    bare = GpuLayer(ctx, cfg, max_tokens=1)
+    try:
+        with pytest.raises(ft.FtError) as e:
+            ft.moe_prefill_workspace_size(bare.handle, 8, ft.FT_PREFILL_MXFP4)
+        assert e.value.code == ft.FT_ESTATE
+        with pytest.raises(ft.FtError) as e:
+            ft.debug_prefill_weights(bare.handle, 0, ws, stream_ptr())
+        assert e.value.code == ft.FT_ESTATE
+    finally:
+        bare.close()
 
 
 def test_prefill_753b_layer(ctx):
@@ -145,4 +206,108 @@ def test_prefill_753b_layer(ctx):
     sample = np.array([0, 1377, 2900, T - 1])
     ref = moe.moe_forward(OL, x[sample], idx=idx[sample])
     check_output(y[sample], ref["y"], "753b-class sampled tokens")
+    assert np.all(np.isfinite(y))
+
+
+# ---- scaled-FP4 mode (both MFMA operands MXFP4) ----------------------------------------------
+
+def _small_layer(ctx, name, fmt, H, I, E, k):
+    cfg = synth.small_config(name, seed=H + E, H=H, I=I, E=E, k=k, fmt=fmt, code_dist="normal",
+                             router_sigma=0.5 / np.sqrt(H), nv_tensor_scale=1 / 64)
+    return cfg, layer_for(ctx, name, cfg)
+
+
+@pytest.mark.parametrize("name,fmt,H,I,E,k,T", SMALL)
+def test_prefill_mxfp4_matches_oracle(ctx, name, fmt, H, I, E, k, T):
+    """Routing and permutation exact, quantised tokens and weights bit-exact, quantised h
+    equal up to fp32-vs-fp64 boundary cases, y within the output bounds of the oracle's
+    "mxfp4" mode."""
+    cfg, L = _small_layer(ctx, name, fmt, H, I, E, k)
+    x = synth.gen_tokens(cfg, T, batch=5)
+    log(f"[gpu] prefill mxfp4 {name} T={T}")
+    y, ws = run_prefill(ctx, L, x, mode=ft.FT_PREFILL_MXFP4)
+    idx, w, counts, offsets, pos = prefill_state(L, ws, T)
+    OL = L.oracle_layer()
+    ref = moe.moe_forward(OL, x, mode="mxfp4")
+    ties = check_routing(idx, w, ref)
+    _check_perm(idx, counts, offsets, pos, E)
+    xr = fp4.bf16_bits_to_f64(x)
+    xc, xs = prefill_quant(L, ws, T, 0)
+    check_mx_quant(xc, xs, xr, "tokens", exact=True)
+    hc, hs = prefill_quant(L, ws, T, 1)
+    xq = mxq.quantize_dequant(xr)
+    ndiff = 0
+    for e in np.unique(idx):
+        wg, wu, _ = check_s1_weights(L, OL, int(e))
+        tt, jj = np.nonzero(idx == e)
+        rows = pos[tt, jj]
+        ndiff += check_mx_quant(hc[rows], hs[rows], moe.swiglu_hidden(xq[tt], wg, wu), f"h of {e}")
+    log(f"[gpu] {name}: {ndiff} h decisions at fp32/fp64 boundaries")
+    if ties:
+        ref = moe.moe_forward(OL, x, idx=idx, mode="mxfp4")
+    check_output(y, ref["y"], name)
+
+
+def test_prefill_mxfp4_token_quantiser_edge_cases(ctx):
+    """Blocks of zeros, -0, bf16 subnormals, values at every rounding midpoint, and very
+    large and very small magnitudes are quantised exactly as the oracle does."""
+    name, fmt, H, I, E, k, T = SMALL[2]
+    cfg, L = _small_layer(ctx, name, fmt, H, I, E, k)
+    x = synth.gen_tokens(cfg, 8, batch=3).copy()
+    xr = fp4.bf16_bits_to_f64(x)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 4.0])
+    xr[0, :] = 0.0
+    xr[1, :32] = -0.0
+    xr[2, :32] = np.ldexp(np.arange(1, 33), -133)           # subnormal in bf16 and fp32
+    xr[2, 32:64] = np.ldexp(np.arange(-16, 16), -126)      # around the smallest normal
+    xr[3, :len(ties)] = ties * 2.0 ** -5
+    xr[3, 32:32 + len(ties)] = -ties * 2.0 ** 7
+    xr[4, :] = xr[4, :] * 2.0 ** 100
+    xr[5, :] = xr[5, :] * 2.0 ** -100
+    xr[6, 0] = 2.0 ** 127
+    xb = synth.f32_to_bf16_bits(xr.astype(np.float32))
+    assert np.array_equal(fp4.bf16_bits_to_f64(xb), xr.astype(np.float32).astype(np.float64))
+    _, ws = run_prefill(ctx, L, xb, mode=ft.FT_PREFILL_MXFP4)
+    xc, xs = prefill_quant(L, ws, 8, 0)
+    check_mx_quant(xc, xs, fp4.bf16_bits_to_f64(xb), "edge-case tokens", exact=True)
+
+
+def test_prefill_mxfp4_is_deterministic(ctx):
+    name, fmt, H, I, E, k, T = SMALL[1]
+    cfg, L = _small_layer(ctx, name, fmt, H, I, E, k)
+    x = synth.gen_tokens(cfg, T, batch=9)
+    a, _ = run_prefill(ctx, L, x, mode=ft.FT_PREFILL_MXFP4)
+    b, _ = run_prefill(ctx, L, x, mode=ft.FT_PREFILL_MXFP4)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_mxfp4_753b_layer(ctx):
+    """The 753B-class NVFP4 layer at T = 4096 in the scaled-FP4 mode: routing, permutation and
+    all quantised tokens exact; one expert's transcoded weights bit-exact and its quantised h
+    rows checked; one sampled token's output against the oracle's "mxfp4" mode."""
+    cfg = synth.CONFIGS["cfg5"]
+    L = layer_for(ctx, "cfg5", cfg, threads=16)
+    T = 4096
+    x = synth.gen_tokens(cfg, T, batch=1)
+    log("[gpu] prefill mxfp4 753b-class T=4096")
+    y, ws = run_prefill(ctx, L, x, mode=ft.FT_PREFILL_MXFP4)
+    idx, w, counts, offsets, pos = prefill_state(L, ws, T)
+    OL = L.oracle_layer()
+    xr = fp4.bf16_bits_to_f64(x)
+    r_idx, r_w, logits, gap = moe.route(xr, OL.router_w, OL.router_b, cfg.k)
+    check_routing(idx, w, dict(idx=r_idx, w=r_w, logits=logits, gap=gap))
+    _check_perm(idx, counts, offsets, pos, cfg.E)
+    xc, xs = prefill_quant(L, ws, T, 0)
+    check_mx_quant(xc, xs, xr, "tokens", exact=True)
+    t_s = 2049
+    e = int(idx[t_s, 0])
+    log(f"[gpu] checking transcoded expert {e} and its h rows")
+    wg, wu, _ = check_s1_weights(L, OL, e, threads=3)
+    hc, hs = prefill_quant(L, ws, T, 1)
+    tt, jj = np.nonzero(idx == e)
+    xq = mxq.quantize_dequant(xr[tt])
+    nd = check_mx_quant(hc[pos[tt, jj]], hs[pos[tt, jj]], moe.swiglu_hidden(xq, wg, wu), "h")
+    log(f"[gpu] 753b h: {len(tt)} rows, {nd} boundary decisions; oracle output of token {t_s}")
+    ref = moe.moe_forward(OL, x[[t_s]], idx=idx[[t_s]], mode="mxfp4", threads=16)
+    check_output(y[[t_s]], ref["y"], "753b-class mxfp4 sampled token")
     assert np.all(np.isfinite(y))

@@ -8,6 +8,8 @@ import pytest
 from mxfp4_expert_layer_amd import synth
 from oracle import fp4, moe, policy
 
+import tiled
+
 ft = pytest.importorskip("mxfp4_expert_layer_amd.ft", reason="libft.so not built")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -44,28 +46,6 @@ def test_blob_bytes_and_alignment():
         ft.blob_bytes("mxfp4", 100, 128)
 
 
-def _unpack_tiled(blob, off_codes, off_scales, R, K, fmt):
-    """Inverse of the tiled layout (test-side restatement of the header's description)."""
-    KC = K // 128
-    codes = np.zeros((R, K // 2), np.uint8)
-    B = 32 if fmt == "mxfp4" else 16
-    scales = np.zeros((R, K // B), np.uint8)
-    sb = 64 if fmt == "mxfp4" else 128
-    for rt in range(R // 16):
-        for kc in range(KC):
-            tile = rt * KC + kc
-            for l in range(64):
-                row, k0 = rt * 16 + l % 16, kc * 128 + 32 * (l // 16)
-                codes[row, k0 // 2:k0 // 2 + 16] = blob[off_codes + tile * 1024 + 16 * l:
-                                                        off_codes + tile * 1024 + 16 * l + 16]
-                if fmt == "mxfp4":
-                    scales[row, k0 // 32] = blob[off_scales + tile * sb + l]
-                else:
-                    scales[row, k0 // 16] = blob[off_scales + tile * sb + 2 * l]
-                    scales[row, k0 // 16 + 1] = blob[off_scales + tile * sb + 2 * l + 1]
-    return codes, scales
-
-
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_pack_roundtrip(fmt):
     cfg = synth.small_config(seed=4, H=256, I=128, fmt=fmt)
@@ -82,10 +62,10 @@ def test_pack_roundtrip(fmt):
         offs.append(o)
         o = (o + s + 4095) // 4096 * 4096
     assert o == blob.size
-    for m, (R, K, cn, sn) in enumerate([(128, 256, "gate_codes", "gate_scales"),
-                                        (128, 256, "up_codes", "up_scales"),
-                                        (256, 128, "down_codes", "down_scales")]):
-        c, s = _unpack_tiled(blob, offs[2 * m], offs[2 * m + 1], R, K, fmt)
+    assert (offs, o) == tiled.blob_offsets(fmt, cfg.H, cfg.I)
+    mats = tiled.matrices(blob, fmt, cfg.H, cfg.I)
+    for (c, s), (cn, sn) in zip(mats, [("gate_codes", "gate_scales"), ("up_codes", "up_scales"),
+                                       ("down_codes", "down_scales")]):
         assert np.array_equal(c, getattr(ex, cn))
         assert np.array_equal(s, getattr(ex, sn))
 

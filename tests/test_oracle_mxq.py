@@ -64,3 +64,30 @@ def test_idempotent_and_nearest_by_exhaustive_search():
 def test_pack_codes_low_nibble_first():
     c = np.array([[1, 2, 15, 8]])
     assert list(mxq.pack_codes(c)[0]) == [0x21, 0x8F]
+
+
+def test_requantising_an_mxfp4_block_keeps_its_values():
+    """An MXFP4 block (E2M1 codes times 2^(s-127)) is a fixed point of the quantiser's
+    values for every scale code 0..254 and every largest code magnitude: scaling its codes
+    by 2^(2 - floor(log2 max|code|)) stays on the E2M1 grid.  The codes themselves may change
+    (a block whose largest code is 1 is re-expressed with a 4x smaller scale)."""
+    rng = np.random.default_rng(11)
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rows = []
+    for s in range(0, 255):
+        for top in range(8):                      # largest code magnitude index in the block
+            c = rng.integers(0, top + 1, 32) | (rng.integers(0, 2, 32) << 3)
+            c[rng.integers(0, 32)] = top
+            rows.append((c, s))
+    codes = np.stack([r[0] for r in rows])
+    scales = np.array([[r[1]] for r in rows])
+    v = fp4.dequant_mxfp4(mxq.pack_codes(codes), scales)
+    assert v.shape == (len(rows), 32)
+    assert np.array_equal(mxq.quantize_dequant(v), v)
+    # a block whose largest magnitude is 4 or 6 keeps its scale and, bar the sign of zeros,
+    # its codes
+    keep = np.array([max(grid[c & 7] for c in r[0]) >= 4.0 for r in rows])
+    c2, s2 = mxq.quantize(v[keep])
+    assert np.array_equal(s2[:, 0], scales[keep, 0])
+    nz = (codes[keep] & 7) != 0
+    assert np.array_equal(c2[nz], codes[keep][nz])
