@@ -30,6 +30,8 @@ extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes,
 extern "C" int ftk_prefill(const PrefillLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_nv_to_mx(const uint8_t* src, uint8_t* dst, const BlobLayout* S,
                             const BlobLayout* D, hipStream_t st);
+extern "C" int ftk_untile_h(const PrefillLaunch* a, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st);
 
 namespace {
 
@@ -767,8 +769,13 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* hperm = mx ? nullptr : take(pairs * d.I * 2);
   uint8_t* xq = mx ? take((size_t)T * d.H / 2) : nullptr;
   uint8_t* xqs = mx ? take((size_t)T * d.H / 32) : nullptr;
-  uint8_t* hq = mx ? take(pairs * d.I / 2) : nullptr;
-  uint8_t* hqs = mx ? take(pairs * d.I / 32) : nullptr;
+  // tiled operands: padded permuted rows (at most T*k + 15 E), 16 per tile row
+  const size_t prows = mx ? (pairs + 15 * (size_t)d.E + 15) / 16 * 16 : 0;
+  uint8_t* poff = mx ? take((size_t)(d.E + 1) * 4) : nullptr;
+  uint8_t* xt = mx ? take(prows * d.H / 2) : nullptr;
+  uint8_t* xts = mx ? take(prows * d.H / 32) : nullptr;
+  uint8_t* ht = mx ? take(prows * d.I / 2) : nullptr;
+  uint8_t* hts = mx ? take(prows * d.I / 32) : nullptr;
   uint8_t* yperm = take(pairs * d.H * 4);
   if (a) {
     a->logits = (float*)logits;
@@ -785,8 +792,11 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     a->hperm = (uint16_t*)hperm;
     a->xq = xq;
     a->xqs = xqs;
-    a->hq = hq;
-    a->hqs = hqs;
+    a->poff = (int32_t*)poff;
+    a->xt = xt;
+    a->xts = xts;
+    a->ht = ht;
+    a->hts = hts;
     a->Yperm = (float*)yperm;
   }
   return off;
@@ -891,10 +901,13 @@ extern "C" FT_API int ft_debug_prefill_quant(const ft_layer* layer, const void* 
   const size_t rows = which == 0 ? (size_t)T : (size_t)T * d.k;
   const size_t K = which == 0 ? (size_t)d.H : (size_t)d.I;
   HIP_TRY(hipSetDevice(layer->ctx->device));
-  HIP_TRY(hipMemcpyAsync(codes, which == 0 ? a.xq : a.hq, rows * K / 2, hipMemcpyDeviceToDevice,
-                         st));
-  HIP_TRY(hipMemcpyAsync(scales, which == 0 ? a.xqs : a.hqs, rows * K / 32,
-                         hipMemcpyDeviceToDevice, st));
+  if (which == 0) {
+    HIP_TRY(hipMemcpyAsync(codes, a.xq, rows * K / 2, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(scales, a.xqs, rows * K / 32, hipMemcpyDeviceToDevice, st));
+  } else {
+    a.T = T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
+    HIP_TRY((hipError_t)ftk_untile_h(&a, codes, scales, st));
+  }
   return FT_OK;
 }
 

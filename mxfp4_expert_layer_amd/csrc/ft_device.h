@@ -45,6 +45,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// silu with the hardware exp and reciprocal (a few ulp); used where h is then quantised to
+// FP4, whose rounding decisions it moves only within 1e-6 of their boundaries.
+__device__ __forceinline__ float silu_fast(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -131,8 +131,15 @@ struct PrefillLaunch {
   uint16_t* hperm;              // [T*k][I] bf16 (exact mode)
   uint8_t* xq;                  // MXFP4 mode: quantised x, codes [T][H/2]
   uint8_t* xqs;                 //   and E8M0 scales [T][H/32]
-  uint8_t* hq;                  // MXFP4 mode: quantised h (permuted rows), codes [T*k][I/2]
-  uint8_t* hqs;                 //   and scales [T*k][I/32]
+  // MXFP4 mode: the grouped GEMMs' token operands in the blob's tile format (16 rows x 128 K
+  // per 1 KB tile, 64 B of scales per tile), rows in permuted order with every expert's rows
+  // padded to a multiple of 16 (expert e's rows start at padded row poff[e]); padding rows
+  // hold zero codes and scales
+  int32_t* poff;                // [E+1]
+  uint8_t* xt;                  // quantised x rows: codes [P/16][H/128][1 KB]
+  uint8_t* xts;                 //   scales [P/16][H/128][64 B]
+  uint8_t* ht;                  // quantised h rows: codes [P/16][I/128][1 KB]
+  uint8_t* hts;                 //   scales [P/16][I/128][64 B]
   float* Yperm;                 // [T*k][H]
   float* y;                     // [T][H]
 };

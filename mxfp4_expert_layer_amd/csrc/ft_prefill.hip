@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
   __shared__ int s_wave[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int NBk = (a.T + kPermBlock - 1) / kPermBlock;
-  int cnt[4], blk[4];
+  int cnt[4], blk[4], pad[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * 4 + i;
@@ -219,12 +219,15 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
       for (int b = 0; b < NBk; ++b) c += a.bcnt[(uint64_t)b * a.E + e];
     cnt[i] = c;
     blk[i] = (c + a.mrows - 1) / a.mrows;
+    pad[i] = (c + 15) & ~15;
   }
-  // two exclusive scans over experts (pairs and 128-row blocks), four experts per thread
-  for (int pass = 0; pass < 2; ++pass) {
+  // exclusive scans over experts (pairs, row blocks and, in the MXFP4 mode, 16-padded rows),
+  // four experts per thread
+  const int npass = a.poff ? 3 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
     int v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = pass == 0 ? cnt[i] : blk[i];
+    for (int i = 0; i < 4; ++i) v[i] = pass == 0 ? cnt[i] : pass == 1 ? blk[i] : pad[i];
     const int mine = v[0] + v[1] + v[2] + v[3];
     int incl = mine;
 #pragma unroll
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
     int base = incl - mine;
     for (int w2 = 0; w2 < wave; ++w2) base += s_wave[w2];
     const int total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    int* out = pass == 0 ? a.offsets : a.tb_off;
+    int* out = pass == 0 ? a.offsets : pass == 1 ? a.tb_off : a.poff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid * 4 + i;
@@ -500,6 +503,18 @@ __device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, const uint4& b, f32x4 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+// D (32 weight rows x 32 tokens) += A (32 x 64 E2M1) * B (64 x 32 E2M1), scales per lane.
+// Lane l holds row / column l % 32, K elements 32 (l / 32) .. +31 (one MX block, one scale);
+// D element (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) is in register r of lane l.  This shape
+// runs at twice the rate of the 16x16x128 one on gfx950 (measured: 8.4 vs 4.3 PFLOP/s).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_fp4_32(const uint4& a, const uint4& b, f32x16 c, uint32_t sa,
+                                              uint32_t sb) {
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // x (bf16 [T][H]) -> codes [T][H/2] + scales [T][H/32]; one thread per 32-value block.
 __global__ __launch_bounds__(256) void k_quant_x(PrefillLaunch a) {
   const uint64_t nblk = (uint64_t)a.T * (a.H / 32);
@@ -531,6 +546,57 @@ __global__ __launch_bounds__(256) void k_quant_x(PrefillLaunch a) {
   }
   *(uint4*)(a.xq + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
   a.xqs[b] = (uint8_t)sc;
+}
+
+// Expert of padded permuted row p: poff[e] <= p < poff[e + 1] (wave-uniform callers).
+__device__ __forceinline__ int expert_of(const int32_t* off, int E, int p) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Quantised token rows -> the GEMM's token operand in tile format, rows in permuted order
+// padded per expert to a multiple of 16.  One thread per 16-byte lane slot of a tile (a wave
+// is one tile): padded row 16 (tile / KC) + l % 16, 32-K block 4 (tile % KC) + l / 16.  The
+// grid covers the largest padded row count; padding rows get zero codes and scales.
+__global__ __launch_bounds__(256) void k_tile_xq(PrefillLaunch a) {
+  const int KC = a.H / kTileK;
+  const uint64_t tile = ((uint64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int l = threadIdx.x & 63;
+  const int P = a.poff[a.E];
+  if (tile >= (uint64_t)(P / 16) * KC) return;
+  const int kc = (int)(tile % KC);
+  const int prow = (int)(tile / KC) * 16 + (l & 15);
+  const int e = expert_of(a.poff, a.E, __builtin_amdgcn_readfirstlane((int)(tile / KC) * 16));
+  const int r = prow - a.poff[e];
+  uint4 c = make_uint4(0u, 0u, 0u, 0u);
+  uint8_t sc = 0;
+  if (r < a.counts[e]) {
+    const uint64_t t = (uint64_t)a.perm_tok[a.offsets[e] + r];
+    const int blk = kc * 4 + (l >> 4);
+    c = *(const uint4*)(a.xq + t * (a.H / 2) + blk * 16);
+    sc = a.xqs[t * (a.H / 32) + blk];
+  }
+  *(uint4*)(a.xt + tile * 1024 + l * 16) = c;
+  a.xts[tile * 64 + l] = sc;
+}
+
+// Test hook: the tiled h back to permuted row order, codes [T*k][I/2] and scales [T*k][I/32].
+// One thread per (row, 32-value block).
+__global__ __launch_bounds__(256) void k_untile_h(PrefillLaunch a, uint8_t* codes, uint8_t* scales) {
+  const int nb = a.I / 32, KC = a.I / kTileK;
+  const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (uint64_t)a.T * a.k * nb) return;
+  const int p = (int)(gid / nb), u = (int)(gid % nb);
+  const int e = expert_of(a.offsets, a.E, p);
+  const int prow = a.poff[e] + p - a.offsets[e];
+  const uint64_t tile = (uint64_t)(prow / 16) * KC + u / 4;
+  const int slotl = (prow % 16) + 16 * (u % 4);
+  *(uint4*)(codes + gid * 16) = *(const uint4*)(a.ht + tile * 1024 + slotl * 16);
+  scales[gid] = a.hts[tile * 64 + slotl];
 }
 
 // NVFP4 blob -> MXFP4 blob of the same expert: every weight's exact value E2M1 x E4M3 x tensor
@@ -593,22 +659,48 @@ __global__ __launch_bounds__(256) void k_nv_to_mx(const uint8_t* __restrict__ sr
 }
 
 // Grouped GEMM on the scaled-FP4 MFMA.  MODE 0: gate/up + SwiGLU + MXFP4 quantise of h;
-// MODE 1: down -> Y_perm.  A workgroup owns 8 weight tiles (MODE 0: 4 gate + the same 4 up
-// row tiles, 64 features; MODE 1: 8 row tiles of W_d) and a block of up to 256 token rows of
-// one expert.  Weights stream from HBM once per block through a double-buffered LDS stage
-// (two chunks of 128 K in flight in registers); each wave takes the token tiles
-// wave, wave + 4, ... and loads their FP4 rows straight into MFMA operands, so tokens are
-// never staged.  Block (token block g, feature block fb) sits on XCD g % 8.
-template <int N>
-struct ic { static constexpr int value = N; };
+// MODE 1: down -> Y_perm.
+//
+// A workgroup owns 16 weight row tiles (MODE 0: 8 gate + the same 8 up tiles, 128 features;
+// MODE 1: 16 row tiles of W_d, 256 outputs) and a block of up to 256 rows of one expert.  Its
+// four waves split that 256 x 256 tile 2 x 2: wave (wm, wn) multiplies 128 weight rows (four
+// 32-row operands) by the 32-token tiles wn, wn + 2, wn + 4, wn + 6 on the 32x32x64 MFMA
+// (fp32 accumulators in the AGPRs); a 32-row operand is two 16-row tiles, read from LDS at
+// the lane slots that hold its K half.  Per 128-K chunk,
+// the weight tiles (16 KB, contiguous in the blob) and the token tiles (16 rows x 64 B
+// gathered per tile) are copied global -> LDS by the DMA form of the vector load, straight
+// into MFMA operand order, so no register holds data in flight: four LDS stages give three
+// chunks of loads in flight while the fourth is multiplied.  Each stage is its own LDS array,
+// which lets the compiler see that reading one stage does not wait on the copies into
+// another; each wave issues the same ten copies per chunk, so an explicit count wait
+// followed by a barrier (no fence, which would drain every copy in flight) makes a stage
+// visible to the whole workgroup.  Block (token block g, feature block fb) sits on XCD g % 8.
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int MODE, int NS, bool TAIL>
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+}
+// s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 field layout)
+#define FT_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+constexpr int kS1Stages = 4;
+constexpr int kS1Copies = 10;   // copies per wave per chunk: 4 weight + 1 scale + 4 token + 1 scale
+
+template <int MODE, bool FAST>
 __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
-  __shared__ uint4 wl[2][8][64];        // [buffer][weight tile][lane] codes, 16 KB
-  __shared__ uint32_t wsl[2][64][2];    // [buffer][lane]: scale byte of tile t at t / 4, t % 4
+  // stage s: weight and token codes [16 tiles][64 lanes], weight and token scales
+  // [16 tiles][64 B]: the tile format throughout
+  __shared__ uint4 wc0[1024], wc1[1024], wc2[1024], wc3[1024];
+  __shared__ uint4 tc0[1024], tc1[1024], tc2[1024], tc3[1024];
+  __shared__ uint32_t ws0[256], ws1[256], ws2[256], ws3[256];
+  __shared__ uint32_t ts0[256], ts1[256], ts2[256], ts3[256];
   __shared__ int s_e;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int n = lane & 15, g = lane >> 4;
   const int Lb = blockIdx.x, xcd = Lb & 7, jj = Lb >> 3;
   const int gblk = xcd + 8 * (jj / NB), fb = jj % NB;
@@ -625,178 +717,256 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   const int e = __builtin_amdgcn_readfirstlane(s_e);
   const int row0 = a.offsets[e] + (gblk - a.tb_off[e]) * kS1Rows;
   const int nrows = min(kS1Rows, a.offsets[e + 1] - row0);
-  const int ntile = (nrows + 15) >> 4;
-  const int nj = __builtin_amdgcn_readfirstlane(max(0, (ntile - wave + 3) >> 2));
+  const int ntile = (nrows + 31) >> 5;   // 32-token tiles
+  const int nj = __builtin_amdgcn_readfirstlane(max(0, (ntile - wn + 1) >> 1));
   const int KC = (MODE == 0 ? a.H : a.I) / kTileK;
+  const int nrt = (MODE == 0 ? a.I : a.H) / kTileRows;   // row tiles of each matrix
   const uint8_t* blob = a.mxpool + (uint64_t)e * a.mxstride;
+  // MODE 1: row tiles past the matrix (H not a multiple of 256) are clamped and never stored
+  const bool wvalid = MODE == 0 || fb * 16 + wm * 8 < nrt;
 
-  // staging roles: 32 code bytes (lanes 2 sp, 2 sp + 1) of tile st; waves 0 and 1 also stage
-  // the scale bytes of lanes 4 sq .. 4 sq + 3 of tile sct
-  const int st = tid >> 5, sp = tid & 31;
-  const int sct = (tid >> 4) & 7, sq = tid & 15;
-  const bool stage_scales = wave < 2;
-  const int mc = MODE == 0 ? (st < 4 ? 0 : 1) : 2;
-  const int rc = MODE == 0 ? fb * 4 + (st & 3) : fb * 8 + st;
-  const int ms = MODE == 0 ? (sct < 4 ? 0 : 1) : 2;
-  const int rs = MODE == 0 ? fb * 4 + (sct & 3) : fb * 8 + sct;
-  const uint8_t* wsrc = blob + a.ML.off[2 * mc] + (uint64_t)rc * KC * kTileCodeBytes + sp * 32;
-  const uint8_t* ssrc = blob + a.ML.off[2 * ms + 1] + (uint64_t)rs * KC * 64 + sq * 4;
-
-  // token operand sources of the wave's tiles (rows past the block's end re-read its last
-  // row, which is valid, and are never stored)
+  // this wave's copies: weight tiles wave + 4i and the scale dwords of tiles 4 wave .. + 3;
+  // token tiles wave + 4i and the scale dwords of rows 64 wave .. + 63 (rows past the block
+  // re-read its last row)
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave + 4 * i;
+    const int m = MODE == 0 ? (q < 8 ? 0 : 1) : 2;
+    const int rt = min(MODE == 0 ? fb * 8 + (q & 7) : fb * 16 + q, nrt - 1);
+    wsrc[i] = blob + a.ML.off[2 * m] + (uint64_t)rt * KC * kTileCodeBytes + lane * 16;
+  }
+  const uint8_t* wssrc;
+  {
+    const int q = 4 * wave + (lane >> 4);
+    const int m = MODE == 0 ? (q < 8 ? 0 : 1) : 2;
+    const int rt = min(MODE == 0 ? fb * 8 + (q & 7) : fb * 16 + q, nrt - 1);
+    wssrc = blob + a.ML.off[2 * m + 1] + (uint64_t)rt * KC * 64 + 4 * (lane & 15);
+  }
+  // token tiles: the block's 16-row tiles of the padded permuted operand (tiles past the
+  // block's last one re-read it; their results are never stored)
+  const int ntile16 = (nrows + 15) >> 4;
+  const int ptile0 = (a.poff[e] >> 4) + (gblk - a.tb_off[e]) * (kS1Rows / 16);
+  const uint8_t* tcodes = MODE == 0 ? a.xt : a.ht;
+  const uint8_t* tscales = MODE == 0 ? a.xts : a.hts;
   const uint8_t* tsrc[4];
-  const uint8_t* tssrc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rr = row0 + min(16 * (wave + 4 * j) + n, nrows - 1);
-    if (MODE == 0) {
-      const uint64_t t = (uint64_t)a.perm_tok[rr];
-      tsrc[j] = a.xq + t * (a.H / 2) + 16 * g;
-      tssrc[j] = a.xqs + t * (a.H / 32) + g;
-    } else {
-      tsrc[j] = a.hq + (uint64_t)rr * (a.I / 2) + 16 * g;
-      tssrc[j] = a.hqs + (uint64_t)rr * (a.I / 32) + g;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t pt = (uint64_t)(ptile0 + min(wave + 4 * i, ntile16 - 1));
+    tsrc[i] = tcodes + pt * KC * kTileCodeBytes + lane * 16;
+  }
+  const uint8_t* tssrc;
+  {
+    const uint64_t pt = (uint64_t)(ptile0 + min(4 * wave + (lane >> 4), ntile16 - 1));
+    tssrc = tscales + pt * KC * 64 + 4 * (lane & 15);
   }
 
-  f32x4 acc[8][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int o = 0; o < 4; ++o)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[o][i][r] = 0.f;
 
-  // NS register sets of weight chunks in flight (chunk kc lives in set kc % NS) and two sets
-  // of token operands (chunk kc in set kc % 2), all in separately named registers.  Every load
-  // is unconditional, so the compiler's wait counts stay exact: chunk indices past the end
-  // re-read the last chunk (an L2 hit) and are never used.
-  static_assert(NS == 2 || NS == 4, "two or four weight chunks in flight");
-  uint4 w0a, w0b, w1a, w1b, w2a, w2b, w3a, w3b;
-  uint32_t s0, s1, s2, s3;
-  uint4 tA[4], tB[4];
-  uint32_t uA[4], uB[4];
+  // first stage tile of this wave's 32-row operand o: MODE 0 gate features wm * 64 + 32 o
+  // (o = 0, 1) and the same up features (o = 2, 3); MODE 1 rows wm * 128 + 32 o
+  auto otile = [&](int o) {
+    return MODE == 0 ? (o < 2 ? 4 * wm + 2 * o : 8 + 4 * wm + 2 * (o - 2)) : 8 * wm + 2 * o;
+  };
+  // lane slot of a 16-row tile holding this lane's 32 K values of K half kh: row lane % 16
+  // of tile (lane / 16) % 2 of the pair, K group 2 kh + lane / 32
+  const int hi = (lane >> 4) & 1, h = lane >> 5;
+  auto slot = [&](int kh) { return (lane & 15) + 16 * (2 * kh + h); };
 
-#define FT_S1_WLOAD(kc_, A_, B_, S_)                                                   \
-  do {                                                                                 \
-    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                  \
-    const uint4* p_ = (const uint4*)(wsrc + c_ * kTileCodeBytes);                      \
-    A_ = p_[0];                                                                        \
-    B_ = p_[1];                                                                        \
-    S_ = *(const uint32_t*)(ssrc + c_ * 64);                                           \
-  } while (0)
-#define FT_S1_TLOAD(kc_, T_, U_)                                                       \
-  do {                                                                                 \
-    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                  \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                 \
-      T_[j_] = *(const uint4*)(tsrc[j_] + c_ * 64);                                    \
-      U_[j_] = tssrc[j_][c_ * 4];                                                      \
-    }                                                                                  \
-  } while (0)
-  // chunk kc: stage its weights into LDS buffer kc & 1 (last read by chunk kc - 2, which every
-  // wave finished before the barrier of chunk kc - 1), load the tokens of chunk kc + 1, refill
-  // the register set with chunk kc + NS, then run chunk kc's MFMAs.  The token loads go out
-  // before the weight loads: waits retire loads in issue order, so waiting for the tokens
-  // of the next chunk leaves the weight chunks in flight.
-#define FT_S1_STEP(kc_, A_, B_, S_, T_, U_, TN_, UN_)                                    \
-  do {                                                                                   \
-    const int buf_ = (kc_) & 1;                                                          \
-    wl[buf_][st][2 * sp] = A_;                                                           \
-    wl[buf_][st][2 * sp + 1] = B_;                                                       \
-    if (stage_scales) {                                                                  \
-      uint8_t* sb_ = (uint8_t*)&wsl[buf_][0][0];                                         \
-      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                   \
-        sb_[(4 * sq + i_) * 8 + sct] = (uint8_t)(S_ >> (8 * i_));                        \
-    }                                                                                    \
-    FT_S1_TLOAD((kc_) + 1, TN_, UN_);                                                    \
-    FT_S1_WLOAD((kc_) + NS, A_, B_, S_);                                                 \
-    __syncthreads();                                                                     \
-    const uint32_t slo_ = wsl[buf_][lane][0], shi_ = wsl[buf_][lane][1];                 \
-    uint4 Aop_[8];                                                                       \
-    _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_) Aop_[f_] = wl[buf_][f_][lane];      \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                   \
-      if (j_ < nj) {                                                                     \
-        _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_)                                 \
-          acc[f_][j_] = mfma_fp4(Aop_[f_], T_[j_], acc[f_][j_],                          \
-                                 (f_ < 4 ? slo_ : shi_) >> (8 * (f_ & 3)), U_[j_]);      \
-      }                                                                                  \
-    }                                                                                    \
+#define FT_S1_ISSUE(kc_, WC_, TC_, WS_, TS_)                                              \
+  do {                                                                                    \
+    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
+      dma16(wsrc[i_] + c_ * kTileCodeBytes, &WC_[(wave + 4 * i_) * 64]);                  \
+    dma4(wssrc + c_ * 64, &WS_[64 * wave]);                                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
+      dma16(tsrc[i_] + c_ * kTileCodeBytes, &TC_[(wave + 4 * i_) * 64]);                  \
+    dma4(tssrc + c_ * 64, &TS_[64 * wave]);                                               \
   } while (0)
 
-  FT_S1_WLOAD(0, w0a, w0b, s0);
-  FT_S1_WLOAD(1, w1a, w1b, s1);
-  if (NS == 4) {
-    FT_S1_WLOAD(2, w2a, w2b, s2);
-    FT_S1_WLOAD(3, w3a, w3b, s3);
-  }
-  FT_S1_TLOAD(0, tA, uA);
-  // without TAIL, KC is a multiple of NS and the loop body has no branches
-  for (int kc = 0; kc < KC; kc += NS) {
-    FT_S1_STEP(kc, w0a, w0b, s0, tA, uA, tB, uB);
-    if (!TAIL || kc + 1 < KC) FT_S1_STEP(kc + 1, w1a, w1b, s1, tB, uB, tA, uA);
-    if (NS == 4) {
-      if (!TAIL || kc + 2 < KC) FT_S1_STEP(kc + 2, w2a, w2b, s2, tA, uA, tB, uB);
-      if (!TAIL || kc + 3 < KC) FT_S1_STEP(kc + 3, w3a, w3b, s3, tB, uB, tA, uA);
+  // Operands are double-buffered in registers: step kc reads chunk kc's operands from its
+  // stage while the MFMAs of chunk kc - 1 (read one step earlier) run, so the LDS reads hide
+  // behind the matrix cores.
+  uint4 PA0[4][2], PB0[4][2], PA1[4][2], PB1[4][2];
+  uint32_t pa0[4][2], pb0[4][2], pa1[4][2], pb1[4][2];
+
+#define FT_S1_READ(WC_, TC_, WS_, TS_, A_, B_, SA_, SB_)                                   \
+  do {                                                                                    \
+    const uint8_t* wsb_ = (const uint8_t*)WS_;                                            \
+    const uint8_t* tsb_ = (const uint8_t*)TS_;                                            \
+    _Pragma("unroll") for (int kh_ = 0; kh_ < 2; ++kh_) {                                 \
+      _Pragma("unroll") for (int o_ = 0; o_ < 4; ++o_) {                                  \
+        const int t_ = otile(o_) + hi;                                                    \
+        A_[o_][kh_] = WC_[t_ * 64 + slot(kh_)];                                           \
+        SA_[o_][kh_] = wsb_[t_ * 64 + slot(kh_)];                                         \
+      }                                                                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
+        const int J_ = wn + 2 * i_;                                                       \
+        B_[i_][kh_] = TC_[(2 * J_ + hi) * 64 + slot(kh_)];                                \
+        SB_[i_][kh_] = tsb_[(2 * J_ + hi) * 64 + slot(kh_)];                              \
+      }                                                                                   \
+    }                                                                                     \
+  } while (0)
+#define FT_S1_MFMA(A_, B_, SA_, SB_)                                                      \
+  do {                                                                                    \
+    _Pragma("unroll") for (int kh_ = 0; kh_ < 2; ++kh_)                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
+        if (FAST || i_ < nj) {                                                            \
+          _Pragma("unroll") for (int o_ = 0; o_ < 4; ++o_)                                \
+            acc[o_][i_] = mfma_fp4_32(A_[o_][kh_], B_[i_][kh_], acc[o_][i_],              \
+                                      SA_[o_][kh_], SB_[i_][kh_]);                        \
+        }                                                                                 \
+      }                                                                                   \
+  } while (0)
+#define FT_S1_SYNC()                                                                      \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(kS1Copies * (kS1Stages - 2)) & ~(15 << 8));       \
+    asm volatile("" ::: "memory");                                                        \
+    __builtin_amdgcn_s_barrier();                                                         \
+    asm volatile("" ::: "memory");                                                        \
+  } while (0)
+
+  // step kc: this wave's LDS reads of every earlier stage have completed (lgkmcnt 0) and at
+  // most the copies of the two later chunks are in flight, so its copies for chunk kc have
+  // landed; the barrier extends both to all waves.  Then the stage of chunk kc - 1 (no longer
+  // read by anyone) is refilled with chunk kc + 3, chunk kc's operands are read and chunk
+  // kc - 1 is multiplied.
+#define FT_S1_STEP(kc_, WC_, TC_, WS_, TS_, WCN_, TCN_, WSN_, TSN_, RA_, RB_, RSA_, RSB_,     \
+                   CA_, CB_, CSA_, CSB_)                                                  \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(kS1Copies * (kS1Stages - 2)) & ~(15 << 8));       \
+    asm volatile("" ::: "memory");                                                        \
+    __builtin_amdgcn_s_barrier();                                                         \
+    asm volatile("" ::: "memory");                                                        \
+    FT_S1_ISSUE((kc_) + kS1Stages - 1, WCN_, TCN_, WSN_, TSN_);                           \
+    if ((kc_) < KC && wvalid) FT_S1_READ(WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_);       \
+    if ((kc_) >= 1 && (kc_) - 1 < KC && wvalid) FT_S1_MFMA(CA_, CB_, CSA_, CSB_);         \
+  } while (0)
+
+  FT_S1_ISSUE(0, wc0, tc0, ws0, ts0);
+  FT_S1_ISSUE(1, wc1, tc1, ws1, ts1);
+  FT_S1_ISSUE(2, wc2, tc2, ws2, ts2);
+  if (FAST) {
+    // KC % 4 == 0: step 0 only reads; steps 1 .. KC each read one chunk and multiply the one
+    // before, on all four token tiles (tiles past the block hold valid rows whose results are
+    // never stored; the barrier makes every wave wait for the busiest one anyway).  No step
+    // has a branch, so the accumulators never pass through a control-flow join.
+    FT_S1_SYNC();
+    FT_S1_ISSUE(3, wc3, tc3, ws3, ts3);
+    FT_S1_READ(wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0);
+    // each phase stays where it is written (scheduling barriers): copies go out first, the
+    // next chunk's operands are read into the other register set, then this chunk's MFMAs
+    // run without waiting on those reads
+#define FT_S1_FAST_STEP(kcn_, WCN_, TCN_, WSN_, TSN_, WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_, \
+                        CA_, CB_, CSA_, CSB_)                                               \
+    do {                                                                                  \
+      FT_S1_SYNC();                                                                       \
+      FT_S1_ISSUE(kcn_, WCN_, TCN_, WSN_, TSN_);                                          \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+      FT_S1_READ(WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_);                               \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+      FT_S1_MFMA(CA_, CB_, CSA_, CSB_);                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    } while (0)
+    for (int kc = 1; kc <= KC; kc += kS1Stages) {
+      FT_S1_FAST_STEP(kc + 3, wc0, tc0, ws0, ts0, wc1, tc1, ws1, ts1, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+      FT_S1_FAST_STEP(kc + 4, wc1, tc1, ws1, ts1, wc2, tc2, ws2, ts2, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+      FT_S1_FAST_STEP(kc + 5, wc2, tc2, ws2, ts2, wc3, tc3, ws3, ts3, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+      FT_S1_FAST_STEP(kc + 6, wc3, tc3, ws3, ts3, wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
     }
+#undef FT_S1_FAST_STEP
+  } else {
+    for (int kc = 0; kc < KC; kc += kS1Stages) {
+      FT_S1_STEP(kc, wc0, tc0, ws0, ts0, wc3, tc3, ws3, ts3, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+      FT_S1_STEP(kc + 1, wc1, tc1, ws1, ts1, wc0, tc0, ws0, ts0, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+      FT_S1_STEP(kc + 2, wc2, tc2, ws2, ts2, wc1, tc1, ws1, ts1, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+      FT_S1_STEP(kc + 3, wc3, tc3, ws3, ts3, wc2, tc2, ws2, ts2, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+    }
+    // the last chunk's MFMAs: when KC % 4 == 0 its operands (odd chunk) are in set 1;
+    // otherwise the loop's padding steps already ran them
+    if (KC % kS1Stages == 0 && wvalid) FT_S1_MFMA(PA1, PB1, pa1, pb1);
   }
 #undef FT_S1_STEP
-#undef FT_S1_TLOAD
-#undef FT_S1_WLOAD
+#undef FT_S1_SYNC
+#undef FT_S1_MFMA
+#undef FT_S1_READ
+#undef FT_S1_ISSUE
+  // the trailing copies (clamped re-reads) land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
 
+  if (!wvalid) return;
   if (MODE == 0) {
-    // h = silu(G) * U per (feature, token); MX block b (32 features) of a token is spread over
-    // the four lanes n, n + 16, n + 32, n + 48 (tiles 2b, 2b + 1, four rows each)
+    // h = silu(G) * U for the 32 features of operand pair (o, o + 2) and token lane % 32: one MX
+    // block, held by lanes l and l ^ 32 (features 8q + 4h + r in register 4q + r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j >= nj) continue;
-      const int row = 16 * (wave + 4 * j) + n;
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nj) continue;
+      const int row = 32 * (wn + 2 * i) + (lane & 31);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float hv[2][4];
+      for (int o = 0; o < 2; ++o) {
+        float hv[16];
         float amax = 0.f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float h = silu_f32(acc[2 * b + t2][j][r]) * acc[4 + 2 * b + t2][j][r];
-            hv[t2][r] = h;
-            amax = fmaxf(amax, fabsf(h));
-          }
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        for (int r = 0; r < 16; ++r) {
+          hv[r] = silu_fast(acc[o][i][r]) * acc[o + 2][i][r];
+          amax = fmaxf(amax, fabsf(hv[r]));
+        }
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const uint32_t sc = mx_scale_code(amax);
-        const float inv = mx_inv_scale(sc);
-        // features 4g .. 4g + 3 of tile 2b + t2 are block bytes 8 t2 + 2g, 8 t2 + 2g + 1
-        uint32_t half[2];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-          half[t2] = mx_code(hv[t2][0], inv) | (mx_code(hv[t2][1], inv) << 4) |
-                     (mx_code(hv[t2][2], inv) << 8) | (mx_code(hv[t2][3], inv) << 12);
-        const uint32_t mine = half[0] | (half[1] << 16);
-        // lane group g writes block bytes 4g .. 4g + 3: the halves t2 = g / 2 of groups
-        // 2 (g % 2) and 2 (g % 2) + 1
-        const int src0 = n + 32 * (g & 1);
-        const uint32_t v0 = (uint32_t)__shfl((int)mine, src0, 64);
-        const uint32_t v1 = (uint32_t)__shfl((int)mine, src0 + 16, 64);
-        const uint32_t word = g < 2 ? ((v0 & 0xffffu) | (v1 << 16))
-                                    : ((v0 >> 16) | (v1 & 0xffff0000u));
-        if (row < nrows) {
-          const uint64_t pr = (uint64_t)(row0 + row);
-          *(uint32_t*)(a.hq + pr * (a.I / 2) + (fb * 64 + 32 * b) / 2 + 4 * g) = word;
-          if (g == 0) a.hqs[pr * (a.I / 32) + fb * 2 + b] = (uint8_t)sc;
+        // the hardware convert rounds v / 2^(sc - 127) to E2M1 exactly as the OCP rule does
+        // (nearest, ties to the even code, saturating, sign kept; checked on gfx950 over every
+        // rounding midpoint and its neighbours, zeros of both signs and subnormal scales).
+        // w01 holds features 4h + {0..3, 8..11} (regs 0..7), w23 regs 8..15: as 16-bit pieces
+        // p[q] = features 8q + 4h .. + 3 = block bytes 4q + 2h, 4q + 2h + 1
+        const float scl = e8m0_f32(sc);
+        uint32_t w01 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, hv[0], hv[1], scl, 0);
+        w01 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w01, hv[2], hv[3], scl, 1);
+        w01 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w01, hv[4], hv[5], scl, 2);
+        w01 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w01, hv[6], hv[7], scl, 3);
+        uint32_t w23 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, hv[8], hv[9], scl, 0);
+        w23 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w23, hv[10], hv[11], scl, 1);
+        w23 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w23, hv[12], hv[13], scl, 2);
+        w23 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w23, hv[14], hv[15], scl, 3);
+        // lane half 0 writes block bytes 0..7, half 1 bytes 8..15; each sends the pieces the
+        // other half writes
+        const uint32_t send = h == 0 ? w23 : w01;
+        const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32, 64);
+        const uint2 out = h == 0 ? make_uint2((w01 & 0xffffu) | (recv << 16),
+                                              (w01 >> 16) | (recv & 0xffff0000u))
+                                 : make_uint2((recv & 0xffffu) | (w23 << 16),
+                                              (recv >> 16) | (w23 & 0xffff0000u));
+        // into the tiled h: padded row ptile0 * 16 + row, 32-K block 4 fb + 2 wm + o of the
+        // down projection's K = I (rows past nrows hold h of zero tokens: zero codes)
+        if (row < 16 * ntile16) {
+          const int prow = ptile0 * 16 + row;
+          const uint64_t tile = (uint64_t)(prow >> 4) * (a.I / kTileK) + fb;
+          const int sl = (prow & 15) + 16 * (2 * wm + o);
+          *(uint2*)(a.ht + tile * kTileCodeBytes + sl * 16 + 8 * h) = out;
+          if (h == 0) a.hts[tile * 64 + sl] = (uint8_t)sc;
         }
       }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j >= nj) continue;
-      const int row = 16 * (wave + 4 * j) + n;
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nj) continue;
+      const int row = 32 * (wn + 2 * i) + (lane & 31);
       if (row < nrows) {
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          const int col = fb * kGemmN + f * 16 + 4 * g;
-          *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + col) =
-              make_float4(acc[f][j][0], acc[f][j][1], acc[f][j][2], acc[f][j][3]);
-        }
+        for (int o = 0; o < 4; ++o)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = fb * 256 + wm * 128 + 32 * o + 8 * q + 4 * h;
+            *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + col) =
+                make_float4(acc[o][i][4 * q], acc[o][i][4 * q + 1], acc[o][i][4 * q + 2],
+                            acc[o][i][4 * q + 3]);
+          }
       }
     }
   }
@@ -867,6 +1037,11 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   hipLaunchKernelGGL(k_perm_masks, dim3(nblk), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_place, dim3(nblk), dim3(256), 0, st, a);
+  if (a.mode == FT_PREFILL_MXFP4) {
+    // tiles of the padded permuted tokens: at most T*k + 15 E rows
+    const uint64_t maxtiles = (uint64_t)((a.T * a.k + 15 * a.E + 15) / 16) * (a.H / kTileK);
+    hipLaunchKernelGGL(k_tile_xq, dim3((unsigned)((maxtiles * 64 + 255) / 256)), dim3(256), 0, st, a);
+  }
   // upper bound on mrows-row token blocks: sum_e ceil(c_e / mrows) <= T*k/mrows + E
   const int gmax = (a.T * a.k + a.mrows - 1) / a.mrows + a.E;
   const int g8 = (gmax + 7) / 8 * 8;
@@ -874,14 +1049,12 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   const int nb0 = a.I / 64, nb1 = a.H / kGemmN;
   if (a.mode == FT_PREFILL_MXFP4) {
-    // four weight chunks in flight when the chunk count allows a branch-free loop
-    const int kc0 = a.H / kTileK, kc1 = a.I / kTileK;
-    if (kc0 % 4 == 0) FT_PLAUNCH((k_s1_gemm<0, 4, false>), dim3(g8 * nb0), e0, e1, a, nb0);
-    else if (kc0 % 2 == 0) FT_PLAUNCH((k_s1_gemm<0, 2, false>), dim3(g8 * nb0), e0, e1, a, nb0);
-    else FT_PLAUNCH((k_s1_gemm<0, 2, true>), dim3(g8 * nb0), e0, e1, a, nb0);
-    if (kc1 % 4 == 0) FT_PLAUNCH((k_s1_gemm<1, 4, false>), dim3(g8 * nb1), e2, e3, a, nb1);
-    else if (kc1 % 2 == 0) FT_PLAUNCH((k_s1_gemm<1, 2, false>), dim3(g8 * nb1), e2, e3, a, nb1);
-    else FT_PLAUNCH((k_s1_gemm<1, 2, true>), dim3(g8 * nb1), e2, e3, a, nb1);
+    const int sb0 = a.I / 128, sb1 = (a.H + 255) / 256;   // feature blocks
+    // the branch-free main loop needs the chunk count to be a multiple of the stage count
+    if ((a.H / kTileK) % kS1Stages == 0) FT_PLAUNCH((k_s1_gemm<0, true>), dim3(g8 * sb0), e0, e1, a, sb0);
+    else FT_PLAUNCH((k_s1_gemm<0, false>), dim3(g8 * sb0), e0, e1, a, sb0);
+    if ((a.I / kTileK) % kS1Stages == 0) FT_PLAUNCH((k_s1_gemm<1, true>), dim3(g8 * sb1), e2, e3, a, sb1);
+    else FT_PLAUNCH((k_s1_gemm<1, false>), dim3(g8 * sb1), e2, e3, a, sb1);
   } else {
     FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
     FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
@@ -897,5 +1070,13 @@ extern "C" int ftk_nv_to_mx(const uint8_t* src, uint8_t* dst, const BlobLayout* 
   const uint64_t n = 3 * lanes;
   hipLaunchKernelGGL(k_nv_to_mx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst,
                      *S, *D, lanes);
+  return (int)hipGetLastError();
+}
+
+// Test hook: the last MXFP4-mode call's h in permuted row order.
+extern "C" int ftk_untile_h(const PrefillLaunch* ap, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const PrefillLaunch& a = *ap;
+  const uint64_t n = (uint64_t)a.T * a.k * (a.I / 32);
+  hipLaunchKernelGGL(k_untile_h, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, codes, scales);
   return (int)hipGetLastError();
 }
