@@ -78,7 +78,7 @@ struct ft_layer {
   float* P = nullptr;
   int32_t* e2s_dev = nullptr;
   int32_t* s2e_dev = nullptr;
-  uint16_t* wr_planes = nullptr;  // [3][E][H] bf16 split of router_w (prefill router)
+  uint16_t* wr_planes = nullptr;  // bf16 split of router_w in MFMA operand order (prefill router)
   // MXFP4 weights of the scaled-FP4 prefill: the pool itself (MXFP4 layers) or a transcoded
   // copy owned here (NVFP4 layers created with FT_LAYER_PREFILL_MXFP4); null if neither
   const uint8_t* mx_pool = nullptr;
@@ -274,7 +274,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   add((size_t)T * l->kk * d.H * 4);                // P
   add((size_t)d.E * 4);
   add((size_t)d.n_slots * 4);
-  add((size_t)3 * d.E * d.H * 2);                  // router planes
+  add(router_plane_bytes(d.E, d.H));               // router planes
   if (hipMalloc(&l->dev, need) != hipSuccess)
     return fail(FT_ENOMEM, "ft_layer_create: device workspace allocation failed");
   HIP_TRY(hipMemset(l->dev, 0, need));
@@ -288,7 +288,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   l->P = carve<float>(p, (size_t)T * l->kk * d.H);
   l->e2s_dev = carve<int32_t>(p, d.E);
   l->s2e_dev = carve<int32_t>(p, d.n_slots);
-  l->wr_planes = carve<uint16_t>(p, (size_t)3 * d.E * d.H);
+  l->wr_planes = carve<uint16_t>(p, router_plane_bytes(d.E, d.H) / 2);
   HIP_TRY((hipError_t)ftk_split_router(d.router_w, d.E, d.H, l->wr_planes, nullptr));
   if (d.format == FT_MXFP4 && d.resident) {
     l->mx_pool = (const uint8_t*)d.pool;
@@ -754,7 +754,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     off += align_up(bytes, 256);
     return r;
   };
-  uint8_t* logits = take((size_t)T * d.E * 4);
+  uint8_t* logits = take((size_t)router_splits(T, d.E, d.H) * T * d.E * 4);
   uint8_t* idx = take(pairs * 4);
   uint8_t* w = take(pairs * 4);
   uint8_t* masks = take(nblk * d.E * 8 * 4);
@@ -845,6 +845,7 @@ extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_
   a.x = x;
   a.T = T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
   a.wr_planes = layer->wr_planes;
+  a.splits = router_splits(T, d.E, d.H);
   a.router_b = d.router_b;
   a.pool = (const uint8_t*)d.pool;
   a.stride = d.blob_stride;

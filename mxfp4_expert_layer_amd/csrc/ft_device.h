@@ -10,6 +10,20 @@ namespace ft {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copies: lane l's 16 (or 4) bytes land at lds + 16 l (4 l); the wait
+// for them is the vector-memory count (checked on gfx950: per-lane sources may be scattered).
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+}
+// s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 field layout)
+#define FT_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
 // E8M0 code -> fp32 scale 2^(e - 127): e = 0 is 2^-127 (an fp32 subnormal), e = 255 NaN.
 // The scaled FP4 converts below use only the exponent field of this value, which for every

@@ -103,10 +103,32 @@ constexpr int kGemmM = 128;       // tokens per grouped-GEMM block
 constexpr int kGemmN = 128;       // weight rows per grouped-GEMM block
 constexpr int kS1Rows = 256;      // token rows per scaled-FP4 grouped-GEMM block
 
+// Prefill router: 128 tokens per workgroup, up to 6 tiles of 32 experts per workgroup, and the
+// contraction over H split into `splits` ranges (partial logits summed in order by the top-k
+// pass) so that the grid covers the chip.
+constexpr int kRouterTokens = 128;
+constexpr int kRouterGroupTiles = 6;
+FT_HD inline int router_expert_tiles(int E) { return (E + 31) / 32; }
+FT_HD inline int router_splits(int T, int E, int H) {
+  const int blocks = ((T + kRouterTokens - 1) / kRouterTokens) *
+                     ((router_expert_tiles(E) + kRouterGroupTiles - 1) / kRouterGroupTiles);
+  int s = 1;
+  while (s < 16 && blocks * s < 256 && (H / 32) % (2 * s) == 0) s *= 2;
+  return s;
+}
+// bytes of the router weight planes: [3 planes][E/32 tiles][H/16 K-steps][64 lanes][16 B]
+FT_HD inline uint64_t router_plane_bytes(int E, int H) {
+  return (uint64_t)3 * router_expert_tiles(E) * (H / 16) * 1024;
+}
+
 struct PrefillLaunch {
   const uint16_t* x;            // device bf16 [T][H]
   int T, H, I, E, k;
-  const uint16_t* wr_planes;    // [3][E][H] bf16, exact split of the fp32 router weights
+  int splits;                   // router contraction splits (router_splits)
+  // the fp32 router weights as three bf16 planes whose sum is exactly W_r, each in the operand
+  // order of the 32x32x16 MFMA: plane p, expert tile et, K-step ks: lane l holds expert
+  // 32 et + l % 32, K 16 ks + 8 (l / 32) .. + 7 (experts past E are zero)
+  const uint16_t* wr_planes;
   const float* router_b;        // [E] or null
   const uint8_t* pool;          // slot e holds expert e
   uint64_t stride;
@@ -117,7 +139,7 @@ struct PrefillLaunch {
   uint64_t mxstride;
   BlobLayout ML;                // layout of those blobs
   // workspace (caller-owned, carved by the host)
-  float* logits;                // [T][E]
+  float* logits;                // [splits][T][E] partial router logits (no bias)
   int32_t* idx;                 // [T][k]
   float* w;                     // [T][k]
   uint32_t* masks;              // [T/256][E][8] token bitmasks per permutation block

@@ -4,10 +4,12 @@
 // item 4): prefill is compute-bound, so the (token, expert) pairs are sorted by expert and
 // each expert's tokens go through one grouped GEMM on the matrix cores.  One call of T
 // tokens through an all-resident layer runs, on the caller's stream:
-//   k_router_prefill  logits = x W_r^T + b: the fp32 router weights are held as three bf16
-//                     planes whose sum is exactly W_r (24 = 3 x 8 significant bits), so the
-//                     16x16x32 bf16 MFMA forms exact products with fp32 accumulation.
-//   k_topk_many       per-token top-k + softmax (the decode routine, 16 tokens a workgroup).
+//   k_router_prefill  partial logits x W_r^T over `splits` ranges of H: the fp32 router
+//                     weights are held as three bf16 planes whose sum is exactly W_r (24 =
+//                     3 x 8 significant bits), so the 32x32x16 bf16 MFMA forms exact products
+//                     with fp32 accumulation.
+//   k_topk_many       logits = sum of the partials in order + b; per-token top-k + softmax
+//                     (the decode routine, 16 tokens a workgroup).
 //   k_perm_masks      per 256-token block: a token bitmask per expert (LDS atomics).
 //   k_perm_scan       counts, offsets (exclusive scan), per-block bases, 128-row block map.
 //   k_perm_place      pos[t][j] = base + (tokens below t in the block's mask); the row of
@@ -33,75 +35,163 @@
 
 namespace ft {
 
-constexpr int kRouterTokens = 64;    // tokens per router workgroup (16 per wave)
-constexpr int kRouterExperts = 32;   // experts per router workgroup (two 16-row tiles)
 
 // ---- router ------------------------------------------------------------------------------
-// planes[p][i] (bf16): w = planes0 + planes1 + planes2 exactly (each plane takes the next 8
-// significant bits by truncation; the remainders are exact in fp32).
-__global__ __launch_bounds__(256) void k_split_router(const float* __restrict__ wr, int n,
+// planes (bf16, tiled, see PrefillLaunch::wr_planes): w = plane0 + plane1 + plane2 exactly
+// (each plane takes the next 8 significant bits by truncation; the remainders are exact in
+// fp32).  One thread per (expert tile, K-step, lane): 8 weights -> 16 bytes in each plane.
+__global__ __launch_bounds__(256) void k_split_router(const float* __restrict__ wr, int E, int H,
                                                       uint16_t* __restrict__ planes) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float w = wr[i];
-  const uint32_t p0 = __float_as_uint(w) & 0xffff0000u;
-  const float r1 = w - __uint_as_float(p0);
-  const uint32_t p1 = __float_as_uint(r1) & 0xffff0000u;
-  const float r2 = r1 - __uint_as_float(p1);
-  const uint32_t p2 = __float_as_uint(r2) & 0xffff0000u;
-  planes[i] = (uint16_t)(p0 >> 16);
-  planes[(uint64_t)n + i] = (uint16_t)(p1 >> 16);
-  planes[2 * (uint64_t)n + i] = (uint16_t)(p2 >> 16);
+  const int NTe = router_expert_tiles(E), KS = H / 16;
+  const uint64_t u = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint64_t per_plane = (uint64_t)NTe * KS * 64;
+  if (u >= per_plane) return;
+  const int l = (int)(u & 63);
+  const uint64_t op = u >> 6;   // et * KS + ks
+  const int et = (int)(op / KS), ks = (int)(op % KS);
+  const int e = et * 32 + (l & 31);
+  const int k0 = ks * 16 + 8 * (l >> 5);
+  uint32_t pw[3][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo[3], hi[3];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float w = e < E ? wr[(uint64_t)e * H + k0 + 2 * i + h2] : 0.f;
+      const uint32_t p0 = __float_as_uint(w) & 0xffff0000u;
+      const float r1 = w - __uint_as_float(p0);
+      const uint32_t p1 = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(p1);
+      const uint32_t p2 = __float_as_uint(r2) & 0xffff0000u;
+      const uint32_t ps[3] = {p0 >> 16, p1 >> 16, p2 >> 16};
+#pragma unroll
+      for (int p = 0; p < 3; ++p) (h2 ? hi : lo)[p] = ps[p];
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) pw[p][i] = lo[p] | (hi[p] << 16);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    *(uint4*)(planes + ((uint64_t)p * per_plane + u) * 8) = make_uint4(pw[p][0], pw[p][1], pw[p][2], pw[p][3]);
 }
 
-// Grid (ceil(T/64), ceil(E/32)).  Experts are the MFMA rows (A, staged in LDS per 128-K
-// chunk in operand order), tokens the columns (B, loaded per lane from x).
+// D (32 rows x 32 columns) += A (32 x 16 bf16) * B (16 x 32 bf16): lane l holds row / column
+// l % 32, K elements 8 (l / 32) .. + 7; D element (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) in
+// register r of lane l (the same result layout as the FP4 32x32 MFMA).
+__device__ __forceinline__ f32x16 mfma_bf16_32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Grid (ceil(T/128), splits, expert groups of up to 6 tiles).  Wave w takes tokens 32 w ..
+// + 31 of the block (the MFMA columns, loaded from x per lane, two chunks ahead); the NT
+// expert tiles x 3 planes x 2 K-steps of each 32-K chunk (one 1 KB operand each) are copied
+// global -> LDS through four stages, shared by the four waves.  Each wave issues the same
+// number of copies per chunk (slots past the last operand get a duplicate, never read).
+template <int NT, bool FAST>
 __global__ __launch_bounds__(256) void k_router_prefill(PrefillLaunch a) {
-  __shared__ uint4 wl[3][2][4][64];  // [plane][expert tile][k-step][lane]  24 KB
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kRouterTokens + wave * 16;
-  const int e0 = blockIdx.y * kRouterExperts;
-  const int tok = min(t0 + n, a.T - 1);
-  const uint16_t* xr = a.x + (uint64_t)tok * a.H + 32 * g;
-  const uint64_t plane = (uint64_t)a.E * a.H;
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const int KC = a.H / kTileK;
-  for (int kc = 0; kc < KC; ++kc) {
-    // stage: 3 planes x 2 tiles x 4 k-steps x 64 lanes = 1536 uint4, 6 per thread
+  constexpr int NOP = 6 * NT;               // operands per chunk: tile j, plane p, K-step ks
+  constexpr int NDMA = (NOP + 3) / 4;       // copies per wave per chunk
+  constexpr int SLOTS = 4 * NDMA * 64;      // uint4 per stage
+  __shared__ uint4 r0[SLOTS], r1[SLOTS], r2[SLOTS], r3[SLOTS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = blockIdx.x, sp = blockIdx.y, grp = blockIdx.z;
+  const int KS = a.H / a.splits, k0 = sp * KS, NC = KS / 32;
+  const int NTe = router_expert_tiles(a.E), et0 = grp * kRouterGroupTiles;
+  const uint64_t per_plane = (uint64_t)NTe * (a.H / 16) * 64;   // uint4 per plane
+  const uint4* planes = (const uint4*)a.wr_planes;
+  // this wave's copies: operand slots wave + 4 i
+  const uint4* osrc[NDMA];
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      const int slotq = q * 256 + tid;
-      const int p = slotq / 512, j = (slotq / 256) & 1, i = (slotq / 64) & 3, l = slotq & 63;
-      const int e = e0 + j * 16 + (l & 15);
-      const int kk = kc * kTileK + 32 * (l >> 4) + 8 * i;
-      uint4 v = *(const uint4*)(a.wr_planes + p * plane + (uint64_t)min(e, a.E - 1) * a.H + kk);
-      if (e >= a.E) v = make_uint4(0u, 0u, 0u, 0u);
-      wl[p][j][i][l] = v;
-    }
-    uint4 xb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xb[i] = *(const uint4*)(xr + kc * kTileK + 8 * i);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wl[p][j][i][lane]),
-                                                           as_bf16x8(xb[i]), acc[j], 0, 0, 0);
-    __syncthreads();
+  for (int i = 0; i < NDMA; ++i) {
+    const int q = min(wave + 4 * i, NOP - 1);
+    const int j = q / 6, pl = (q / 2) % 3, ks = q % 2;
+    const int et = min(et0 + j, NTe - 1);
+    osrc[i] = planes + (uint64_t)pl * per_plane + ((uint64_t)et * (a.H / 16) + k0 / 16 + ks) * 64 + lane;
   }
-  if (t0 + n < a.T) {
+  const int t = min(tb * kRouterTokens + 32 * wave + (lane & 31), a.T - 1);
+  const uint16_t* xsrc = a.x + (uint64_t)t * a.H + k0 + 8 * (lane >> 5);
+
+  f32x16 acc[NT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = e0 + j * 16 + 4 * g + r;
-        if (e < a.E)
-          a.logits[(uint64_t)(t0 + n) * a.E + e] = acc[j][r] + (a.router_b ? a.router_b[e] : 0.f);
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  uint4 b0[2], b1[2], b2[2], b3[2];
+#define FT_RT_ISSUE(c_, ST_)                                                               \
+  do {                                                                                     \
+    const int cc_ = min((c_), NC - 1);                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < NDMA; ++i_)                                    \
+      dma16(osrc[i_] + (uint64_t)cc_ * 2 * 64, &ST_[(wave + 4 * i_) * 64]);                \
+  } while (0)
+#define FT_RT_XLOAD(c_, B_)                                                                \
+  do {                                                                                     \
+    const int cc_ = min((c_), NC - 1);                                                     \
+    B_[0] = *(const uint4*)(xsrc + cc_ * 32);                                              \
+    B_[1] = *(const uint4*)(xsrc + cc_ * 32 + 16);                                         \
+  } while (0)
+#define FT_RT_SYNC()                                                                       \
+  do {                                                                                     \
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(NDMA + 2) & ~(15 << 8));                           \
+    asm volatile("" ::: "memory");                                                         \
+    __builtin_amdgcn_s_barrier();                                                          \
+    asm volatile("" ::: "memory");                                                         \
+  } while (0)
+  // chunk c: its copies (issued three chunks earlier) and tokens (two chunks earlier) have
+  // landed once at most the next chunk's copies and tokens are in flight
+#define FT_RT_STEP(c_, ST_, STN_, B_, BN_)                                                 \
+  do {                                                                                     \
+    FT_RT_SYNC();                                                                          \
+    FT_RT_ISSUE((c_) + 3, STN_);                                                           \
+    FT_RT_XLOAD((c_) + 2, BN_);                                                            \
+    if (FAST || (c_) < NC) {                                                               \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < 2; ++ks_)                                  \
+        _Pragma("unroll") for (int j_ = 0; j_ < NT; ++j_)                                  \
+          _Pragma("unroll") for (int p_ = 0; p_ < 3; ++p_)                                 \
+            acc[j_] = mfma_bf16_32(ST_[(j_ * 6 + p_ * 2 + ks_) * 64 + lane], B_[ks_], acc[j_]); \
+    }                                                                                      \
+  } while (0)
+
+  FT_RT_ISSUE(0, r0);
+  FT_RT_ISSUE(1, r1);
+  FT_RT_XLOAD(0, b0);
+  FT_RT_ISSUE(2, r2);
+  FT_RT_XLOAD(1, b1);
+  for (int c = 0; c < NC; c += 4) {
+    FT_RT_STEP(c, r0, r3, b0, b2);
+    if (FAST || c + 1 < NC) FT_RT_STEP(c + 1, r1, r0, b1, b3);
+    if (FAST || c + 2 < NC) FT_RT_STEP(c + 2, r2, r1, b2, b0);
+    if (FAST || c + 3 < NC) FT_RT_STEP(c + 3, r3, r2, b3, b1);
+  }
+#undef FT_RT_STEP
+#undef FT_RT_SYNC
+#undef FT_RT_XLOAD
+#undef FT_RT_ISSUE
+  __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
+
+  // partial logits [sp][t][e]: register 4q + r of lane l is expert 32 et + 8q + 4 (l / 32) + r,
+  // token 32 wave + l % 32 of the block
+  const int tok = tb * kRouterTokens + 32 * wave + (lane & 31);
+  if (tok < a.T) {
+    float* out = a.logits + ((uint64_t)sp * a.T + tok) * a.E;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int et = et0 + j;
+      if (et >= NTe) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = et * 32 + 8 * q + 4 * (lane >> 5);
+        if (e + 3 < a.E && (a.E & 3) == 0) {
+          *(float4*)(out + e) = make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2],
+                                            acc[j][4 * q + 3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (e + r < a.E) out[e + r] = acc[j][4 * q + r];
+        }
       }
+    }
   }
 }
 
@@ -113,7 +203,8 @@ __device__ __forceinline__ uint32_t order_key_p(float f) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk_many(const float* __restrict__ logits, int T, int E,
+__global__ __launch_bounds__(256) void k_topk_many(const float* __restrict__ logits, int splits,
+                                                   const float* __restrict__ bias, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
   __shared__ float c_val[16][FT_MAX_TOPK];
@@ -126,8 +217,14 @@ __global__ __launch_bounds__(256) void k_topk_many(const float* __restrict__ log
     const int t = tb + tl;
     float v[EPL];
     uint32_t key[EPL];
+    // logit = (partial 0 + partial 1 + ...) + b, in that order
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = logits[(uint64_t)t * E + min(lane + 64 * i, E - 1)];
+    for (int i = 0; i < EPL; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      float acc = logits[(uint64_t)t * E + e];
+      for (int sp = 1; sp < splits; ++sp) acc += logits[((uint64_t)sp * T + t) * E + e];
+      v[i] = acc + (bias ? bias[e] : 0.f);
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       if (v[i] != v[i]) v[i] = -INFINITY;
@@ -490,7 +587,6 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
 }
 
 // ---- scaled-FP4 mode (both MFMA operands FP4) ------------------------------------------------
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // D (16 weight rows x 16 tokens) += A (16 x 128 E2M1, E8M0 scale sa per lane) * B (128 x 16
 // E2M1, scale sb per lane).  Lane l holds row / column l % 16, K elements 32 (l / 16) .. +31:
@@ -507,7 +603,6 @@ __device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, const uint4& b, f32x4 
 // Lane l holds row / column l % 32, K elements 32 (l / 32) .. +31 (one MX block, one scale);
 // D element (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) is in register r of lane l.  This shape
 // runs at twice the rate of the 16x16x128 one on gfx950 (measured: 8.4 vs 4.3 PFLOP/s).
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma_fp4_32(const uint4& a, const uint4& b, f32x16 c, uint32_t sa,
                                               uint32_t sb) {
   const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -675,16 +770,6 @@ __global__ __launch_bounds__(256) void k_nv_to_mx(const uint8_t* __restrict__ sr
 // another; each wave issues the same ten copies per chunk, so an explicit count wait
 // followed by a barrier (no fence, which would drain every copy in flight) makes a stage
 // visible to the whole workgroup.  Block (token block g, feature block fb) sits on XCD g % 8.
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
-}
-// s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 field layout)
-#define FT_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
 constexpr int kS1Stages = 4;
 constexpr int kS1Copies = 10;   // copies per wave per chunk: 4 weight + 1 scale + 4 token + 1 scale
@@ -1005,8 +1090,9 @@ __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
 using namespace ft;
 
 extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes, hipStream_t st) {
-  const int n = E * H;
-  hipLaunchKernelGGL(k_split_router, dim3((n + 255) / 256), dim3(256), 0, st, wr, n, planes);
+  const uint64_t n = (uint64_t)router_expert_tiles(E) * (H / 16) * 64;
+  hipLaunchKernelGGL(k_split_router, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, wr, E,
+                     H, planes);
   return (int)hipGetLastError();
 }
 
@@ -1021,19 +1107,36 @@ extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes,
 extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
   const PrefillLaunch& a = *ap;
   const int nblk = (a.T + kPermBlock - 1) / kPermBlock;
-  hipLaunchKernelGGL(k_router_prefill,
-                     dim3((a.T + kRouterTokens - 1) / kRouterTokens,
-                          (a.E + kRouterExperts - 1) / kRouterExperts),
-                     dim3(256), 0, st, a);
+  {
+    const int NTe = router_expert_tiles(a.E);
+    const int NT = min(NTe, kRouterGroupTiles);
+    const dim3 rg((a.T + kRouterTokens - 1) / kRouterTokens, a.splits,
+                  (NTe + kRouterGroupTiles - 1) / kRouterGroupTiles);
+    const bool fast = ((a.H / a.splits) / 32) % 4 == 0;
+#define FT_RT_LAUNCH(N)                                                                      \
+  if (fast) hipLaunchKernelGGL((k_router_prefill<N, true>), rg, dim3(256), 0, st, a);        \
+  else hipLaunchKernelGGL((k_router_prefill<N, false>), rg, dim3(256), 0, st, a)
+    switch (NT) {
+      case 1: FT_RT_LAUNCH(1); break;
+      case 2: FT_RT_LAUNCH(2); break;
+      case 3: FT_RT_LAUNCH(3); break;
+      case 4: FT_RT_LAUNCH(4); break;
+      case 5: FT_RT_LAUNCH(5); break;
+      default: FT_RT_LAUNCH(6); break;
+    }
+#undef FT_RT_LAUNCH
+  }
+  const dim3 tg((a.T + 15) / 16);
+#define FT_TK_ARGS a.logits, a.splits, a.router_b, a.T, a.E, a.k, a.idx, a.w
+  if (a.E <= 64) hipLaunchKernelGGL(k_topk_many<1>, tg, dim3(256), 0, st, FT_TK_ARGS);
+  else if (a.E <= 128) hipLaunchKernelGGL(k_topk_many<2>, tg, dim3(256), 0, st, FT_TK_ARGS);
+  else if (a.E <= 256) hipLaunchKernelGGL(k_topk_many<4>, tg, dim3(256), 0, st, FT_TK_ARGS);
+  else hipLaunchKernelGGL(k_topk_many<16>, tg, dim3(256), 0, st, FT_TK_ARGS);
+#undef FT_TK_ARGS
   if (a.mode == FT_PREFILL_MXFP4) {
     const uint64_t nq = (uint64_t)a.T * (a.H / 32);
     hipLaunchKernelGGL(k_quant_x, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, a);
   }
-  const dim3 tg((a.T + 15) / 16);
-  if (a.E <= 64) hipLaunchKernelGGL(k_topk_many<1>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
-  else if (a.E <= 128) hipLaunchKernelGGL(k_topk_many<2>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
-  else if (a.E <= 256) hipLaunchKernelGGL(k_topk_many<4>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
-  else hipLaunchKernelGGL(k_topk_many<16>, tg, dim3(256), 0, st, a.logits, a.T, a.E, a.k, a.idx, a.w);
   hipLaunchKernelGGL(k_perm_masks, dim3(nblk), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_place, dim3(nblk), dim3(256), 0, st, a);
