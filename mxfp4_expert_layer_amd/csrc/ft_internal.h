@@ -108,12 +108,13 @@ constexpr int kS1Rows = 256;      // token rows per scaled-FP4 grouped-GEMM bloc
 // pass) so that the grid covers the chip.
 constexpr int kRouterTokens = 128;
 constexpr int kRouterGroupTiles = 6;
+constexpr int kRouterMaxSplits = 8;
 FT_HD inline int router_expert_tiles(int E) { return (E + 31) / 32; }
 FT_HD inline int router_splits(int T, int E, int H) {
   const int blocks = ((T + kRouterTokens - 1) / kRouterTokens) *
                      ((router_expert_tiles(E) + kRouterGroupTiles - 1) / kRouterGroupTiles);
   int s = 1;
-  while (s < 16 && blocks * s < 256 && (H / 32) % (2 * s) == 0) s *= 2;
+  while (s < kRouterMaxSplits && blocks * s < 256 && (H / 32) % (2 * s) == 0) s *= 2;
   return s;
 }
 // bytes of the router weight planes: [3 planes][E/32 tiles][H/16 K-steps][64 lanes][16 B]

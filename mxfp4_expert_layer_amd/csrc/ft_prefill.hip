@@ -217,12 +217,19 @@ __global__ __launch_bounds__(256) void k_topk_many(const float* __restrict__ log
     const int t = tb + tl;
     float v[EPL];
     uint32_t key[EPL];
-    // logit = (partial 0 + partial 1 + ...) + b, in that order
+    // logit = (partial 0 + partial 1 + ...) + b, in that order; every partial is loaded
+    // before the sum (unconditional loads of a clamped split index, unused ones ignored)
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = min(lane + 64 * i, E - 1);
-      float acc = logits[(uint64_t)t * E + e];
-      for (int sp = 1; sp < splits; ++sp) acc += logits[((uint64_t)sp * T + t) * E + e];
+      float part[kRouterMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kRouterMaxSplits; ++sp)
+        part[sp] = logits[((uint64_t)min(sp, splits - 1) * T + t) * E + e];
+      float acc = part[0];
+#pragma unroll
+      for (int sp = 1; sp < kRouterMaxSplits; ++sp)
+        if (sp < splits) acc += part[sp];
       v[i] = acc + (bias ? bias[e] : 0.f);
     }
 #pragma unroll
