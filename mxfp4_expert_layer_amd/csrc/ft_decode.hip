@@ -176,6 +176,111 @@ __device__ __forceinline__ void topk_tokens(const float* logits, int T, int E, i
   __syncthreads();
 }
 
+// Single-token top-k for E <= 256 by sorting networks: wave w sorts experts 64 w .. + 63 (one
+// per lane) by the composite key (logit order key, then the lower index first) with a bitonic
+// network of lane-pair exchanges; wave 0 then sorts the four waves' k best and keeps the first
+// k, which are the k largest logits in rank order (ties to the lower index, as the radix
+// select).  No scalar round trip per step.  Weights are the softmax over the kept logits (the
+// hardware exp: a few ulp).  Called by all 256 threads; ends synchronised.
+struct SortLds {
+  uint32_t hi[4][FT_MAX_TOPK];
+  uint32_t lo[4][FT_MAX_TOPK];
+};
+
+// v of lane (lane ^ J), with the VALU's own lane exchanges instead of the LDS crossbar
+// (checked on gfx950): DPP quad permutes for 1 and 2, row rotates for 4 and 8 (row_ror:n
+// gives lane i the value of lane i - n within its row of 16), and the gfx950 permlane swaps
+// for 16 and 32.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  if (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+  if (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);
+  if (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xf, 0xf, false);
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xf, 0xf, false);
+    return (lane & 4) ? dn : up;
+  }
+  if (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
+  if (J == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? sw[0] : sw[1];
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane & 32) ? sw[0] : sw[1];
+}
+
+template <int J>
+__device__ __forceinline__ void xor_pair(uint32_t& ohi, uint32_t& olo, uint32_t hi, uint32_t lo,
+                                         int lane) {
+  ohi = xor_lane<J>(hi, lane);
+  olo = xor_lane<J>(lo, lane);
+}
+
+__device__ __forceinline__ void bitonic64_desc(uint32_t& hi, uint32_t& lo, int lane) {
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      uint32_t ohi, olo;
+      switch (j) {
+        case 1: xor_pair<1>(ohi, olo, hi, lo, lane); break;
+        case 2: xor_pair<2>(ohi, olo, hi, lo, lane); break;
+        case 4: xor_pair<4>(ohi, olo, hi, lo, lane); break;
+        case 8: xor_pair<8>(ohi, olo, hi, lo, lane); break;
+        case 16: xor_pair<16>(ohi, olo, hi, lo, lane); break;
+        default: xor_pair<32>(ohi, olo, hi, lo, lane); break;
+      }
+      const bool other_bigger = ohi > hi || (ohi == hi && olo > lo);
+      // the lower lane of a pair keeps the larger key in descending segments
+      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
+      if (keep_max == other_bigger) { hi = ohi; lo = olo; }
+    }
+  }
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+__device__ __forceinline__ void topk_one_token(const float* logits, int E, int k, TopkLds& tk,
+                                               SortLds& sl) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = 64 * wave + lane;
+  float v = logits[min(e, E - 1)];
+  if (v != v) v = -INFINITY;                         // NaN logits never win
+  uint32_t hi = e < E ? order_key(v) : 0u;           // padding ranks below -inf
+  uint32_t lo = e < E ? ~(uint32_t)e : 0u;           // lower index first among equals
+  if (64 * wave < E) bitonic64_desc(hi, lo, lane);
+  if (lane < k) {
+    sl.hi[wave][lane] = 64 * wave < E ? hi : 0u;
+    sl.lo[wave][lane] = 64 * wave < E ? lo : 0u;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    if (E > 64) {
+      const int q = lane / k, j = lane % k;
+      hi = q < 4 ? sl.hi[q][j] : 0u;
+      lo = q < 4 ? sl.lo[q][j] : 0u;
+      bitonic64_desc(hi, lo, lane);
+    }
+    const float vl = key_value(hi);
+    const float vmax = __shfl(vl, 0, 64);
+    float p = lane < k ? __expf(vl - vmax) : 0.f;
+    float sum = p;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane < k) {
+      tk.idx[0][lane] = (int)~lo;
+      tk.w[0][lane] = p / sum;
+    }
+  }
+  __syncthreads();
+}
+
+// The list of a single token: item j is winner j (all distinct), then the shared experts.
+__device__ __forceinline__ void list_one_token(const TopkLds& tk, int k, int n_shared,
+                                               const int32_t* e2s, struct ListLds& L);
+
 struct ListLds {
   int n_items;
   int wave_tot[4];
@@ -244,6 +349,22 @@ __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int 
     if (t < T) { L.tok[it][t] = (uint8_t)t; L.jj[it][t] = (uint8_t)(k + sh); }
   }
   if (tid == 0) L.n_items = n_routed + n_shared;
+  __syncthreads();
+}
+
+__device__ __forceinline__ void list_one_token(const TopkLds& tk, int k, int n_shared,
+                                               const int32_t* e2s, ListLds& L) {
+  const int tid = threadIdx.x;
+  if (tid < k + n_shared) {
+    const bool sh = tid >= k;
+    const int e = sh ? -1 - (tid - k) : tk.idx[0][tid];
+    L.expert[tid] = e;
+    L.slot[tid] = sh ? e : e2s[e];
+    L.ntok[tid] = 1;
+    L.tok[tid][0] = 0;
+    L.jj[tid][0] = (uint8_t)tid;
+  }
+  if (tid == 0) L.n_items = k + n_shared;
   __syncthreads();
 }
 
@@ -382,10 +503,15 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
   __shared__ ListLds ls;
   __shared__ f32x4 red[4][2][64];
   if (EPL > 0) {
-    topk_tokens<(EPL > 0 ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk,
-                                     (float (*)[FT_MAX_TOPK])&red[0][0][0],
-                                     (int (*)[FT_MAX_TOPK])&red[2][0][0]);
-    build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
+    if (a.T == 1 && a.E <= 256) {
+      topk_one_token(a.logits, a.E, a.k, tk, *(SortLds*)&red[0][0][0]);
+      list_one_token(tk, a.k, a.n_shared, a.e2s, ls);
+    } else {
+      topk_tokens<(EPL > 0 ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk,
+                                       (float (*)[FT_MAX_TOPK])&red[0][0][0],
+                                       (int (*)[FT_MAX_TOPK])&red[2][0][0]);
+      build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
+    }
     if (blockIdx.x == 0)
       store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items, true);
   } else if (EPL < 0) {
