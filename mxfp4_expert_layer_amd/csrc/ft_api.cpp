@@ -22,6 +22,7 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
                         int32_t* idx_host, float* w_host, const uint16_t* x, uint16_t* x_host,
                         int H, hipStream_t st);
 extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
+extern "C" int ftk_down_combines(const DecodeLaunch* a);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
                            float* y, hipStream_t st);
 extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
@@ -409,9 +410,11 @@ static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipS
   if (route == 2)
     HIP_TRY((hipError_t)ftk_topk(l->logits, T, d.E, d.k, l->idx, l->w, nullptr, nullptr, nullptr,
                                  nullptr, d.H, st));
-  const DecodeLaunch a = launch_args(l, x, T, route, l->items, l->n_items, T * d.k + d.n_shared);
+  DecodeLaunch a = launch_args(l, x, T, route, l->items, l->n_items, T * d.k + d.n_shared);
+  a.y = y;
   HIP_TRY((hipError_t)ftk_decode_experts(&a, st, prof_events(l)));
-  HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
+  if (!ftk_down_combines(&a))
+    HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, d.k, d.n_shared, y, st));
   return FT_OK;
 }
 

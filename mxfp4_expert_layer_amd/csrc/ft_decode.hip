@@ -176,110 +176,86 @@ __device__ __forceinline__ void topk_tokens(const float* logits, int T, int E, i
   __syncthreads();
 }
 
-// Single-token top-k for E <= 256 by sorting networks: wave w sorts experts 64 w .. + 63 (one
-// per lane) by the composite key (logit order key, then the lower index first) with a bitonic
-// network of lane-pair exchanges; wave 0 then sorts the four waves' k best and keeps the first
-// k, which are the k largest logits in rank order (ties to the lower index, as the radix
-// select).  No scalar round trip per step.  Weights are the softmax over the kept logits (the
-// hardware exp: a few ulp).  Called by all 256 threads; ends synchronised.
+// Single-token top-k for E <= 256 by sorting networks on 64-bit keys: high word = the logit's
+// order key, low word = (255 - expert) << 24 | (slot + 1), so among equal logits the lower
+// expert ranks first and the expert's pool slot rides along as payload (the index field is
+// unique, so the payload never decides a comparison).  Wave w sorts experts 64 w .. + 63 (one
+// per lane) with a bitonic network of lane-pair exchanges; wave 0 then merges the four waves'
+// R best (R = 8 or 16 >= k) with the bitonic merge network, which leaves the k largest
+// logits in rank order in lanes 0 .. k-1.
 struct SortLds {
-  uint32_t hi[4][FT_MAX_TOPK];
-  uint32_t lo[4][FT_MAX_TOPK];
+  uint64_t key[4][FT_MAX_TOPK];
 };
 
 // v of lane (lane ^ J), with the VALU's own lane exchanges instead of the LDS crossbar
 // (checked on gfx950): DPP quad permutes for 1 and 2, row rotates for 4 and 8 (row_ror:n
 // gives lane i the value of lane i - n within its row of 16), and the gfx950 permlane swaps
-// for 16 and 32.
+// for 16 and 32.  Lane-dependent choices use constant lane masks (one v_cndmask).
 template <int J>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   if (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
   if (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);
   if (J == 4) {
     const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xf, 0xf, false);
     const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xf, 0xf, false);
-    return (lane & 4) ? dn : up;
+    return __builtin_amdgcn_inverse_ballot_w64(0xF0F0F0F0F0F0F0F0ull) ? dn : up;
   }
   if (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
   if (J == 16) {
     const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? sw[0] : sw[1];
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? sw[0] : sw[1];
   }
   const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return (lane & 32) ? sw[0] : sw[1];
+  return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? sw[0] : sw[1];
 }
 
-template <int J>
-__device__ __forceinline__ void xor_pair(uint32_t& ohi, uint32_t& olo, uint32_t hi, uint32_t lo,
-                                         int lane) {
-  ohi = xor_lane<J>(hi, lane);
-  olo = xor_lane<J>(lo, lane);
+// Lanes of a bitonic compare-exchange step (merge size kk, distance j) that keep the larger
+// key: the lower lane of a pair in descending blocks, the upper one in ascending blocks.
+constexpr uint64_t keep_max_lanes(int kk, int j) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & j) == 0) == ((l & kk) == 0)) m |= 1ull << l;
+  return m;
 }
 
-__device__ __forceinline__ void bitonic64_desc(uint32_t& hi, uint32_t& lo, int lane) {
-#pragma unroll
-  for (int kk = 2; kk <= 64; kk <<= 1) {
-#pragma unroll
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      uint32_t ohi, olo;
-      switch (j) {
-        case 1: xor_pair<1>(ohi, olo, hi, lo, lane); break;
-        case 2: xor_pair<2>(ohi, olo, hi, lo, lane); break;
-        case 4: xor_pair<4>(ohi, olo, hi, lo, lane); break;
-        case 8: xor_pair<8>(ohi, olo, hi, lo, lane); break;
-        case 16: xor_pair<16>(ohi, olo, hi, lo, lane); break;
-        default: xor_pair<32>(ohi, olo, hi, lo, lane); break;
-      }
-      const bool other_bigger = ohi > hi || (ohi == hi && olo > lo);
-      // the lower lane of a pair keeps the larger key in descending segments
-      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
-      if (keep_max == other_bigger) { hi = ohi; lo = olo; }
-    }
-  }
+template <int KK, int J>
+__device__ __forceinline__ void cmpx(uint64_t& key) {
+  const uint32_t ohi = xor_lane<J>((uint32_t)(key >> 32));
+  const uint32_t olo = xor_lane<J>((uint32_t)key);
+  const uint64_t other = ((uint64_t)ohi << 32) | olo;
+  // take the partner's key where (partner larger) == (this lane keeps the max)
+  const uint64_t gt = __builtin_amdgcn_ballot_w64(other > key);
+  if (__builtin_amdgcn_inverse_ballot_w64(gt ^ ~keep_max_lanes(KK, J))) key = other;
+}
+
+// bitonic merge stage of size KK: distances KK/2 .. 1
+template <int KK, int J = KK / 2>
+__device__ __forceinline__ void bitonic_merge(uint64_t& key) {
+  cmpx<KK, J>(key);
+  if constexpr (J > 1) bitonic_merge<KK, J / 2>(key);
+}
+
+// sort of the 64 lanes' keys, descending from lane 0
+__device__ __forceinline__ void bitonic64_desc(uint64_t& key) {
+  bitonic_merge<2>(key);
+  bitonic_merge<4>(key);
+  bitonic_merge<8>(key);
+  bitonic_merge<16>(key);
+  bitonic_merge<32>(key);
+  bitonic_merge<64>(key);
 }
 
 __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-__device__ __forceinline__ void topk_one_token(const float* logits, int E, int k, TopkLds& tk,
-                                               SortLds& sl) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = 64 * wave + lane;
-  float v = logits[min(e, E - 1)];
-  if (v != v) v = -INFINITY;                         // NaN logits never win
-  uint32_t hi = e < E ? order_key(v) : 0u;           // padding ranks below -inf
-  uint32_t lo = e < E ? ~(uint32_t)e : 0u;           // lower index first among equals
-  if (64 * wave < E) bitonic64_desc(hi, lo, lane);
-  if (lane < k) {
-    sl.hi[wave][lane] = 64 * wave < E ? hi : 0u;
-    sl.lo[wave][lane] = 64 * wave < E ? lo : 0u;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    if (E > 64) {
-      const int q = lane / k, j = lane % k;
-      hi = q < 4 ? sl.hi[q][j] : 0u;
-      lo = q < 4 ? sl.lo[q][j] : 0u;
-      bitonic64_desc(hi, lo, lane);
-    }
-    const float vl = key_value(hi);
-    const float vmax = __shfl(vl, 0, 64);
-    float p = lane < k ? __expf(vl - vmax) : 0.f;
-    float sum = p;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    if (lane < k) {
-      tk.idx[0][lane] = (int)~lo;
-      tk.w[0][lane] = p / sum;
-    }
-  }
-  __syncthreads();
-}
+struct ListLds;
 
-// The list of a single token: item j is winner j (all distinct), then the shared experts.
-__device__ __forceinline__ void list_one_token(const TopkLds& tk, int k, int n_shared,
-                                               const int32_t* e2s, struct ListLds& L);
+// Top-k of one token's logits and its work list (item j = winner j, then the shared
+// experts).  Called by all 256 threads; ends synchronised.
+__device__ __forceinline__ void route_one_token(const float* logits, const int32_t* e2s, int E,
+                                                int k, int n_shared, TopkLds& tk, ListLds& L,
+                                                SortLds& sl);
 
 struct ListLds {
   int n_items;
@@ -352,19 +328,65 @@ __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int 
   __syncthreads();
 }
 
-__device__ __forceinline__ void list_one_token(const TopkLds& tk, int k, int n_shared,
-                                               const int32_t* e2s, ListLds& L) {
-  const int tid = threadIdx.x;
-  if (tid < k + n_shared) {
-    const bool sh = tid >= k;
-    const int e = sh ? -1 - (tid - k) : tk.idx[0][tid];
-    L.expert[tid] = e;
-    L.slot[tid] = sh ? e : e2s[e];
-    L.ntok[tid] = 1;
-    L.tok[tid][0] = 0;
-    L.jj[tid][0] = (uint8_t)tid;
+__device__ __forceinline__ void route_one_token(const float* logits, const int32_t* e2s, int E,
+                                                int k, int n_shared, TopkLds& tk, ListLds& L,
+                                                SortLds& sl) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = 64 * wave + lane, ec = min(e, E - 1);
+  float v = logits[ec];
+  const int slot = e2s[ec];                          // issued with the logit load
+  if (v != v) v = -INFINITY;                         // NaN logits never win
+  uint64_t key = e < E ? ((uint64_t)order_key(v) << 32) |
+                             ((uint32_t)(255 - e) << 24) | ((uint32_t)(slot + 1) & 0xFFFFFFu)
+                       : 0ull;                       // padding ranks below -inf
+  const bool live = 64 * wave < E;
+  if (live) bitonic64_desc(key);
+  if (lane < FT_MAX_TOPK) sl.key[wave][lane] = live && lane < k ? key : 0ull;
+  __syncthreads();
+  if (wave == 0) {
+    if (E > 64) {
+      // runs of R >= k: run q in lanes R q .. R q + R - 1, odd runs reversed, so every pair of
+      // runs is a bitonic sequence; the merge network then sorts lanes descending
+      if (k <= 8) {
+        const int q = lane >> 3, i = lane & 7;
+        key = q < 4 ? sl.key[q][(q & 1) ? 7 - i : i] : 0ull;
+        bitonic_merge<16>(key);
+        bitonic_merge<32>(key);
+      } else {
+        const int q = lane >> 4, i = lane & 15;
+        key = sl.key[q][(q & 1) ? 15 - i : i];
+        bitonic_merge<32>(key);
+        bitonic_merge<64>(key);
+      }
+    }
+    const float vl = key_value((uint32_t)(key >> 32));
+    const float vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vl)));
+    const float p = lane < k ? __expf(vl - vmax) : 0.f;
+    // the k <= 16 terms sit in lanes 0..15: a butterfly over the row gives every lane of it
+    // the same sum
+    float sum = p;
+    sum += __uint_as_float(xor_lane<1>(__float_as_uint(sum)));
+    sum += __uint_as_float(xor_lane<2>(__float_as_uint(sum)));
+    sum += __uint_as_float(xor_lane<4>(__float_as_uint(sum)));
+    sum += __uint_as_float(xor_lane<8>(__float_as_uint(sum)));
+    const uint32_t lo = (uint32_t)key;
+    const int ew = 255 - (int)(lo >> 24);
+    if (lane < k) {
+      tk.idx[0][lane] = ew;
+      tk.w[0][lane] = p / sum;
+      L.expert[lane] = ew;
+      L.slot[lane] = (int)(lo & 0xFFFFFFu) - 1;
+    } else if (lane < k + n_shared) {
+      L.expert[lane] = k - 1 - lane;
+      L.slot[lane] = k - 1 - lane;
+    }
+    if (lane < k + n_shared) {
+      L.ntok[lane] = 1;
+      L.tok[lane][0] = 0;
+      L.jj[lane][0] = (uint8_t)lane;
+    }
+    if (lane == 0) L.n_items = k + n_shared;
   }
-  if (tid == 0) L.n_items = k + n_shared;
   __syncthreads();
 }
 
@@ -504,8 +526,7 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
   __shared__ f32x4 red[4][2][64];
   if (EPL > 0) {
     if (a.T == 1 && a.E <= 256) {
-      topk_one_token(a.logits, a.E, a.k, tk, *(SortLds*)&red[0][0][0]);
-      list_one_token(tk, a.k, a.n_shared, a.e2s, ls);
+      route_one_token(a.logits, a.e2s, a.E, a.k, a.n_shared, tk, ls, *(SortLds*)&red[0][0][0]);
     } else {
       topk_tokens<(EPL > 0 ? EPL : 1)>(a.logits, a.T, a.E, a.k, tk,
                                        (float (*)[FT_MAX_TOPK])&red[0][0][0],
@@ -608,6 +629,53 @@ __global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
   }
 }
 
+// Down projection and weighted combine in one pass, for calls whose experts all run on the
+// GPU.  A workgroup owns one 16-row tile of y for every token; wave w walks items w, w + NW,
+// ... (all K chunks of an item, loads issued UNR chunks at a time) and folds each item's
+// columns into its own per-token partial in LDS with the routing weight (weight 1 for shared
+// experts); the waves' partials are then summed in wave order.  Every sum has a fixed order,
+// so the result does not depend on timing.
+template <int NW, int UNR>
+__global__ __launch_bounds__(64 * NW) void k_down_combine(DecodeLaunch a) {
+  __shared__ float part[NW][kMaxCols][kTileRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int RT = a.H / kTileRows, KC = a.I / kTileK;
+  const int n_items = min(*a.n_items, kMaxItems);
+  const int kk = a.k + a.n_shared;
+  for (int rt = blockIdx.x; rt < RT; rt += gridDim.x) {
+    for (int i = lane; i < a.T * kTileRows; i += 64) part[wave][i / kTileRows][i % kTileRows] = 0.f;
+    __builtin_amdgcn_wave_barrier();
+    for (int iti = wave; iti < n_items; iti += NW) {
+      const WorkItem& it = a.items[iti];
+      const int ntok = it.ntok;
+      const bool col = n < ntok;
+      const uint8_t* blob = blob_of(it.expert, it.slot, a.pool, a.shared, a.stride);
+      const uint8_t* codes[1] = {blob + a.L.off[4]};
+      const uint8_t* scales[1] = {blob + a.L.off[5]};
+      const uint16_t* brow = a.h + ((uint64_t)iti * kMaxCols + n) * a.I + 32 * g;
+      f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+      tile_gemv<1, UNR>(codes, scales, (uint64_t)rt * KC, KC, 0, 1, brow, col, lane, acc);
+      if (col) {
+        const int pr = it.pair[n], t = pr / kk, j = pr % kk;
+        const float wt = j < a.k ? a.w_out[t * a.k + j] : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          part[wave][t][4 * g + r] = fmaf(wt, acc[0][r], part[wave][t][4 * g + r]);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.T * kTileRows; i += 64 * NW) {
+      const int t = i / kTileRows, r = i % kTileRows;
+      float s = part[0][t][r];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) s += part[w2][t][r];
+      a.y[(uint64_t)t * a.H + rt * kTileRows + r] = s;
+    }
+    __syncthreads();
+  }
+}
+
 // y[t][r] = sum_{j<k} w[t][j] P[t*kk + j][r] + sum_s P[t*kk + k + s][r]; all loads of an
 // output are issued together.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ P,
@@ -674,12 +742,13 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
 
 // ev: null, or 4 events [gate/up start, stop, down start, stop] that the dispatches record
 // themselves (hipExtLaunchKernelGGL), so host-side gaps are not counted.
-#define FT_LAUNCH(kern, grid, evs, eve, arg)                                                \
+#define FT_LAUNCH_NT(kern, grid, nt, evs, eve, arg)                                         \
   do {                                                                                      \
     auto* kfn_ = kern;                                                                      \
-    if (evs) hipExtLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, evs, eve, 0, arg);         \
-    else hipLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, arg);                             \
+    if (evs) hipExtLaunchKernelGGL(kfn_, grid, dim3(nt), 0, st, evs, eve, 0, arg);          \
+    else hipLaunchKernelGGL(kfn_, grid, dim3(nt), 0, st, arg);                              \
   } while (0)
+#define FT_LAUNCH(kern, grid, evs, eve, arg) FT_LAUNCH_NT(kern, grid, 256, evs, eve, arg)
 
 // EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts;
 // EPL < 0: list built from routed indices
@@ -694,6 +763,14 @@ static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, 
     FT_LAUNCH((k_gateup<1, 4, EPL>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e0, e1, a);
 }
 
+// Whether the down kernel also combines into y: for calls whose experts all run on the GPU,
+// when the one-workgroup-per-row-tile grid covers the chip or the list is short (latency
+// bound); otherwise down writes per-(token, choice) partials for k_combine.
+extern "C" int ftk_down_combines(const DecodeLaunch* ap) {
+  const DecodeLaunch& a = *ap;
+  return a.route != 0 && (a.max_items <= 16 || a.H / kTileRows >= 256);
+}
+
 extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
   const DecodeLaunch& a = *ap;
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
@@ -705,10 +782,20 @@ extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const 
   else if (a.E <= 256) launch_gateup<4>(a, st, e0, e1);
   else launch_gateup<16>(a, st, e0, e1);
   const int cap = 2048, KC = a.I / kTileK, RT = a.H / kTileRows;
-  if (KC >= 8)
+  if (ftk_down_combines(ap)) {
+    // down and combine in one kernel, one workgroup per row tile
+    const dim3 grid(RT);
+    if (a.max_items <= 16) {
+      if (KC >= 8) FT_LAUNCH_NT((k_down_combine<8, 8>), grid, 512, e2, e3, a);
+      else FT_LAUNCH_NT((k_down_combine<8, 4>), grid, 512, e2, e3, a);
+    } else {
+      FT_LAUNCH_NT((k_down_combine<16, 4>), grid, 1024, e2, e3, a);
+    }
+  } else if (KC >= 8) {
     FT_LAUNCH((k_down<2, 4>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e2, e3, a);
-  else
+  } else {
     FT_LAUNCH((k_down<1, 4>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e2, e3, a);
+  }
   return (int)hipGetLastError();
 }
 

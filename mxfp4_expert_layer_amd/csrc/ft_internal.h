@@ -94,7 +94,8 @@ struct DecodeLaunch {
   uint64_t stride;
   BlobLayout L;
   uint16_t* h;                  // [max_items][16][I]
-  float* P;                     // [T * (k + n_shared)][H]
+  float* P;                     // [T * (k + n_shared)][H] (miss path: combined by k_combine)
+  float* y;                     // [T][H]: all-resident calls combine inside the down kernel
 };
 
 // Prefill of T tokens through an all-resident layer (slot e = expert e).
