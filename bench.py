@@ -3,6 +3,7 @@
 
 Workloads (seeded synthetic layers, no trained weights exist for these shapes):
   decode-35b-a3b   hidden 2048, 256 experts, top-8, intermediate 512, MXFP4   (default)
+  decode-35b-a3b-nvfp4  the same layer with NVFP4 experts (E4M3 per 16, tensor scale 1/64)
   decode-284b      hidden 4096, 256 experts + 1 shared, top-6, intermediate 2048, MXFP4
   miss-path-284b   the 284B-class layer with a 48-slot pool, q* split of misses
   prefill-753b     4096 tokens through hidden 6144, 160 experts, top-8, intermediate 2048,
@@ -13,9 +14,9 @@ layer is replicated to several device copies (different addresses) so repeated s
 not served from the 256 MB Infinity Cache.
 
 roofline: the gate/up kernel reads two thirds of the expert bytes and dominates; its
-algorithmic bytes per launch = distinct experts of the call x 2*I*H*(1/2 + 1/32) bytes
-(codes + E8M0 scales), divided by its mean duration from HIP events recorded on its own
-stream around it inside a captured replay.  peak = 8 TB/s (MI355X HBM3E).
+algorithmic bytes per launch = distinct experts of the call x 2*I*H*(1/2 + 1/B) bytes
+(codes + one scale byte per block of B = 32 (MXFP4) or 16 (NVFP4)), divided by its mean
+duration from start/stop events that its dispatches record.  peak = 8 TB/s (MI355X HBM3E).
 cpu_baseline: the float64 oracle on a bounded sample of the same steps (host cores).
 """
 from __future__ import annotations
@@ -35,6 +36,7 @@ HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
     "decode-35b-a3b": dict(cfg="cfg2", T=1, copies=8, steps=2048, warmup=128),
+    "decode-35b-a3b-nvfp4": dict(cfg="cfg2nv", T=1, copies=8, steps=2048, warmup=128),
     "decode-284b": dict(cfg="cfg3", T=1, copies=4, steps=2048, warmup=128),
     "miss-path-284b": dict(cfg="cfg4", T=1, copies=1, steps=64, warmup=64),
     "prefill-753b": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3),
@@ -195,8 +197,9 @@ def bench_decode(args, wl):
         torch.cuda.synchronize()
         uniq.append(len(np.unique(idx.cpu().numpy())) + cfg.n_shared)
     n_exp = float(np.mean(uniq))
-    gu_bytes_expert = 2 * cfg.I * cfg.H * (0.5 + 1 / 32)
-    dn_bytes_expert = cfg.H * cfg.I * (0.5 + 1 / 32)
+    per_weight = 0.5 + 1 / cfg.block          # E2M1 code + one scale byte per block
+    gu_bytes_expert = 2 * cfg.I * cfg.H * per_weight
+    dn_bytes_expert = cfg.H * cfg.I * per_weight
     router_bytes = cfg.E * cfg.H * 4
     achieved = n_exp * gu_bytes_expert / (gate_us * 1e-6) / 1e9
     step_bytes = n_exp * (gu_bytes_expert + dn_bytes_expert) + router_bytes

@@ -151,7 +151,9 @@ typedef struct ft_decode_stats {
  * slots on the internal copy stream, enqueues the GPU experts on `stream`, computes the
  * other misses on host cores, enqueues their results and the combine, and returns; y is
  * valid after `stream` syncs.  stats may be NULL (asynchronous path: counts are filled
- * only where known on the host, i.e. in the miss path).
+ * only where known on the host, i.e. in the miss path).  Both weight formats decode on the
+ * GPU and on the host: an NVFP4 weight is its E2M1 value times its block's E4M3 scale, and
+ * each matrix's fp32 tensor scale (blob header) multiplies that matrix's product.
  */
 FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T, float* y,
                          ft_decode_stats* stats, void* stream);

@@ -14,6 +14,11 @@
 //   k_down     per (expert, 16-row tile of W_d): y_e = W_d h into the partial buffer
 //              P[t * kk + j] (j = top-k rank, k + s for shared expert s).
 //   k_combine  y_t = sum_j w_tj P[t][j] + sum_s P[t][k + s], in that order.
+// (k_down_combine does both of the last two in one pass where its grid fills the chip.)
+// Both block-scaled formats run through the same kernels (template parameter FMT): MXFP4
+// scales are powers of two and go into the hardware FP4 -> bf16 convert; an NVFP4 weight is
+// E2M1 x E4M3 (at most 6 significant bits, so exact in bf16) and its fp32 tensor scale,
+// read from the blob header, multiplies the fp32 result of each matrix.
 // Workgroups never wait on each other inside a kernel: on this chip a device-scope fence
 // writes back and invalidates the issuing XCD's L2, so data moves between workgroups only
 // at kernel boundaries.
@@ -466,12 +471,21 @@ __device__ __forceinline__ const uint8_t* blob_of(int expert, int slot, const ui
   return expert >= 0 ? pool + (uint64_t)slot * stride : shared + (uint64_t)(-1 - expert) * stride;
 }
 
+// Tensor scale of matrix m (0 gate, 1 up, 2 down) of a blob: the header's field for NVFP4,
+// 1 for MXFP4 (whose header holds 1 too, but the read is skipped).
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const uint8_t* blob, int m) {
+  return FMT == FT_MXFP4 ? 1.f : ((const float*)(blob + offsetof(BlobHeader, tensor_scale)))[m];
+}
+
 // acc[m] += W_m[tile rows][chunks ks, ks+kstep, ...] x B for NM matrices sharing the B
 // operand (gate and up share x).  Each lane owns 32 K values of one tile row per chunk: one
 // 128-bit code load, one scale byte and four MFMA k-steps.  The loads of UNR chunks are all
 // issued before any is consumed.  brow: this lane's B column (token row or h row) at K
 // offset 32*g; bcol false makes the column zero without loading it.
-template <int NM, int UNR>
+// Scales: MXFP4 one E8M0 byte per lane per tile; NVFP4 two E4M3 bytes per lane per tile (the
+// blocks of the lane's first and second 16 K values).
+template <int NM, int UNR, int FMT>
 __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uint8_t* const* scales,
                                           uint64_t tile0, int KC, int ks, int kstep,
                                           const uint16_t* brow, bool bcol, int lane, f32x4* acc) {
@@ -487,7 +501,8 @@ __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uin
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         cw[u][m] = ok ? ((const uint4*)codes[m])[tile * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
-        sc[u][m] = ok ? scales[m][tile * 64 + lane] : 127u;
+        if (FMT == FT_MXFP4) sc[u][m] = ok ? scales[m][tile * 64 + lane] : 127u;
+        else sc[u][m] = ok ? ((const uint16_t*)scales[m])[tile * 64 + lane] : 0x3838u;
       }
     }
 #pragma unroll
@@ -501,12 +516,20 @@ __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uin
     for (int u = 0; u < UNR; ++u) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const float s = e8m0_f32(sc[u][m]);
         const uint32_t wv[4] = {cw[u][m].x, cw[u][m].y, cw[u][m].z, cw[u][m].w};
+        if (FMT == FT_MXFP4) {
+          const float s = e8m0_f32(sc[u][m]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(wv[i], s),
-                                                           as_bf16x8(xb[u][i]), acc[m], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16(wv[i], s),
+                                                             as_bf16x8(xb[u][i]), acc[m], 0, 0, 0);
+        } else {
+          const float s0 = e4m3_f32_fast(sc[u][m] & 0xffu), s1 = e4m3_f32_fast(sc[u][m] >> 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_bf16_mul(wv[i], i < 2 ? s0 : s1),
+                                                             as_bf16x8(xb[u][i]), acc[m], 0, 0, 0);
+        }
       }
     }
   }
@@ -518,7 +541,7 @@ __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uin
 // EPL > 0: the prologue takes the top-k of the logits (E <= 64 * EPL); EPL == 0: the
 // work list is read from memory (miss path); EPL < 0: the list is built from the routed
 // indices a previous k_topk wrote.  Workgroup 0 publishes the list for k_down.
-template <int KSPLIT, int UNR, int EPL>
+template <int KSPLIT, int UNR, int EPL, int FMT>
 __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
   constexpr int RPW = 4 / KSPLIT;
   __shared__ TopkLds tk;
@@ -556,13 +579,17 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
     const int expert = ls.expert[iti], slot = ls.slot[iti], ntok = ls.ntok[iti];
     const bool active = rt < RT && (expert < 0 || slot >= 0);
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float tsg = 1.f, tsu = 1.f;
     if (active) {
       const uint8_t* blob = blob_of(expert, slot, a.pool, a.shared, a.stride);
       const uint8_t* codes[2] = {blob + a.L.off[0], blob + a.L.off[2]};
       const uint8_t* scales[2] = {blob + a.L.off[1], blob + a.L.off[3]};
       const bool col = n < ntok;
       const uint16_t* brow = a.x + (uint64_t)(col ? ls.tok[iti][n] : 0) * a.H + 32 * g;
-      tile_gemv<2, UNR>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane, acc);
+      tile_gemv<2, UNR, FMT>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane,
+                             acc);
+      tsg = tensor_scale<FMT>(blob, 0);
+      tsu = tensor_scale<FMT>(blob, 1);
     }
     if (KSPLIT > 1) {
       red[wave][0][lane] = acc[0];
@@ -579,7 +606,8 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
     if (ks == 0 && active && n < ntok) {
       uint16_t hv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[r] = f32_to_bf16_rne(silu_f32(acc[0][r]) * acc[1][r]);
+      for (int r = 0; r < 4; ++r)
+        hv[r] = f32_to_bf16_rne(silu_f32(tsg * acc[0][r]) * (tsu * acc[1][r]));
       const uint2 pk = make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
                                   (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
       *(uint2*)(a.h + ((uint64_t)iti * kMaxCols + n) * a.I + rt * kTileRows + 4 * g) = pk;
@@ -588,7 +616,7 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
   }
 }
 
-template <int KSPLIT, int UNR>
+template <int KSPLIT, int UNR, int FMT>
 __global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
   constexpr int RPW = 4 / KSPLIT;
   __shared__ f32x4 red[4][64];
@@ -605,13 +633,16 @@ __global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
     const bool active = rt < RT && (it.expert < 0 || it.slot >= 0);
     const int ntok = it.ntok;
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    float tsd = 1.f;
     if (active) {
       const uint8_t* blob = blob_of(it.expert, it.slot, a.pool, a.shared, a.stride);
       const uint8_t* codes[1] = {blob + a.L.off[4]};
       const uint8_t* scales[1] = {blob + a.L.off[5]};
       const bool col = n < ntok;
       const uint16_t* brow = a.h + ((uint64_t)iti * kMaxCols + n) * a.I + 32 * g;
-      tile_gemv<1, UNR>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane, acc);
+      tile_gemv<1, UNR, FMT>(codes, scales, (uint64_t)rt * KC, KC, ks, KSPLIT, brow, col, lane,
+                             acc);
+      tsd = tensor_scale<FMT>(blob, 2);
     }
     if (KSPLIT > 1) {
       red[wave][lane] = acc[0];
@@ -623,7 +654,8 @@ __global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
     }
     if (ks == 0 && active && n < ntok) {
       float* dst = a.P + (uint64_t)it.pair[n] * a.H + rt * kTileRows + 4 * g;
-      *(float4*)dst = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+      *(float4*)dst = make_float4(tsd * acc[0][0], tsd * acc[0][1], tsd * acc[0][2],
+                                  tsd * acc[0][3]);
     }
     if (KSPLIT > 1) __syncthreads();
   }
@@ -635,7 +667,7 @@ __global__ __launch_bounds__(256) void k_down(DecodeLaunch a) {
 // columns into its own per-token partial in LDS with the routing weight (weight 1 for shared
 // experts); the waves' partials are then summed in wave order.  Every sum has a fixed order,
 // so the result does not depend on timing.
-template <int NW, int UNR>
+template <int NW, int UNR, int FMT>
 __global__ __launch_bounds__(64 * NW) void k_down_combine(DecodeLaunch a) {
   __shared__ float part[NW][kMaxCols][kTileRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -655,13 +687,14 @@ __global__ __launch_bounds__(64 * NW) void k_down_combine(DecodeLaunch a) {
       const uint8_t* scales[1] = {blob + a.L.off[5]};
       const uint16_t* brow = a.h + ((uint64_t)iti * kMaxCols + n) * a.I + 32 * g;
       f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-      tile_gemv<1, UNR>(codes, scales, (uint64_t)rt * KC, KC, 0, 1, brow, col, lane, acc);
+      tile_gemv<1, UNR, FMT>(codes, scales, (uint64_t)rt * KC, KC, 0, 1, brow, col, lane, acc);
+      const float tsd = tensor_scale<FMT>(blob, 2);
       if (col) {
         const int pr = it.pair[n], t = pr / kk, j = pr % kk;
         const float wt = j < a.k ? a.w_out[t * a.k + j] : 1.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          part[wave][t][4 * g + r] = fmaf(wt, acc[0][r], part[wave][t][4 * g + r]);
+          part[wave][t][4 * g + r] = fmaf(wt, tsd * acc[0][r], part[wave][t][4 * g + r]);
       }
     }
     __syncthreads();
@@ -750,19 +783,6 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
   } while (0)
 #define FT_LAUNCH(kern, grid, evs, eve, arg) FT_LAUNCH_NT(kern, grid, 256, evs, eve, arg)
 
-// EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts;
-// EPL < 0: list built from routed indices
-template <int EPL>
-static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const int cap = 2048, KC = a.H / kTileK, RT = a.I / kTileRows;
-  if (KC >= 16)
-    FT_LAUNCH((k_gateup<4, 4, EPL>), dim3(grid_for(a.max_items * RT, cap)), e0, e1, a);
-  else if (KC >= 8)
-    FT_LAUNCH((k_gateup<2, 4, EPL>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e0, e1, a);
-  else
-    FT_LAUNCH((k_gateup<1, 4, EPL>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e0, e1, a);
-}
-
 // Whether the down kernel also combines into y: for calls whose experts all run on the GPU,
 // when the one-workgroup-per-row-tile grid covers the chip or the list is short (latency
 // bound); otherwise down writes per-(token, choice) partials for k_combine.
@@ -771,31 +791,51 @@ extern "C" int ftk_down_combines(const DecodeLaunch* ap) {
   return a.route != 0 && (a.max_items <= 16 || a.H / kTileRows >= 256);
 }
 
-extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
-  const DecodeLaunch& a = *ap;
+// EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts;
+// EPL < 0: list built from routed indices
+template <int EPL, int FMT>
+static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const int cap = 2048, KC = a.H / kTileK, RT = a.I / kTileRows;
+  if (KC >= 16)
+    FT_LAUNCH((k_gateup<4, 4, EPL, FMT>), dim3(grid_for(a.max_items * RT, cap)), e0, e1, a);
+  else if (KC >= 8)
+    FT_LAUNCH((k_gateup<2, 4, EPL, FMT>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e0,
+              e1, a);
+  else
+    FT_LAUNCH((k_gateup<1, 4, EPL, FMT>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e0,
+              e1, a);
+}
+
+template <int FMT>
+static void launch_experts(const DecodeLaunch& a, hipStream_t st, const hipEvent_t* ev) {
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-  if (a.route == 0) launch_gateup<0>(a, st, e0, e1);
-  else if (a.route == 2) launch_gateup<-1>(a, st, e0, e1);
-  else if (a.E <= 64) launch_gateup<1>(a, st, e0, e1);
-  else if (a.E <= 128) launch_gateup<2>(a, st, e0, e1);
-  else if (a.E <= 256) launch_gateup<4>(a, st, e0, e1);
-  else launch_gateup<16>(a, st, e0, e1);
+  if (a.route == 0) launch_gateup<0, FMT>(a, st, e0, e1);
+  else if (a.route == 2) launch_gateup<-1, FMT>(a, st, e0, e1);
+  else if (a.E <= 64) launch_gateup<1, FMT>(a, st, e0, e1);
+  else if (a.E <= 128) launch_gateup<2, FMT>(a, st, e0, e1);
+  else if (a.E <= 256) launch_gateup<4, FMT>(a, st, e0, e1);
+  else launch_gateup<16, FMT>(a, st, e0, e1);
   const int cap = 2048, KC = a.I / kTileK, RT = a.H / kTileRows;
-  if (ftk_down_combines(ap)) {
+  if (ftk_down_combines(&a)) {
     // down and combine in one kernel, one workgroup per row tile
     const dim3 grid(RT);
     if (a.max_items <= 16) {
-      if (KC >= 8) FT_LAUNCH_NT((k_down_combine<8, 8>), grid, 512, e2, e3, a);
-      else FT_LAUNCH_NT((k_down_combine<8, 4>), grid, 512, e2, e3, a);
+      if (KC >= 8) FT_LAUNCH_NT((k_down_combine<8, 8, FMT>), grid, 512, e2, e3, a);
+      else FT_LAUNCH_NT((k_down_combine<8, 4, FMT>), grid, 512, e2, e3, a);
     } else {
-      FT_LAUNCH_NT((k_down_combine<16, 4>), grid, 1024, e2, e3, a);
+      FT_LAUNCH_NT((k_down_combine<16, 4, FMT>), grid, 1024, e2, e3, a);
     }
   } else if (KC >= 8) {
-    FT_LAUNCH((k_down<2, 4>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e2, e3, a);
+    FT_LAUNCH((k_down<2, 4, FMT>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e2, e3, a);
   } else {
-    FT_LAUNCH((k_down<1, 4>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e2, e3, a);
+    FT_LAUNCH((k_down<1, 4, FMT>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e2, e3, a);
   }
+}
+
+extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
+  if (ap->L.fmt == FT_MXFP4) launch_experts<FT_MXFP4>(*ap, st, ev);
+  else launch_experts<FT_NVFP4>(*ap, st, ev);
   return (int)hipGetLastError();
 }
 

@@ -46,6 +46,22 @@ __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float scale) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Eight E2M1 codes times an arbitrary fp32 scale s -> eight bf16, for NVFP4 (s = an E4M3
+// value): each code is converted to fp32 exactly (unit scale), multiplied by s in fp32 and
+// truncated to its upper 16 bits.  E2M1 x E4M3 has at most 6 significant bits and lies within
+// [2^-10, 2688], so the product and its truncation are exact (a NaN s gives NaN).
+__device__ __forceinline__ bf16x8 fp4x8_bf16_mul(uint32_t w, float s) {
+#define FT_FP4PAIR(b)                                                                      \
+  [&] {                                                                                     \
+    const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, b);                   \
+    return __builtin_amdgcn_perm(__float_as_uint(f[1] * s), __float_as_uint(f[0] * s),     \
+                                 0x07060302u);                                              \
+  }()
+  const uint4 d = make_uint4(FT_FP4PAIR(0), FT_FP4PAIR(1), FT_FP4PAIR(2), FT_FP4PAIR(3));
+#undef FT_FP4PAIR
+  return __builtin_bit_cast(bf16x8, d);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -74,6 +90,14 @@ __device__ __forceinline__ float e2m1_f32(uint32_t c) {
   const float m = (c & 4) ? ((c & 2) ? ((c & 1) ? 6.f : 4.f) : ((c & 1) ? 3.f : 2.f))
                           : ((c & 2) ? ((c & 1) ? 1.5f : 1.f) : ((c & 1) ? 0.5f : 0.f));
   return (c & 8) ? -m : m;
+}
+// The same E4M3 decode by bit assembly: a normal code's fp32 exponent field is e + 120 with
+// its 3 mantissa bits on top of the fp32 mantissa; a subnormal is m x 2^-9.
+__device__ __forceinline__ float e4m3_f32_fast(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  if ((c & 0x7fu) == 0x7fu) v = __uint_as_float(0x7fc00000u);
+  return (c & 0x80u) ? -v : v;
 }
 __device__ __forceinline__ float e4m3_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15, m = c & 7;

@@ -79,6 +79,11 @@ CONFIGS = {
                         n_slots=48, router_sigma=1.0 / math.sqrt(4096), zipf_c=1.1,
                         scale_lo=127 - 8, scale_hi=127 - 3, batches=(1,)),
     # NVFP4 scales: the 49 E4M3 codes 0x08..0x38 (values 2^-6 .. 2^0), tensor scale 1/64.
+    # The 35B-A3B class with NVFP4 experts (the format of the pages' laptop decode result).
+    "cfg2nv": LayerConfig("35b-a3b-decode-nvfp4", 1006, H=2048, I=512, E=256, k=8, n_shared=0,
+                          fmt=NVFP4, n_slots=256, router_sigma=1.0 / math.sqrt(2048),
+                          scale_lo=0x08, scale_hi=0x38, nv_tensor_scale=1.0 / 64.0,
+                          batches=(1, 8)),
     "cfg5": LayerConfig("753b-prefill", 1005, H=6144, I=2048, E=160, k=8, n_shared=0, fmt=NVFP4,
                         n_slots=160, router_sigma=0.5 / math.sqrt(6144),
                         scale_lo=0x08, scale_hi=0x38, nv_tensor_scale=1.0 / 64.0,

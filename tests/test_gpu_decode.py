@@ -182,7 +182,8 @@ def _decode_and_check(ctx, L, T, batch):
 
 
 @pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8),
-                                    ("cfg3", 1), ("cfg3", 4), ("cfg3", 16)])
+                                    ("cfg3", 1), ("cfg3", 4), ("cfg3", 16),
+                                    ("cfg2nv", 1), ("cfg2nv", 8)])
 def test_decode_matches_oracle(ctx, name, T):
     L = layer_for(ctx, name, max_tokens=16)
     err = _decode_and_check(ctx, L, T, batch=100 + T)
@@ -198,6 +199,18 @@ def test_decode_ragged_shapes(ctx, H, I, E, k, ns, T):
                              code_dist="normal", router_sigma=1 / np.sqrt(H))
     L = layer_for(ctx, cfg.name, cfg=cfg, max_tokens=16)
     _decode_and_check(ctx, L, T, batch=1)
+
+
+@pytest.mark.parametrize("H,I,E,k,ns,T,ts", [(256, 128, 5, 2, 1, 1, 0.7), (384, 640, 7, 3, 1, 5, 1 / 64),
+                                             (1152, 256, 9, 4, 0, 16, 3.0)])
+def test_decode_nvfp4_shapes(ctx, H, I, E, k, ns, T, ts):
+    """NVFP4 experts (E4M3 scales per 16 over all 256 codes' normal range, a tensor scale that
+    is not a power of two in two of the cases), shared experts, ragged chunk counts."""
+    cfg = synth.small_config(f"nv{H}_{I}", seed=H + 3 * I, H=H, I=I, E=E, k=k, n_shared=ns,
+                             fmt=synth.NVFP4, code_dist="normal", router_sigma=1 / np.sqrt(H),
+                             scale_lo=0x01, scale_hi=0x7e, nv_tensor_scale=ts)
+    L = layer_for(ctx, cfg.name, cfg=cfg, max_tokens=16)
+    _decode_and_check(ctx, L, T, batch=2)
 
 
 def test_decode_is_deterministic(ctx):
@@ -251,6 +264,16 @@ def test_miss_path_small_pool(ctx):
                              code_dist="normal", router_sigma=1 / 16, zipf_c=0.7)
     L = layer_for(ctx, "misssmall", cfg=cfg, resident=False, n_slots=5, max_tokens=4)
     _miss_sequence(ctx, L, steps=30, bp=1.0, bh=2.5, check_every=3, T=2)
+
+
+def test_miss_path_nvfp4_small_pool(ctx):
+    """NVFP4 experts through the slot pool: streamed misses, host-computed misses (the host
+    FFN decodes E4M3 scales and the tensor scale) and hits in one sequence."""
+    cfg = synth.small_config("missnv", seed=79, H=384, I=256, E=14, k=3, n_shared=1,
+                             fmt=synth.NVFP4, code_dist="normal", router_sigma=1 / 20,
+                             zipf_c=0.7, nv_tensor_scale=1 / 64)
+    L = layer_for(ctx, "missnv", cfg=cfg, resident=False, n_slots=5, max_tokens=2)
+    _miss_sequence(ctx, L, steps=24, bp=1.0, bh=2.5, check_every=2, T=2)
 
 
 @pytest.mark.parametrize("q_force", [0, 2, 99])
