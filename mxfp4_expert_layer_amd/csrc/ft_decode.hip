@@ -395,24 +395,29 @@ __device__ __forceinline__ void route_one_token(const float* logits, const int32
   __syncthreads();
 }
 
-// Publish the routing (when write_route) and the list for the next kernel (global memory).
+// Publish the routing (when write_route) and the list for the next kernel (global memory):
+// entries n_items .. max_items - 1 get ntok = 0, so a reader may walk max_items entries
+// without the count; every column carries its routing weight.
 __device__ void store_route(const TopkLds& tk, const ListLds& L, int T, int k, int n_shared,
                             int32_t* idx_out, float* w_out, WorkItem* items, int* n_items,
-                            bool write_route) {
+                            int max_items, bool write_route) {
   const int tid = threadIdx.x, kk = k + n_shared;
   if (write_route && tid < T * k) {
     idx_out[tid] = tk.idx[tid / k][tid % k];
     w_out[tid] = tk.w[tid / k][tid % k];
   }
-  for (int i = tid; i < L.n_items; i += 256) {
+  for (int i = tid; i < max_items; i += 256) {
     WorkItem& it = items[i];
-    it.expert = L.expert[i];
-    it.slot = L.slot[i];
-    it.ntok = L.ntok[i];
+    const bool used = i < L.n_items;
+    it.expert = used ? L.expert[i] : 0;
+    it.slot = used ? L.slot[i] : 0;
+    it.ntok = used ? L.ntok[i] : 0;
     it.pad = 0;
-    for (int n = 0; n < L.ntok[i]; ++n) {
-      it.tok[n] = L.tok[i][n];
-      it.pair[n] = L.tok[i][n] * kk + L.jj[i][n];
+    for (int n = 0; used && n < L.ntok[i]; ++n) {
+      const int t = L.tok[i][n], j = L.jj[i][n];
+      it.tok[n] = t;
+      it.pair[n] = t * kk + j;
+      it.wt[n] = j < k ? tk.w[t][j] : 1.f;
     }
   }
   if (tid == 0) *n_items = L.n_items;
@@ -557,13 +562,18 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
       build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
     }
     if (blockIdx.x == 0)
-      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items, true);
+      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items,
+                  a.max_items, true);
   } else if (EPL < 0) {
-    if (threadIdx.x < a.T * a.k) tk.idx[threadIdx.x / a.k][threadIdx.x % a.k] = a.idx_out[threadIdx.x];
+    if (threadIdx.x < a.T * a.k) {
+      tk.idx[threadIdx.x / a.k][threadIdx.x % a.k] = a.idx_out[threadIdx.x];
+      tk.w[threadIdx.x / a.k][threadIdx.x % a.k] = a.w_out[threadIdx.x];
+    }
     __syncthreads();
     build_list(tk, a.T, a.E, a.k, a.n_shared, a.e2s, ls);
     if (blockIdx.x == 0)
-      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items, false);
+      store_route(tk, ls, a.T, a.k, a.n_shared, a.idx_out, a.w_out, a.items, a.n_items,
+                  a.max_items, false);
   } else {
     load_list(a.items, a.n_items, ls);
   }
@@ -673,15 +683,19 @@ __global__ __launch_bounds__(64 * NW) void k_down_combine(DecodeLaunch a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int RT = a.H / kTileRows, KC = a.I / kTileK;
-  const int n_items = min(*a.n_items, kMaxItems);
-  const int kk = a.k + a.n_shared;
+  // the list's entries past its count have ntok = 0: walking all max_items entries spares
+  // every workgroup a dependent read of the count before its first item
+  const int n_entries = min(a.max_items, kMaxItems);
   for (int rt = blockIdx.x; rt < RT; rt += gridDim.x) {
     for (int i = lane; i < a.T * kTileRows; i += 64) part[wave][i / kTileRows][i % kTileRows] = 0.f;
     __builtin_amdgcn_wave_barrier();
-    for (int iti = wave; iti < n_items; iti += NW) {
+    for (int iti = wave; iti < n_entries; iti += NW) {
       const WorkItem& it = a.items[iti];
       const int ntok = it.ntok;
       const bool col = n < ntok;
+      const int t = it.tok[n];
+      const float wt = it.wt[n];
+      if (ntok == 0) continue;
       const uint8_t* blob = blob_of(it.expert, it.slot, a.pool, a.shared, a.stride);
       const uint8_t* codes[1] = {blob + a.L.off[4]};
       const uint8_t* scales[1] = {blob + a.L.off[5]};
@@ -690,8 +704,6 @@ __global__ __launch_bounds__(64 * NW) void k_down_combine(DecodeLaunch a) {
       tile_gemv<1, UNR, FMT>(codes, scales, (uint64_t)rt * KC, KC, 0, 1, brow, col, lane, acc);
       const float tsd = tensor_scale<FMT>(blob, 2);
       if (col) {
-        const int pr = it.pair[n], t = pr / kk, j = pr % kk;
-        const float wt = j < a.k ? a.w_out[t * a.k + j] : 1.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           part[wave][t][4 * g + r] = fmaf(wt, tsd * acc[0][r], part[wave][t][4 * g + r]);

@@ -69,10 +69,11 @@ constexpr int kMaxCols = 16;
 struct WorkItem {
   int32_t expert;    // routed expert id, or -1 - s for shared expert s
   int32_t slot;      // pool slot, or -1 - s for shared expert s
-  int32_t ntok;      // columns in use (1..16)
+  int32_t ntok;      // columns in use (1..16; 0 marks an unused entry of a GPU-built list)
   int32_t pad;
   int32_t tok[kMaxCols];
   int32_t pair[kMaxCols];
+  float wt[kMaxCols];  // GPU-built lists: the column's routing weight (1 for shared experts)
 };
 
 // Arguments of one decode expert pass (gate/up + SwiGLU, then down) as the host hands them

@@ -22,10 +22,12 @@
 //   k_unpermute       y[t] = sum_j w[t][j] Y_perm[pos[t][j]].
 // The scaled-FP4 mode replaces the two GEMMs (both operands FP4):
 //   k_quant_x         x -> MXFP4 per 32 along H (OCP MX rule), once per token.
-//   k_s1_gemm<0>      per (expert, 256-row block, 64 gate + 64 up features): G, U on the
-//                     16x16x128 scaled-FP4 MFMA; h = silu(G) * U quantised to MXFP4 per 32
+//   k_tile_xq         the quantised rows, in permuted order with every expert padded to a
+//                     multiple of 16 rows, into the tile format of the GEMM operand.
+//   k_s1_gemm<0>      per (expert, 256-row block, 128 gate + 128 up features): G, U on the
+//                     32x32x64 scaled-FP4 MFMA; h = silu(G) * U quantised to MXFP4 per 32
 //                     features in the epilogue.
-//   k_s1_gemm<1>      per (expert, row block, 128 rows of W_d): Y_perm = W_d h.
+//   k_s1_gemm<1>      per (expert, row block, 256 rows of W_d): Y_perm = W_d h.
 // and its NVFP4 weights come from k_nv_to_mx, run once when the layer is created.
 // Workgroups of one kernel never wait on each other.
 #include <hip/hip_runtime.h>
@@ -1064,15 +1066,17 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   }
 }
 
-// y[t][h] = sum_j w[t][j] Y_perm[pos[t][j]][h], j in rank order; four h per thread.
+// y[t][h] = sum_j w[t][j] Y_perm[pos[t][j]][h], j in rank order; four h per thread.  KMAX
+// (>= k) bounds the rows loaded, all issued before the first is used.
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (h >= a.H) return;
-  float4 v[FT_MAX_TOPK];
-  float wj[FT_MAX_TOPK];
+  float4 v[KMAX];
+  float wj[KMAX];
 #pragma unroll
-  for (int j = 0; j < FT_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     const int jc = min(j, a.k - 1);
     const int p = a.pos[(uint64_t)t * a.k + jc];
     wj[j] = a.w[(uint64_t)t * a.k + jc];
@@ -1080,7 +1084,7 @@ __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int j = 0; j < FT_MAX_TOPK; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     if (j < a.k) {
       acc.x = fmaf(wj[j], v[j].x, acc.x);
       acc.y = fmaf(wj[j], v[j].y, acc.y);
@@ -1169,7 +1173,11 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
     FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
   }
-  hipLaunchKernelGGL(k_unpermute, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, st, a);
+  if (a.k <= 8)
+    hipLaunchKernelGGL(k_unpermute<8>, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_unpermute<FT_MAX_TOPK>, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0,
+                       st, a);
   return (int)hipGetLastError();
 }
 
