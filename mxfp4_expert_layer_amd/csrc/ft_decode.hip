@@ -192,28 +192,6 @@ struct SortLds {
   uint64_t key[4][FT_MAX_TOPK];
 };
 
-// v of lane (lane ^ J), with the VALU's own lane exchanges instead of the LDS crossbar
-// (checked on gfx950): DPP quad permutes for 1 and 2, row rotates for 4 and 8 (row_ror:n
-// gives lane i the value of lane i - n within its row of 16), and the gfx950 permlane swaps
-// for 16 and 32.  Lane-dependent choices use constant lane masks (one v_cndmask).
-template <int J>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  if (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
-  if (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);
-  if (J == 4) {
-    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xf, 0xf, false);
-    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xf, 0xf, false);
-    return __builtin_amdgcn_inverse_ballot_w64(0xF0F0F0F0F0F0F0F0ull) ? dn : up;
-  }
-  if (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
-  if (J == 16) {
-    const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? sw[0] : sw[1];
-  }
-  const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? sw[0] : sw[1];
-}
-
 // Lanes of a bitonic compare-exchange step (merge size kk, distance j) that keep the larger
 // key: the lower lane of a pair in descending blocks, the upper one in ascending blocks.
 constexpr uint64_t keep_max_lanes(int kk, int j) {

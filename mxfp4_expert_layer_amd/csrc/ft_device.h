@@ -79,9 +79,36 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)
 // FP4, whose rounding decisions it moves only within 1e-6 of their boundaries.
 __device__ __forceinline__ float silu_fast(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
+// v of lane (lane ^ J), with the VALU's own lane exchanges instead of the LDS crossbar
+// (checked on gfx950): DPP quad permutes for 1 and 2, row rotates for 4 and 8 (row_ror:n
+// gives lane i the value of lane i - n within its row of 16), and the gfx950 permlane swaps
+// for 16 and 32.  Lane-dependent choices use constant lane masks (one v_cndmask).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+  if (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);
+  if (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xf, 0xf, false);
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xf, 0xf, false);
+    return __builtin_amdgcn_inverse_ballot_w64(0xF0F0F0F0F0F0F0F0ull) ? dn : up;
+  }
+  if (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
+  if (J == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? sw[0] : sw[1];
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? sw[0] : sw[1];
+}
+
+// Sum over the 64 lanes by a butterfly of lane exchanges: every lane gets the same value.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += __uint_as_float(xor_lane<1>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<2>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<4>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<8>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<16>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<32>(__float_as_uint(v)));
   return v;
 }
 

@@ -1011,7 +1011,7 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
           hv[r] = silu_fast(acc[o][i][r]) * acc[o + 2][i][r];
           amax = fmaxf(amax, fabsf(hv[r]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        amax = fmaxf(amax, __uint_as_float(xor_lane<32>(__float_as_uint(amax))));
         const uint32_t sc = mx_scale_code(amax);
         // the hardware convert rounds v / 2^(sc - 127) to E2M1 exactly as the OCP rule does
         // (nearest, ties to the even code, saturating, sign kept; checked on gfx950 over every
@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
         // lane half 0 writes block bytes 0..7, half 1 bytes 8..15; each sends the pieces the
         // other half writes
         const uint32_t send = h == 0 ? w23 : w01;
-        const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32, 64);
+        const uint32_t recv = xor_lane<32>(send);
         const uint2 out = h == 0 ? make_uint2((w01 & 0xffffu) | (recv << 16),
                                               (w01 >> 16) | (recv & 0xffff0000u))
                                  : make_uint2((recv & 0xffffu) | (w23 << 16),
