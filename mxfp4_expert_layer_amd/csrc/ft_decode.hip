@@ -25,6 +25,10 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "ft_device.h"
 
 namespace ft {
@@ -733,6 +737,27 @@ static int grid_for(int units_max, int cap) {
   return g < 1 ? 1 : g;
 }
 
+// Workgroups of a kernel that the device holds at once (256 threads each), cached per kernel
+// and device.  Grid-stride kernels whose workgroups start with fixed work (the routing
+// prologue) launch no more than this, so no workgroup waits for another to finish before it
+// can start and each pays the prologue once.
+static int resident_workgroups(const void* kern) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 2048;
+  std::lock_guard<std::mutex> g(mu);
+  const auto key = std::make_pair(kern, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      per_cu < 1 || cus < 1)
+    return 2048;
+  return cache[key] = per_cu * cus;
+}
+
 extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, int T, int H, int E,
                           float* logits, hipStream_t st) {
   if (T <= 1)
@@ -785,15 +810,17 @@ extern "C" int ftk_down_combines(const DecodeLaunch* ap) {
 // EPL < 0: list built from routed indices
 template <int EPL, int FMT>
 static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const int cap = 2048, KC = a.H / kTileK, RT = a.I / kTileRows;
-  if (KC >= 16)
-    FT_LAUNCH((k_gateup<4, 4, EPL, FMT>), dim3(grid_for(a.max_items * RT, cap)), e0, e1, a);
-  else if (KC >= 8)
-    FT_LAUNCH((k_gateup<2, 4, EPL, FMT>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e0,
-              e1, a);
-  else
-    FT_LAUNCH((k_gateup<1, 4, EPL, FMT>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e0,
-              e1, a);
+  const int KC = a.H / kTileK, RT = a.I / kTileRows;
+#define FT_GATEUP(KS_, RPW_)                                                                \
+  do {                                                                                      \
+    auto* k_ = k_gateup<KS_, 4, EPL, FMT>;                                                  \
+    const int cap_ = resident_workgroups((const void*)k_);                                  \
+    FT_LAUNCH(k_, dim3(grid_for(a.max_items * ((RT + (RPW_) - 1) / (RPW_)), cap_)), e0, e1, a); \
+  } while (0)
+  if (KC >= 16) FT_GATEUP(4, 1);
+  else if (KC >= 8) FT_GATEUP(2, 2);
+  else FT_GATEUP(1, 4);
+#undef FT_GATEUP
 }
 
 template <int FMT>
@@ -806,7 +833,7 @@ static void launch_experts(const DecodeLaunch& a, hipStream_t st, const hipEvent
   else if (a.E <= 128) launch_gateup<2, FMT>(a, st, e0, e1);
   else if (a.E <= 256) launch_gateup<4, FMT>(a, st, e0, e1);
   else launch_gateup<16, FMT>(a, st, e0, e1);
-  const int cap = 2048, KC = a.I / kTileK, RT = a.H / kTileRows;
+  const int KC = a.I / kTileK, RT = a.H / kTileRows;
   if (ftk_down_combines(&a)) {
     // down and combine in one kernel, one workgroup per row tile
     const dim3 grid(RT);
@@ -817,9 +844,13 @@ static void launch_experts(const DecodeLaunch& a, hipStream_t st, const hipEvent
       FT_LAUNCH_NT((k_down_combine<16, 4, FMT>), grid, 1024, e2, e3, a);
     }
   } else if (KC >= 8) {
-    FT_LAUNCH((k_down<2, 4, FMT>), dim3(grid_for(a.max_items * ((RT + 1) / 2), cap)), e2, e3, a);
+    auto* k = k_down<2, 4, FMT>;
+    FT_LAUNCH(k, dim3(grid_for(a.max_items * ((RT + 1) / 2), resident_workgroups((const void*)k))),
+              e2, e3, a);
   } else {
-    FT_LAUNCH((k_down<1, 4, FMT>), dim3(grid_for(a.max_items * ((RT + 3) / 4), cap)), e2, e3, a);
+    auto* k = k_down<1, 4, FMT>;
+    FT_LAUNCH(k, dim3(grid_for(a.max_items * ((RT + 3) / 4), resident_workgroups((const void*)k))),
+              e2, e3, a);
   }
 }
 
