@@ -406,7 +406,8 @@ static int decode_resident(ft_layer* l, const uint16_t* x, int T, float* y, hipS
   HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, d.E, l->logits, st));
   // few tokens: the gate/up kernel takes the top-k itself (one launch less); more tokens:
   // a top-k kernel with one wave per token first, so no workgroup routes tokens serially
-  const int route = T <= 2 ? 1 : 2;
+  // (measured: in-kernel routing wins up to 4 tokens, the separate pass from 8)
+  const int route = T <= 4 ? 1 : 2;
   if (route == 2)
     HIP_TRY((hipError_t)ftk_topk(l->logits, T, d.E, d.k, l->idx, l->w, nullptr, nullptr, nullptr,
                                  nullptr, d.H, st));
