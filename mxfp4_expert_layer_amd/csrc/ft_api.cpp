@@ -781,6 +781,8 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* ht = mx ? take(prows * d.I / 2) : nullptr;
   uint8_t* hts = mx ? take(prows * d.I / 32) : nullptr;
   uint8_t* yperm = take(pairs * d.H * 4);
+  // MXFP4 mode: the expert of each kS1Rows-row token block (at most pairs / kS1Rows + E)
+  uint8_t* blk_e = mx ? take(((pairs + kS1Rows - 1) / kS1Rows + d.E) * 4) : nullptr;
   if (a) {
     a->logits = (float*)logits;
     a->idx = (int32_t*)idx;
@@ -802,6 +804,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     a->ht = ht;
     a->hts = hts;
     a->Yperm = (float*)yperm;
+    a->blk_e = (int32_t*)blk_e;
   }
   return off;
 }

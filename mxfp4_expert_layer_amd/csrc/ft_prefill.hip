@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "ft_device.h"
 
 namespace ft {
@@ -353,6 +355,8 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
       const int e = tid * 4 + i;
       if (e < a.E) {
         out[e] = base;
+        if (pass == 1 && a.blk_e)   // the expert of every row block
+          for (int j = 0; j < v[i]; ++j) a.blk_e[base + j] = e;
         if (pass == 0) {
           a.counts[e] = cnt[i];
           int run = base;
@@ -791,77 +795,81 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   __shared__ uint4 tc0[1024], tc1[1024], tc2[1024], tc3[1024];
   __shared__ uint32_t ws0[256], ws1[256], ws2[256], ws3[256];
   __shared__ uint32_t ts0[256], ts1[256], ts2[256], ts3[256];
-  __shared__ int s_e;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n = lane & 15, g = lane >> 4;
-  const int Lb = blockIdx.x, xcd = Lb & 7, jj = Lb >> 3;
-  const int gblk = xcd + 8 * (jj / NB), fb = jj % NB;
-  if (gblk >= a.tb_off[a.E]) return;
-  if (tid == 0) {  // expert of this token block: tb_off[e] <= gblk < tb_off[e + 1]
-    int lo = 0, hi = a.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.tb_off[mid] <= gblk) lo = mid; else hi = mid - 1;
-    }
-    s_e = lo;
-  }
-  __syncthreads();
-  const int e = __builtin_amdgcn_readfirstlane(s_e);
-  const int row0 = a.offsets[e] + (gblk - a.tb_off[e]) * kS1Rows;
-  const int nrows = min(kS1Rows, a.offsets[e + 1] - row0);
-  const int ntile = (nrows + 31) >> 5;   // 32-token tiles
-  const int nj = __builtin_amdgcn_readfirstlane(max(0, (ntile - wn + 1) >> 1));
   const int KC = (MODE == 0 ? a.H : a.I) / kTileK;
   const int nrt = (MODE == 0 ? a.I : a.H) / kTileRows;   // row tiles of each matrix
-  const uint8_t* blob = a.mxpool + (uint64_t)e * a.mxstride;
-  // MODE 1: row tiles past the matrix (H not a multiple of 256) are clamped and never stored
-  const bool wvalid = MODE == 0 || fb * 16 + wm * 8 < nrt;
-
-  // this wave's copies: weight tiles wave + 4i and the scale dwords of tiles 4 wave .. + 3;
-  // token tiles wave + 4i and the scale dwords of rows 64 wave .. + 63 (rows past the block
-  // re-read its last row)
-  const uint8_t* wsrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave + 4 * i;
-    const int m = MODE == 0 ? (q < 8 ? 0 : 1) : 2;
-    const int rt = min(MODE == 0 ? fb * 8 + (q & 7) : fb * 16 + q, nrt - 1);
-    wsrc[i] = blob + a.ML.off[2 * m] + (uint64_t)rt * KC * kTileCodeBytes + lane * 16;
-  }
-  const uint8_t* wssrc;
-  {
-    const int q = 4 * wave + (lane >> 4);
-    const int m = MODE == 0 ? (q < 8 ? 0 : 1) : 2;
-    const int rt = min(MODE == 0 ? fb * 8 + (q & 7) : fb * 16 + q, nrt - 1);
-    wssrc = blob + a.ML.off[2 * m + 1] + (uint64_t)rt * KC * 64 + 4 * (lane & 15);
-  }
-  // token tiles: the block's 16-row tiles of the padded permuted operand (tiles past the
-  // block's last one re-read it; their results are never stored)
-  const int ntile16 = (nrows + 15) >> 4;
-  const int ptile0 = (a.poff[e] >> 4) + (gblk - a.tb_off[e]) * (kS1Rows / 16);
   const uint8_t* tcodes = MODE == 0 ? a.xt : a.ht;
   const uint8_t* tscales = MODE == 0 ? a.xts : a.hts;
+  const int tb_total = a.tb_off[a.E];
+  // A block (token block gblk, feature block fb) has index Lb = 8 (NB (gblk / 8) + fb) +
+  // gblk % 8, so its workgroup, and all of the token block's, sits on XCD gblk % 8 (the
+  // token tiles stay in that L2).  The down GEMM's fast path is persistent: workgroup b takes
+  // blocks b, b + grid, b + 2 grid, ... (grid a multiple of 8), whose token blocks only grow,
+  // and the next block's first copies run during this block's epilogue.  (The gate/up GEMM
+  // keeps one block per workgroup: the next block's addresses would cost it spills.)
+  constexpr bool PERSIST = FAST && MODE == 1;
+#define FT_S1_BLOCK(Lb_, gblk_, fb_)                                                      \
+  do {                                                                                    \
+    const int jj_ = (Lb_) >> 3;                                                           \
+    gblk_ = ((Lb_) & 7) + 8 * (jj_ / NB);                                                 \
+    fb_ = jj_ % NB;                                                                       \
+  } while (0)
+  // the per-block scalars (expert from the block map k_perm_scan wrote; all uniform)
+#define FT_S1_SCALARS(gblk_, fb_, e_, row0_, nrows_, nj_, ntile16_, ptile0_, wvalid_)        \
+  do {                                                                                    \
+    e_ = a.blk_e[gblk_];                                                                  \
+    row0_ = a.offsets[e_] + ((gblk_) - a.tb_off[e_]) * kS1Rows;                           \
+    nrows_ = min(kS1Rows, a.offsets[(e_) + 1] - (row0_));                                 \
+    nj_ = max(0, ((((nrows_) + 31) >> 5) - wn + 1) >> 1);                                 \
+    ntile16_ = ((nrows_) + 15) >> 4;                                                      \
+    ptile0_ = (a.poff[e_] >> 4) + ((gblk_) - a.tb_off[e_]) * (kS1Rows / 16);              \
+    wvalid_ = MODE == 0 || (fb_) * 16 + wm * 8 < nrt;                                     \
+  } while (0)
+  // this wave's copy sources: weight tiles wave + 4i and the scale dwords of tiles
+  // 4 wave .. + 3; token tiles wave + 4i and the scale dwords of rows 64 wave .. + 63 (rows
+  // past the block re-read its last row; MODE 1 row tiles past the matrix are clamped, their
+  // results never stored)
+#define FT_S1_SOURCES(e_, fb_, ntile16_, ptile0_)                                            \
+  do {                                                                                    \
+    const uint8_t* blob_ = a.mxpool + (uint64_t)(e_) * a.mxstride;                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                    \
+      const int q_ = wave + 4 * i_;                                                       \
+      const int m_ = MODE == 0 ? (q_ < 8 ? 0 : 1) : 2;                                    \
+      const int rt_ = min(MODE == 0 ? (fb_) * 8 + (q_ & 7) : (fb_) * 16 + q_, nrt - 1);   \
+      wsrc[i_] = blob_ + a.ML.off[2 * m_] + (uint64_t)rt_ * KC * kTileCodeBytes + lane * 16; \
+    }                                                                                     \
+    {                                                                                     \
+      const int q_ = 4 * wave + (lane >> 4);                                              \
+      const int m_ = MODE == 0 ? (q_ < 8 ? 0 : 1) : 2;                                    \
+      const int rt_ = min(MODE == 0 ? (fb_) * 8 + (q_ & 7) : (fb_) * 16 + q_, nrt - 1);   \
+      wssrc = blob_ + a.ML.off[2 * m_ + 1] + (uint64_t)rt_ * KC * 64 + 4 * (lane & 15);   \
+    }                                                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                    \
+      const uint64_t pt_ = (uint64_t)((ptile0_) + min(wave + 4 * i_, (ntile16_) - 1));    \
+      tsrc[i_] = tcodes + pt_ * KC * kTileCodeBytes + lane * 16;                          \
+    }                                                                                     \
+    {                                                                                     \
+      const uint64_t pt_ = (uint64_t)((ptile0_) + min(4 * wave + (lane >> 4), (ntile16_) - 1)); \
+      tssrc = tscales + pt_ * KC * 64 + 4 * (lane & 15);                                  \
+    }                                                                                     \
+  } while (0)
+
+  int Lb = blockIdx.x, gblk, fb;
+  FT_S1_BLOCK(Lb, gblk, fb);
+  if (gblk >= tb_total) return;
+  int e, row0, nrows, nj, ntile16, ptile0;
+  bool wvalid;
+  FT_S1_SCALARS(gblk, fb, e, row0, nrows, nj, ntile16, ptile0, wvalid);
+  const uint8_t* wsrc[4];
+  const uint8_t* wssrc;
   const uint8_t* tsrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t pt = (uint64_t)(ptile0 + min(wave + 4 * i, ntile16 - 1));
-    tsrc[i] = tcodes + pt * KC * kTileCodeBytes + lane * 16;
-  }
   const uint8_t* tssrc;
-  {
-    const uint64_t pt = (uint64_t)(ptile0 + min(4 * wave + (lane >> 4), ntile16 - 1));
-    tssrc = tscales + pt * KC * 64 + 4 * (lane & 15);
-  }
+  FT_S1_SOURCES(e, fb, ntile16, ptile0);
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int o = 0; o < 4; ++o)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[o][i][r] = 0.f;
 
   // first stage tile of this wave's 32-row operand o: MODE 0 gate features wm * 64 + 32 o
   // (o = 0, 1) and the same up features (o = 2, 3); MODE 1 rows wm * 128 + 32 o
@@ -875,7 +883,7 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
 
 #define FT_S1_ISSUE(kc_, WC_, TC_, WS_, TS_)                                              \
   do {                                                                                    \
-    const uint64_t c_ = (uint64_t)min((kc_), KC - 1);                                     \
+    const uint64_t c_ = (uint64_t)((kc_) < KC ? (kc_) : (nxt ? (kc_) - KC : KC - 1));    \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
       dma16(wsrc[i_] + c_ * kTileCodeBytes, &WC_[(wave + 4 * i_) * 64]);                  \
     dma4(wssrc + c_ * 64, &WS_[64 * wave]);                                               \
@@ -943,58 +951,79 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
     if ((kc_) >= 1 && (kc_) - 1 < KC && wvalid) FT_S1_MFMA(CA_, CB_, CSA_, CSB_);         \
   } while (0)
 
+  bool nxt = false;   // the next block's first chunks go out in the last four steps
   FT_S1_ISSUE(0, wc0, tc0, ws0, ts0);
   FT_S1_ISSUE(1, wc1, tc1, ws1, ts1);
   FT_S1_ISSUE(2, wc2, tc2, ws2, ts2);
   if (FAST) {
-    // KC % 4 == 0: step 0 only reads; steps 1 .. KC each read one chunk and multiply the one
-    // before, on all four token tiles (tiles past the block hold valid rows whose results are
-    // never stored; the barrier makes every wave wait for the busiest one anyway).  No step
-    // has a branch, so the accumulators never pass through a control-flow join.
     FT_S1_SYNC();
     FT_S1_ISSUE(3, wc3, tc3, ws3, ts3);
     FT_S1_READ(wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0);
-    // each phase stays where it is written (scheduling barriers): copies go out first, the
-    // next chunk's operands are read into the other register set, then this chunk's MFMAs
-    // run without waiting on those reads
+  }
+  for (;;) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[o][i][r] = 0.f;
+    int n_gblk = 0, n_fb = 0, n_e = 0, n_row0 = 0, n_nrows = 0, n_nj = 0, n_ntile16 = 0;
+    int n_ptile0 = 0;
+    bool n_wvalid = false;
+    if (FAST) {
+      // KC % 4 == 0: steps 1 .. KC each read one chunk and multiply the one before, on all
+      // four token tiles (tiles past the block hold valid rows whose results are never
+      // stored; the barrier makes every wave wait for the busiest one anyway).  No step has a
+      // branch, so the accumulators never pass through a control-flow join.  The next
+      // block's scalars are loaded here (scalar loads, long before they are needed); its
+      // copy sources replace this block's in the last iteration, whose four steps issue its
+      // chunks 0 .. 3 into stages 0 .. 3, just as this block's chunks KC .. KC + 3 would go.
+      if (PERSIST) {
+        const int Lb2 = Lb + (int)gridDim.x;
+        FT_S1_BLOCK(Lb2, n_gblk, n_fb);
+        nxt = n_gblk < tb_total;
+        if (nxt)
+          FT_S1_SCALARS(n_gblk, n_fb, n_e, n_row0, n_nrows, n_nj, n_ntile16, n_ptile0, n_wvalid);
+      }
+      // each phase stays where it is written (scheduling barriers): copies go out first, the
+      // next chunk's operands are read into the other register set, then this chunk's MFMAs
+      // run without waiting on those reads
 #define FT_S1_FAST_STEP(kcn_, WCN_, TCN_, WSN_, TSN_, WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_, \
                         CA_, CB_, CSA_, CSB_)                                               \
-    do {                                                                                  \
-      FT_S1_SYNC();                                                                       \
-      FT_S1_ISSUE(kcn_, WCN_, TCN_, WSN_, TSN_);                                          \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-      FT_S1_READ(WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_);                               \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-      FT_S1_MFMA(CA_, CB_, CSA_, CSB_);                                                   \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    } while (0)
-    for (int kc = 1; kc <= KC; kc += kS1Stages) {
-      FT_S1_FAST_STEP(kc + 3, wc0, tc0, ws0, ts0, wc1, tc1, ws1, ts1, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
-      FT_S1_FAST_STEP(kc + 4, wc1, tc1, ws1, ts1, wc2, tc2, ws2, ts2, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
-      FT_S1_FAST_STEP(kc + 5, wc2, tc2, ws2, ts2, wc3, tc3, ws3, ts3, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
-      FT_S1_FAST_STEP(kc + 6, wc3, tc3, ws3, ts3, wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
-    }
+      do {                                                                                \
+        FT_S1_SYNC();                                                                     \
+        FT_S1_ISSUE(kcn_, WCN_, TCN_, WSN_, TSN_);                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                \
+        FT_S1_READ(WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_);                             \
+        __builtin_amdgcn_sched_barrier(0);                                                \
+        FT_S1_MFMA(CA_, CB_, CSA_, CSB_);                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                \
+      } while (0)
+      for (int kc = 1; kc <= KC; kc += kS1Stages) {
+        if (PERSIST && nxt && kc + kS1Stages - 1 >= KC)
+          FT_S1_SOURCES(n_e, n_fb, n_ntile16, n_ptile0);
+        FT_S1_FAST_STEP(kc + 3, wc0, tc0, ws0, ts0, wc1, tc1, ws1, ts1, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+        FT_S1_FAST_STEP(kc + 4, wc1, tc1, ws1, ts1, wc2, tc2, ws2, ts2, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+        FT_S1_FAST_STEP(kc + 5, wc2, tc2, ws2, ts2, wc3, tc3, ws3, ts3, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+        FT_S1_FAST_STEP(kc + 6, wc3, tc3, ws3, ts3, wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+      }
 #undef FT_S1_FAST_STEP
-  } else {
-    for (int kc = 0; kc < KC; kc += kS1Stages) {
-      FT_S1_STEP(kc, wc0, tc0, ws0, ts0, wc3, tc3, ws3, ts3, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
-      FT_S1_STEP(kc + 1, wc1, tc1, ws1, ts1, wc0, tc0, ws0, ts0, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
-      FT_S1_STEP(kc + 2, wc2, tc2, ws2, ts2, wc1, tc1, ws1, ts1, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
-      FT_S1_STEP(kc + 3, wc3, tc3, ws3, ts3, wc2, tc2, ws2, ts2, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+    } else {
+      for (int kc = 0; kc < KC; kc += kS1Stages) {
+        FT_S1_STEP(kc, wc0, tc0, ws0, ts0, wc3, tc3, ws3, ts3, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+        FT_S1_STEP(kc + 1, wc1, tc1, ws1, ts1, wc0, tc0, ws0, ts0, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+        FT_S1_STEP(kc + 2, wc2, tc2, ws2, ts2, wc1, tc1, ws1, ts1, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
+        FT_S1_STEP(kc + 3, wc3, tc3, ws3, ts3, wc2, tc2, ws2, ts2, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
+      }
+      // the last chunk's MFMAs: when KC % 4 == 0 its operands (odd chunk) are in set 1;
+      // otherwise the loop's padding steps already ran them
+      if (KC % kS1Stages == 0 && wvalid) FT_S1_MFMA(PA1, PB1, pa1, pb1);
     }
-    // the last chunk's MFMAs: when KC % 4 == 0 its operands (odd chunk) are in set 1;
-    // otherwise the loop's padding steps already ran them
-    if (KC % kS1Stages == 0 && wvalid) FT_S1_MFMA(PA1, PB1, pa1, pb1);
-  }
-#undef FT_S1_STEP
-#undef FT_S1_SYNC
-#undef FT_S1_MFMA
-#undef FT_S1_READ
-#undef FT_S1_ISSUE
-  // the trailing copies (clamped re-reads) land before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
+    // without a next block, the trailing copies (clamped re-reads) land before the
+    // workgroup's LDS is released; with one, they are its first chunks, left in flight
+    if (!nxt) __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
 
-  if (!wvalid) return;
+    if (wvalid) {
   if (MODE == 0) {
     // h = silu(G) * U for the 32 features of operand pair (o, o + 2) and token lane % 32: one MX
     // block, held by lanes l and l ^ 32 (features 8q + 4h + r in register 4q + r)
@@ -1064,6 +1093,26 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
       }
     }
   }
+    }   // wvalid
+    if (!nxt) break;
+    Lb += (int)gridDim.x;
+    gblk = n_gblk; fb = n_fb; e = n_e; row0 = n_row0; nrows = n_nrows; nj = n_nj;
+    ntile16 = n_ntile16; ptile0 = n_ptile0; wvalid = n_wvalid;
+    // the epilogue's stores and the next block's copies share the count, and loads and
+    // stores need not complete in issue order: wait for all of them, then read chunk 0 (it
+    // landed, for every wave, at the last step's barrier)
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
+    asm volatile("" ::: "memory");
+    FT_S1_READ(wc0, tc0, ws0, ts0, PA0, PB0, pa0, pb0);
+  }
+#undef FT_S1_STEP
+#undef FT_S1_SYNC
+#undef FT_S1_MFMA
+#undef FT_S1_READ
+#undef FT_S1_ISSUE
+#undef FT_S1_SOURCES
+#undef FT_S1_SCALARS
+#undef FT_S1_BLOCK
 }
 
 // y[t][h] = sum_j w[t][j] Y_perm[pos[t][j]][h], j in rank order; four h per thread.  KMAX
@@ -1115,6 +1164,17 @@ extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes,
   } while (0)
 
 // ev: null or 4 events (gate/up start, stop, down start, stop).
+// Workgroups of a persistent S1 kernel: the device's resident count, rounded down to a
+// multiple of 8 (at least 8).
+static int s1_slots(const void* kern) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return std::max(8, per_cu * cus / 8 * 8);
+}
+
 extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEvent_t* ev) {
   const PrefillLaunch& a = *ap;
   const int nblk = (a.T + kPermBlock - 1) / kPermBlock;
@@ -1164,10 +1224,15 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   const int nb0 = a.I / 64, nb1 = a.H / kGemmN;
   if (a.mode == FT_PREFILL_MXFP4) {
     const int sb0 = a.I / 128, sb1 = (a.H + 255) / 256;   // feature blocks
-    // the branch-free main loop needs the chunk count to be a multiple of the stage count
-    if ((a.H / kTileK) % kS1Stages == 0) FT_PLAUNCH((k_s1_gemm<0, true>), dim3(g8 * sb0), e0, e1, a, sb0);
+    // The branch-free main loop needs the chunk count to be a multiple of the stage count.
+    // The down GEMM's is persistent, one workgroup per resident slot (a multiple of 8, so
+    // every workgroup keeps to one XCD); the others take one block per workgroup.
+    if ((a.H / kTileK) % kS1Stages == 0)
+      FT_PLAUNCH((k_s1_gemm<0, true>), dim3(g8 * sb0), e0, e1, a, sb0);
     else FT_PLAUNCH((k_s1_gemm<0, false>), dim3(g8 * sb0), e0, e1, a, sb0);
-    if ((a.I / kTileK) % kS1Stages == 0) FT_PLAUNCH((k_s1_gemm<1, true>), dim3(g8 * sb1), e2, e3, a, sb1);
+    const int slots = s1_slots((const void*)k_s1_gemm<1, true>);
+    if ((a.I / kTileK) % kS1Stages == 0)
+      FT_PLAUNCH((k_s1_gemm<1, true>), dim3(std::min(g8 * sb1, slots)), e2, e3, a, sb1);
     else FT_PLAUNCH((k_s1_gemm<1, false>), dim3(g8 * sb1), e2, e3, a, sb1);
   } else {
     FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
