@@ -809,7 +809,8 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   // token tiles stay in that L2).  The down GEMM's fast path is persistent: workgroup b takes
   // blocks b, b + grid, b + 2 grid, ... (grid a multiple of 8), whose token blocks only grow,
   // and the next block's first copies run during this block's epilogue.  (The gate/up GEMM
-  // keeps one block per workgroup: the next block's addresses would cost it spills.)
+  // keeps one block per workgroup: carrying the next block's state through its epilogue
+  // spills registers, and every reload there waits for the copies in flight.)
   constexpr bool PERSIST = FAST && MODE == 1;
 #define FT_S1_BLOCK(Lb_, gblk_, fb_)                                                      \
   do {                                                                                    \
@@ -1000,8 +1001,13 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
         __builtin_amdgcn_sched_barrier(0);                                                \
       } while (0)
       for (int kc = 1; kc <= KC; kc += kS1Stages) {
-        if (PERSIST && nxt && kc + kS1Stages - 1 >= KC)
-          FT_S1_SOURCES(n_e, n_fb, n_ntile16, n_ptile0);
+        if (PERSIST && nxt && kc + kS1Stages - 1 >= KC) {
+          // an opaque zero keeps the address arithmetic here instead of hoisted out of the
+          // loop, where its registers would stay live through every step
+          int z_;
+          asm volatile("s_mov_b32 %0, 0" : "=s"(z_));
+          FT_S1_SOURCES(n_e + z_, n_fb + z_, n_ntile16, n_ptile0 + z_);
+        }
         FT_S1_FAST_STEP(kc + 3, wc0, tc0, ws0, ts0, wc1, tc1, ws1, ts1, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
         FT_S1_FAST_STEP(kc + 4, wc1, tc1, ws1, ts1, wc2, tc2, ws2, ts2, PA0, PB0, pa0, pb0, PA1, PB1, pa1, pb1);
         FT_S1_FAST_STEP(kc + 5, wc2, tc2, ws2, ts2, wc3, tc3, ws3, ts3, PA1, PB1, pa1, pb1, PA0, PB0, pa0, pb0);
@@ -1098,6 +1104,8 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
     Lb += (int)gridDim.x;
     gblk = n_gblk; fb = n_fb; e = n_e; row0 = n_row0; nrows = n_nrows; nj = n_nj;
     ntile16 = n_ntile16; ptile0 = n_ptile0; wvalid = n_wvalid;
+    // recomputed rather than carried through the epilogue (registers)
+    FT_S1_SOURCES(e, fb, ntile16, ptile0);
     // the epilogue's stores and the next block's copies share the count, and loads and
     // stores need not complete in issue order: wait for all of them, then read chunk 0 (it
     // landed, for every wave, at the last step's barrier)
