@@ -783,6 +783,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* yperm = take(pairs * d.H * 4);
   // MXFP4 mode: the expert of each kS1Rows-row token block (at most pairs / kS1Rows + E)
   uint8_t* blk_e = mx ? take(((pairs + kS1Rows - 1) / kS1Rows + d.E) * 4) : nullptr;
+  uint8_t* tile_e = mx ? take(prows / 16 * 4) : nullptr;   // expert of each 16-row tile row
   if (a) {
     a->logits = (float*)logits;
     a->idx = (int32_t*)idx;
@@ -805,6 +806,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     a->hts = hts;
     a->Yperm = (float*)yperm;
     a->blk_e = (int32_t*)blk_e;
+    a->tile_e = (int32_t*)tile_e;
   }
   return off;
 }

@@ -152,6 +152,7 @@ struct PrefillLaunch {
   int32_t* base;                // [T/256][E]
   int32_t* tb_off;              // [E+1] prefix of mrows-row token blocks per expert
   int32_t* blk_e;               // MXFP4 mode: [T*k/mrows + E] expert of each token block
+  int32_t* tile_e;              // MXFP4 mode: [P/16] expert of each padded 16-row tile row
   int32_t* pos;                 // [T][k]
   int32_t* perm_tok;            // [T*k]
   uint16_t* hperm;              // [T*k][I] bf16 (exact mode)

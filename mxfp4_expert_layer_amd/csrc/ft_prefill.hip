@@ -318,16 +318,27 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
   __shared__ int s_wave[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int NBk = (a.T + kPermBlock - 1) / kPermBlock;
-  int cnt[4], blk[4], pad[4];
+  int cnt[4] = {0, 0, 0, 0}, blk[4], pad[4];
+  // the per-block counts of this thread's four experts, eight blocks at a time with every
+  // load of a round in flight together (clamped addresses, masked sums)
+  for (int b0 = 0; b0 < NBk; b0 += 8) {
+    int v[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = min(b0 + u, NBk - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[u][i] = a.bcnt[(uint64_t)b * a.E + min(tid * 4 + i, a.E - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (b0 + u < NBk && tid * 4 + i < a.E) cnt[i] += v[u][i];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    int c = 0;
-    if (e < a.E)
-      for (int b = 0; b < NBk; ++b) c += a.bcnt[(uint64_t)b * a.E + e];
-    cnt[i] = c;
-    blk[i] = (c + a.mrows - 1) / a.mrows;
-    pad[i] = (c + 15) & ~15;
+    blk[i] = (cnt[i] + a.mrows - 1) / a.mrows;
+    pad[i] = (cnt[i] + 15) & ~15;
   }
   // exclusive scans over experts (pairs, row blocks and, in the MXFP4 mode, 16-padded rows),
   // four experts per thread
@@ -357,12 +368,21 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
         out[e] = base;
         if (pass == 1 && a.blk_e)   // the expert of every row block
           for (int j = 0; j < v[i]; ++j) a.blk_e[base + j] = e;
+        if (pass == 2 && a.tile_e)  // the expert of every padded 16-row tile row
+          for (int j = 0; j < v[i] / 16; ++j) a.tile_e[base / 16 + j] = e;
         if (pass == 0) {
           a.counts[e] = cnt[i];
           int run = base;
-          for (int b = 0; b < NBk; ++b) {
-            a.base[(uint64_t)b * a.E + e] = run;
-            run += a.bcnt[(uint64_t)b * a.E + e];
+          for (int b0 = 0; b0 < NBk; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = a.bcnt[(uint64_t)min(b0 + u, NBk - 1) * a.E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (b0 + u < NBk) {
+                a.base[(uint64_t)(b0 + u) * a.E + e] = run;
+                run += v[u];
+              }
           }
         }
       }
@@ -667,29 +687,40 @@ __device__ __forceinline__ int expert_of(const int32_t* off, int E, int p) {
 }
 
 // Quantised token rows -> the GEMM's token operand in tile format, rows in permuted order
-// padded per expert to a multiple of 16.  One thread per 16-byte lane slot of a tile (a wave
-// is one tile): padded row 16 (tile / KC) + l % 16, 32-K block 4 (tile % KC) + l / 16.  The
-// grid covers the largest padded row count; padding rows get zero codes and scales.
+// padded per expert to a multiple of 16.  One workgroup per 16-row tile row (every such row
+// belongs to one expert, from the tile map the scan wrote): the 16 rows' tokens are read
+// once, then wave w writes K tiles w, w + 4, ... of the row (lane l: row l % 16, 32-K block
+// 4 kc + l / 16), four tiles' loads in flight at a time.  Padding rows get zero codes and
+// scales.  The grid covers the largest padded row count.
 __global__ __launch_bounds__(256) void k_tile_xq(PrefillLaunch a) {
   const int KC = a.H / kTileK;
-  const uint64_t tile = ((uint64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int l = threadIdx.x & 63;
-  const int P = a.poff[a.E];
-  if (tile >= (uint64_t)(P / 16) * KC) return;
-  const int kc = (int)(tile % KC);
-  const int prow = (int)(tile / KC) * 16 + (l & 15);
-  const int e = expert_of(a.poff, a.E, __builtin_amdgcn_readfirstlane((int)(tile / KC) * 16));
-  const int r = prow - a.poff[e];
-  uint4 c = make_uint4(0u, 0u, 0u, 0u);
-  uint8_t sc = 0;
-  if (r < a.counts[e]) {
-    const uint64_t t = (uint64_t)a.perm_tok[a.offsets[e] + r];
-    const int blk = kc * 4 + (l >> 4);
-    c = *(const uint4*)(a.xq + t * (a.H / 2) + blk * 16);
-    sc = a.xqs[t * (a.H / 32) + blk];
+  const int trow = blockIdx.x;                    // 16-row tile row
+  if (trow >= (a.poff[a.E] >> 4)) return;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int e = a.tile_e[trow];
+  const int r = trow * 16 + (l & 15) - a.poff[e];
+  const bool valid = r < a.counts[e];
+  const uint64_t t = valid ? (uint64_t)a.perm_tok[min(a.offsets[e] + r, a.T * a.k - 1)] : 0;
+  for (int kc0 = wave; kc0 < KC; kc0 += 16) {
+    uint4 c[4];
+    uint8_t sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kc = min(kc0 + 4 * u, KC - 1);
+      const int blk = kc * 4 + (l >> 4);
+      c[u] = *(const uint4*)(a.xq + t * (a.H / 2) + blk * 16);
+      sc[u] = a.xqs[t * (a.H / 32) + blk];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kc = kc0 + 4 * u;
+      if (kc < KC) {
+        const uint64_t tile = (uint64_t)trow * KC + kc;
+        *(uint4*)(a.xt + tile * 1024 + l * 16) = valid ? c[u] : make_uint4(0u, 0u, 0u, 0u);
+        a.xts[tile * 64 + l] = valid ? sc[u] : (uint8_t)0;
+      }
+    }
   }
-  *(uint4*)(a.xt + tile * 1024 + l * 16) = c;
-  a.xts[tile * 64 + l] = sc;
 }
 
 // Test hook: the tiled h back to permuted row order, codes [T*k][I/2] and scales [T*k][I/32].
@@ -1221,8 +1252,8 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   hipLaunchKernelGGL(k_perm_place, dim3(nblk), dim3(256), 0, st, a);
   if (a.mode == FT_PREFILL_MXFP4) {
     // tiles of the padded permuted tokens: at most T*k + 15 E rows
-    const uint64_t maxtiles = (uint64_t)((a.T * a.k + 15 * a.E + 15) / 16) * (a.H / kTileK);
-    hipLaunchKernelGGL(k_tile_xq, dim3((unsigned)((maxtiles * 64 + 255) / 256)), dim3(256), 0, st, a);
+    const unsigned maxtrows = (unsigned)((a.T * a.k + 15 * a.E + 15) / 16);
+    hipLaunchKernelGGL(k_tile_xq, dim3(maxtrows), dim3(256), 0, st, a);
   }
   // upper bound on mrows-row token blocks: sum_e ceil(c_e / mrows) <= T*k/mrows + E
   const int gmax = (a.T * a.k + a.mrows - 1) / a.mrows + a.E;
