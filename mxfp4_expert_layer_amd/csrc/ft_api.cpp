@@ -780,7 +780,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* xts = mx ? take(prows * d.H / 32) : nullptr;
   uint8_t* ht = mx ? take(prows * d.I / 2) : nullptr;
   uint8_t* hts = mx ? take(prows * d.I / 32) : nullptr;
-  uint8_t* yperm = take(pairs * d.H * 4);
+  uint8_t* yperm = take(pairs * d.H * (mx ? 3 : 4));   // S1: 24-bit floats
   // MXFP4 mode: the expert of each kS1Rows-row token block (at most pairs / kS1Rows + E)
   uint8_t* blk_e = mx ? take(((pairs + kS1Rows - 1) / kS1Rows + d.E) * 4) : nullptr;
   uint8_t* tile_e = mx ? take(prows / 16 * 4) : nullptr;   // expert of each 16-row tile row

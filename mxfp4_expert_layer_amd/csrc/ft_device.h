@@ -135,6 +135,32 @@ __device__ __forceinline__ float e4m3_f32(uint32_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+// ---- 24-bit floats (fp32 with the low 8 mantissa bits rounded away, to nearest even) ----
+// Four values in 12 bytes, value i in bits 24 i .. 24 i + 23.  Infinities stay infinite, a
+// NaN stays a NaN, finite values keep their exponent range (a value may round up to inf only
+// from within 2^-16 of the fp32 maximum); the relative rounding error is at most 2^-16.
+// fp32 bits rounded at bit 8, to nearest even (the value sits in bytes 1..3); a NaN becomes
+// the quiet NaN of its sign
+__device__ __forceinline__ uint32_t f32_round24(float f) {
+  const uint32_t b = __float_as_uint(f);
+  const uint32_t r = b + 0x7fu + ((b >> 8) & 1u);
+  return f != f ? ((b & 0x80000000u) | 0x7fc00000u) : r;
+}
+__device__ __forceinline__ uint3 pack_f24x4(float v0, float v1, float v2, float v3) {
+  const uint32_t r0 = f32_round24(v0), r1 = f32_round24(v1), r2 = f32_round24(v2),
+                 r3 = f32_round24(v3);
+  // bytes 1..3 of each, in order: [r0.1 r0.2 r0.3 r1.1] [r1.2 r1.3 r2.1 r2.2] [r2.3 r3.1 r3.2 r3.3]
+  return make_uint3(__builtin_amdgcn_perm(r1, r0, 0x05030201u),
+                    __builtin_amdgcn_perm(r2, r1, 0x06050302u),
+                    __builtin_amdgcn_perm(r3, r2, 0x07060503u));
+}
+__device__ __forceinline__ float4 unpack_f24x4(uint3 w) {
+  return make_float4(__uint_as_float(w.x << 8),
+                     __uint_as_float(((w.x >> 24) | (w.y << 8)) << 8),
+                     __uint_as_float(((w.y >> 16) | (w.z << 16)) << 8),
+                     __uint_as_float(w.z & 0xffffff00u));
+}
+
 // ---- OCP MX quantiser (32-value blocks, E8M0 scale, E2M1 codes) -----------------------------
 // Block scale 2^(floor(log2 amax) - 2) (2 is E2M1's largest exponent) with the exponent
 // clamped to [-127, 127]: for a finite fp32 amax with biased exponent field f that is the E8M0

@@ -167,7 +167,7 @@ struct PrefillLaunch {
   uint8_t* xts;                 //   scales [P/16][H/128][64 B]
   uint8_t* ht;                  // quantised h rows: codes [P/16][I/128][1 KB]
   uint8_t* hts;                 //   scales [P/16][I/128][64 B]
-  float* Yperm;                 // [T*k][H]
+  float* Yperm;                 // [T*k][H] fp32; MXFP4 mode: 24-bit floats, 4 in 12 bytes
   float* y;                     // [T][H]
 };
 

@@ -1113,19 +1113,24 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
       }
     }
   } else {
+    // lane-derived values recomputed here from an opaque copy of the thread index, so the
+    // compiler cannot keep them live (or spilled) across the main loop
+    int tid_e;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_e) : "v"((int)threadIdx.x));
+    const int lane_e = tid_e & 63, h_e = lane_e >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nj) continue;
-      const int row = 32 * (wn + 2 * i) + (lane & 31);
+      const int row = 32 * (wn + 2 * i) + (lane_e & 31);
       if (row < nrows) {
 #pragma unroll
         for (int o = 0; o < 4; ++o)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = fb * 256 + wm * 128 + 32 * o + 8 * q + 4 * h;
-            *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + col) =
-                make_float4(acc[o][i][4 * q], acc[o][i][4 * q + 1], acc[o][i][4 * q + 2],
-                            acc[o][i][4 * q + 3]);
+            const int col = fb * 256 + wm * 128 + 32 * o + 8 * q + 4 * h_e;
+            *(uint3*)((uint8_t*)a.Yperm + ((uint64_t)(row0 + row) * a.H + col) * 3) =
+                pack_f24x4(acc[o][i][4 * q], acc[o][i][4 * q + 1], acc[o][i][4 * q + 2],
+                           acc[o][i][4 * q + 3]);
           }
       }
     }
@@ -1155,8 +1160,9 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
 }
 
 // y[t][h] = sum_j w[t][j] Y_perm[pos[t][j]][h], j in rank order; four h per thread.  KMAX
-// (>= k) bounds the rows loaded, all issued before the first is used.
-template <int KMAX>
+// (>= k) bounds the rows loaded, all issued before the first is used.  F24: Y_perm holds
+// 24-bit floats (the scaled-FP4 mode), else fp32.
+template <int KMAX, bool F24>
 __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -1168,7 +1174,8 @@ __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
     const int jc = min(j, a.k - 1);
     const int p = a.pos[(uint64_t)t * a.k + jc];
     wj[j] = a.w[(uint64_t)t * a.k + jc];
-    v[j] = *(const float4*)(a.Yperm + (uint64_t)p * a.H + h);
+    if (F24) v[j] = unpack_f24x4(*(const uint3*)((const uint8_t*)a.Yperm + ((uint64_t)p * a.H + h) * 3));
+    else v[j] = *(const float4*)(a.Yperm + (uint64_t)p * a.H + h);
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1277,11 +1284,15 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
     FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
   }
-  if (a.k <= 8)
-    hipLaunchKernelGGL(k_unpermute<8>, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_unpermute<FT_MAX_TOPK>, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0,
-                       st, a);
+  const dim3 ug((a.H / 4 + 255) / 256, a.T);
+  const bool f24 = a.mode == FT_PREFILL_MXFP4;
+  if (a.k <= 8) {
+    if (f24) hipLaunchKernelGGL((k_unpermute<8, true>), ug, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_unpermute<8, false>), ug, dim3(256), 0, st, a);
+  } else {
+    if (f24) hipLaunchKernelGGL((k_unpermute<FT_MAX_TOPK, true>), ug, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_unpermute<FT_MAX_TOPK, false>), ug, dim3(256), 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 
