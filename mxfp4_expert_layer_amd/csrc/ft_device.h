@@ -75,9 +75,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
-// silu with the hardware exp and reciprocal (a few ulp); used where h is then quantised to
-// FP4, whose rounding decisions it moves only within 1e-6 of their boundaries.
-__device__ __forceinline__ float silu_fast(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
+// silu with the hardware exp and reciprocal (v_exp_f32, v_rcp_f32: a few ulp); used where h
+// is then quantised to FP4, whose rounding decisions it moves only within 1e-6 of their
+// boundaries.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // v of lane (lane ^ J), with the VALU's own lane exchanges instead of the LDS crossbar
 // (checked on gfx950): DPP quad permutes for 1 and 2, row rotates for 4 and 8 (row_ror:n

@@ -815,6 +815,14 @@ __global__ __launch_bounds__(256) void k_nv_to_mx(const uint8_t* __restrict__ sr
 // followed by a barrier (no fence, which would drain every copy in flight) makes a stage
 // visible to the whole workgroup.  Block (token block g, feature block fb) sits on XCD g % 8.
 
+// The lane index, computed where it is used: volatile, so the compiler neither merges it with
+// an earlier copy nor keeps one live across a loop.
+__device__ __forceinline__ int lane_index_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 constexpr int kS1Stages = 4;
 constexpr int kS1Copies = 10;   // copies per wave per chunk: 4 weight + 1 scale + 4 token + 1 scale
 
@@ -1063,11 +1071,14 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
     if (wvalid) {
   if (MODE == 0) {
     // h = silu(G) * U for the 32 features of operand pair (o, o + 2) and token lane % 32: one MX
-    // block, held by lanes l and l ^ 32 (features 8q + 4h + r in register 4q + r)
+    // block, held by lanes l and l ^ 32 (features 8q + 4h + r in register 4q + r).  The lane
+    // index is recomputed rather than kept across the main loop.
+    const int lane_e = lane_index_here();
+    const int h = lane_e >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nj) continue;
-      const int row = 32 * (wn + 2 * i) + (lane & 31);
+      const int row = 32 * (wn + 2 * i) + (lane_e & 31);
 #pragma unroll
       for (int o = 0; o < 2; ++o) {
         float hv[16];
@@ -1113,11 +1124,10 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
       }
     }
   } else {
-    // lane-derived values recomputed here from an opaque copy of the thread index, so the
-    // compiler cannot keep them live (or spilled) across the main loop
-    int tid_e;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_e) : "v"((int)threadIdx.x));
-    const int lane_e = tid_e & 63, h_e = lane_e >> 5;
+    // the lane index recomputed here, so no lane value is kept live (or spilled) across the
+    // main loop
+    const int lane_e = lane_index_here();
+    const int h_e = lane_e >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nj) continue;
