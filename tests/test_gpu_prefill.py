@@ -248,6 +248,26 @@ def test_prefill_mxfp4_matches_oracle(ctx, name, fmt, H, I, E, k, T):
     check_output(y, ref["y"], name)
 
 
+def test_prefill_mxfp4_down_blocks_per_workgroup(ctx):
+    """More down-GEMM blocks than resident workgroups (H = 6016: 24 feature blocks, the last
+    one half outside the matrix), so workgroups take a second block and the first chunks of
+    that block load during the first block's epilogue; the whole output is checked."""
+    name, fmt, H, I, E, k, T = "pf_persist", synth.MXFP4, 6016, 256, 6, 2, 1200
+    cfg, L = _small_layer(ctx, name, fmt, H, I, E, k)
+    x = synth.gen_tokens(cfg, T, batch=11)
+    log(f"[gpu] prefill mxfp4 {name} T={T}")
+    y, ws = run_prefill(ctx, L, x, mode=ft.FT_PREFILL_MXFP4)
+    idx, w, counts, offsets, pos = prefill_state(L, ws, T)
+    assert ((counts + 255) // 256).sum() * ((H + 255) // 256) > 256
+    OL = L.oracle_layer()
+    ref = moe.moe_forward(OL, x, mode="mxfp4", threads=16)
+    ties = check_routing(idx, w, ref)
+    _check_perm(idx, counts, offsets, pos, E)
+    if ties:
+        ref = moe.moe_forward(OL, x, idx=idx, mode="mxfp4", threads=16)
+    check_output(y, ref["y"], name)
+
+
 def test_prefill_mxfp4_token_quantiser_edge_cases(ctx):
     """Blocks of zeros, -0, bf16 subnormals, values at every rounding midpoint, and very
     large and very small magnitudes are quantised exactly as the oracle does."""
