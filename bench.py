@@ -248,6 +248,8 @@ def bench_miss_path(args, wl):
     L = GpuLayer(ctx, cfg, resident=False, n_slots=cfg.n_slots, max_tokens=1, threads=16)
     bp, bh = ft.measure_bandwidth(ctx, L.handle)
     log(f"[bench] measured Bp {bp / 1e9:.1f} GB/s, Bh {bh / 1e9:.1f} GB/s")
+    rule = ft.FT_SPLIT_MAKESPAN if args.split == "makespan" else ft.FT_SPLIT_ROUND
+    ft.set_miss_policy(L.handle, rule, args.adaptive)
     xs = [torch.from_numpy(synth.gen_tokens(cfg, 1, batch=2000 + b).view(np.int16)).to("cuda")
           for b in range(W + K)]
     y = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
@@ -258,6 +260,7 @@ def bench_miss_path(args, wl):
     torch.cuda.synchronize()
     hits = sel = m_sum = q_sum = streamed = host = 0
     host_us = wait_us = 0.0
+    bp_obs, bh_obs = [], []
     t0 = time.perf_counter()
     for i in range(K):
         ft.moe_decode(ctx, L.handle, xs[W + i], 1, y, s, st)
@@ -269,6 +272,10 @@ def bench_miss_path(args, wl):
         host += st.n_host
         host_us += st.host_us
         wait_us += st.wait_us
+        if st.bp_obs > 0:
+            bp_obs.append(st.bp_obs)
+        if st.bh_obs > 0:
+            bh_obs.append(st.bh_obs)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     blob = L.stride
@@ -283,7 +290,11 @@ def bench_miss_path(args, wl):
                       "mean_m": m_sum / K, "mean_q": q_sum / K, "streamed": streamed,
                       "host_computed": host, "pcie_GBps": streamed * blob / dt / 1e9,
                       "host_GBps": host * blob / max(host_us * 1e-6, 1e-9) / 1e9,
-                      "mean_host_us": host_us / K, "mean_wait_us": wait_us / K},
+                      "mean_host_us": host_us / K, "mean_wait_us": wait_us / K,
+                      "split_rule": args.split, "adaptive_alpha": args.adaptive,
+                      "final_Bp_GBps": st.bp / 1e9, "final_Bh_GBps": st.bh / 1e9,
+                      "median_Bp_obs_GBps": float(np.median(bp_obs)) / 1e9 if bp_obs else None,
+                      "median_Bh_obs_GBps": float(np.median(bh_obs)) / 1e9 if bh_obs else None},
         "roofline": None,
     }
     L.close()
@@ -440,6 +451,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--zipf-c", type=float, default=None,
                     help="miss path: router bias strength c of b_e = -c ln(rank_e)")
+    ap.add_argument("--split", choices=["round", "makespan"], default="round",
+                    help="miss path: split rule (round(q*) or the makespan variant)")
+    ap.add_argument("--adaptive", type=float, default=0.0,
+                    help="miss path: running-average weight for re-measuring Bp, Bh (0: fixed)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

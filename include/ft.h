@@ -142,6 +142,10 @@ typedef struct ft_decode_stats {
   double bp, bh;        /* bandwidths used (bytes/s) */
   double host_us;       /* wall time of the host experts */
   double wait_us;       /* wall time blocked on the routing read-back */
+  /* runtime measurements taken by this call (0 where there was nothing to measure):
+     bp_obs from the previous call's streamed copies, bh_obs from this call's host experts
+     (see ft_set_miss_policy) */
+  double bp_obs, bh_obs;
 } ft_decode_stats;
 
 /*
@@ -189,6 +193,16 @@ FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T
 FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
 
 /*
+ * The split's makespan variant: both sides run at once, the copies at Bp and the host experts
+ * with the bandwidth the copies leave, Bh - Bp (lowalt.boxinlu2.cn article, section 二), and
+ * the q with the earlier finish wins: the integer q in [0, m] minimising
+ * max(q / Bp, (m - q) / (Bh - Bp)), lowest q on ties; Bh <= Bp gives m.  FT_EINVAL as
+ * ft_qstar_split.  Pure host function.
+ */
+enum { FT_SPLIT_ROUND = 0, FT_SPLIT_MAKESPAN = 1 };
+FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
+
+/*
  * Startup probes: Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
  * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.
  * Needs host_blobs.  Blocks.  The values are stored in the layer and used by decode.
@@ -198,6 +212,24 @@ FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double
 FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh);
 /* Force q for every later decode call (q >= 0, clamped to m), or restore the rule (q < 0). */
 FT_API int ft_force_q(ft_layer* layer, int q);
+
+/*
+ * Miss-path policy of a layer (the pages let q* follow the hardware as it runs: smzdm
+ * explainer a825qpgl, section 二; lowalt.boxinlu2.cn article, section 二).
+ *   rule: FT_SPLIT_ROUND (default: q = round(q*)) or FT_SPLIT_MAKESPAN.
+ *   alpha in [0, 1]: 0 (default) keeps Bp and Bh as measured or set.  alpha > 0 re-measures
+ *     them during decode and moves each estimate toward its observation by alpha
+ *     (est += alpha (obs - est)), before the next call's split:
+ *       Bp_obs = bytes of the streamed blobs / their copy time on the copy stream (events
+ *                around the copies, read at the next miss-path call);
+ *       Bh_obs = bytes of the host-computed blobs / the host experts' wall time, plus the
+ *                current Bp when copies ran at the same time (the copies take Bp of the
+ *                host's memory bandwidth while they run).
+ *     Calls with nothing streamed (or nothing computed on the host) leave that estimate.
+ * The values a call used are in its ft_decode_stats (bp, bh), its observations in bp_obs,
+ * bh_obs.  FT_EINVAL for an unknown rule or alpha outside [0, 1].
+ */
+FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha);
 
 FT_API const char* ft_last_error(void);
 

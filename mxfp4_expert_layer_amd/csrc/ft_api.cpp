@@ -98,10 +98,14 @@ struct ft_layer {
   int32_t* s2e_h = nullptr;
   hipEvent_t ev_copy = nullptr;
   hipEvent_t ev_route = nullptr;
+  hipEvent_t ev_cp0 = nullptr, ev_cp1 = nullptr;   // timing events around streamed copies
   // policy state
   LruState lru;
   double bp = 0.0, bh = 0.0;
   int force_q = -1;
+  int split_rule = FT_SPLIT_ROUND;
+  double alpha = 0.0;            // running-estimate weight (0: Bp and Bh fixed)
+  uint64_t pend_copy_bytes = 0;  // streamed bytes of the last call, timed by ev_cp0/ev_cp1
   // kernel timing events: [n][4] = gate/up start, stop, down start, stop
   std::vector<hipEvent_t> prof;
   int prof_n = 0, prof_i = 0;
@@ -221,6 +225,8 @@ static void free_layer(ft_layer* l) {
   for (hipEvent_t e : l->prof) hipEventDestroy(e);
   if (l->ev_copy) hipEventDestroy(l->ev_copy);
   if (l->ev_route) hipEventDestroy(l->ev_route);
+  if (l->ev_cp0) hipEventDestroy(l->ev_cp0);
+  if (l->ev_cp1) hipEventDestroy(l->ev_cp1);
   if (l->dev) hipFree(l->dev);
   if (l->mx_owned) hipFree(l->mx_owned);
   if (l->pin) hipHostFree(l->pin);
@@ -342,6 +348,8 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipMemcpy(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_copy, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_route, hipEventDisableTiming));
+  HIP_TRY(hipEventCreate(&l->ev_cp0));
+  HIP_TRY(hipEventCreate(&l->ev_cp1));
   *out = l.release();
   return FT_OK;
 }
@@ -472,8 +480,21 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   if (l->bp <= 0.0 || l->bh <= 0.0)
     return fail(FT_ESTATE, "ft_moe_decode: Bp/Bh unknown; call ft_measure_bandwidth or "
                            "ft_set_bandwidth first");
+  // the previous call's streamed copies have finished by now (its kernels waited for them
+  // before the routing of this call ran): their copy time gives an observation of Bp
+  if (l->pend_copy_bytes > 0 && hipEventQuery(l->ev_cp1) == hipSuccess) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, l->ev_cp0, l->ev_cp1) == hipSuccess && ms > 0.f)
+      S.bp_obs = (double)l->pend_copy_bytes / (ms * 1e-3);
+    l->pend_copy_bytes = 0;
+    if (l->alpha > 0.0) l->bp = bandwidth_update(l->bp, S.bp_obs, l->alpha);
+  }
   int rc = qstar_split(m, l->bp, l->bh, &q, &qstar);
   if (rc) return rc;
+  if (l->split_rule == FT_SPLIT_MAKESPAN) {
+    rc = qstar_makespan(m, l->bp, l->bh, &q);
+    if (rc) return rc;
+  }
   if (l->force_q >= 0) q = std::min(m, l->force_q);
   std::vector<int> streamed, host;
   for (int n = 0; n < m; ++n) {
@@ -523,13 +544,18 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
   std::copy(l->lru.s2e.begin(), l->lru.s2e.end(), l->s2e_h);
 
-  // copies of streamed experts into their slots, on the copy stream
+  // copies of streamed experts into their slots, on the copy stream (timed)
+  if (!streamed.empty()) {
+    HIP_TRY(hipEventRecord(l->ev_cp0, ctx->copy_stream));
+    l->pend_copy_bytes = (uint64_t)streamed.size() * l->L.bytes;
+  }
   for (int e : streamed) {
     const int s = l->lru.e2s[e];
     HIP_TRY(hipMemcpyAsync((uint8_t*)d.pool + (uint64_t)s * d.blob_stride,
                            (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride,
                            l->L.bytes, hipMemcpyHostToDevice, ctx->copy_stream));
   }
+  if (!streamed.empty()) HIP_TRY(hipEventRecord(l->ev_cp1, ctx->copy_stream));
   HIP_TRY(hipEventRecord(l->ev_copy, ctx->copy_stream));
   // work lists and tables to the device (compute stream, before the kernels)
   HIP_TRY(hipMemcpyAsync(l->items, l->items_h, (size_t)2 * l->max_items * sizeof(WorkItem),
@@ -549,6 +575,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
 
   // host experts, concurrently with the GPU work enqueued above
   auto th = clk::now();
+  double ffn_s = 0.0;   // wall time in the expert FFN itself
   std::vector<float> yt((size_t)T * d.H);
   std::vector<uint16_t> xt((size_t)T * d.H);
   for (int e : host) {
@@ -559,10 +586,12 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
         if (l->idx_h[t * k + j] == e) { cols[c] = t; js[c] = j; ++c; }
     for (int i = 0; i < c; ++i)
       std::memcpy(&xt[(size_t)i * d.H], l->x_h + (size_t)cols[i] * d.H, (size_t)d.H * 2);
+    const auto tf = clk::now();
     rc = host_expert_ffn(ctx->pool.get(), l->L,
                          (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride, xt.data(), c,
                          yt.data());
     if (rc) return rc;
+    ffn_s += us_since(tf) * 1e-6;
     for (int i = 0; i < c; ++i) {
       const int pair = cols[i] * kk + js[i];
       std::memcpy(l->P_h + (size_t)pair * d.H, &yt[(size_t)i * d.H], (size_t)d.H * 4);
@@ -571,6 +600,12 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     }
   }
   S.host_us = us_since(th);
+  // an observation of Bh: the host experts' rate, plus the bandwidth the copies took from
+  // the host while they ran alongside
+  if (!host.empty() && ffn_s > 0.0) {
+    S.bh_obs = (double)host.size() * l->L.bytes / ffn_s + (streamed.empty() ? 0.0 : l->bp);
+    if (l->alpha > 0.0) l->bh = bandwidth_update(l->bh, S.bh_obs, l->alpha);
+  }
   HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, k, d.n_shared, y, st));
   if (stats) *stats = S;
   return FT_OK;
@@ -606,6 +641,21 @@ extern "C" FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh) {
     return fail(FT_EINVAL, "ft_set_bandwidth: need a layer and Bp, Bh > 0");
   layer->bp = Bp;
   layer->bh = Bh;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q) {
+  return qstar_makespan(m, Bp, Bh, q);
+}
+
+extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha) {
+  if (!layer) return fail(FT_EINVAL, "ft_set_miss_policy: null layer");
+  if (rule != FT_SPLIT_ROUND && rule != FT_SPLIT_MAKESPAN)
+    return fail(FT_EINVAL, "ft_set_miss_policy: unknown split rule");
+  if (!(alpha >= 0.0 && alpha <= 1.0))
+    return fail(FT_EINVAL, "ft_set_miss_policy: alpha must be in [0, 1]");
+  layer->split_rule = rule;
+  layer->alpha = alpha;
   return FT_OK;
 }
 

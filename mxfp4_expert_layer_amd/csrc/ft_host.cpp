@@ -300,6 +300,29 @@ int qstar_split(int m, double Bp, double Bh, int* q, double* qstar) {
   return FT_OK;
 }
 
+// Both sides of the split run at once: q experts over PCIe at Bp while the host computes the
+// other m - q with the bandwidth the copies leave it, Bh - Bp (lowalt article, section 二).
+// The finishing time of q is the later of the two.
+int qstar_makespan(int m, double Bp, double Bh, int* q) {
+  if (m < 0 || !(Bp > 0.0) || !(Bh > 0.0))
+    return fail(FT_EINVAL, "ft_qstar_split_makespan: need m >= 0, Bp > 0 and Bh > 0");
+  int best = m;
+  if (Bh > Bp) {
+    double best_t = 0.0;
+    for (int c = 0; c <= m; ++c) {
+      const double t = std::max((double)c / Bp, (double)(m - c) / (Bh - Bp));
+      if (c == 0 || t < best_t) { best = c; best_t = t; }
+    }
+  }
+  if (q) *q = best;
+  return FT_OK;
+}
+
+double bandwidth_update(double est, double obs, double alpha) {
+  if (!(obs > 0.0) || !std::isfinite(obs)) return est;
+  return est + alpha * (obs - est);
+}
+
 // ---- LRU ------------------------------------------------------------------------------------
 void LruState::init(int E, int S, bool resident) {
   e2s.assign(E, -1);

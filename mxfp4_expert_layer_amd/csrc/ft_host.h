@@ -44,6 +44,12 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
 
 // The split rule: q = floor(m Bp / Bh + 1/2) clamped to [0, m].
 int qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
+// Its makespan variant: the integer q in [0, m] minimising max(q / Bp, (m - q) / (Bh - Bp)),
+// lowest q on ties; Bh <= Bp gives m.
+int qstar_makespan(int m, double Bp, double Bh, int* q);
+// One step of the running estimate of a bandwidth: est + alpha (obs - est); observations
+// that are not positive and finite leave it unchanged.
+double bandwidth_update(double est, double obs, double alpha);
 
 // Expert-slot LRU: streamed misses are admitted into the lowest empty slot, else into the
 // slot with the oldest last use among slots not used in this step (ties: lower slot).

@@ -18,6 +18,7 @@ FT_OK, FT_EINVAL, FT_ENOMEM, FT_EHIP, FT_EUNSUPPORTED, FT_ESTATE = 0, -1, -2, -3
 FT_MXFP4, FT_NVFP4 = 0, 1
 FT_PREFILL_EXACT, FT_PREFILL_MXFP4 = 0, 1
 FT_LAYER_PREFILL_MXFP4 = 1
+FT_SPLIT_ROUND, FT_SPLIT_MAKESPAN = 0, 1
 MAX_DECODE_TOKENS = 16
 FORMATS = {"mxfp4": FT_MXFP4, "nvfp4": FT_NVFP4}
 
@@ -48,7 +49,7 @@ class DecodeStats(C.Structure):
                 ("q", C.c_int32), ("n_streamed", C.c_int32), ("n_host", C.c_int32),
                 ("n_evicted", C.c_int32), ("step", C.c_int32), ("qstar", C.c_double),
                 ("bp", C.c_double), ("bh", C.c_double), ("host_us", C.c_double),
-                ("wait_us", C.c_double)]
+                ("wait_us", C.c_double), ("bp_obs", C.c_double), ("bh_obs", C.c_double)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -70,6 +71,8 @@ _sig = {
     "ft_measure_bandwidth": [_vp, _vp, C.POINTER(_d), C.POINTER(_d)],
     "ft_set_bandwidth": [_vp, _d, _d],
     "ft_force_q": [_vp, _i],
+    "ft_qstar_split_makespan": [_i, _d, _d, C.POINTER(_i)],
+    "ft_set_miss_policy": [_vp, _i, _d],
     "ft_debug_dequant": [_vp, _i, _i, _vp, _vp],
     "ft_debug_tables": [_vp, _vp, _vp],
     "ft_host_expert_ffn": [_vp, _i, _i, _i, _vp, _vp, _i, _vp],
@@ -203,6 +206,16 @@ def set_bandwidth(layer_h, Bp, Bh):
 
 def force_q(layer_h, q):
     check(lib.ft_force_q(layer_h, q))
+
+
+def qstar_split_makespan(m: int, Bp: float, Bh: float) -> int:
+    q = C.c_int()
+    check(lib.ft_qstar_split_makespan(m, Bp, Bh, C.byref(q)))
+    return q.value
+
+
+def set_miss_policy(layer_h, rule=FT_SPLIT_ROUND, alpha=0.0):
+    check(lib.ft_set_miss_policy(layer_h, rule, alpha))
 
 
 def debug_dequant(layer_h, slot, matrix, out, stream=None):

@@ -87,8 +87,10 @@ class LruPool:
         s = min(cand, key=lambda s: (self.last_use[s], s))
         return s, int(self.s2e[s])
 
-    def step(self, idx: np.ndarray, w: np.ndarray, Bp: float, Bh: float, q_override=None):
-        """One decode call: idx/w [T][k] routing of its tokens."""
+    def step(self, idx: np.ndarray, w: np.ndarray, Bp: float, Bh: float, q_override=None,
+             rule: str = "round"):
+        """One decode call: idx/w [T][k] routing of its tokens; rule "round" (the contract's
+        q = round(q*)) or "makespan" (the variant)."""
         step = self.step_no
         weight = {}
         for t in range(idx.shape[0]):
@@ -101,7 +103,12 @@ class LruPool:
             self.last_use[self.e2s[e]] = step
         misses = order_misses([e for e in selected if self.e2s[e] < 0], weight)
         m = len(misses)
-        q = qstar_split(m, Bp, Bh)[0] if q_override is None else max(0, min(m, q_override))
+        if q_override is not None:
+            q = max(0, min(m, q_override))
+        elif rule == "makespan":
+            q = qstar_makespan(m, Bp, Bh)
+        else:
+            q = qstar_split(m, Bp, Bh)[0]
         streamed, host, evicted = [], [], []
         for n, e in enumerate(misses):
             if n >= q:

@@ -284,6 +284,52 @@ def test_miss_path_forced_split_gives_same_outputs(ctx, q_force):
     _miss_sequence(ctx, L, steps=8, bp=1.0, bh=3.0, check_every=1, T=1, q_force=q_force)
 
 
+@pytest.mark.parametrize("rule", [0, 1])
+def test_miss_path_adaptive_bandwidths(ctx, rule):
+    """Bp and Bh re-measured during decode (running average, alpha = 1/2) under both split
+    rules: the oracle's pool replays each call's split with the Bp, Bh that call reports, so
+    the slot tables stay bit-exact; each estimate moves toward its observation by alpha."""
+    cfg = synth.small_config("missadapt", seed=81, H=384, I=256, E=14, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 20, zipf_c=0.7)
+    L = layer_for(ctx, f"missadapt{rule}", cfg=cfg, resident=False, n_slots=5, max_tokens=2)
+    with pytest.raises(ft.FtError) as e:
+        ft.set_miss_policy(L.handle, 7, 0.5)
+    assert e.value.code == ft.FT_EINVAL
+    with pytest.raises(ft.FtError) as e:
+        ft.set_miss_policy(L.handle, rule, 1.5)
+    assert e.value.code == ft.FT_EINVAL
+    ft.set_bandwidth(L.handle, 1.0e9, 3.0e9)
+    ft.force_q(L.handle, -1)
+    ft.set_miss_policy(L.handle, rule, 0.5)
+    OL = L.oracle_layer()
+    pool = policy.LruPool(cfg.E, L.n_slots)
+    prev, seen_bp, seen_bh = None, 0, 0
+    try:
+        for s in range(24):
+            x = synth.gen_tokens(cfg, 2, batch=300 + s)
+            st = ft.DecodeStats()
+            y = run_decode(ctx, L, x, st)
+            r_idx, r_w, logits, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+            assert np.all(gap >= 1e-6), "near-tie in a miss-path step; choose another seed"
+            res = pool.step(r_idx, r_w, st.bp, st.bh, rule="makespan" if rule else "round")
+            e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+            assert np.array_equal(e2s, res.e2s) and np.array_equal(s2e, res.s2e), f"step {s}"
+            assert (st.q, st.n_streamed, st.n_host) == (res.q, len(res.streamed), len(res.host)), s
+            if prev is not None:
+                bp = prev.bp + 0.5 * (st.bp_obs - prev.bp) if st.bp_obs > 0 else prev.bp
+                bh = prev.bh + 0.5 * (prev.bh_obs - prev.bh) if prev.bh_obs > 0 else prev.bh
+                assert st.bp == pytest.approx(bp, rel=1e-12) and st.bh == pytest.approx(bh, rel=1e-12), s
+            seen_bp += st.bp_obs > 0
+            seen_bh += prev is not None and prev.bh_obs > 0
+            if s % 4 == 0:
+                check_output(y, moe.moe_forward(OL, x)["y"], f"adaptive step {s}")
+            prev = st
+    finally:
+        ft.set_miss_policy(L.handle, ft.FT_SPLIT_ROUND, 0.0)
+    assert seen_bp > 0 and seen_bh > 0, (seen_bp, seen_bh)
+    log(f"[gpu] adaptive rule {rule}: final Bp {prev.bp / 1e9:.2f} GB/s, Bh {prev.bh / 1e9:.2f} GB/s")
+
+
 def test_miss_path_284b_layer(ctx):
     """The 284B-class layer with a 48-slot pool: 64 warm-up and 64 timed single tokens with the
     slot tables checked after every step and the outputs every 8th step."""

@@ -119,3 +119,18 @@ def test_host_expert_ffn_nan_scale_propagates():
     assert np.array_equal(np.isnan(y), np.isnan(ref)) and np.isnan(y[0, 5])
     fin = ~np.isnan(ref)
     assert moe.rel_l2(y[fin], ref[fin]) <= 1e-3
+
+
+def test_makespan_split_matches_oracle():
+    """The library's makespan variant against the oracle's on a grid that includes the
+    pages' four measured bandwidth pairs, and its argument checks."""
+    pairs = [(49.0, 53.8), (52.7, 77.3), (25.1, 63.2), (11.8, 47.5), (60.0, 50.0), (1.0, 2.0)]
+    rng = np.random.default_rng(3)
+    pairs += [(float(a), float(b)) for a, b in rng.uniform(1.0, 100.0, size=(200, 2))]
+    for Bp, Bh in pairs:
+        for m in range(0, 17):
+            assert ft.qstar_split_makespan(m, Bp, Bh) == policy.qstar_makespan(m, Bp, Bh), (m, Bp, Bh)
+    for bad in ((-1, 1.0, 1.0), (1, 0.0, 1.0), (1, 1.0, 0.0), (1, float("nan"), 1.0)):
+        with pytest.raises(ft.FtError) as e:
+            ft.qstar_split_makespan(*bad)
+        assert e.value.code == ft.FT_EINVAL

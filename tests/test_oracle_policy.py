@@ -1,6 +1,8 @@
 """Pins for the oracle's q* split, miss ordering, LRU pool and prefill permutation (CPU)."""
 import os
 
+import math
+
 import numpy as np
 import pytest
 
@@ -56,6 +58,35 @@ def test_makespan_variant_differs_where_expected():
     assert policy.qstar_makespan(2, 52.7, 77.3) == 2
     assert policy.qstar_makespan(3, 11.8, 47.5) == 0
     assert policy.qstar_split(3, 11.8, 47.5)[0] == 1
+
+
+def test_makespan_variant_brackets_qstar():
+    """Both sides finish together at the continuous optimum of max(q/Bp, (m-q)/(Bh-Bp)):
+    q/Bp = (m-q)/(Bh-Bp) solves to q = m Bp / Bh = q*, and the cost falls then rises in q, so
+    the best integer is floor(q*) or ceil(q*) (m when Bh <= Bp)."""
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        m = int(rng.integers(0, 17))
+        Bp = float(rng.uniform(1.0, 100.0))
+        Bh = float(rng.uniform(1.0, 120.0))
+        q = policy.qstar_makespan(m, Bp, Bh)
+        if Bh <= Bp:
+            assert q == m
+            continue
+        qs = m * Bp / Bh
+        assert q in (math.floor(qs), math.ceil(qs)), (m, Bp, Bh, q, qs)
+    # an exact tie between the two candidates goes to the lower q: m = 1, Bh = 2 Bp
+    assert policy.qstar_makespan(1, 1.0, 2.0) == 0
+
+
+def test_lru_makespan_rule_uses_the_variant():
+    P = policy.LruPool(E=8, S=8)
+    # 5090 desktop bandwidths, six misses: round gives 5, the makespan variant 6
+    r = P.step(np.array([[0, 1, 2, 3, 4, 5]]), np.full((1, 6), 1 / 6), 49.0, 53.8, rule="makespan")
+    assert r.q == 6 and len(r.streamed) == 6
+    P2 = policy.LruPool(E=8, S=8)
+    r2 = P2.step(np.array([[0, 1, 2, 3, 4, 5]]), np.full((1, 6), 1 / 6), 49.0, 53.8)
+    assert r2.q == 5 and len(r2.host) == 1
 
 
 def test_miss_order():
