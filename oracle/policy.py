@@ -19,6 +19,19 @@ Readings where the pages are silent:
     the occupied slot with the smallest last-use step among slots not used in this step,
     ties to the lower slot index.  When no slot can be taken the expert is computed on the
     host instead (so at most the number of takeable slots are streamed).
+
+Cross-layer prefetch.  While the GPU computes one layer, the experts the next layer will
+probably use are streamed into VRAM in the background, with double buffering (mubeitech
+article, closing section; lpnh.cn article, section 2.3, predictive prefetch).  The pages give
+no predictor; the reading taken here:
+  * the prediction for layer l+1 is layer l+1's own routing (top-k softmax) applied to layer
+    l's input;
+  * at the next layer's upcoming step n (its call counter), every predicted expert already
+    resident has its slot's last use set to n, so no prefetch of that batch evicts it;
+  * the predicted experts not resident, in descending summed predicted weight (ties to the
+    lower id), are admitted one by one through the same slot rule at step n, at most `depth`
+    of them; a prefetched slot's last use is n, so the step-n call cannot evict it either;
+  * a step-n hit on a slot filled by a prefetch and not used since counts as a prefetch hit.
 """
 from __future__ import annotations
 
@@ -65,6 +78,17 @@ class StepResult:
     evicted: list        # (slot, expert) pairs evicted this step
     e2s: np.ndarray = field(repr=False, default=None)
     s2e: np.ndarray = field(repr=False, default=None)
+    prefetch_hits: int = 0   # hits on slots a prefetch filled and nothing used since
+
+
+@dataclass
+class PrefetchResult:
+    step: int            # the pool's upcoming step the prefetch is for
+    predicted: list      # distinct predicted experts, in admission order
+    admitted: list       # experts copied into slots, in order
+    evicted: list        # (slot, expert) pairs evicted
+    e2s: np.ndarray = field(repr=False, default=None)
+    s2e: np.ndarray = field(repr=False, default=None)
 
 
 class LruPool:
@@ -75,6 +99,7 @@ class LruPool:
         self.e2s = np.full(E, -1, dtype=np.int64)
         self.s2e = np.full(S, -1, dtype=np.int64)
         self.last_use = np.full(S, -1, dtype=np.int64)
+        self.pref = np.zeros(S, dtype=bool)   # filled by a prefetch, not used since
         self.step_no = 0
 
     def _take_slot(self, step: int):
@@ -99,8 +124,12 @@ class LruPool:
                 weight[e] = weight.get(e, 0.0) + float(w[t, j])
         selected = sorted(weight)
         hits = [e for e in selected if self.e2s[e] >= 0]
+        prefetch_hits = 0
         for e in hits:
-            self.last_use[self.e2s[e]] = step
+            s = self.e2s[e]
+            self.last_use[s] = step
+            prefetch_hits += int(self.pref[s])
+            self.pref[s] = False
         misses = order_misses([e for e in selected if self.e2s[e] < 0], weight)
         m = len(misses)
         if q_override is not None:
@@ -124,7 +153,39 @@ class LruPool:
             self.s2e[s] = e
             self.e2s[e] = s
             self.last_use[s] = step
+            self.pref[s] = False
             streamed.append(e)
         self.step_no += 1
         return StepResult(step, selected, hits, misses, q, streamed, host, evicted,
-                          self.e2s.copy(), self.s2e.copy())
+                          self.e2s.copy(), self.s2e.copy(), prefetch_hits)
+
+    def prefetch(self, idx: np.ndarray, w: np.ndarray, depth: int):
+        """Prefetch before this pool's next step: idx/w [T][k] the predicted routing."""
+        step = self.step_no
+        weight = {}
+        for t in range(idx.shape[0]):
+            for j in range(idx.shape[1]):
+                e = int(idx[t, j])
+                weight[e] = weight.get(e, 0.0) + float(w[t, j])
+        order = order_misses(list(weight), weight)
+        for e in order:
+            if self.e2s[e] >= 0:
+                self.last_use[self.e2s[e]] = step
+        admitted, evicted = [], []
+        for e in order:
+            if len(admitted) >= depth:
+                break
+            if self.e2s[e] >= 0:
+                continue
+            s, old = self._take_slot(step)
+            if s is None:
+                break
+            if old is not None:
+                self.e2s[old] = -1
+                evicted.append((s, old))
+            self.s2e[s] = e
+            self.e2s[e] = s
+            self.last_use[s] = step
+            self.pref[s] = True
+            admitted.append(e)
+        return PrefetchResult(step, order, admitted, evicted, self.e2s.copy(), self.s2e.copy())

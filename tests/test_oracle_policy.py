@@ -142,6 +142,65 @@ def test_lru_invariants_random():
             assert r.e2s[e] >= 0
 
 
+def test_prefetch_scripted_sequence():
+    """Worked by hand from the prefetch reading: predicted residents are protected, new ones
+    are admitted in weight order up to the depth, and a prefetched slot survives the step it
+    was fetched for and counts as a prefetch hit when used."""
+    P = policy.LruPool(E=8, S=3)
+    r = P.step(np.array([[0, 1]]), np.array([[0.6, 0.4]]), 1.0, 1.0)
+    assert list(r.s2e) == [0, 1, -1]
+    # predicted weights: 0 -> 1.2, 2 -> 0.5, 3 -> 0.3; 0 is resident and gets protected
+    f = P.prefetch(np.array([[2, 0], [3, 0]]), np.array([[0.5, 0.5], [0.3, 0.7]]), depth=2)
+    assert f.step == 1 and f.predicted == [0, 2, 3]
+    assert f.admitted == [2, 3] and f.evicted == [(1, 1)] and list(f.s2e) == [0, 3, 2]
+    # step 1: 2 is a prefetch hit; 4 misses, but every slot was used or fetched for step 1
+    r = P.step(np.array([[2, 4]]), np.array([[0.8, 0.2]]), 1.0, 1.0)
+    assert r.hits == [2] and r.prefetch_hits == 1 and r.host == [4] and r.streamed == []
+    # step 2: 3 (fetched for step 1, unused there) still counts; 5 evicts slot 0 (last use 1,
+    # tied with slot 2, lower index)
+    r = P.step(np.array([[3, 5]]), np.array([[0.5, 0.5]]), 1.0, 1.0)
+    assert r.hits == [3] and r.prefetch_hits == 1 and r.evicted == [(0, 0)]
+    assert list(r.s2e) == [5, 3, 2]
+    # a used slot is no longer a prefetched one
+    r = P.step(np.array([[3, 2]]), np.array([[0.5, 0.5]]), 1.0, 1.0)
+    assert r.prefetch_hits == 0
+    # depth 0 admits nothing; all-resident predictions admit nothing
+    assert P.prefetch(np.array([[7]]), np.array([[1.0]]), depth=0).admitted == []
+    assert P.prefetch(np.array([[3, 2]]), np.array([[0.5, 0.5]]), depth=4).admitted == []
+
+
+def test_prefetch_invariants_random():
+    rng = np.random.default_rng(11)
+    E, S, k = 24, 5, 3
+    P = policy.LruPool(E, S)
+    pending = set()          # experts a prefetch brought in that no step has used since
+    for it in range(400):
+        T = int(rng.integers(1, 3))
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+        w = rng.random((T, k))
+        w /= w.sum(1, keepdims=True)
+        if rng.random() < 0.5:
+            depth = int(rng.integers(0, 4))
+            before = set(int(e) for e in np.nonzero(P.e2s >= 0)[0])
+            f = P.prefetch(idx, w, depth)
+            pred = set(int(e) for e in idx.ravel())
+            assert len(f.admitted) <= depth and set(f.admitted) <= pred - before
+            for e in pred & before:          # predicted residents are never evicted
+                assert f.e2s[e] >= 0
+            for e in f.admitted:
+                assert f.e2s[e] >= 0 and f.s2e[f.e2s[e]] == e
+            pending -= {old for _, old in f.evicted}
+            pending |= set(f.admitted)
+            continue
+        r = P.step(idx, w, 1.0, float(rng.uniform(0.5, 3.0)))
+        assert r.prefetch_hits == len(pending & set(r.hits))
+        pending -= set(r.hits)
+        pending -= {old for _, old in r.evicted}
+        for s in range(S):
+            if r.s2e[s] >= 0:
+                assert r.e2s[r.s2e[s]] == s
+
+
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (7, 2, 5), (64, 8, 16), (200, 6, 256)])
 def test_permutation_matches_stable_sort(T, k, E):
     rng = np.random.default_rng(T * 31 + k)
