@@ -6,6 +6,7 @@ Workloads (seeded synthetic layers, no trained weights exist for these shapes):
   decode-35b-a3b-nvfp4  the same layer with NVFP4 experts (E4M3 per 16, tensor scale 1/64)
   decode-284b      hidden 4096, 256 experts + 1 shared, top-6, intermediate 2048, MXFP4
   miss-path-284b   the 284B-class layer with a 48-slot pool, q* split of misses
+                   (--layers N chains N such layers, --prefetch D adds cross-layer prefetch)
   prefill-753b     4096 tokens through hidden 6144, 160 experts, top-8, intermediate 2048,
                    NVFP4 (exact bf16-MFMA grouped GEMMs)
 A step is one ft_moe_decode call of T tokens (routing, gate/up + SwiGLU, down, combine).
@@ -231,73 +232,116 @@ def bench_decode(args, wl):
 
 
 def bench_miss_path(args, wl):
+    """Miss-path decode of single tokens through `--layers` chained layers of the 284B class
+    (48-slot pools over one shared pinned store; each layer has its own router draw and pool;
+    layer l+1's input is bf16(x_l + y_l)); `--prefetch D` links every layer to the next for
+    cross-layer prefetch of up to D predicted experts.  A step is one token through all
+    layers; value = tokens/s.  `--residual-scale g` makes layer l+1's input bf16(x_l + g y_l):
+    with random weights an expert output is several times its input, so g sets how far the
+    input drifts per layer (reported as residual_ratio = |g y| / |x|, measured in warm-up),
+    and with it how well the next router on x_l predicts its routing on x_{l+1}."""
+    import dataclasses
+
     import numpy as np
     import torch
 
     from mxfp4_expert_layer_amd import ft, synth
     from mxfp4_expert_layer_amd.layer import GpuLayer
 
-    import dataclasses
     cfg = synth.CONFIGS[wl["cfg"]]
     if args.zipf_c is not None:
         cfg = dataclasses.replace(cfg, zipf_c=args.zipf_c)
     K = args.steps if args.steps is not None else wl["steps"]
     W = args.warmup if args.warmup is not None else wl["warmup"]
+    NL = max(1, args.layers)
     ctx = ft.Context(0)
-    log(f"[bench] building the miss-path layer ({cfg.n_slots} of {cfg.E} slots, pinned store)")
-    L = GpuLayer(ctx, cfg, resident=False, n_slots=cfg.n_slots, max_tokens=1, threads=16)
-    bp, bh = ft.measure_bandwidth(ctx, L.handle)
+    log(f"[bench] building {NL} miss-path layer(s) ({cfg.n_slots} of {cfg.E} slots, pinned store)")
+    Ls = [GpuLayer(ctx, cfg, resident=False, n_slots=cfg.n_slots, max_tokens=1, threads=16)]
+    for li in range(1, NL):
+        router = synth.gen_router(dataclasses.replace(cfg, seed=cfg.seed + 100 * li))
+        Ls.append(GpuLayer(ctx, cfg, resident=False, n_slots=cfg.n_slots, max_tokens=1,
+                           router=router, host_store=Ls[0].host_blobs))
+    bp, bh = ft.measure_bandwidth(ctx, Ls[0].handle)
     log(f"[bench] measured Bp {bp / 1e9:.1f} GB/s, Bh {bh / 1e9:.1f} GB/s")
     rule = ft.FT_SPLIT_MAKESPAN if args.split == "makespan" else ft.FT_SPLIT_ROUND
-    ft.set_miss_policy(L.handle, rule, args.adaptive)
+    for li, L in enumerate(Ls):
+        ft.set_bandwidth(L.handle, bp, bh)
+        ft.set_miss_policy(L.handle, rule, args.adaptive)
+        if args.prefetch > 0 and li + 1 < NL:
+            ft.set_prefetch(L.handle, Ls[li + 1].handle, args.prefetch)
     xs = [torch.from_numpy(synth.gen_tokens(cfg, 1, batch=2000 + b).view(np.int16)).to("cuda")
           for b in range(W + K)]
+    xl = torch.empty((1, cfg.H), dtype=torch.int16, device="cuda")
     y = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     st = ft.DecodeStats()
-    for i in range(W):
-        ft.moe_decode(ctx, L.handle, xs[i], 1, y, s, st)
-    torch.cuda.synchronize()
-    hits = sel = m_sum = q_sum = streamed = host = 0
+    tot = dict(hits=0, sel=0, m=0, q=0, streamed=0, host=0, pf=0, pf_hits=0)
     host_us = wait_us = 0.0
     bp_obs, bh_obs = [], []
+
+    def token(x, count):
+        nonlocal host_us, wait_us
+        for li, L in enumerate(Ls):
+            ft.moe_decode(ctx, L.handle, x if li == 0 else xl, 1, y, s, st)
+            if li + 1 < NL:
+                if ratios is not None:
+                    xin = (x if li == 0 else xl).view(torch.bfloat16).float()
+                    ratios.append(float(args.residual_scale * y.norm() / xin.norm()))
+                ft.residual_bf16(ctx, x if li == 0 else xl, y, cfg.H, xl, s, args.residual_scale)
+            if not count:
+                continue
+            for key, v in (("hits", st.n_hits), ("sel", st.n_selected), ("m", st.n_miss),
+                           ("q", st.q), ("streamed", st.n_streamed), ("host", st.n_host),
+                           ("pf", st.n_prefetched), ("pf_hits", st.n_prefetch_hits)):
+                tot[key] += v
+            host_us += st.host_us
+            wait_us += st.wait_us
+            if st.bp_obs > 0:
+                bp_obs.append(st.bp_obs)
+            if st.bh_obs > 0:
+                bh_obs.append(st.bh_obs)
+
+    ratios = []     # |g y| / |x| of the first warm-up tokens (syncs; not timed)
+    for i in range(W):
+        token(xs[i], False)
+        if i == 7:
+            ratios_w, ratios = ratios, None
+    if ratios is not None:
+        ratios_w, ratios = ratios, None
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        ft.moe_decode(ctx, L.handle, xs[W + i], 1, y, s, st)
-        hits += st.n_hits
-        sel += st.n_selected
-        m_sum += st.n_miss
-        q_sum += st.q
-        streamed += st.n_streamed
-        host += st.n_host
-        host_us += st.host_us
-        wait_us += st.wait_us
-        if st.bp_obs > 0:
-            bp_obs.append(st.bp_obs)
-        if st.bh_obs > 0:
-            bh_obs.append(st.bh_obs)
+        token(xs[W + i], True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    blob = L.stride
+    blob = Ls[0].stride
+    calls = K * NL
     res = {
         "metric": METRIC, "value": K / dt, "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": dt / K * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
-                   "slots": cfg.n_slots, "zipf_c": cfg.zipf_c, "weights": cfg.fmt},
-        "miss_path": {"Bp_GBps": bp / 1e9, "Bh_GBps": bh / 1e9, "hit_rate": hits / max(1, sel),
-                      "mean_m": m_sum / K, "mean_q": q_sum / K, "streamed": streamed,
-                      "host_computed": host, "pcie_GBps": streamed * blob / dt / 1e9,
-                      "host_GBps": host * blob / max(host_us * 1e-6, 1e-9) / 1e9,
-                      "mean_host_us": host_us / K, "mean_wait_us": wait_us / K,
+                   "slots": cfg.n_slots, "zipf_c": cfg.zipf_c, "weights": cfg.fmt,
+                   "layers": NL, "prefetch_depth": args.prefetch,
+                   "residual_scale": args.residual_scale},
+        "miss_path": {"Bp_GBps": bp / 1e9, "Bh_GBps": bh / 1e9,
+                      "hit_rate": tot["hits"] / max(1, tot["sel"]),
+                      "mean_m": tot["m"] / calls, "mean_q": tot["q"] / calls,
+                      "streamed": tot["streamed"], "host_computed": tot["host"],
+                      "prefetched": tot["pf"], "prefetch_hits": tot["pf_hits"],
+                      "residual_ratio": float(np.mean(ratios_w)) if ratios_w else None,
+                      "pcie_GBps": (tot["streamed"] + tot["pf"]) * blob / dt / 1e9,
+                      "host_GBps": tot["host"] * blob / max(host_us * 1e-6, 1e-9) / 1e9,
+                      "mean_host_us": host_us / calls, "mean_wait_us": wait_us / calls,
                       "split_rule": args.split, "adaptive_alpha": args.adaptive,
                       "final_Bp_GBps": st.bp / 1e9, "final_Bh_GBps": st.bh / 1e9,
                       "median_Bp_obs_GBps": float(np.median(bp_obs)) / 1e9 if bp_obs else None,
                       "median_Bh_obs_GBps": float(np.median(bh_obs)) / 1e9 if bh_obs else None},
         "roofline": None,
     }
-    L.close()
+    for L in Ls:
+        L.close()
     ctx.close()
     return res
 
@@ -455,6 +499,12 @@ def main():
                     help="miss path: split rule (round(q*) or the makespan variant)")
     ap.add_argument("--adaptive", type=float, default=0.0,
                     help="miss path: running-average weight for re-measuring Bp, Bh (0: fixed)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="miss path: chained layers per token (input of l+1 = bf16(x_l + y_l))")
+    ap.add_argument("--prefetch", type=int, default=0,
+                    help="miss path: cross-layer prefetch depth (0: off)")
+    ap.add_argument("--residual-scale", type=float, default=1.0,
+                    help="miss path: input of layer l+1 = bf16(x_l + g * y_l)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

@@ -146,6 +146,10 @@ typedef struct ft_decode_stats {
      bp_obs from the previous call's streamed copies, bh_obs from this call's host experts
      (see ft_set_miss_policy) */
   double bp_obs, bh_obs;
+  /* cross-layer prefetch (see ft_set_prefetch): experts this call admitted to and started
+     copying into the linked next layer's pool, and this call's hits on slots that a prefetch
+     filled and nothing has used since */
+  int32_t n_prefetched, n_prefetch_hits;
 } ft_decode_stats;
 
 /*
@@ -230,6 +234,43 @@ FT_API int ft_force_q(ft_layer* layer, int q);
  * bh_obs.  FT_EINVAL for an unknown rule or alpha outside [0, 1].
  */
 FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha);
+
+/*
+ * Cross-layer prefetch with double buffering: while the GPU computes one layer, the experts
+ * the next layer will probably need stream into VRAM in the background (mubeitech article,
+ * closing section; lpnh.cn article, section 2.3, predictive prefetch).  Links `layer` to
+ * `next`, both miss-path layers (partial pools) of one context with the same H.  Each later
+ * ft_moe_decode of `layer`:
+ *   - predicts next's routing by applying next's router (top-k softmax) to layer's own input
+ *     x, on an internal stream beside layer's routing;
+ *   - after enqueueing layer's own copies and kernels, marks the predicted experts already in
+ *     next's pool as used at next's coming call, then admits up to `depth` of the others, by
+ *     descending summed predicted weight (ties to the lower id), through next's slot rule
+ *     (lowest empty slot, else the least recently used one not used or fetched for that call)
+ *     and copies them on the copy stream, behind layer's own copies and after next's previous
+ *     kernels;
+ *   - reports the count in ft_decode_stats.n_prefetched.
+ * next's following ft_moe_decode finds them resident; its kernels wait for those copies, and
+ * its n_prefetch_hits counts its hits on them.  The two pools are separate buffers, so the
+ * copies into next's never touch what layer's kernels read (the double buffer).
+ * next = NULL or depth = 0 unlinks.  A layer prefetches for at most one next, and a layer
+ * is the next of at most one layer; destroying either unlinks.  FT_EINVAL for a null layer,
+ * depth < 0 or above next's n_slots, next == layer, another context, a resident pool, a
+ * different H, or a next already linked from another layer.  FT_ENOMEM if the prediction
+ * buffers cannot be allocated.
+ */
+FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth);
+
+/*
+ * out[i] = bf16(float(x[i]) + scale * y[i]) for 0 <= i < n: the product and the sum each
+ * rounded to fp32 (no fused multiply-add), the result rounded to nearest even bf16 (NaN stays
+ * NaN).  A residual step for chaining decode layers (one layer's scaled output added to its
+ * input gives the next layer's input); x, y and out are device arrays (bf16 bits, fp32, bf16
+ * bits), out may alias x.  n >= 0 (0 does nothing).  FT_EINVAL for a null context, n < 0 or
+ * null arrays with n > 0.  Asynchronous on `stream`.
+ */
+FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const float* y, float scale,
+                            int64_t n, uint16_t* out, void* stream);
 
 FT_API const char* ft_last_error(void);
 

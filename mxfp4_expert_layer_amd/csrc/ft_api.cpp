@@ -23,6 +23,8 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
                         int H, hipStream_t st);
 extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_down_combines(const DecodeLaunch* a);
+extern "C" int ftk_residual(const uint16_t* x, const float* y, float sc, int64_t n, uint16_t* out,
+                            hipStream_t st);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
                            float* y, hipStream_t st);
 extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix, float ts,
@@ -58,6 +60,7 @@ int env_int(const char* name, int dflt) {
 struct ft_ctx {
   int device = 0;
   hipStream_t copy_stream = nullptr;
+  hipStream_t pred_stream = nullptr;   // routing of a linked next layer (prefetch prediction)
   std::unique_ptr<ThreadPool> pool;
 };
 
@@ -106,6 +109,23 @@ struct ft_layer {
   int split_rule = FT_SPLIT_ROUND;
   double alpha = 0.0;            // running-estimate weight (0: Bp and Bh fixed)
   uint64_t pend_copy_bytes = 0;  // streamed bytes of the last call, timed by ev_cp0/ev_cp1
+  hipEvent_t ev_done = nullptr;  // after the kernels of the last miss-path call
+  // cross-layer prefetch: this layer predicts and fills `next`'s pool (ft_set_prefetch)
+  ft_layer* next = nullptr;
+  ft_layer* prev = nullptr;      // the layer whose calls prefetch into this one
+  int pf_depth = 0;
+  void* pf_dev = nullptr;        // prediction logits [16][1024], idx, w [16][16]
+  float* pf_logits = nullptr;
+  int32_t* pf_idx = nullptr;
+  float* pf_w = nullptr;
+  void* pf_pin = nullptr;        // mapped pinned idx, w of the prediction
+  int32_t* pf_idx_h = nullptr;
+  float* pf_w_h = nullptr;
+  int32_t* pf_idx_hd = nullptr;  // their device addresses
+  float* pf_w_hd = nullptr;
+  hipEvent_t ev_x = nullptr, ev_pred = nullptr;
+  hipEvent_t ev_pref = nullptr;  // after the prefetch copies into this layer's pool
+  bool pref_pending = false;
   // kernel timing events: [n][4] = gate/up start, stop, down start, stop
   std::vector<hipEvent_t> prof;
   int prof_n = 0, prof_i = 0;
@@ -194,6 +214,7 @@ extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) {
   if (!c) return fail(FT_ENOMEM, "ft_ctx_create: out of host memory");
   c->device = device;
   HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
+  HIP_TRY(hipStreamCreateWithFlags(&c->pred_stream, hipStreamNonBlocking));
   const int hw = (int)std::thread::hardware_concurrency();
   const int nt = env_int("FT_HOST_THREADS", std::max(1, std::min(16, hw)));
   c->pool.reset(new ThreadPool(std::max(1, nt)));
@@ -207,6 +228,11 @@ extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
     hipSetDevice(ctx->device);
     hipStreamSynchronize(ctx->copy_stream);
     hipStreamDestroy(ctx->copy_stream);
+  }
+  if (ctx->pred_stream) {
+    hipSetDevice(ctx->device);
+    hipStreamSynchronize(ctx->pred_stream);
+    hipStreamDestroy(ctx->pred_stream);
   }
   delete ctx;
   return FT_OK;
@@ -227,6 +253,12 @@ static void free_layer(ft_layer* l) {
   if (l->ev_route) hipEventDestroy(l->ev_route);
   if (l->ev_cp0) hipEventDestroy(l->ev_cp0);
   if (l->ev_cp1) hipEventDestroy(l->ev_cp1);
+  if (l->ev_done) hipEventDestroy(l->ev_done);
+  if (l->ev_x) hipEventDestroy(l->ev_x);
+  if (l->ev_pred) hipEventDestroy(l->ev_pred);
+  if (l->ev_pref) hipEventDestroy(l->ev_pref);
+  if (l->pf_dev) hipFree(l->pf_dev);
+  if (l->pf_pin) hipHostFree(l->pf_pin);
   if (l->dev) hipFree(l->dev);
   if (l->mx_owned) hipFree(l->mx_owned);
   if (l->pin) hipHostFree(l->pin);
@@ -350,6 +382,9 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipEventCreateWithFlags(&l->ev_route, hipEventDisableTiming));
   HIP_TRY(hipEventCreate(&l->ev_cp0));
   HIP_TRY(hipEventCreate(&l->ev_cp1));
+  HIP_TRY(hipEventCreateWithFlags(&l->ev_done, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&l->ev_pref, hipEventDisableTiming));
+  HIP_TRY(hipEventRecord(l->ev_done, nullptr));
   *out = l.release();
   return FT_OK;
 }
@@ -358,6 +393,12 @@ extern "C" FT_API int ft_layer_destroy(ft_layer* layer) {
   if (!layer) return FT_OK;
   hipSetDevice(layer->ctx->device);
   hipDeviceSynchronize();
+  // unlink prefetching in both directions
+  if (layer->prev && layer->prev->next == layer) {
+    layer->prev->next = nullptr;
+    layer->prev->pf_depth = 0;
+  }
+  if (layer->next && layer->next->prev == layer) layer->next->prev = nullptr;
   free_layer(layer);
   return FT_OK;
 }
@@ -434,12 +475,80 @@ static void add_item(WorkItem* list, int* n, int expert, int slot) {
   it.slot = slot;
 }
 
+// Cross-layer prefetch into nx's pool for its next call, from the predicted routing idx/w
+// [T][k of nx]: the predicted experts already resident are marked used at that call's step
+// (so this batch evicts none of them); the others, by descending summed predicted weight
+// (ties to the lower id), are admitted through the pool's slot rule at that step, at most
+// depth of them, and copied on the copy stream once nx's previous kernels are done.
+static int prefetch_into(ft_ctx* ctx, ft_layer* nx, const int32_t* idx, const float* w, int T,
+                         int depth, int32_t* n_admitted) {
+  const ft_layer_desc& nd = nx->d;
+  const int k = nd.k, E = nd.E;
+  const int64_t now = nx->lru.step;
+  std::vector<double> ws(E, 0.0);
+  std::vector<char> sel(E, 0);
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) return fail(FT_ESTATE, "ft_moe_decode: prediction gave a bad index");
+      sel[e] = 1;
+      ws[e] += w[t * k + j];
+    }
+  std::vector<int> order;
+  for (int e = 0; e < E; ++e)
+    if (sel[e]) order.push_back(e);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return ws[a] > ws[b] || (ws[a] == ws[b] && a < b);
+  });
+  LruState& P = nx->lru;
+  for (int e : order)
+    if (P.e2s[e] >= 0) P.last_use[P.e2s[e]] = now;
+  std::vector<std::pair<int, int>> adm;   // (expert, slot)
+  for (int e : order) {
+    if ((int)adm.size() >= depth) break;
+    if (P.e2s[e] >= 0) continue;
+    int32_t old = -1;
+    const int s = P.take_slot(now, &old);
+    if (s < 0) break;
+    if (old >= 0) P.e2s[old] = -1;
+    P.s2e[s] = e;
+    P.e2s[e] = s;
+    P.last_use[s] = now;
+    P.pref[s] = 1;
+    adm.emplace_back(e, s);
+  }
+  if (!adm.empty()) {
+    HIP_TRY(hipStreamWaitEvent(ctx->copy_stream, nx->ev_done, 0));
+    for (const auto& es : adm)
+      HIP_TRY(hipMemcpyAsync((uint8_t*)nd.pool + (uint64_t)es.second * nd.blob_stride,
+                             (const uint8_t*)nd.host_blobs + (uint64_t)es.first * nd.blob_stride,
+                             nx->L.bytes, hipMemcpyHostToDevice, ctx->copy_stream));
+    HIP_TRY(hipEventRecord(nx->ev_pref, ctx->copy_stream));
+    nx->pref_pending = true;
+  }
+  *n_admitted = (int32_t)adm.size();
+  return FT_OK;
+}
+
 static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, float* y,
                             ft_decode_stats* stats, hipStream_t st) {
   const ft_layer_desc& d = l->d;
   const int k = d.k, kk = l->kk, E = d.E;
   ft_decode_stats S{};
   auto t0 = clk::now();
+  // a linked next layer's prediction: its router on this input, on the side stream, beside
+  // this layer's own routing (x is ready on `st` when the call is made)
+  ft_layer* nx = (l->next && l->pf_depth > 0) ? l->next : nullptr;
+  if (nx) {
+    const ft_layer_desc& nd = nx->d;
+    HIP_TRY(hipEventRecord(l->ev_x, st));
+    HIP_TRY(hipStreamWaitEvent(ctx->pred_stream, l->ev_x, 0));
+    HIP_TRY((hipError_t)ftk_logits(x, nd.router_w, nd.router_b, T, d.H, nd.E, l->pf_logits,
+                                   ctx->pred_stream));
+    HIP_TRY((hipError_t)ftk_topk(l->pf_logits, T, nd.E, nd.k, l->pf_idx, l->pf_w, l->pf_idx_hd,
+                                 l->pf_w_hd, nullptr, nullptr, d.H, ctx->pred_stream));
+    HIP_TRY(hipEventRecord(l->ev_pred, ctx->pred_stream));
+  }
   HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, E, l->logits, st));
   // the top-k kernel writes idx, w and the token rows into the mapped pinned staging
   auto dev_of = [&](const void* hp) { return l->pin_dev + ((const uint8_t*)hp - (const uint8_t*)l->pin); };
@@ -466,7 +575,9 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     ++S.n_selected;
     if (l->lru.e2s[e] >= 0) {
       hits.push_back(e);
-      l->lru.last_use[l->lru.e2s[e]] = now;
+      const int s = l->lru.e2s[e];
+      l->lru.last_use[s] = now;
+      if (l->lru.pref[s]) { ++S.n_prefetch_hits; l->lru.pref[s] = 0; }
     } else {
       misses.push_back(e);
     }
@@ -507,6 +618,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     l->lru.s2e[s] = e;
     l->lru.e2s[e] = s;
     l->lru.last_use[s] = now;
+    l->lru.pref[s] = 0;
     streamed.push_back(e);
   }
   l->lru.step++;
@@ -544,8 +656,10 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
   std::copy(l->lru.s2e.begin(), l->lru.s2e.end(), l->s2e_h);
 
-  // copies of streamed experts into their slots, on the copy stream (timed)
+  // copies of streamed experts into their slots, on the copy stream (timed), after this
+  // layer's previous kernels (which may have run on another stream) are done with the slots
   if (!streamed.empty()) {
+    HIP_TRY(hipStreamWaitEvent(ctx->copy_stream, l->ev_done, 0));
     HIP_TRY(hipEventRecord(l->ev_cp0, ctx->copy_stream));
     l->pend_copy_bytes = (uint64_t)streamed.size() * l->L.bytes;
   }
@@ -563,6 +677,11 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   HIP_TRY(hipMemcpyAsync(l->n_items, l->n_items_h, 2 * sizeof(int), hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(l->e2s_dev, l->e2s_h, (size_t)E * 4, hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice, st));
+  // hits may sit in slots a prefetch from the previous layer is still filling
+  if (l->pref_pending) {
+    HIP_TRY(hipStreamWaitEvent(st, l->ev_pref, 0));
+    l->pref_pending = false;
+  }
   if (n0 > 0) {
     const DecodeLaunch a = launch_args(l, x, T, 0, l->items, l->n_items, n0);
     HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
@@ -571,6 +690,12 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   if (n1 > 0) {
     const DecodeLaunch a = launch_args(l, x, T, 0, l->items + l->max_items, l->n_items + 1, n1);
     HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
+  }
+  // prefetch for the next layer, behind this layer's own copies, while its kernels run
+  if (nx) {
+    HIP_TRY(hipEventSynchronize(l->ev_pred));
+    rc = prefetch_into(ctx, nx, l->pf_idx_h, l->pf_w_h, T, l->pf_depth, &S.n_prefetched);
+    if (rc) return rc;
   }
 
   // host experts, concurrently with the GPU work enqueued above
@@ -607,6 +732,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     if (l->alpha > 0.0) l->bh = bandwidth_update(l->bh, S.bh_obs, l->alpha);
   }
   HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, k, d.n_shared, y, st));
+  HIP_TRY(hipEventRecord(l->ev_done, st));
   if (stats) *stats = S;
   return FT_OK;
 }
@@ -656,6 +782,62 @@ extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha
     return fail(FT_EINVAL, "ft_set_miss_policy: alpha must be in [0, 1]");
   layer->split_rule = rule;
   layer->alpha = alpha;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth) {
+  if (!layer) return fail(FT_EINVAL, "ft_set_prefetch: null layer");
+  if (depth < 0) return fail(FT_EINVAL, "ft_set_prefetch: depth must be >= 0");
+  auto unlink = [&]() {
+    if (layer->next && layer->next->prev == layer) layer->next->prev = nullptr;
+    layer->next = nullptr;
+    layer->pf_depth = 0;
+  };
+  if (!next || depth == 0) {
+    unlink();
+    return FT_OK;
+  }
+  if (next == layer) return fail(FT_EINVAL, "ft_set_prefetch: a layer cannot prefetch for itself");
+  if (next->ctx != layer->ctx) return fail(FT_EINVAL, "ft_set_prefetch: layers of different contexts");
+  if (layer->all_resident || next->all_resident)
+    return fail(FT_EINVAL, "ft_set_prefetch: both layers need a partial pool (miss path)");
+  if (next->d.H != layer->d.H) return fail(FT_EINVAL, "ft_set_prefetch: hidden sizes differ");
+  if (depth > next->d.n_slots) return fail(FT_EINVAL, "ft_set_prefetch: depth above next's slots");
+  if (next->prev && next->prev != layer)
+    return fail(FT_EINVAL, "ft_set_prefetch: next is already the target of another layer");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  if (!layer->pf_dev) {
+    const size_t nl = (size_t)FT_MAX_DECODE_TOKENS * 1024, nk = (size_t)FT_MAX_DECODE_TOKENS * FT_MAX_TOPK;
+    if (hipMalloc(&layer->pf_dev, nl * 4 + 2 * nk * 4) != hipSuccess)
+      return fail(FT_ENOMEM, "ft_set_prefetch: device allocation failed");
+    layer->pf_logits = (float*)layer->pf_dev;
+    layer->pf_idx = (int32_t*)(layer->pf_logits + nl);
+    layer->pf_w = (float*)(layer->pf_idx + nk);
+    if (hipHostMalloc(&layer->pf_pin, 2 * nk * 4, hipHostMallocMapped) != hipSuccess)
+      return fail(FT_ENOMEM, "ft_set_prefetch: pinned allocation failed");
+    layer->pf_idx_h = (int32_t*)layer->pf_pin;
+    layer->pf_w_h = (float*)(layer->pf_idx_h + nk);
+    void* dp = nullptr;
+    HIP_TRY(hipHostGetDevicePointer(&dp, layer->pf_pin, 0));
+    layer->pf_idx_hd = (int32_t*)dp;
+    layer->pf_w_hd = (float*)(layer->pf_idx_hd + nk);
+    HIP_TRY(hipEventCreateWithFlags(&layer->ev_x, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&layer->ev_pred, hipEventDisableTiming));
+  }
+  unlink();
+  layer->next = next;
+  next->prev = layer;
+  layer->pf_depth = depth;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const float* y, float scale,
+                                       int64_t n, uint16_t* out, void* stream) {
+  if (!ctx || n < 0) return fail(FT_EINVAL, "ft_residual_bf16: null context or n < 0");
+  if (n == 0) return FT_OK;
+  if (!x || !y || !out) return fail(FT_EINVAL, "ft_residual_bf16: null array");
+  HIP_TRY(hipSetDevice(ctx->device));
+  HIP_TRY((hipError_t)ftk_residual(x, y, scale, n, out, (hipStream_t)stream));
   return FT_OK;
 }
 

@@ -860,6 +860,50 @@ extern "C" int ftk_decode_experts(const DecodeLaunch* ap, hipStream_t st, const 
   return (int)hipGetLastError();
 }
 
+// out = bf16(float(x) + s*y): the product and the sum each rounded to fp32 (no fused
+// multiply-add), then rounded to nearest even bf16, a NaN kept quiet.  Eight
+// elements per thread per round (16-byte bf16 and 2 x 16-byte fp32 accesses when vec, which
+// the host sets for 16-byte aligned arrays), grid-stride; out may alias x.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void k_residual(const uint16_t* x, const float* y, float sc,
+                                                  int64_t n, uint16_t* out, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += stride) {
+    if (vec && i + 8 <= n) {
+      const uint4 xv = *(const uint4*)(x + i);
+      const float4 y0 = *(const float4*)(y + i), y1 = *(const float4*)(y + i + 4);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __fadd_rn(__uint_as_float(xw[q] << 16), __fmul_rn(sc, yv[2 * q]));
+        const float hi = __fadd_rn(__uint_as_float(xw[q] & 0xffff0000u), __fmul_rn(sc, yv[2 * q + 1]));
+        o[q] = (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+      }
+      *(uint4*)(out + i) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (int64_t j = i; j < n && j < i + 8; ++j)
+        out[j] = bf16_rne(__fadd_rn(__uint_as_float((uint32_t)x[j] << 16), __fmul_rn(sc, y[j])));
+    }
+  }
+}
+
+extern "C" int ftk_residual(const uint16_t* x, const float* y, float sc, int64_t n, uint16_t* out,
+                            hipStream_t st) {
+  if (n <= 0) return 0;
+  const int vec = ((uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0 && (uintptr_t)out % 16 == 0);
+  const int64_t want = (n + 2047) / 2048;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(k_residual, dim3(grid), dim3(256), 0, st, x, y, sc, n, out, vec);
+  return (int)hipGetLastError();
+}
+
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
                            float* y, hipStream_t st) {
   hipLaunchKernelGGL(k_combine, dim3((H + 255) / 256, T), dim3(256), 0, st, P, w, T, H, k,

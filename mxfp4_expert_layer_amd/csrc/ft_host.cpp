@@ -328,6 +328,7 @@ void LruState::init(int E, int S, bool resident) {
   e2s.assign(E, -1);
   s2e.assign(S, -1);
   last_use.assign(S, -1);
+  pref.assign(S, 0);
   step = 0;
   if (resident)
     for (int e = 0; e < E && e < S; ++e) { e2s[e] = e; s2e[e] = e; }

@@ -56,6 +56,7 @@ double bandwidth_update(double est, double obs, double alpha);
 struct LruState {
   std::vector<int32_t> e2s, s2e;
   std::vector<int64_t> last_use;
+  std::vector<uint8_t> pref;   // slot filled by a cross-layer prefetch and not used since
   int64_t step = 0;
   void init(int E, int S, bool resident);
   // returns the slot to admit into and the evicted expert (-1 if none), or slot -1 when no

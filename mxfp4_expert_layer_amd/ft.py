@@ -49,7 +49,8 @@ class DecodeStats(C.Structure):
                 ("q", C.c_int32), ("n_streamed", C.c_int32), ("n_host", C.c_int32),
                 ("n_evicted", C.c_int32), ("step", C.c_int32), ("qstar", C.c_double),
                 ("bp", C.c_double), ("bh", C.c_double), ("host_us", C.c_double),
-                ("wait_us", C.c_double), ("bp_obs", C.c_double), ("bh_obs", C.c_double)]
+                ("wait_us", C.c_double), ("bp_obs", C.c_double), ("bh_obs", C.c_double),
+                ("n_prefetched", C.c_int32), ("n_prefetch_hits", C.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -73,6 +74,8 @@ _sig = {
     "ft_force_q": [_vp, _i],
     "ft_qstar_split_makespan": [_i, _d, _d, C.POINTER(_i)],
     "ft_set_miss_policy": [_vp, _i, _d],
+    "ft_set_prefetch": [_vp, _vp, _i],
+    "ft_residual_bf16": [_vp, _vp, _vp, C.c_float, C.c_int64, _vp, _vp],
     "ft_debug_dequant": [_vp, _i, _i, _vp, _vp],
     "ft_debug_tables": [_vp, _vp, _vp],
     "ft_host_expert_ffn": [_vp, _i, _i, _i, _vp, _vp, _i, _vp],
@@ -216,6 +219,16 @@ def qstar_split_makespan(m: int, Bp: float, Bh: float) -> int:
 
 def set_miss_policy(layer_h, rule=FT_SPLIT_ROUND, alpha=0.0):
     check(lib.ft_set_miss_policy(layer_h, rule, alpha))
+
+
+def set_prefetch(layer_h, next_h, depth):
+    """Link layer_h's decode calls to prefetch next_h's predicted experts (None/0 unlinks)."""
+    check(lib.ft_set_prefetch(layer_h, next_h, depth))
+
+
+def residual_bf16(ctx, x, y, n, out, stream=None, scale=1.0):
+    """out = bf16(x + scale * y) on the device (x, out bf16 bits; y fp32)."""
+    check(lib.ft_residual_bf16(ctx.handle, _ptr(x), _ptr(y), scale, n, _ptr(out), stream))
 
 
 def debug_dequant(layer_h, slot, matrix, out, stream=None):

@@ -29,14 +29,15 @@ class GpuLayer:
     """A libft layer over torch-owned memory.
 
     resident=True: the pool holds all E experts (slot e = expert e).  resident=False: the
-    pool has n_slots empty slots and all E blobs live in pinned host memory (miss path).
+    pool has n_slots empty slots and all E blobs live in pinned host memory (miss path);
+    host_store reuses another miss-path layer's pinned blobs instead of packing new ones.
     copies > 1 packs the pool once and replicates it to further device buffers (separate
     addresses with the same bytes) that ``select_copy`` switches between; each copy has its
     own router bias draw so hot experts differ between copies."""
 
     def __init__(self, ctx: ft.Context, cfg: synth.LayerConfig, *, resident=True,
                  n_slots=None, max_tokens=16, threads=8, copies=1, device="cuda",
-                 experts=None, router=None, prefill_mxfp4=False):
+                 experts=None, router=None, prefill_mxfp4=False, host_store=None):
         self.ctx, self.cfg = ctx, cfg
         self.device = device
         self.stride = ft.blob_bytes(cfg.fmt, cfg.H, cfg.I)
@@ -44,9 +45,15 @@ class GpuLayer:
         self.n_slots = E if resident else (n_slots or cfg.n_slots)
         self.max_tokens = max_tokens
         self.resident = resident
-        host = torch.empty(E * self.stride, dtype=torch.uint8, pin_memory=not resident)
         self.override = experts or {}
-        _pack_all(cfg, list(range(E)), host.numpy(), self.stride, threads, override=self.override)
+        if host_store is not None:
+            # share another layer's pinned blob store (same expert bytes, e.g. for timing)
+            assert not resident and host_store.numel() == E * self.stride and host_store.is_pinned()
+            host = host_store
+        else:
+            host = torch.empty(E * self.stride, dtype=torch.uint8, pin_memory=not resident)
+            _pack_all(cfg, list(range(E)), host.numpy(), self.stride, threads,
+                      override=self.override)
         if resident:
             self.pools = [host.to(device)]
             for _ in range(1, copies):

@@ -336,3 +336,152 @@ def test_miss_path_284b_layer(ctx):
     L = layer_for(ctx, "cfg4", resident=False, n_slots=48, max_tokens=1)
     rate = _miss_sequence(ctx, L, steps=128, bp=50e9, bh=120e9, check_every=16, T=1)
     log(f"[gpu] cfg4 hit rate over 128 steps: {rate:.3f}")
+
+
+def _bf16_rne_bits(f32):
+    """float32 array -> bf16 bits, round to nearest even (the definition, NaNs made quiet)."""
+    u = f32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(f32)
+    r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+@pytest.mark.parametrize("n,offset,scale", [(0, 0, 1.0), (1, 0, 1.0), (7, 0, 0.25),
+                                            (8, 0, 1.0), (4096 * 3 + 5, 0, 1.0),
+                                            (4096 * 3 + 5, 0, 0.1), (1000, 1, 0.3)])
+def test_residual_bf16_exact(ctx, n, offset, scale):
+    """x + scale*y rounded to bf16: bit-exact against the fp32 product and sum (numpy float32
+    arithmetic) rounded to nearest even, on ragged sizes, a misaligned view (scalar path) and
+    in place (out aliasing x)."""
+    rng = np.random.default_rng(n + 17 * offset)
+    xf = (rng.standard_normal(n + offset) * 4).astype(np.float32)
+    xb = _bf16_rne_bits(xf)
+    y = (rng.standard_normal(n + offset) * rng.choice([1e-3, 1.0, 300.0], n + offset)).astype(np.float32)
+    if n > 10:
+        xb[:4] = [0x7F80, 0xFF80, 0x7F7F, 0x0001]     # +inf, -inf, max finite, subnormal
+        y[2] = 3.0e38                                  # overflows to inf
+        y[5] = np.nan
+    xs = (xb.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = _bf16_rne_bits((xs + np.float32(scale) * y)[offset:])
+    xd = torch.from_numpy(xb.view(np.int16).copy()).to("cuda")
+    yd = torch.from_numpy(y).to("cuda")
+    out = torch.empty_like(xd)
+    ft.residual_bf16(ctx, xd[offset:], yd[offset:], n, out[offset:], stream_ptr(), scale)
+    ft.residual_bf16(ctx, xd[offset:], yd[offset:], n, xd[offset:], stream_ptr(), scale)
+    torch.cuda.synchronize()
+    for got in (out[offset:], xd[offset:]):
+        g = got.cpu().numpy().view(np.uint16)
+        nan_ref = np.isnan((ref.astype(np.uint32) << 16).view(np.float32))
+        assert np.array_equal(g[~nan_ref], ref[~nan_ref])
+        assert np.all(np.isnan((g[nan_ref].astype(np.uint32) << 16).view(np.float32)))
+
+
+def _stack(ctx, tag, n_layers, **kw):
+    layers = []
+    for li in range(n_layers):
+        cfg = synth.small_config(f"{tag}{li}", seed=91 + 7 * li, **kw)
+        layers.append(layer_for(ctx, f"{tag}{li}", cfg=cfg, resident=False, n_slots=5,
+                                max_tokens=2))
+    return layers
+
+
+def test_prefetch_layer_stack_matches_oracle(ctx):
+    """Three chained miss-path layers (input of layer l+1 = bf16(x_l + g y_l), g = 2^-14 so
+    that |g y| is about a third of |x| for these random weights), layer 0 prefetching for
+    layer 1 (depth 2) and layer 1 for layer 2 (depth 3): after every call the slot tables
+    equal the oracle's pools replaying the same steps and prefetches, the prefetch counts
+    agree, and the outputs match the oracle.  The pools order experts by routing weight, an
+    ordering the library takes on fp32 weights, so the oracle's weights enter the pools
+    rounded to fp32 (a weight that underflows in fp32 ties at zero on both sides)."""
+    Ls = _stack(ctx, "pfstack", 3, H=384, I=256, E=14, k=3, n_shared=1, code_dist="normal",
+                router_sigma=1 / 20, zipf_c=0.7)
+    depths = [2, 3]
+    OLs = [L.oracle_layer() for L in Ls]
+    pools = [policy.LruPool(L.cfg.E, L.n_slots) for L in Ls]
+    for L in Ls:
+        ft.set_bandwidth(L.handle, 1.0, 2.5)
+        ft.force_q(L.handle, -1)
+    ft.set_prefetch(Ls[0].handle, Ls[1].handle, depths[0])
+    ft.set_prefetch(Ls[1].handle, Ls[2].handle, depths[1])
+    n_pf = n_pf_hits = 0
+    try:
+        for s in range(20):
+            T = 1 + s % 2
+            xb = synth.gen_tokens(Ls[0].cfg, T, batch=500 + s)
+            for li, L in enumerate(Ls):
+                cfg = L.cfg
+                st = ft.DecodeStats()
+                y = run_decode(ctx, L, xb, st)
+                xr = fp4.bf16_bits_to_f64(xb)
+                r_idx, r_w, _, gap = moe.route(xr, OLs[li].router_w, OLs[li].router_b, cfg.k)
+                assert np.all(gap >= 1e-6), "near-tie; choose another seed"
+                res = pools[li].step(r_idx, r_w.astype(np.float32), 1.0, 2.5)
+                e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+                assert np.array_equal(e2s, res.e2s) and np.array_equal(s2e, res.s2e), (s, li)
+                assert st.n_prefetch_hits == res.prefetch_hits, (s, li)
+                assert (st.n_hits, st.n_streamed, st.n_host) == (
+                    len(res.hits), len(res.streamed), len(res.host)), (s, li)
+                if li + 1 < len(Ls):
+                    nO = OLs[li + 1]
+                    p_idx, p_w, _, pgap = moe.route(xr, nO.router_w, nO.router_b, Ls[li + 1].cfg.k)
+                    assert np.all(pgap >= 1e-6), "near-tie in the prediction; choose another seed"
+                    f = pools[li + 1].prefetch(p_idx, p_w.astype(np.float32), depths[li])
+                    assert st.n_prefetched == len(f.admitted), (s, li)
+                    n_pf += len(f.admitted)
+                else:
+                    assert st.n_prefetched == 0
+                n_pf_hits += st.n_prefetch_hits
+                if s % 3 == 0 or s == 19:
+                    check_output(y, moe.moe_forward(OLs[li], xb)["y"], f"stack step {s} layer {li}")
+                # the next layer's input: bf16(x + g y) on the device
+                g = 2.0 ** -14
+                xd = to_dev(xb)
+                yd = torch.from_numpy(y).to("cuda")
+                ft.residual_bf16(ctx, xd, yd, xd.numel(), xd, stream_ptr(), g)
+                torch.cuda.synchronize()
+                xn = xd.cpu().numpy().view(np.uint16).reshape(xb.shape)
+                xs = (xb.astype(np.uint32) << 16).view(np.float32)
+                assert np.array_equal(xn, _bf16_rne_bits(xs + np.float32(g) * y)), (s, li)
+                xb = xn
+    finally:
+        ft.set_prefetch(Ls[0].handle, None, 0)
+        ft.set_prefetch(Ls[1].handle, None, 0)
+    assert n_pf > 0 and n_pf_hits > 0, (n_pf, n_pf_hits)
+    log(f"[gpu] prefetch stack: {n_pf} prefetched, {n_pf_hits} prefetch hits")
+
+
+def test_set_prefetch_rejects_bad_links(ctx):
+    a, b = _stack(ctx, "pflink", 2, H=256, I=128, E=12, k=2, n_shared=0, code_dist="normal",
+                  router_sigma=1 / 16)
+    res = layer_for(ctx, "pfres", cfg=synth.small_config("pfres", seed=5, H=256, I=128, E=6,
+                                                        k=2), resident=True, max_tokens=2)
+    c = GpuLayer(ctx, synth.small_config("pflink_c", seed=6, H=256, I=128, E=12, k=2),
+                 resident=False, n_slots=4, max_tokens=2)
+    odd = GpuLayer(ctx, synth.small_config("pflink_h", seed=8, H=384, I=128, E=12, k=2),
+                   resident=False, n_slots=4, max_tokens=2)
+    try:
+        for args in [(a.handle, a.handle, 1), (a.handle, b.handle, -1),
+                     (a.handle, b.handle, b.n_slots + 1), (a.handle, res.handle, 1),
+                     (res.handle, a.handle, 1), (a.handle, odd.handle, 1)]:
+            with pytest.raises(ft.FtError) as e:
+                ft.set_prefetch(*args)
+            assert e.value.code == ft.FT_EINVAL, args
+        ft.set_prefetch(a.handle, b.handle, 2)
+        with pytest.raises(ft.FtError) as e:      # b already has a predecessor
+            ft.set_prefetch(c.handle, b.handle, 1)
+        assert e.value.code == ft.FT_EINVAL
+        ft.set_prefetch(a.handle, c.handle, 1)    # relinking a moves its target
+        ft.set_prefetch(b.handle, a.handle, 1)
+        ft.set_prefetch(c.handle, b.handle, 1)    # b is free again
+        c.close()                                  # destroying c unlinks a -> c and c -> b
+        ft.set_bandwidth(a.handle, 1.0, 1.0)
+        ft.force_q(a.handle, -1)
+        st = ft.DecodeStats()
+        run_decode(ctx, a, synth.gen_tokens(a.cfg, 1, batch=3), st)
+        assert st.n_prefetched == 0
+        ft.set_prefetch(b.handle, None, 0)
+    finally:
+        c.close()
+        odd.close()
