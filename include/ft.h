@@ -242,7 +242,7 @@ FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha);
  * `next`, both miss-path layers (partial pools) of one context with the same H.  Each later
  * ft_moe_decode of `layer`:
  *   - predicts next's routing by applying next's router (top-k softmax) to layer's own input
- *     x, on an internal stream beside layer's routing;
+ *     x, in the same kernel launch as layer's own routing;
  *   - after enqueueing layer's own copies and kernels, marks the predicted experts already in
  *     next's pool as used at next's coming call, then admits up to `depth` of the others, by
  *     descending summed predicted weight (ties to the lower id), through next's slot rule

@@ -23,6 +23,7 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
                         int H, hipStream_t st);
 extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_down_combines(const DecodeLaunch* a);
+extern "C" int ftk_route_small(const RouteSmall* a, hipStream_t st);
 extern "C" int ftk_residual(const uint16_t* x, const float* y, float sc, int64_t n, uint16_t* out,
                             hipStream_t st);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
@@ -60,7 +61,6 @@ int env_int(const char* name, int dflt) {
 struct ft_ctx {
   int device = 0;
   hipStream_t copy_stream = nullptr;
-  hipStream_t pred_stream = nullptr;   // routing of a linked next layer (prefetch prediction)
   std::unique_ptr<ThreadPool> pool;
 };
 
@@ -76,12 +76,17 @@ struct ft_layer {
   float* logits = nullptr;
   int32_t* idx = nullptr;
   float* w = nullptr;
-  WorkItem* items = nullptr;     // [2][max_items] (second list: streamed misses)
+  // n_items, e2s_dev, s2e_dev and items are one block laid out as the pinned n_items_h ..
+  // items_h block, so the miss path refreshes them with one copy
+  WorkItem* items = nullptr;     // 2 * max_items (miss path: hits, then streamed misses)
   int* n_items = nullptr;        // [2]
   uint16_t* h = nullptr;
   float* P = nullptr;
   int32_t* e2s_dev = nullptr;
   int32_t* s2e_dev = nullptr;
+  unsigned int* route_counter = nullptr;   // k_route_small's workgroup counter
+  uint32_t* route_flag_h = nullptr;        // pinned: the last routing launch's sequence number
+  uint32_t route_seq = 0;
   uint16_t* wr_planes = nullptr;  // bf16 split of router_w in MFMA operand order (prefill router)
   // MXFP4 weights of the scaled-FP4 prefill: the pool itself (MXFP4 layers) or a transcoded
   // copy owned here (NVFP4 layers created with FT_LAYER_PREFILL_MXFP4); null if neither
@@ -94,8 +99,8 @@ struct ft_layer {
   int32_t* idx_h = nullptr;
   float* w_h = nullptr;
   uint16_t* x_h = nullptr;
-  WorkItem* items_h = nullptr;   // [2][max_items] followed by int counts[2]
-  int* n_items_h = nullptr;
+  WorkItem* items_h = nullptr;   // 2 * max_items
+  int* n_items_h = nullptr;      // [2]
   float* P_h = nullptr;          // host expert outputs [T * kk][H]
   int32_t* e2s_h = nullptr;
   int32_t* s2e_h = nullptr;
@@ -123,7 +128,6 @@ struct ft_layer {
   float* pf_w_h = nullptr;
   int32_t* pf_idx_hd = nullptr;  // their device addresses
   float* pf_w_hd = nullptr;
-  hipEvent_t ev_x = nullptr, ev_pred = nullptr;
   hipEvent_t ev_pref = nullptr;  // after the prefetch copies into this layer's pool
   bool pref_pending = false;
   // kernel timing events: [n][4] = gate/up start, stop, down start, stop
@@ -214,7 +218,6 @@ extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) {
   if (!c) return fail(FT_ENOMEM, "ft_ctx_create: out of host memory");
   c->device = device;
   HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
-  HIP_TRY(hipStreamCreateWithFlags(&c->pred_stream, hipStreamNonBlocking));
   const int hw = (int)std::thread::hardware_concurrency();
   const int nt = env_int("FT_HOST_THREADS", std::max(1, std::min(16, hw)));
   c->pool.reset(new ThreadPool(std::max(1, nt)));
@@ -229,11 +232,7 @@ extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
     hipStreamSynchronize(ctx->copy_stream);
     hipStreamDestroy(ctx->copy_stream);
   }
-  if (ctx->pred_stream) {
-    hipSetDevice(ctx->device);
-    hipStreamSynchronize(ctx->pred_stream);
-    hipStreamDestroy(ctx->pred_stream);
-  }
+
   delete ctx;
   return FT_OK;
 }
@@ -254,8 +253,6 @@ static void free_layer(ft_layer* l) {
   if (l->ev_cp0) hipEventDestroy(l->ev_cp0);
   if (l->ev_cp1) hipEventDestroy(l->ev_cp1);
   if (l->ev_done) hipEventDestroy(l->ev_done);
-  if (l->ev_x) hipEventDestroy(l->ev_x);
-  if (l->ev_pred) hipEventDestroy(l->ev_pred);
   if (l->ev_pref) hipEventDestroy(l->ev_pref);
   if (l->pf_dev) hipFree(l->pf_dev);
   if (l->pf_pin) hipHostFree(l->pf_pin);
@@ -314,6 +311,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   add((size_t)d.E * 4);
   add((size_t)d.n_slots * 4);
   add(router_plane_bytes(d.E, d.H));               // router planes
+  add(sizeof(unsigned int));                       // routing counter
   if (hipMalloc(&l->dev, need) != hipSuccess)
     return fail(FT_ENOMEM, "ft_layer_create: device workspace allocation failed");
   HIP_TRY(hipMemset(l->dev, 0, need));
@@ -321,13 +319,14 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   l->logits = carve<float>(p, (size_t)T * d.E);
   l->idx = carve<int32_t>(p, (size_t)T * d.k);
   l->w = carve<float>(p, (size_t)T * d.k);
-  l->items = carve<WorkItem>(p, (size_t)2 * l->max_items);
   l->n_items = carve<int>(p, 2);
-  l->h = carve<uint16_t>(p, (size_t)l->max_items * kMaxCols * d.I);
-  l->P = carve<float>(p, (size_t)T * l->kk * d.H);
   l->e2s_dev = carve<int32_t>(p, d.E);
   l->s2e_dev = carve<int32_t>(p, d.n_slots);
+  l->items = carve<WorkItem>(p, (size_t)2 * l->max_items);
+  l->h = carve<uint16_t>(p, (size_t)l->max_items * kMaxCols * d.I);
+  l->P = carve<float>(p, (size_t)T * l->kk * d.H);
   l->wr_planes = carve<uint16_t>(p, router_plane_bytes(d.E, d.H) / 2);
+  l->route_counter = carve<unsigned int>(p, 1);
   HIP_TRY((hipError_t)ftk_split_router(d.router_w, d.E, d.H, l->wr_planes, nullptr));
   if (d.format == FT_MXFP4 && d.resident) {
     l->mx_pool = (const uint8_t*)d.pool;
@@ -351,10 +350,12 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   padd((size_t)T * d.k * 4);
   padd((size_t)T * d.k * 4);
   padd((size_t)T * d.H * 2);
-  padd((size_t)2 * l->max_items * sizeof(WorkItem) + 2 * sizeof(int));
+  padd((size_t)2 * l->max_items * sizeof(WorkItem));
+  padd(2 * sizeof(int));
   padd((size_t)T * l->kk * d.H * 4);
   padd((size_t)d.E * 4);
   padd((size_t)d.n_slots * 4);
+  padd(sizeof(uint32_t));
   if (hipHostMalloc(&l->pin, pneed, hipHostMallocMapped) != hipSuccess)
     return fail(FT_ENOMEM, "ft_layer_create: pinned staging allocation failed");
   {
@@ -366,12 +367,13 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   l->idx_h = carve<int32_t>(q, (size_t)T * d.k);
   l->w_h = carve<float>(q, (size_t)T * d.k);
   l->x_h = carve<uint16_t>(q, (size_t)T * d.H);
-  l->items_h = (WorkItem*)q;
-  l->n_items_h = (int*)(q + (size_t)2 * l->max_items * sizeof(WorkItem));
-  q += align_up((size_t)2 * l->max_items * sizeof(WorkItem) + 2 * sizeof(int), 256);
-  l->P_h = carve<float>(q, (size_t)T * l->kk * d.H);
+  l->n_items_h = carve<int>(q, 2);
   l->e2s_h = carve<int32_t>(q, d.E);
   l->s2e_h = carve<int32_t>(q, d.n_slots);
+  l->items_h = carve<WorkItem>(q, (size_t)2 * l->max_items);
+  l->P_h = carve<float>(q, (size_t)T * l->kk * d.H);
+  l->route_flag_h = carve<uint32_t>(q, 1);
+  *l->route_flag_h = 0;
 
   l->lru.init(d.E, d.n_slots, l->all_resident);
   std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
@@ -475,6 +477,24 @@ static void add_item(WorkItem* list, int* n, int expert, int slot) {
   it.slot = slot;
 }
 
+// Wait for the routing kernel's host-memory flag to reach seq: it is set once the routing is
+// in host memory, so neither an event round trip nor a sleeping thread's wake-up sits on the
+// critical path of the call.  The launch's event bounds the spin: once the kernel has
+// finished, the flag must be there.
+static hipError_t wait_route(const uint32_t* flag, uint32_t seq, hipEvent_t ev) {
+  for (uint32_t n = 1;; ++n) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return hipSuccess;
+    __builtin_ia32_pause();
+    if ((n & 1023) == 0) {
+      const hipError_t e = hipEventQuery(ev);
+      if (e == hipErrorNotReady) continue;
+      if (e != hipSuccess) return e;
+      if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return hipSuccess;
+      return hipErrorLaunchFailure;
+    }
+  }
+}
+
 // Cross-layer prefetch into nx's pool for its next call, from the predicted routing idx/w
 // [T][k of nx]: the predicted experts already resident are marked used at that call's step
 // (so this batch evicts none of them); the others, by descending summed predicted weight
@@ -536,26 +556,42 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   const int k = d.k, kk = l->kk, E = d.E;
   ft_decode_stats S{};
   auto t0 = clk::now();
-  // a linked next layer's prediction: its router on this input, on the side stream, beside
-  // this layer's own routing (x is ready on `st` when the call is made)
+  // routing in one launch, written straight into the mapped pinned staging: the layer's own
+  // and, for a linked next layer, that layer's router on the same input (the prediction)
   ft_layer* nx = (l->next && l->pf_depth > 0) ? l->next : nullptr;
-  if (nx) {
-    const ft_layer_desc& nd = nx->d;
-    HIP_TRY(hipEventRecord(l->ev_x, st));
-    HIP_TRY(hipStreamWaitEvent(ctx->pred_stream, l->ev_x, 0));
-    HIP_TRY((hipError_t)ftk_logits(x, nd.router_w, nd.router_b, T, d.H, nd.E, l->pf_logits,
-                                   ctx->pred_stream));
-    HIP_TRY((hipError_t)ftk_topk(l->pf_logits, T, nd.E, nd.k, l->pf_idx, l->pf_w, l->pf_idx_hd,
-                                 l->pf_w_hd, nullptr, nullptr, d.H, ctx->pred_stream));
-    HIP_TRY(hipEventRecord(l->ev_pred, ctx->pred_stream));
-  }
-  HIP_TRY((hipError_t)ftk_logits(x, d.router_w, d.router_b, T, d.H, E, l->logits, st));
-  // the top-k kernel writes idx, w and the token rows into the mapped pinned staging
   auto dev_of = [&](const void* hp) { return l->pin_dev + ((const uint8_t*)hp - (const uint8_t*)l->pin); };
-  HIP_TRY((hipError_t)ftk_topk(l->logits, T, E, k, l->idx, l->w, (int32_t*)dev_of(l->idx_h),
-                               (float*)dev_of(l->w_h), x, (uint16_t*)dev_of(l->x_h), d.H, st));
+  RouteSmall ra{};
+  ra.x = x;
+  ra.x_host = (uint16_t*)dev_of(l->x_h);
+  ra.T = T;
+  ra.H = d.H;
+  ra.n_routers = nx ? 2 : 1;
+  ra.wr[0] = d.router_w;
+  ra.b[0] = d.router_b;
+  ra.E[0] = E;
+  ra.k[0] = k;
+  ra.logits[0] = l->logits;
+  ra.idx[0] = l->idx;
+  ra.w[0] = l->w;
+  ra.idx_host[0] = (int32_t*)dev_of(l->idx_h);
+  ra.w_host[0] = (float*)dev_of(l->w_h);
+  if (nx) {
+    ra.wr[1] = nx->d.router_w;
+    ra.b[1] = nx->d.router_b;
+    ra.E[1] = nx->d.E;
+    ra.k[1] = nx->d.k;
+    ra.logits[1] = l->pf_logits;
+    ra.idx[1] = l->pf_idx;
+    ra.w[1] = l->pf_w;
+    ra.idx_host[1] = l->pf_idx_hd;
+    ra.w_host[1] = l->pf_w_hd;
+  }
+  ra.counter = l->route_counter;
+  ra.flag_host = (uint32_t*)dev_of(l->route_flag_h);
+  ra.seq = ++l->route_seq;
+  HIP_TRY((hipError_t)ftk_route_small(&ra, st));
   HIP_TRY(hipEventRecord(l->ev_route, st));
-  HIP_TRY(hipEventSynchronize(l->ev_route));
+  HIP_TRY(wait_route(l->route_flag_h, ra.seq, l->ev_route));
   S.wait_us = us_since(t0);
 
   // classify: selected experts with their summed routing weight
@@ -632,15 +668,20 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   S.bh = l->bh;
   S.step = (int)now;
 
-  // work lists: list 0 = hits + shared experts, list 1 = streamed misses
+  // work lists: list 0 = hits + shared experts, list 1 = streamed misses right after it;
+  // each column carries its routing weight (for a down kernel that combines)
   WorkItem* L0 = l->items_h;
-  WorkItem* L1 = l->items_h + l->max_items;
   int n0 = 0, n1 = 0;
   auto fill_cols = [&](WorkItem& it, int e) {
     int c = 0;
     for (int t = 0; t < T; ++t)
       for (int j = 0; j < k; ++j)
-        if (l->idx_h[t * k + j] == e) { it.tok[c] = t; it.pair[c] = t * kk + j; ++c; }
+        if (l->idx_h[t * k + j] == e) {
+          it.tok[c] = t;
+          it.pair[c] = t * kk + j;
+          it.wt[c] = l->w_h[t * k + j];
+          ++c;
+        }
     it.ntok = c;
   };
   for (int e : hits) { add_item(L0, &n0, e, l->lru.e2s[e]); fill_cols(L0[n0 - 1], e); }
@@ -648,8 +689,9 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     add_item(L0, &n0, -1 - s, -1 - s);
     WorkItem& it = L0[n0 - 1];
     it.ntok = T;
-    for (int t = 0; t < T; ++t) { it.tok[t] = t; it.pair[t] = t * kk + k + s; }
+    for (int t = 0; t < T; ++t) { it.tok[t] = t; it.pair[t] = t * kk + k + s; it.wt[t] = 1.f; }
   }
+  WorkItem* L1 = L0 + n0;
   for (int e : streamed) { add_item(L1, &n1, e, l->lru.e2s[e]); fill_cols(L1[n1 - 1], e); }
   l->n_items_h[0] = n0;
   l->n_items_h[1] = n1;
@@ -669,31 +711,37 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
                            (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride,
                            l->L.bytes, hipMemcpyHostToDevice, ctx->copy_stream));
   }
-  if (!streamed.empty()) HIP_TRY(hipEventRecord(l->ev_cp1, ctx->copy_stream));
-  HIP_TRY(hipEventRecord(l->ev_copy, ctx->copy_stream));
-  // work lists and tables to the device (compute stream, before the kernels)
-  HIP_TRY(hipMemcpyAsync(l->items, l->items_h, (size_t)2 * l->max_items * sizeof(WorkItem),
+  if (!streamed.empty()) {
+    HIP_TRY(hipEventRecord(l->ev_cp1, ctx->copy_stream));
+    HIP_TRY(hipEventRecord(l->ev_copy, ctx->copy_stream));
+  }
+  // counts, tables and both work lists to the device in one copy (compute stream, before the
+  // kernels): the pinned block and the device block have the same layout
+  HIP_TRY(hipMemcpyAsync(l->n_items, l->n_items_h,
+                         (size_t)((const uint8_t*)(l->items_h + n0 + n1) - (const uint8_t*)l->n_items_h),
                          hipMemcpyHostToDevice, st));
-  HIP_TRY(hipMemcpyAsync(l->n_items, l->n_items_h, 2 * sizeof(int), hipMemcpyHostToDevice, st));
-  HIP_TRY(hipMemcpyAsync(l->e2s_dev, l->e2s_h, (size_t)E * 4, hipMemcpyHostToDevice, st));
-  HIP_TRY(hipMemcpyAsync(l->s2e_dev, l->s2e_h, (size_t)d.n_slots * 4, hipMemcpyHostToDevice, st));
   // hits may sit in slots a prefetch from the previous layer is still filling
   if (l->pref_pending) {
     HIP_TRY(hipStreamWaitEvent(st, l->ev_pref, 0));
     l->pref_pending = false;
   }
+  // every expert of the call a hit (or shared): list 0's down kernel also combines into y
+  const bool fuse = n1 == 0 && host.empty();
   if (n0 > 0) {
-    const DecodeLaunch a = launch_args(l, x, T, 0, l->items, l->n_items, n0);
+    DecodeLaunch a = launch_args(l, x, T, 0, l->items, l->n_items, n0);
+    if (fuse) {
+      a.fuse_combine = 1;
+      a.y = y;
+    }
     HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
   }
-  HIP_TRY(hipStreamWaitEvent(st, l->ev_copy, 0));
   if (n1 > 0) {
-    const DecodeLaunch a = launch_args(l, x, T, 0, l->items + l->max_items, l->n_items + 1, n1);
+    HIP_TRY(hipStreamWaitEvent(st, l->ev_copy, 0));
+    const DecodeLaunch a = launch_args(l, x, T, 0, l->items + n0, l->n_items + 1, n1);
     HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
   }
   // prefetch for the next layer, behind this layer's own copies, while its kernels run
   if (nx) {
-    HIP_TRY(hipEventSynchronize(l->ev_pred));
     rc = prefetch_into(ctx, nx, l->pf_idx_h, l->pf_w_h, T, l->pf_depth, &S.n_prefetched);
     if (rc) return rc;
   }
@@ -731,7 +779,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     S.bh_obs = (double)host.size() * l->L.bytes / ffn_s + (streamed.empty() ? 0.0 : l->bp);
     if (l->alpha > 0.0) l->bh = bandwidth_update(l->bh, S.bh_obs, l->alpha);
   }
-  HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, k, d.n_shared, y, st));
+  if (!fuse) HIP_TRY((hipError_t)ftk_combine(l->P, l->w, T, d.H, k, d.n_shared, y, st));
   HIP_TRY(hipEventRecord(l->ev_done, st));
   if (stats) *stats = S;
   return FT_OK;
@@ -821,8 +869,6 @@ extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth
     HIP_TRY(hipHostGetDevicePointer(&dp, layer->pf_pin, 0));
     layer->pf_idx_hd = (int32_t*)dp;
     layer->pf_w_hd = (float*)(layer->pf_idx_hd + nk);
-    HIP_TRY(hipEventCreateWithFlags(&layer->ev_x, hipEventDisableTiming));
-    HIP_TRY(hipEventCreateWithFlags(&layer->ev_pred, hipEventDisableTiming));
   }
   unlink();
   layer->next = next;

@@ -21,7 +21,8 @@
 // read from the blob header, multiplies the fp32 result of each matrix.
 // Workgroups never wait on each other inside a kernel: on this chip a device-scope fence
 // writes back and invalidates the issuing XCD's L2, so data moves between workgroups only
-// at kernel boundaries.
+// at kernel boundaries (except in the small routing kernel of the miss path, k_route_small,
+// whose last workgroup reads what the others released).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -42,12 +43,11 @@ constexpr int kRouteMaxEPerLane = 16;  // E <= 1024
 // and positions past H are clamped and masked at the FMA, so no load sits behind a branch
 // and a lane's weight and token loads are all in flight together.
 template <int TB>
-__global__ __launch_bounds__(256) void k_logits(const uint16_t* __restrict__ x,
-                                                const float* __restrict__ wr,
-                                                const float* __restrict__ b, int T, int H, int E,
-                                                float* __restrict__ logits) {
+__device__ __forceinline__ void logit_row(const uint16_t* __restrict__ x,
+                                          const float* __restrict__ wr,
+                                          const float* __restrict__ b, int T, int H, int E,
+                                          int e, float* __restrict__ logits) {
   constexpr int NI = TB >= 8 ? 2 : (TB >= 4 ? 4 : 6);
-  const int e = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float acc[TB];
 #pragma unroll
@@ -87,6 +87,14 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t* __restrict__ x,
   if (tid < T)
     logits[(uint64_t)tid * E + e] =
         ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) + (b ? b[e] : 0.f);
+}
+
+template <int TB>
+__global__ __launch_bounds__(256) void k_logits(const uint16_t* __restrict__ x,
+                                                const float* __restrict__ wr,
+                                                const float* __restrict__ b, int T, int H, int E,
+                                                float* __restrict__ logits) {
+  logit_row<TB>(x, wr, b, T, H, E, blockIdx.x, logits);
 }
 
 // ---- top-k and the work list in LDS -------------------------------------------------------
@@ -758,6 +766,84 @@ static int resident_workgroups(const void* kern) {
   return cache[key] = per_cu * cus;
 }
 
+// Routing of a miss-path call in one launch: one workgroup per router row (the layer's own
+// router, then optionally a second one: the linked next layer's, whose routing of the same
+// tokens is the prefetch prediction); the last workgroup to finish (device-scope counter,
+// reset by that workgroup; agent-scope release by every workgroup before it counts itself in,
+// acquire by the last) takes the top-k of every token for each router, writes it to device
+// and host memory with the token rows, and then sets a host-memory flag to the call's
+// sequence number, which the host polls.  This is the one kernel where workgroups hand data
+// to each other: one release per workgroup, no waiting.
+template <int TB, int EPL>
+__global__ __launch_bounds__(256) void k_route_small(RouteSmall a) {
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int r = g < a.E[0] ? 0 : 1;
+  logit_row<TB>(a.x, a.wr[r], a.b[r], a.T, a.H, a.E[r], r ? g - a.E[0] : g, a.logits[r]);
+  // release this workgroup's logits, count it in; the last one in acquires everyone's
+  __shared__ int last;
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    last = atomicAdd(a.counter, 1u) == gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (!last) return;
+  __shared__ TopkLds tk;
+  __shared__ float c_val[kMaxCols][FT_MAX_TOPK];
+  __shared__ int c_idx[kMaxCols][FT_MAX_TOPK];
+  for (int rr = 0; rr < a.n_routers; ++rr) {
+    const int k = a.k[rr];
+    topk_tokens<EPL>(a.logits[rr], a.T, a.E[rr], k, tk, c_val, c_idx);
+    if (tid < a.T * k) {
+      const int32_t e = tk.idx[tid / k][tid % k];
+      const float wv = tk.w[tid / k][tid % k];
+      a.idx[rr][tid] = e;
+      a.w[rr][tid] = wv;
+      a.idx_host[rr][tid] = e;
+      a.w_host[rr][tid] = wv;
+    }
+    __syncthreads();
+  }
+  if (a.x_host) {
+    if ((uintptr_t)a.x % 16 == 0) {
+      const uint4* src = (const uint4*)a.x;
+      uint4* dst = (uint4*)a.x_host;
+      for (int i = tid; i < a.T * a.H / 8; i += 256) dst[i] = src[i];
+    } else {
+      for (int i = tid; i < a.T * a.H; i += 256) a.x_host[i] = a.x[i];
+    }
+  }
+  // everything above is in host memory before the flag: each wave's stores complete (system
+  // release), then one release store of the call's sequence number
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+  __syncthreads();
+  if (tid == 0) {
+    atomicExch(a.counter, 0u);
+    __hip_atomic_store(a.flag_host, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+extern "C" int ftk_route_small(const RouteSmall* ap, hipStream_t st) {
+  const RouteSmall& a = *ap;
+  const int Emax = a.n_routers > 1 ? max(a.E[0], a.E[1]) : a.E[0];
+  const dim3 grid(a.E[0] + (a.n_routers > 1 ? a.E[1] : 0));
+#define FT_RS(TBV, EPLV) hipLaunchKernelGGL((k_route_small<TBV, EPLV>), grid, dim3(256), 0, st, a)
+#define FT_RS_T(EPLV)                 \
+  if (a.T <= 1) FT_RS(1, EPLV);       \
+  else if (a.T <= 2) FT_RS(2, EPLV);  \
+  else if (a.T <= 4) FT_RS(4, EPLV);  \
+  else if (a.T <= 8) FT_RS(8, EPLV);  \
+  else FT_RS(16, EPLV)
+  if (Emax <= 64) { FT_RS_T(1); }
+  else if (Emax <= 128) { FT_RS_T(2); }
+  else if (Emax <= 256) { FT_RS_T(4); }
+  else { FT_RS_T(16); }
+#undef FT_RS_T
+#undef FT_RS
+  return (int)hipGetLastError();
+}
+
 extern "C" int ftk_logits(const uint16_t* x, const float* wr, const float* b, int T, int H, int E,
                           float* logits, hipStream_t st) {
   if (T <= 1)
@@ -803,7 +889,7 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
 // bound); otherwise down writes per-(token, choice) partials for k_combine.
 extern "C" int ftk_down_combines(const DecodeLaunch* ap) {
   const DecodeLaunch& a = *ap;
-  return a.route != 0 && (a.max_items <= 16 || a.H / kTileRows >= 256);
+  return a.fuse_combine || (a.route != 0 && (a.max_items <= 16 || a.H / kTileRows >= 256));
 }
 
 // EPL = 0: work list read from memory; EPL > 0: routing prologue for E <= 64 * EPL experts;

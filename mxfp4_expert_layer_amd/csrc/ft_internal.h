@@ -97,6 +97,27 @@ struct DecodeLaunch {
   uint16_t* h;                  // [max_items][16][I]
   float* P;                     // [T * (k + n_shared)][H] (miss path: combined by k_combine)
   float* y;                     // [T][H]: all-resident calls combine inside the down kernel
+  int fuse_combine;             // list mode: 1 = the down kernel combines the whole list into y
+                                // (the items carry their weights)
+};
+
+// One-launch routing of a miss-path call (k_route_small): the layer's own router and, when
+// n_routers == 2, a second router over the same tokens (cross-layer prefetch prediction).
+struct RouteSmall {
+  const uint16_t* x;            // device bf16 [T][H]
+  uint16_t* x_host;             // mapped pinned copy of x, or null
+  int T, H, n_routers;
+  const float* wr[2];           // [E][H]
+  const float* b[2];            // [E] or null
+  int E[2], k[2];
+  float* logits[2];             // [T][E]
+  int32_t* idx[2];              // [T][k], device
+  float* w[2];
+  int32_t* idx_host[2];         // [T][k], mapped pinned
+  float* w_host[2];
+  unsigned int* counter;        // device, zero between launches
+  uint32_t* flag_host;          // mapped pinned word: set to seq once the outputs are in host memory
+  uint32_t seq;
 };
 
 // Prefill of T tokens through an all-resident layer (slot e = expert e).
