@@ -32,6 +32,15 @@ no predictor; the reading taken here:
     lower id), are admitted one by one through the same slot rule at step n, at most `depth`
     of them; a prefetched slot's last use is n, so the step-n call cannot evict it either;
   * a step-n hit on a slot filled by a prefetch and not used since counts as a prefetch hit.
+
+Three tiers.  Weights sit on disk, in system memory and in VRAM; the hot ones are in system
+memory and the recently used ones in VRAM slots (smzdm explainer aomxznrn, "FreeToken干的事",
+items 1 and 2).  The reading for the host-memory tier when it holds fewer than E experts:
+  * it is a second pool of the same kind (R slots, its own call counter);
+  * every miss of a call's VRAM step needs its blob in host memory (a streamed miss is
+    copied from there, a host-computed one is computed there): in miss order, the ones
+    already there have their last use set to the call's counter first, then the others are
+    read from disk into slots taken by the same slot rule at that counter.
 """
 from __future__ import annotations
 
@@ -189,3 +198,36 @@ class LruPool:
             self.pref[s] = True
             admitted.append(e)
         return PrefetchResult(step, order, admitted, evicted, self.e2s.copy(), self.s2e.copy())
+
+
+@dataclass
+class TierResult:
+    needed: list         # experts the call needed from this tier, in order
+    loaded: list         # of those, read from the tier below (disk), in order
+    evicted: list        # (slot, expert) pairs evicted
+    e2s: np.ndarray = field(repr=False, default=None)
+    s2e: np.ndarray = field(repr=False, default=None)
+
+
+def tier_step(pool: LruPool, needed):
+    """One call's use of a lower tier (host memory over disk): `needed` in order."""
+    step = pool.step_no
+    for e in needed:
+        if pool.e2s[e] >= 0:
+            pool.last_use[pool.e2s[e]] = step
+    loaded, evicted = [], []
+    for e in needed:
+        if pool.e2s[e] >= 0:
+            continue
+        s, old = pool._take_slot(step)
+        if s is None:
+            raise ValueError("host-memory tier smaller than one call's misses")
+        if old is not None:
+            pool.e2s[old] = -1
+            evicted.append((s, old))
+        pool.s2e[s] = e
+        pool.e2s[e] = s
+        pool.last_use[s] = step
+        loaded.append(e)
+    pool.step_no += 1
+    return TierResult(list(needed), loaded, evicted, pool.e2s.copy(), pool.s2e.copy())

@@ -201,6 +201,45 @@ def test_prefetch_invariants_random():
                 assert r.e2s[r.s2e[s]] == s
 
 
+def test_host_tier_scripted_sequence():
+    """Worked by hand: the host-memory tier under the VRAM pool (3 host slots, 2 VRAM slots)."""
+    V, H = policy.LruPool(E=8, S=2), policy.LruPool(E=8, S=3)
+    r = V.step(np.array([[3, 5]]), np.array([[0.6, 0.4]]), 1.0, 1.0)
+    t = policy.tier_step(H, r.misses)
+    assert r.misses == [3, 5] and t.loaded == [3, 5] and list(t.s2e) == [3, 5, -1]
+    r = V.step(np.array([[5, 1]]), np.array([[0.7, 0.3]]), 1.0, 1.0)
+    t = policy.tier_step(H, r.misses)          # 1 misses VRAM, read into the empty slot 2
+    assert r.misses == [1] and t.loaded == [1] and list(t.s2e) == [3, 5, 1]
+    r = V.step(np.array([[3, 6]]), np.array([[0.4, 0.6]]), 1.0, 1.0)
+    # VRAM held [1, 5]: both miss, 6 first (heavier); host tier: 3 resident (touched at 2),
+    # 6 evicts the oldest untouched slot: slot 1 (expert 5, last use 0)
+    t = policy.tier_step(H, r.misses)
+    assert r.misses == [6, 3] and t.loaded == [6] and t.evicted == [(1, 5)]
+    assert list(t.s2e) == [3, 6, 1]
+    r = V.step(np.array([[6, 3]]), np.array([[0.5, 0.5]]), 1.0, 1.0)
+    t = policy.tier_step(H, r.misses)          # all VRAM hits: nothing needed
+    assert r.misses == [] and t.loaded == [] and list(t.s2e) == [3, 6, 1]
+    with pytest.raises(ValueError):
+        policy.tier_step(policy.LruPool(E=8, S=1), [2, 4])
+
+
+def test_host_tier_invariants_random():
+    rng = np.random.default_rng(5)
+    E, S, R, k = 30, 4, 9, 3
+    V, H = policy.LruPool(E, S), policy.LruPool(E, R)
+    for it in range(300):
+        T = int(rng.integers(1, 4))
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+        w = rng.random((T, k))
+        r = V.step(idx, w, 1.0, float(rng.uniform(0.5, 3.0)))
+        before = set(int(e) for e in np.nonzero(H.e2s >= 0)[0])
+        t = policy.tier_step(H, r.misses)
+        assert set(t.loaded) == set(r.misses) - before
+        for e in r.misses:                    # every miss is in host memory afterwards
+            assert t.e2s[e] >= 0 and t.s2e[t.e2s[e]] == e
+        assert len(set(int(e) for e in t.s2e if e >= 0)) == int((t.s2e >= 0).sum())
+
+
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (7, 2, 5), (64, 8, 16), (200, 6, 256)])
 def test_permutation_matches_stable_sort(T, k, E):
     rng = np.random.default_rng(T * 31 + k)
