@@ -48,7 +48,8 @@ enum {
   FT_ENOMEM = -2,        /* host or device allocation failed */
   FT_EHIP = -3,          /* a HIP runtime call failed; the message names it */
   FT_EUNSUPPORTED = -4,  /* valid request this build does not implement */
-  FT_ESTATE = -5         /* call not valid in the object's current state */
+  FT_ESTATE = -5,        /* call not valid in the object's current state */
+  FT_EIO = -6            /* a file operation failed; the message names it and errno */
 };
 
 enum { FT_MXFP4 = 0, FT_NVFP4 = 1 };
@@ -99,8 +100,9 @@ typedef struct ft_layer_desc {
   const float* router_b;      /* device fp32 [E], or NULL for no bias */
   void* pool;                 /* device, n_slots * blob_stride bytes */
   const void* shared_blobs;   /* device, n_shared blobs at blob_stride, or NULL if none */
-  const void* host_blobs;     /* pinned host, E blobs at blob_stride (needed when not all
-                                 experts are resident), or NULL */
+  const void* host_blobs;     /* pinned host, E blobs at blob_stride, or NULL; a layer that is
+                                 not resident decodes from these or from a disk tier
+                                 (ft_layer_set_disk_tier) */
   uint64_t blob_stride;       /* >= ft_blob_bytes(), multiple of 4096 */
   int32_t resident;           /* 1: slot e already holds expert e for every e (needs
                                  n_slots == E); 0: the pool starts empty */
@@ -150,6 +152,10 @@ typedef struct ft_decode_stats {
      copying into the linked next layer's pool, and this call's hits on slots that a prefetch
      filled and nothing has used since */
   int32_t n_prefetched, n_prefetch_hits;
+  /* host-memory tier over an FTW file (see ft_layer_set_disk_tier): blobs this call read from
+     disk, and the wall time of those reads */
+  int32_t n_disk;
+  double disk_us;
 } ft_decode_stats;
 
 /*
@@ -209,7 +215,9 @@ FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
 /*
  * Startup probes: Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
  * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.
- * Needs host_blobs.  Blocks.  The values are stored in the layer and used by decode.
+ * Needs host_blobs, or a disk tier not yet used by a decode call (the probe then reads
+ * experts 0 and 1 into its first host-memory slots).  Blocks.  The values are stored in the
+ * layer and used by decode.
  */
 FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh);
 /* Override Bp and Bh (bytes/s, both > 0). */
@@ -271,6 +279,81 @@ FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth);
  */
 FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const float* y, float scale,
                             int64_t n, uint16_t* out, void* stream);
+
+/*
+ * FTW expert files (smzdm explainer a825qpgl, section 三: every tensor 4096-aligned, so a
+ * blob moves from disk in a few large direct reads instead of many fragmented ones).
+ * Layout: bytes [0, 4096) hold the header (magic "FTW1", version 1, format, H, I, E,
+ * n_shared, blob bytes, blob stride, data offset, file bytes; little-endian); blob i sits at
+ * 4096 + i * stride for i < E + n_shared (routed experts first, then shared ones), stride =
+ * ft_blob_bytes(format, H, I), which is a multiple of 4096, and inside a blob every tensor
+ * starts on a 4096 boundary.  The blobs are the bytes ft_pack_expert writes, unchanged.
+ */
+typedef struct ft_ftw ft_ftw;
+typedef struct ft_ftw_info {
+  int32_t format, H, I, E, n_shared;
+  int32_t direct;          /* 1 if the file is read with O_DIRECT (page cache bypassed) */
+  int32_t staged;          /* 1 once direct reads go through aligned host buffers and a copy
+                              (the kernel refuses O_DIRECT into some memory, such as the GPU
+                              driver's pinned host memory, or FT_FTW_STAGED asked for it) */
+  int32_t reserved;
+  uint64_t blob_bytes;     /* = blob stride in the file */
+  uint64_t file_bytes;
+} ft_ftw_info;
+
+/*
+ * Write an FTW file from E + n_shared packed blobs in host memory at src_stride bytes apart
+ * (routed experts 0..E-1, then the shared ones).  Each blob's header must name the given
+ * format, H and I.  The file is created or truncated, written and flushed to the device.
+ * FT_EINVAL for bad dimensions, pointers, a stride below the blob size or a blob of other
+ * dimensions; FT_EIO for a file error.  Host only, blocks.
+ */
+FT_API int ft_ftw_write(const char* path, int format, int H, int I, int E, int n_shared,
+                        const void* blobs, uint64_t src_stride);
+
+/*
+ * Open an FTW file for reading and validate its header against its size.  flags:
+ * FT_FTW_DIRECT asks for O_DIRECT reads; where the file system refuses them the file is read
+ * through the page cache instead (ft_ftw_info.direct says which).  A direct read into memory
+ * the kernel cannot pin for it (EFAULT) is redone through an aligned staging buffer per
+ * thread and a copy, and so are all later reads of the file; FT_FTW_STAGED asks for that from
+ * the start.  FT_EIO for a file error, FT_EINVAL for a file that is not a valid FTW file.
+ * Host only.
+ */
+enum { FT_FTW_DIRECT = 1, FT_FTW_STAGED = 2 };
+FT_API int ft_ftw_open(const char* path, int flags, ft_ftw** out);
+FT_API int ft_ftw_get_info(const ft_ftw* f, ft_ftw_info* info);
+FT_API int ft_ftw_close(ft_ftw* f);
+
+/*
+ * Read blobs ids[0..n-1] (each < E + n_shared) into dst + i * dst_stride, in requests of
+ * `chunk` bytes (0: one request per blob), spread over ctx's host threads (ctx may be NULL:
+ * the calling thread alone).  dst is host memory (pinned or not); with O_DIRECT, dst,
+ * dst_stride and chunk must be multiples of 4096.  seconds (may be NULL) receives the wall
+ * time.  FT_EINVAL for bad ids, sizes or alignment; FT_EIO for a read error or a short file.
+ * Host only, blocks.
+ */
+FT_API int ft_ftw_read(ft_ctx* ctx, ft_ftw* f, const int32_t* ids, int n, void* dst,
+                       uint64_t dst_stride, uint64_t chunk, double* seconds);
+
+/*
+ * Three-tier store for a miss-path layer (smzdm explainer aomxznrn, "FreeToken干的事", item 1:
+ * disk -> system memory -> VRAM): host memory holds n_ram expert blobs in `ram` (caller-owned
+ * pinned memory, n_ram * blob_stride bytes, 4096-aligned) as a second slot pool, and the rest
+ * stay in the FTW file f (same format, H, I, E and n_shared as the layer; f must stay open
+ * while attached).  Each later ft_moe_decode takes its VRAM misses, in miss order: those in
+ * host memory are marked used at the tier's call counter, the others are read from the file
+ * (one read per blob, over the host threads) into slots taken by the pool's slot rule (lowest
+ * empty, else least recently used among those not used in this call); streamed misses are then
+ * copied from, and host-computed ones computed in, those slots.  ft_decode_stats.n_disk and
+ * disk_us report the reads.  Attaching empties the tier; f = NULL detaches (the layer goes back
+ * to host_blobs, FT_ESTATE at decode if it has none).  n_ram must be in
+ * [max_tokens * k, E].  FT_EINVAL for a resident layer, a file of other dimensions, bad n_ram
+ * or alignment, or a layer linked by ft_set_prefetch (prefetch copies read host_blobs).
+ */
+FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* ram, int n_ram);
+/* Test hook: the host-memory tier's tables, expert -> slot [E] and slot -> expert [n_ram]. */
+FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e);
 
 FT_API const char* ft_last_error(void);
 

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["ft_decode.hip", "ft_prefill.hip", "ft_debug.hip"]
-CXX_SOURCES = ["ft_api.cpp", "ft_host.cpp"]
+CXX_SOURCES = ["ft_api.cpp", "ft_host.cpp", "ft_ftw.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "ft_ftw.h"
 #include "ft_host.h"
 
 using namespace ft;
@@ -63,6 +64,10 @@ struct ft_ctx {
   hipStream_t copy_stream = nullptr;
   std::unique_ptr<ThreadPool> pool;
 };
+
+namespace ft {
+ThreadPool* ctx_pool(ft_ctx* c) { return c ? c->pool.get() : nullptr; }
+}  // namespace ft
 
 struct ft_layer {
   ft_ctx* ctx = nullptr;
@@ -130,6 +135,11 @@ struct ft_layer {
   float* pf_w_hd = nullptr;
   hipEvent_t ev_pref = nullptr;  // after the prefetch copies into this layer's pool
   bool pref_pending = false;
+  // host-memory tier over an FTW file (ft_layer_set_disk_tier): n_ram slots in `ram`
+  ft_ftw* ftw = nullptr;
+  uint8_t* ram = nullptr;
+  int n_ram = 0;
+  LruState ram_lru;
   // kernel timing events: [n][4] = gate/up start, stop, down start, stop
   std::vector<hipEvent_t> prof;
   int prof_n = 0, prof_i = 0;
@@ -281,8 +291,6 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
                            "multiple of 4096");
   if (d.resident && d.n_slots != d.E)
     return fail(FT_EINVAL, "ft_layer_create: resident layers need n_slots == E");
-  if (!d.resident && !d.host_blobs)
-    return fail(FT_EINVAL, "ft_layer_create: a non-resident layer needs host_blobs");
   if (d.flags & ~FT_LAYER_PREFILL_MXFP4)
     return fail(FT_EINVAL, "ft_layer_create: unknown flags");
   if ((d.flags & FT_LAYER_PREFILL_MXFP4) && d.format == FT_NVFP4 && !d.resident)
@@ -387,6 +395,7 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipEventCreateWithFlags(&l->ev_done, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_pref, hipEventDisableTiming));
   HIP_TRY(hipEventRecord(l->ev_done, nullptr));
+  HIP_TRY(hipEventRecord(l->ev_copy, nullptr));
   *out = l.release();
   return FT_OK;
 }
@@ -550,11 +559,48 @@ static int prefetch_into(ft_ctx* ctx, ft_layer* nx, const int32_t* idx, const fl
   return FT_OK;
 }
 
+// One call's use of the host-memory tier (see ft_layer_set_disk_tier): `needed`, the call's
+// VRAM misses in miss order, must be in host memory.  The ones there are marked used at the
+// tier's call counter first; the others take slots by the pool's slot rule and are read from
+// the FTW file, one read per blob over the host threads.
+static int host_tier_step(ft_ctx* ctx, ft_layer* l, const std::vector<int>& needed,
+                          ft_decode_stats* S) {
+  LruState& P = l->ram_lru;
+  const int64_t now = P.step;
+  for (int e : needed)
+    if (P.e2s[e] >= 0) P.last_use[P.e2s[e]] = now;
+  std::vector<int32_t> ids;
+  std::vector<uint8_t*> dst;
+  for (int e : needed) {
+    if (P.e2s[e] >= 0) continue;
+    int32_t old = -1;
+    const int s = P.take_slot(now, &old);
+    if (s < 0) return fail(FT_ESTATE, "ft_moe_decode: host-memory tier smaller than the call's misses");
+    if (old >= 0) P.e2s[old] = -1;
+    P.s2e[s] = e;
+    P.e2s[e] = s;
+    P.last_use[s] = now;
+    ids.push_back(e);
+    dst.push_back(l->ram + (uint64_t)s * l->d.blob_stride);
+  }
+  P.step++;
+  if (ids.empty()) return FT_OK;
+  // a refilled slot may still be the source of this layer's earlier copies
+  HIP_TRY(hipEventSynchronize(l->ev_copy));
+  const auto t0 = clk::now();
+  const int rc = ftw_read(ctx->pool.get(), l->ftw, ids.data(), (int)ids.size(), dst.data(), 0);
+  S->disk_us = us_since(t0);
+  S->n_disk = (int32_t)ids.size();
+  return rc;
+}
+
 static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, float* y,
                             ft_decode_stats* stats, hipStream_t st) {
   const ft_layer_desc& d = l->d;
   const int k = d.k, kk = l->kk, E = d.E;
   ft_decode_stats S{};
+  if (!l->ftw && !d.host_blobs)
+    return fail(FT_ESTATE, "ft_moe_decode: the layer has neither host_blobs nor a disk tier");
   auto t0 = clk::now();
   // routing in one launch, written straight into the mapped pinned staging: the layer's own
   // and, for a linked next layer, that layer's router on the same input (the prediction)
@@ -698,6 +744,15 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   std::copy(l->lru.e2s.begin(), l->lru.e2s.end(), l->e2s_h);
   std::copy(l->lru.s2e.begin(), l->lru.s2e.end(), l->s2e_h);
 
+  // every miss's blob in host memory: from host_blobs, or through the host-memory tier
+  if (l->ftw) {
+    rc = host_tier_step(ctx, l, misses, &S);
+    if (rc) return rc;
+  }
+  auto host_src = [&](int e) -> const uint8_t* {
+    return l->ftw ? l->ram + (uint64_t)l->ram_lru.e2s[e] * d.blob_stride
+                  : (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride;
+  };
   // copies of streamed experts into their slots, on the copy stream (timed), after this
   // layer's previous kernels (which may have run on another stream) are done with the slots
   if (!streamed.empty()) {
@@ -707,8 +762,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   }
   for (int e : streamed) {
     const int s = l->lru.e2s[e];
-    HIP_TRY(hipMemcpyAsync((uint8_t*)d.pool + (uint64_t)s * d.blob_stride,
-                           (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride,
+    HIP_TRY(hipMemcpyAsync((uint8_t*)d.pool + (uint64_t)s * d.blob_stride, host_src(e),
                            l->L.bytes, hipMemcpyHostToDevice, ctx->copy_stream));
   }
   if (!streamed.empty()) {
@@ -760,9 +814,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     for (int i = 0; i < c; ++i)
       std::memcpy(&xt[(size_t)i * d.H], l->x_h + (size_t)cols[i] * d.H, (size_t)d.H * 2);
     const auto tf = clk::now();
-    rc = host_expert_ffn(ctx->pool.get(), l->L,
-                         (const uint8_t*)d.host_blobs + (uint64_t)e * d.blob_stride, xt.data(), c,
-                         yt.data());
+    rc = host_expert_ffn(ctx->pool.get(), l->L, host_src(e), xt.data(), c, yt.data());
     if (rc) return rc;
     ffn_s += us_since(tf) * 1e-6;
     for (int i = 0; i < c; ++i) {
@@ -853,6 +905,9 @@ extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth
   if (depth > next->d.n_slots) return fail(FT_EINVAL, "ft_set_prefetch: depth above next's slots");
   if (next->prev && next->prev != layer)
     return fail(FT_EINVAL, "ft_set_prefetch: next is already the target of another layer");
+  if (layer->ftw || next->ftw)
+    return fail(FT_EINVAL, "ft_set_prefetch: a layer with a disk tier cannot be linked");
+  if (!next->d.host_blobs) return fail(FT_EINVAL, "ft_set_prefetch: next has no host_blobs");
   HIP_TRY(hipSetDevice(layer->ctx->device));
   if (!layer->pf_dev) {
     const size_t nl = (size_t)FT_MAX_DECODE_TOKENS * 1024, nk = (size_t)FT_MAX_DECODE_TOKENS * FT_MAX_TOPK;
@@ -887,6 +942,48 @@ extern "C" FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const flo
   return FT_OK;
 }
 
+extern "C" FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* ram, int n_ram) {
+  if (!layer) return fail(FT_EINVAL, "ft_layer_set_disk_tier: null layer");
+  if (layer->all_resident) return fail(FT_EINVAL, "ft_layer_set_disk_tier: the layer is resident");
+  if (layer->next || layer->prev)
+    return fail(FT_EINVAL, "ft_layer_set_disk_tier: the layer is linked by ft_set_prefetch");
+  const ft_layer_desc& d = layer->d;
+  if (!f) {
+    layer->ftw = nullptr;
+    layer->ram = nullptr;
+    layer->n_ram = 0;
+    return FT_OK;
+  }
+  int fmt, H, I, E, ns;
+  ftw_dims(f, &fmt, &H, &I, &E, &ns);
+  if (fmt != d.format || H != d.H || I != d.I || E != d.E || ns != d.n_shared)
+    return fail(FT_EINVAL, "ft_layer_set_disk_tier: the file's dimensions differ from the layer's");
+  if (n_ram < d.max_tokens * d.k || n_ram > d.E)
+    return fail(FT_EINVAL, "ft_layer_set_disk_tier: n_ram must be in [max_tokens * k, E]");
+  if (!ram || (uintptr_t)ram % kAlign)
+    return fail(FT_EINVAL, "ft_layer_set_disk_tier: ram must be 4096-aligned");
+  HIP_TRY(hipSetDevice(layer->ctx->device));
+  hipPointerAttribute_t pa{};
+  if (hipPointerGetAttributes(&pa, ram) != hipSuccess || pa.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(FT_EINVAL, "ft_layer_set_disk_tier: ram is not pinned host memory");
+  }
+  HIP_TRY(hipEventSynchronize(layer->ev_copy));   // copies from the previous source are done
+  layer->ftw = f;
+  layer->ram = (uint8_t*)ram;
+  layer->n_ram = n_ram;
+  layer->ram_lru.init(d.E, n_ram, false);
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e) {
+  if (!layer || !e2r || !r2e) return fail(FT_EINVAL, "ft_debug_host_tier: null argument");
+  if (!layer->ftw) return fail(FT_ESTATE, "ft_debug_host_tier: the layer has no disk tier");
+  std::copy(layer->ram_lru.e2s.begin(), layer->ram_lru.e2s.end(), e2r);
+  std::copy(layer->ram_lru.s2e.begin(), layer->ram_lru.s2e.end(), r2e);
+  return FT_OK;
+}
+
 extern "C" FT_API int ft_force_q(ft_layer* layer, int q) {
   if (!layer) return fail(FT_EINVAL, "ft_force_q: null layer");
   layer->force_q = q < 0 ? -1 : q;
@@ -901,8 +998,25 @@ static double median(std::vector<double> v) {
 extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh) {
   if (!ctx || !layer) return fail(FT_EINVAL, "ft_measure_bandwidth: null argument");
   const ft_layer_desc& d = layer->d;
-  if (!d.host_blobs) return fail(FT_ESTATE, "ft_measure_bandwidth: the layer has no host_blobs");
   HIP_TRY(hipSetDevice(ctx->device));
+  // probe sources: two host blobs, from host_blobs or read into the first slots of a disk
+  // tier that no decode call has used yet
+  const uint8_t* srcs[2];
+  if (d.host_blobs) {
+    for (int i = 0; i < 2; ++i)
+      srcs[i] = (const uint8_t*)d.host_blobs + (uint64_t)(i % d.E) * d.blob_stride;
+  } else if (layer->ftw) {
+    for (int32_t e : layer->ram_lru.s2e)
+      if (e >= 0) return fail(FT_ESTATE, "ft_measure_bandwidth: the disk tier is already in use");
+    int32_t ids[2] = {0, d.E > 1 ? 1 : 0};
+    uint8_t* dst[2] = {layer->ram, layer->ram + (layer->n_ram > 1 ? d.blob_stride : 0)};
+    const int rc = ftw_read(ctx->pool.get(), layer->ftw, ids, layer->n_ram > 1 ? 2 : 1, dst, 0);
+    if (rc) return rc;
+    srcs[0] = dst[0];
+    srcs[1] = dst[1];
+  } else {
+    return fail(FT_ESTATE, "ft_measure_bandwidth: the layer has neither host_blobs nor a disk tier");
+  }
   const uint64_t bytes = layer->L.bytes;
   void* tmp = nullptr;
   if (hipMalloc(&tmp, bytes) != hipSuccess)
@@ -913,7 +1027,7 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   std::vector<double> bps;
   const int reps = env_int("FT_PROBE_REPS", 7);
   for (int r = 0; r < reps + 1; ++r) {
-    const uint8_t* src = (const uint8_t*)d.host_blobs + (uint64_t)(r % d.E) * d.blob_stride;
+    const uint8_t* src = srcs[r % 2];
     hipEventRecord(a, ctx->copy_stream);
     hipMemcpyAsync(tmp, src, bytes, hipMemcpyHostToDevice, ctx->copy_stream);
     hipEventRecord(b, ctx->copy_stream);
@@ -929,7 +1043,7 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   std::vector<uint16_t> x(d.H, 0x3f80);  // ones
   std::vector<float> y(d.H);
   for (int r = 0; r < reps + 1; ++r) {
-    const uint8_t* src = (const uint8_t*)d.host_blobs + (uint64_t)((r + 1) % d.E) * d.blob_stride;
+    const uint8_t* src = srcs[(r + 1) % 2];
     auto t0 = clk::now();
     int rc = host_expert_ffn(ctx->pool.get(), layer->L, src, x.data(), 1, y.data());
     if (rc) return rc;

@@ -14,7 +14,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FT_LIB", os.path.join(_HERE, "libft.so"))
 
-FT_OK, FT_EINVAL, FT_ENOMEM, FT_EHIP, FT_EUNSUPPORTED, FT_ESTATE = 0, -1, -2, -3, -4, -5
+FT_OK, FT_EINVAL, FT_ENOMEM, FT_EHIP, FT_EUNSUPPORTED, FT_ESTATE, FT_EIO = 0, -1, -2, -3, -4, -5, -6
+FT_FTW_DIRECT, FT_FTW_STAGED = 1, 2
 FT_MXFP4, FT_NVFP4 = 0, 1
 FT_PREFILL_EXACT, FT_PREFILL_MXFP4 = 0, 1
 FT_LAYER_PREFILL_MXFP4 = 1
@@ -50,10 +51,17 @@ class DecodeStats(C.Structure):
                 ("n_evicted", C.c_int32), ("step", C.c_int32), ("qstar", C.c_double),
                 ("bp", C.c_double), ("bh", C.c_double), ("host_us", C.c_double),
                 ("wait_us", C.c_double), ("bp_obs", C.c_double), ("bh_obs", C.c_double),
-                ("n_prefetched", C.c_int32), ("n_prefetch_hits", C.c_int32)]
+                ("n_prefetched", C.c_int32), ("n_prefetch_hits", C.c_int32),
+                ("n_disk", C.c_int32), ("disk_us", C.c_double)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class FtwInfo(C.Structure):
+    _fields_ = [("format", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32),
+                ("n_shared", C.c_int32), ("direct", C.c_int32), ("staged", C.c_int32),
+                ("reserved", C.c_int32), ("blob_bytes", C.c_uint64), ("file_bytes", C.c_uint64)]
 
 
 _vp, _i, _u64, _d = C.c_void_p, C.c_int, C.c_uint64, C.c_double
@@ -75,6 +83,13 @@ _sig = {
     "ft_qstar_split_makespan": [_i, _d, _d, C.POINTER(_i)],
     "ft_set_miss_policy": [_vp, _i, _d],
     "ft_set_prefetch": [_vp, _vp, _i],
+    "ft_ftw_write": [C.c_char_p, _i, _i, _i, _i, _i, _vp, _u64],
+    "ft_ftw_open": [C.c_char_p, _i, C.POINTER(_vp)],
+    "ft_ftw_get_info": [_vp, C.POINTER(FtwInfo)],
+    "ft_ftw_close": [_vp],
+    "ft_ftw_read": [_vp, _vp, _vp, _i, _vp, _u64, _u64, C.POINTER(_d)],
+    "ft_layer_set_disk_tier": [_vp, _vp, _vp, _i],
+    "ft_debug_host_tier": [_vp, _vp, _vp],
     "ft_residual_bf16": [_vp, _vp, _vp, C.c_float, C.c_int64, _vp, _vp],
     "ft_debug_dequant": [_vp, _i, _i, _vp, _vp],
     "ft_debug_tables": [_vp, _vp, _vp],
@@ -270,3 +285,57 @@ def debug_prefill_quant(layer_h, ws, T, which, codes, scales, stream=None):
 
 def debug_prefill_weights(layer_h, e, out, stream=None):
     check(lib.ft_debug_prefill_weights(layer_h, e, _ptr(out), stream))
+
+
+def ftw_write(path, fmt, H, I, E, n_shared, blobs, src_stride):
+    """Write an FTW file from packed blobs (a host buffer: numpy array or CPU tensor)."""
+    check(lib.ft_ftw_write(os.fsencode(path), FORMATS[fmt] if isinstance(fmt, str) else fmt,
+                           H, I, E, n_shared, _ptr(blobs), src_stride))
+
+
+class Ftw:
+    """An open FTW file (closed by close() or when collected)."""
+
+    def __init__(self, path, direct=True, staged=False):
+        h = C.c_void_p()
+        flags = (FT_FTW_DIRECT if direct else 0) | (FT_FTW_STAGED if staged else 0)
+        check(lib.ft_ftw_open(os.fsencode(path), flags, C.byref(h)))
+        self.handle = h.value
+
+    def info(self) -> FtwInfo:
+        inf = FtwInfo()
+        check(lib.ft_ftw_get_info(self.handle, C.byref(inf)))
+        return inf
+
+    def read(self, ids, dst, dst_stride, chunk=0, ctx=None) -> float:
+        """Read blobs ids into dst (host buffer) at dst_stride; returns the seconds taken."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        sec = C.c_double()
+        check(lib.ft_ftw_read(ctx.handle if ctx is not None else None, self.handle,
+                              ids.ctypes.data, len(ids), _ptr(dst), dst_stride, chunk,
+                              C.byref(sec)))
+        return sec.value
+
+    def close(self):
+        if self.handle:
+            lib.ft_ftw_close(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def set_disk_tier(layer_h, ftw, ram, n_ram):
+    """Attach a host-memory tier of n_ram pinned slots over an open FTW file (None detaches)."""
+    check(lib.ft_layer_set_disk_tier(layer_h, ftw.handle if ftw is not None else None,
+                                     _ptr(ram) if ram is not None else None, n_ram))
+
+
+def debug_host_tier(layer_h, E, n_ram):
+    e2r = np.empty(E, dtype=np.int32)
+    r2e = np.empty(n_ram, dtype=np.int32)
+    check(lib.ft_debug_host_tier(layer_h, e2r.ctypes.data, r2e.ctypes.data))
+    return e2r, r2e

@@ -485,3 +485,64 @@ def test_set_prefetch_rejects_bad_links(ctx):
     finally:
         c.close()
         odd.close()
+
+
+def _pinned_aligned(nbytes):
+    raw = torch.empty(nbytes + 4096, dtype=torch.uint8, pin_memory=True)
+    off = (-raw.data_ptr()) % 4096
+    return raw, raw[off:off + nbytes]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_disk_tier_matches_oracle(ctx, tmp_path, fmt):
+    """Three tiers: the layer's blobs in an FTW file, 7 host-memory slots over it, 5 VRAM
+    slots.  After every call the VRAM tables and the host-memory tier's tables equal the
+    oracle's two pools replaying the same calls, the disk reads are the oracle's loads, and
+    the outputs match the oracle."""
+    extra = dict(fmt=synth.NVFP4, nv_tensor_scale=1 / 64) if fmt == "nvfp4" else {}
+    cfg = synth.small_config(f"disk{fmt}", seed=83, H=384, I=256, E=14, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 20, zipf_c=0.5, **extra)
+    L = layer_for(ctx, f"disk{fmt}", cfg=cfg, resident=False, n_slots=5, max_tokens=2)
+    path = str(tmp_path / "layer.ftw")
+    # the file holds the routed experts and the shared one (packed like the layer's)
+    store = np.zeros((cfg.E + 1) * L.stride, dtype=np.uint8)
+    store[:cfg.E * L.stride] = L.host_blobs.numpy()
+    ft.pack_expert_into(cfg.fmt, cfg.H, cfg.I, synth.gen_expert(cfg, 0, shared=True),
+                        store[cfg.E * L.stride:])
+    ft.ftw_write(path, cfg.fmt, cfg.H, cfg.I, cfg.E, 1, store, L.stride)
+    f = ft.Ftw(path)
+    n_ram = 7
+    keep, ram = _pinned_aligned(n_ram * L.stride)
+    with pytest.raises(ft.FtError) as e:
+        ft.set_disk_tier(L.handle, f, ram, 5)          # below max_tokens * k
+    assert e.value.code == ft.FT_EINVAL
+    ft.set_disk_tier(L.handle, f, ram, n_ram)
+    OL = L.oracle_layer()
+    vram, host = policy.LruPool(cfg.E, L.n_slots), policy.LruPool(cfg.E, n_ram)
+    ft.set_bandwidth(L.handle, 1.0, 2.5)
+    ft.force_q(L.handle, -1)
+    reads = 0
+    try:
+        for s in range(24):
+            T = 1 + s % 2
+            x = synth.gen_tokens(cfg, T, batch=700 + s)
+            st = ft.DecodeStats()
+            y = run_decode(ctx, L, x, st)
+            r_idx, r_w, _, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+            assert np.all(gap >= 1e-6), "near-tie; choose another seed"
+            res = vram.step(r_idx, r_w.astype(np.float32), 1.0, 2.5)
+            tr = policy.tier_step(host, res.misses)
+            e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+            assert np.array_equal(e2s, res.e2s) and np.array_equal(s2e, res.s2e), s
+            e2r, r2e = ft.debug_host_tier(L.handle, cfg.E, n_ram)
+            assert np.array_equal(e2r, tr.e2s) and np.array_equal(r2e, tr.s2e), s
+            assert (st.n_disk, st.n_streamed, st.n_host) == (
+                len(tr.loaded), len(res.streamed), len(res.host)), s
+            reads += st.n_disk
+            if s % 3 == 0 or s == 23:
+                check_output(y, moe.moe_forward(OL, x)["y"], f"disk tier step {s}")
+    finally:
+        ft.set_disk_tier(L.handle, None, None, 0)
+        f.close()
+    assert reads > n_ram, reads          # the tier was refilled from disk
+    log(f"[gpu] disk tier {fmt}: {reads} blob reads over 24 calls")

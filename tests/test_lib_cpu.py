@@ -134,3 +134,99 @@ def test_makespan_split_matches_oracle():
         with pytest.raises(ft.FtError) as e:
             ft.qstar_split_makespan(*bad)
         assert e.value.code == ft.FT_EINVAL
+
+
+def _aligned(nbytes):
+    """A 4096-aligned uint8 view of nbytes (O_DIRECT destinations)."""
+    raw = np.zeros(nbytes + 4096, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 4096
+    return raw[off:off + nbytes]
+
+
+def _packed_store(fmt, E, n_shared, seed=12):
+    cfg = synth.small_config(seed=seed, H=256, I=128, E=E, fmt=fmt, n_shared=n_shared)
+    stride = ft.blob_bytes(fmt, cfg.H, cfg.I)
+    store = np.zeros((E + n_shared) * stride, dtype=np.uint8)
+    for e in range(E):
+        ft.pack_expert_into(fmt, cfg.H, cfg.I, synth.gen_expert(cfg, e),
+                            store[e * stride:(e + 1) * stride])
+    for s in range(n_shared):
+        ft.pack_expert_into(fmt, cfg.H, cfg.I, synth.gen_expert(cfg, s, shared=True),
+                            store[(E + s) * stride:(E + s + 1) * stride])
+    return cfg, stride, store
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("direct,staged", [(True, False), (False, False), (True, True)])
+def test_ftw_roundtrip_and_layout(tmp_path, fmt, direct, staged):
+    """An FTW file holds the packed blobs unchanged, with its header page first and every
+    tensor on a 4096-byte boundary of the file; reads in whole blobs or in 4 KiB requests,
+    on one thread, return the same bytes."""
+    cfg, stride, store = _packed_store(fmt, E=5, n_shared=1)
+    path = str(tmp_path / "layer.ftw")
+    ft.ftw_write(path, fmt, cfg.H, cfg.I, 5, 1, store, stride)
+    raw = np.fromfile(path, dtype=np.uint8)
+    hdr = raw[:4096]
+    assert hdr[:8].view(np.uint32).tolist() == [0x31575446, 1]
+    assert hdr[8:28].view(np.int32).tolist() == [ft.FORMATS[fmt], 256, 128, 5, 1]
+    blob_bytes, blob_stride, data_off, file_bytes = hdr[32:64].view(np.uint64).tolist()
+    assert (blob_bytes, blob_stride, data_off) == (stride, stride, 4096)
+    assert file_bytes == raw.size == 4096 + 6 * stride
+    offs, _ = tiled.blob_offsets(fmt, cfg.H, cfg.I)
+    for i in range(6):
+        base = data_off + i * blob_stride
+        assert all((base + o) % 4096 == 0 for o in [0] + offs)
+        assert np.array_equal(raw[base:base + stride], store[i * stride:(i + 1) * stride])
+    f = ft.Ftw(path, direct=direct, staged=staged)
+    try:
+        inf = f.info()
+        assert (inf.E, inf.n_shared, inf.blob_bytes, inf.file_bytes) == (5, 1, stride, raw.size)
+        assert direct or inf.direct == 0
+        assert inf.staged == (inf.direct and staged)
+        ids = [5, 0, 3, 3]
+        for chunk in (0, 4096, 3 * 4096):
+            dst = _aligned(len(ids) * stride)
+            f.read(ids, dst, stride, chunk=chunk)
+            for j, e in enumerate(ids):
+                assert np.array_equal(dst[j * stride:(j + 1) * stride],
+                                      store[e * stride:(e + 1) * stride]), (chunk, j)
+        with pytest.raises(ft.FtError) as e:
+            f.read([6], _aligned(stride), stride)
+        assert e.value.code == ft.FT_EINVAL
+        if inf.direct:
+            with pytest.raises(ft.FtError) as e:     # O_DIRECT needs aligned destinations
+                f.read([0], _aligned(stride + 8)[8:], stride)
+            assert e.value.code == ft.FT_EINVAL
+    finally:
+        f.close()
+
+
+def test_ftw_rejects_bad_files(tmp_path):
+    cfg, stride, store = _packed_store("mxfp4", E=3, n_shared=0)
+    good = str(tmp_path / "good.ftw")
+    ft.ftw_write(good, "mxfp4", cfg.H, cfg.I, 3, 0, store, stride)
+    raw = np.fromfile(good, dtype=np.uint8)
+
+    def expect(code, data=None, path=None):
+        p = path or str(tmp_path / "bad.ftw")
+        if data is not None:
+            data.tofile(p)
+        with pytest.raises(ft.FtError) as e:
+            ft.Ftw(p)
+        assert e.value.code == code
+
+    bad = raw.copy(); bad[0] ^= 1
+    expect(ft.FT_EINVAL, bad)                       # magic
+    bad = raw.copy(); bad[4] = 9
+    expect(ft.FT_EINVAL, bad)                       # version
+    expect(ft.FT_EINVAL, raw[:-4096].copy())        # truncated
+    bad = raw.copy(); bad[32:40] = np.array([stride + 16], dtype=np.uint64).view(np.uint8)
+    expect(ft.FT_EINVAL, bad)                       # blob size of other dimensions
+    expect(ft.FT_EIO, path=str(tmp_path / "missing.ftw"))
+    # the writer checks each blob's header against the dimensions it is given
+    with pytest.raises(ft.FtError) as e:
+        ft.ftw_write(str(tmp_path / "x.ftw"), "mxfp4", 384, cfg.I, 3, 0, store, stride)
+    assert e.value.code == ft.FT_EINVAL
+    with pytest.raises(ft.FtError) as e:
+        ft.ftw_write(str(tmp_path / "x.ftw"), "mxfp4", cfg.H, cfg.I, 3, 0, store, stride - 4096)
+    assert e.value.code == ft.FT_EINVAL
