@@ -263,6 +263,9 @@ def bench_miss_path(args, wl):
                            router=router, host_store=Ls[0].host_blobs))
     bp, bh = ft.measure_bandwidth(ctx, Ls[0].handle)
     log(f"[bench] measured Bp {bp / 1e9:.1f} GB/s, Bh {bh / 1e9:.1f} GB/s")
+    disk = None
+    if args.disk_dir is not None:
+        disk = disk_tier_setup(args, ctx, Ls, cfg)
     rule = ft.FT_SPLIT_MAKESPAN if args.split == "makespan" else ft.FT_SPLIT_ROUND
     for li, L in enumerate(Ls):
         ft.set_bandwidth(L.handle, bp, bh)
@@ -275,12 +278,13 @@ def bench_miss_path(args, wl):
     y = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     st = ft.DecodeStats()
-    tot = dict(hits=0, sel=0, m=0, q=0, streamed=0, host=0, pf=0, pf_hits=0)
+    tot = dict(hits=0, sel=0, m=0, q=0, streamed=0, host=0, pf=0, pf_hits=0, disk=0)
+    disk_us = 0.0
     host_us = wait_us = 0.0
     bp_obs, bh_obs = [], []
 
     def token(x, count):
-        nonlocal host_us, wait_us
+        nonlocal host_us, wait_us, disk_us
         for li, L in enumerate(Ls):
             ft.moe_decode(ctx, L.handle, x if li == 0 else xl, 1, y, s, st)
             if li + 1 < NL:
@@ -292,8 +296,10 @@ def bench_miss_path(args, wl):
                 continue
             for key, v in (("hits", st.n_hits), ("sel", st.n_selected), ("m", st.n_miss),
                            ("q", st.q), ("streamed", st.n_streamed), ("host", st.n_host),
-                           ("pf", st.n_prefetched), ("pf_hits", st.n_prefetch_hits)):
+                           ("pf", st.n_prefetched), ("pf_hits", st.n_prefetch_hits),
+                           ("disk", st.n_disk)):
                 tot[key] += v
+            disk_us += st.disk_us
             host_us += st.host_us
             wait_us += st.wait_us
             if st.bp_obs > 0:
@@ -340,10 +346,71 @@ def bench_miss_path(args, wl):
                       "median_Bh_obs_GBps": float(np.median(bh_obs)) / 1e9 if bh_obs else None},
         "roofline": None,
     }
+    if disk is not None:
+        disk.update({"reads": tot["disk"], "reads_per_token": tot["disk"] / K,
+                     "read_GBps": tot["disk"] * blob / max(disk_us * 1e-6, 1e-9) / 1e9,
+                     "mean_read_ms": disk_us / max(1, tot["disk"]) / 1e3})
+        res["config"]["ram_slots"] = args.ram_slots
+        res["miss_path"]["disk_tier"] = disk
+        disk["staged"] = disk["_ftw"].info().staged
+        ft.set_disk_tier(Ls[0].handle, None, None, 0)
+        disk["_ftw"].close()
+        del disk["_ftw"], disk["_ram"]
+        os.remove(disk.pop("_path"))
     for L in Ls:
         L.close()
     ctx.close()
     return res
+
+
+def disk_tier_setup(args, ctx, Ls, cfg):
+    """Write layer 0's blobs to an FTW file, time direct reads of random blobs at several
+    request sizes, and attach a host-memory tier of --ram-slots pinned slots over the file."""
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    from mxfp4_expert_layer_amd import ft
+
+    if len(Ls) != 1 or args.prefetch:
+        raise SystemExit("--disk-dir runs one layer without prefetch")
+    L = Ls[0]
+    d = tempfile.mkdtemp(prefix="ftw_", dir=args.disk_dir)
+    path = os.path.join(d, "layer.ftw")
+    store = L.host_blobs.numpy()
+    shared = np.zeros(cfg.n_shared * L.stride, dtype=np.uint8)
+    from mxfp4_expert_layer_amd import synth
+    for s_ in range(cfg.n_shared):
+        ft.pack_expert_into(cfg.fmt, cfg.H, cfg.I, synth.gen_expert(cfg, s_, shared=True),
+                            shared[s_ * L.stride:(s_ + 1) * L.stride])
+    both = np.concatenate([store, shared]) if cfg.n_shared else store
+    t0 = time.perf_counter()
+    ft.ftw_write(path, cfg.fmt, cfg.H, cfg.I, cfg.E, cfg.n_shared, both, L.stride)
+    write_s = time.perf_counter() - t0
+    del both
+    f = ft.Ftw(path, direct=True)
+    inf = f.info()
+    log(f"[bench] FTW file {inf.file_bytes / 1e9:.2f} GB written in {write_s:.1f} s; "
+        f"direct={inf.direct}")
+    # request-size sweep: 24 random blobs into plain aligned memory, per request size
+    rng = np.random.default_rng(5)
+    n = 24
+    raw = np.empty(n * L.stride + 4096, dtype=np.uint8)
+    dst = raw[(-raw.ctypes.data) % 4096:][:n * L.stride]
+    sweep = {}
+    for chunk in (0, 1 << 20, 1 << 16, 1 << 12):
+        ids = rng.choice(cfg.E, n, replace=False)
+        sec = f.read(ids, dst, L.stride, chunk=chunk, ctx=ctx)
+        sweep["whole_blob" if chunk == 0 else f"{chunk // 1024}KiB"] = n * L.stride / sec / 1e9
+    log(f"[bench] direct reads GB/s by request size: {sweep}")
+    del raw
+    keep = torch.empty(args.ram_slots * L.stride + 4096, dtype=torch.uint8, pin_memory=True)
+    off = (-keep.data_ptr()) % 4096
+    ram = keep[off:off + args.ram_slots * L.stride]
+    ft.set_disk_tier(L.handle, f, ram, args.ram_slots)
+    return {"file_GB": inf.file_bytes / 1e9, "direct": inf.direct, "write_s": write_s,
+            "read_GBps_by_request": sweep, "_ftw": f, "_ram": (keep, ram), "_path": path}
 
 
 def cpu_baseline_prefill(cfg, x, seconds, mode="exact"):
@@ -505,6 +572,11 @@ def main():
                     help="miss path: cross-layer prefetch depth (0: off)")
     ap.add_argument("--residual-scale", type=float, default=1.0,
                     help="miss path: input of layer l+1 = bf16(x_l + g * y_l)")
+    ap.add_argument("--disk-dir", default=None,
+                    help="miss path: put the experts in an FTW file under this directory, with "
+                         "a host-memory tier of --ram-slots over it")
+    ap.add_argument("--ram-slots", type=int, default=96,
+                    help="miss path: host-memory slots over the FTW file")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

@@ -343,7 +343,7 @@ FT_API int ft_ftw_read(ft_ctx* ctx, ft_ftw* f, const int32_t* ids, int n, void* 
  * stay in the FTW file f (same format, H, I, E and n_shared as the layer; f must stay open
  * while attached).  Each later ft_moe_decode takes its VRAM misses, in miss order: those in
  * host memory are marked used at the tier's call counter, the others are read from the file
- * (one read per blob, over the host threads) into slots taken by the pool's slot rule (lowest
+ * (1 MiB requests over the host threads) into slots taken by the pool's slot rule (lowest
  * empty, else least recently used among those not used in this call); streamed misses are then
  * copied from, and host-computed ones computed in, those slots.  ft_decode_stats.n_disk and
  * disk_us report the reads.  Attaching empties the tier; f = NULL detaches (the layer goes back

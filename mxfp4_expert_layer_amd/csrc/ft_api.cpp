@@ -562,7 +562,7 @@ static int prefetch_into(ft_ctx* ctx, ft_layer* nx, const int32_t* idx, const fl
 // One call's use of the host-memory tier (see ft_layer_set_disk_tier): `needed`, the call's
 // VRAM misses in miss order, must be in host memory.  The ones there are marked used at the
 // tier's call counter first; the others take slots by the pool's slot rule and are read from
-// the FTW file, one read per blob over the host threads.
+// the FTW file in 1 MiB requests over the host threads.
 static int host_tier_step(ft_ctx* ctx, ft_layer* l, const std::vector<int>& needed,
                           ft_decode_stats* S) {
   LruState& P = l->ram_lru;
@@ -588,7 +588,11 @@ static int host_tier_step(ft_ctx* ctx, ft_layer* l, const std::vector<int>& need
   // a refilled slot may still be the source of this layer's earlier copies
   HIP_TRY(hipEventSynchronize(l->ev_copy));
   const auto t0 = clk::now();
-  const int rc = ftw_read(ctx->pool.get(), l->ftw, ids.data(), (int)ids.size(), dst.data(), 0);
+  // 1 MiB requests spread over the host threads: a whole-blob request is one queue entry,
+  // and small requests pay per-request costs (measured on the box: 1 MiB direct reads move
+  // 7.1 GB/s, 64 KiB 4.8 GB/s, 4 KiB 0.7 GB/s)
+  const int rc = ftw_read(ctx->pool.get(), l->ftw, ids.data(), (int)ids.size(), dst.data(),
+                          1u << 20);
   S->disk_us = us_since(t0);
   S->n_disk = (int32_t)ids.size();
   return rc;
