@@ -87,7 +87,12 @@ FT_API int ft_pack_expert(int format, int H, int I,
                           const uint8_t* down_codes, const uint8_t* down_scales,
                           const float* tensor_scales, void* blob);
 
-/* Context: device, internal copy stream, host thread pool for host-computed experts. */
+/*
+ * Context: device, internal copy stream, host thread pool for host-computed experts and disk
+ * reads (FT_HOST_THREADS threads, default min(16, hardware threads); after a job its workers
+ * spin for 0.5 ms before they sleep).  Calls that use one context (or its layers) must not run
+ * concurrently from several host threads.
+ */
 FT_API int ft_ctx_create(int device, ft_ctx** out);
 FT_API int ft_ctx_destroy(ft_ctx* ctx);
 

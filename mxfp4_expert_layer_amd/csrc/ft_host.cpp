@@ -4,6 +4,7 @@
 #include <immintrin.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -32,28 +33,35 @@ ThreadPool::ThreadPool(int n_threads) : n_(std::max(1, n_threads)) {
 ThreadPool::~ThreadPool() {
   {
     std::lock_guard<std::mutex> lk(mu_);
-    stop_ = true;
+    stop_.store(true);
   }
   cv_.notify_all();
   for (auto& t : threads_) t.join();
 }
 
 void ThreadPool::worker(int id) {
+  using sclock = std::chrono::steady_clock;
+  constexpr auto kSpin = std::chrono::microseconds(500);
   uint64_t seen = 0;
   for (;;) {
-    const std::function<void(int, int)>* job;
-    {
-      std::unique_lock<std::mutex> lk(mu_);
-      cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
-      if (stop_) return;
-      seen = gen_;
-      job = job_;
+    // spin for the next job, then sleep until one comes (gen_ changes under mu_, and a
+    // sleeper registers under mu_, so no wake-up is lost)
+    uint64_t g = gen_.load(std::memory_order_acquire);
+    const auto t0 = sclock::now();
+    for (int i = 0; g == seen && !stop_.load(std::memory_order_relaxed); ++i) {
+      __builtin_ia32_pause();
+      if ((i & 255) == 255 && sclock::now() - t0 > kSpin) {
+        std::unique_lock<std::mutex> lk(mu_);
+        sleepers_.fetch_add(1);
+        cv_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        sleepers_.fetch_sub(1);
+      }
+      g = gen_.load(std::memory_order_acquire);
     }
-    (*job)(id, n_);
-    {
-      std::lock_guard<std::mutex> lk(mu_);
-      if (--pending_ == 0) done_cv_.notify_one();
-    }
+    if (stop_.load()) return;
+    seen = g;
+    (*job_)(id, n_);
+    pending_.fetch_sub(1, std::memory_order_release);
   }
 }
 
@@ -62,16 +70,15 @@ void ThreadPool::run(const std::function<void(int, int)>& fn) {
     fn(0, 1);
     return;
   }
+  job_ = &fn;
+  pending_.store(n_ - 1, std::memory_order_relaxed);
   {
     std::lock_guard<std::mutex> lk(mu_);
-    job_ = &fn;
-    pending_ = n_ - 1;
-    ++gen_;
+    gen_.fetch_add(1, std::memory_order_release);
   }
-  cv_.notify_all();
+  if (sleepers_.load() > 0) cv_.notify_all();
   fn(n_ - 1, n_);
-  std::unique_lock<std::mutex> lk(mu_);
-  done_cv_.wait(lk, [&] { return pending_ == 0; });
+  while (pending_.load(std::memory_order_acquire) != 0) __builtin_ia32_pause();
 }
 
 // ---- host expert FFN ------------------------------------------------------------------------
@@ -155,11 +162,28 @@ static void gemv_tiles(const BlobLayout& L, const uint8_t* codes, const uint8_t*
 // AVX-512 (BF16) path for MXFP4 tiles.  Per 32-value lane block: the 16 code bytes expand
 // to 32 nibble indices in 16-bit lanes, which index a 16-entry bf16 table of E2M1 values
 // scaled by the block's E8M0 scale (the scale is added to the exponent field of the nonzero
-// entries, exact for normal results), and vdpbf16ps accumulates the products with the bf16
-// activations into 16 fp32 lanes per row.  acc[row] sums for rows rt*16 .. rt*16+15.
+// entries), and vdpbf16ps accumulates the products with the bf16 activations into 16 fp32
+// lanes per row.  acc[row] sums for rows rt*16 .. rt*16+15.  The table trick is exact when
+// every scaled E2M1 value is a normal bf16 number: scale codes 2..253 (0.5 * 2^-125 ..
+// 6 * 2^126).  A row tile with any other scale code (including the NaN code 255) goes to the
+// scalar path, which follows the format definition for every code (xs: x as fp32).
+// Whether the KC * 64 E8M0 codes of one row tile all lie in 2..253.
+__attribute__((target("avx512f,avx512bw")))
+static bool mx_scale_row_in_range(const uint8_t* s, int KC) {
+  __mmask64 bad = 0;
+  for (int kc = 0; kc < KC; ++kc) {
+    const __m512i v = _mm512_loadu_si512((const void*)(s + 64 * kc));
+    bad |= _mm512_cmp_epu8_mask(v, _mm512_set1_epi8(2), _MM_CMPINT_LT) |
+           _mm512_cmp_epu8_mask(v, _mm512_set1_epi8((char)253), _MM_CMPINT_NLE);
+  }
+  return bad == 0;
+}
+
 __attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl")))
-static void gemv_tiles_mx_avx512(const uint8_t* codes, const uint8_t* scales, int K, int rt0,
-                                 int rt1, const uint16_t* xb, int T, float* acc_out, int R) {
+static void gemv_tiles_mx_avx512(const BlobLayout& L, const uint8_t* codes,
+                                 const uint8_t* scales, int K, int rt0, int rt1,
+                                 const uint16_t* xb, const float* xs, int T, float* acc_out,
+                                 int R) {
   const int KC = K / kTileK;
   // bf16 bits of E2M1 codes 0..15 (0, .5, 1, 1.5, 2, 3, 4, 6 and their negatives)
   alignas(64) static const uint16_t kBase[32] = {
@@ -169,9 +193,13 @@ static void gemv_tiles_mx_avx512(const uint8_t* codes, const uint8_t* scales, in
   const __m512i base = _mm512_load_si512((const void*)kBase);
   const __mmask32 nonzero = 0x0000FEFEu;  // entries 1..7 and 9..15
   const __m512i m15 = _mm512_set1_epi32(15);
-  for (int t = 0; t < T; ++t) {
-    const uint16_t* xt = xb + (uint64_t)t * K;
-    for (int rt = rt0; rt < rt1; ++rt) {
+  for (int rt = rt0; rt < rt1; ++rt) {
+    if (!mx_scale_row_in_range(scales + (uint64_t)rt * KC * 64, KC)) {
+      gemv_tiles(L, codes, scales, K, rt, rt + 1, xs, T, 1.0f, acc_out, R);
+      continue;
+    }
+    for (int t = 0; t < T; ++t) {
+      const uint16_t* xt = xb + (uint64_t)t * K;
       __m512 acc[16];
       for (int r = 0; r < 16; ++r) acc[r] = _mm512_setzero_ps();
       for (int kc = 0; kc < KC; ++kc) {
@@ -203,20 +231,6 @@ static bool have_avx512_bf16() {
   return ok;
 }
 
-// The table trick is exact when every scaled E2M1 value is a normal bf16 number: scale codes
-// 2..253 (0.5 * 2^-125 .. 6 * 2^126).  Other codes (including the NaN code 255) take the
-// scalar path, which follows the format definition for every code.
-static bool mx_scales_in_fast_range(const BlobLayout& L, const uint8_t* blob) {
-  for (int m = 0; m < 3; ++m) {
-    const uint8_t* s = blob + L.off[2 * m + 1];
-    const int R = m == 2 ? L.H : L.I, K = m == 2 ? L.I : L.H;
-    const uint64_t n = (uint64_t)(R / kTileRows) * (K / kTileK) * 64;
-    for (uint64_t i = 0; i < n; ++i)
-      if (s[i] < 2 || s[i] > 253) return false;
-  }
-  return true;
-}
-
 int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
                     const uint16_t* x, int T, float* y) {
   const int H = L.H, I = L.I;
@@ -231,7 +245,8 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
   const int RTg = I / kTileRows, RTd = H / kTileRows;
   const char* force_scalar = std::getenv("FT_HOST_SCALAR");
   const bool fast = L.fmt == FT_MXFP4 && have_avx512_bf16() &&
-                    !(force_scalar && *force_scalar == '1') && mx_scales_in_fast_range(L, blob);
+                    !(force_scalar && *force_scalar == '1');
+  for (size_t i = 0; i < xs.size(); ++i) xs[i] = bf16_to_f32(x[i]);
   if (fast) {
     auto part = [&](int n, int i, int total, int* a, int* b) {
       *a = (int)((int64_t)total * i / n);
@@ -240,26 +255,32 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
     auto job = [&](int i, int n) {
       int a, b;
       part(n, i, RTg, &a, &b);
-      gemv_tiles_mx_avx512(blob + L.off[0], blob + L.off[1], H, a, b, x, T, g.data(), I);
-      gemv_tiles_mx_avx512(blob + L.off[2], blob + L.off[3], H, a, b, x, T, u.data(), I);
+      gemv_tiles_mx_avx512(L, blob + L.off[0], blob + L.off[1], H, a, b, x, xs.data(), T,
+                           g.data(), I);
+      gemv_tiles_mx_avx512(L, blob + L.off[2], blob + L.off[3], H, a, b, x, xs.data(), T,
+                           u.data(), I);
+      // SwiGLU of this thread's rows
+      for (int t = 0; t < T; ++t)
+        for (int r = a * kTileRows; r < b * kTileRows; ++r) {
+          const size_t q = (size_t)t * I + r;
+          const float z = g[q];
+          const float hv = round_to_bf16(z / (1.0f + std::exp(-z)) * u[q]);
+          uint32_t bits;
+          std::memcpy(&bits, &hv, 4);
+          hb[q] = (uint16_t)(bits >> 16);
+          h[q] = hv;
+        }
     };
     if (pool) pool->run(job); else job(0, 1);
-    for (size_t i = 0; i < hb.size(); ++i) {
-      const float z = g[i];
-      const float hv = round_to_bf16(z / (1.0f + std::exp(-z)) * u[i]);
-      uint32_t bits;
-      std::memcpy(&bits, &hv, 4);
-      hb[i] = (uint16_t)(bits >> 16);
-    }
     auto job2 = [&](int i, int n) {
       int a, b;
       part(n, i, RTd, &a, &b);
-      gemv_tiles_mx_avx512(blob + L.off[4], blob + L.off[5], I, a, b, hb.data(), T, y, H);
+      gemv_tiles_mx_avx512(L, blob + L.off[4], blob + L.off[5], I, a, b, hb.data(), h.data(), T,
+                           y, H);
     };
     if (pool) pool->run(job2); else job2(0, 1);
     return FT_OK;
   }
-  for (size_t i = 0; i < xs.size(); ++i) xs[i] = bf16_to_f32(x[i]);
   auto part = [&](int n, int i, int total, int* a, int* b) {
     *a = (int)((int64_t)total * i / n);
     *b = (int)((int64_t)total * (i + 1) / n);
@@ -271,6 +292,11 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
                g.data(), I);
     gemv_tiles(L, blob + L.off[2], blob + L.off[3], H, a, b, xs.data(), T, hdr.tensor_scale[1],
                u.data(), I);
+    for (int t = 0; t < T; ++t)      // SwiGLU of this thread's rows
+      for (int r = a * kTileRows; r < b * kTileRows; ++r) {
+        const size_t q = (size_t)t * I + r;
+        h[q] = round_to_bf16(g[q] / (1.0f + std::exp(-g[q])) * u[q]);
+      }
   };
   auto job2 = [&](int i, int n) {
     int a, b;
@@ -279,10 +305,6 @@ int host_expert_ffn(ThreadPool* pool, const BlobLayout& L, const uint8_t* blob,
                y, H);
   };
   if (pool) pool->run(job); else job(0, 1);
-  for (size_t i = 0; i < h.size(); ++i) {
-    const float z = g[i];
-    h[i] = round_to_bf16(z / (1.0f + std::exp(-z)) * u[i]);
-  }
   if (pool) pool->run(job2); else job2(0, 1);
   return FT_OK;
 }

@@ -1,6 +1,7 @@
 // Host-side pieces of libft: error reporting, thread pool, host expert FFN, LRU policy.
 #pragma once
 
+#include <atomic>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -17,7 +18,10 @@ void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
 
 // Fixed set of worker threads; run(fn) calls fn(i, n) for i in [0, n) on the workers and the
-// calling thread (i = n - 1) and returns when all have finished.
+// calling thread (i = n - 1) and returns when all have finished.  Jobs are short (one expert's
+// FFN, a few blob reads) and come in bursts, so a worker spins for a while after each job
+// before it sleeps, and the caller spins for the workers to finish: a sleeping thread's
+// wake-up costs more than such a job's share.
 class ThreadPool {
  public:
   explicit ThreadPool(int n_threads);
@@ -30,11 +34,12 @@ class ThreadPool {
   int n_;
   std::vector<std::thread> threads_;
   std::mutex mu_;
-  std::condition_variable cv_, done_cv_;
+  std::condition_variable cv_;
   const std::function<void(int, int)>* job_ = nullptr;
-  uint64_t gen_ = 0;
-  int pending_ = 0;
-  bool stop_ = false;
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<int> pending_{0};
+  std::atomic<int> sleepers_{0};
+  std::atomic<bool> stop_{false};
 };
 
 // SwiGLU FFN of one expert blob on host cores: y[t] = W_d bf16(silu(W_g x_t) * (W_u x_t)),

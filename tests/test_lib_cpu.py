@@ -230,3 +230,25 @@ def test_ftw_rejects_bad_files(tmp_path):
     with pytest.raises(ft.FtError) as e:
         ft.ftw_write(str(tmp_path / "x.ftw"), "mxfp4", cfg.H, cfg.I, 3, 0, store, stride - 4096)
     assert e.value.code == ft.FT_EINVAL
+
+
+def test_host_expert_ffn_mixed_scale_ranges():
+    """A gate row tile holding E8M0 codes 0 and 1 (outside the range the AVX-512 table path
+    takes exactly) next to ordinary tiles: that tile goes to the scalar path, the rest stay
+    vectorised, and the whole FFN still matches the oracle."""
+    cfg = synth.small_config(seed=9, H=256, I=128, code_dist="normal")
+    ex = synth.gen_expert(cfg, 4)
+    ex.gate_scales = ex.gate_scales.copy()
+    ex.gate_scales[3, :] = 1          # row 3 of the gate: every block scale 2^-126
+    ex.gate_scales[20, 2] = 0         # one block of row 20 (another row tile): 2^-127
+    blob = ft.pack_expert("mxfp4", cfg.H, cfg.I, ex)
+    x = synth.gen_tokens(cfg, 2)
+    y = ft.host_expert_ffn("mxfp4", cfg.H, cfg.I, blob, x)
+
+    class _L:
+        pass
+    L = _L()
+    L.cfg = cfg
+    wg, wu, wd = moe.expert_weights(L, ex)
+    ref = moe.swiglu_ffn(fp4.bf16_bits_to_f64(x), wg, wu, wd)
+    assert moe.rel_l2(y, ref) <= 1e-3
