@@ -15,7 +15,7 @@
 //   k_perm_place      pos[t][j] = base + (tokens below t in the block's mask); the row of
 //                     every pair, expert ascending then token ascending (stable).
 //   k_ggemm<0>        per (expert, 128-token block, 64 gate + 64 up features): G, U on the
-//                     bf16 MFMA with NVFP4 weights decoded to bf16 in LDS (E2M1 x E4M3 has at
+//                     32x32x16 bf16 MFMA with NVFP4 weights decoded to bf16 in LDS (E2M1 x E4M3 has at
 //                     most 6 significant bits, so the decode is exact; the fp32 tensor scale
 //                     is applied in the epilogue), h = bf16(silu(ts_g G) * (ts_u U)).
 //   k_ggemm<1>        per (expert, token block, 128 rows of W_d): Y_perm = ts_d (W_d h).
@@ -477,7 +477,6 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
   __shared__ uint4 ws[8][4][64];               // 32 KB: [weight tile][k-step][lane]
   __shared__ int s_e;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, g = lane >> 4;
   const int Lb = blockIdx.x, xcd = Lb & 7, jj = Lb >> 3;
   const int gblk = xcd + 8 * (jj / NB), fb = jj % NB;
   const int G = a.tb_off[a.E];
@@ -520,16 +519,22 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
     wsc[d] = blob + a.L.off[2 * m + 1];
     wrow[d] = (uint64_t)rt * KC;
   }
-  // the wave's four weight tiles in the block tile (gate/up: two gate + the same two up)
-  int wt[4];
+  // the wave's two 32-row weight operands, each a pair of 16-row tiles of the block tile
+  // (gate/up: 32 gate rows and the same 32 up rows; down: 64 rows of W_d)
+  int wt[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wt[j] = MODE == 0 ? ((j < 2) ? 2 * wn + j : 4 + 2 * wn + j - 2) : 4 * wn + j;
+  for (int o = 0; o < 2; ++o) wt[o] = MODE == 0 ? (o == 0 ? 2 * wn : 4 + 2 * wn) : 4 * wn + 2 * o;
 
-  f32x4 acc[4][4];
+  // 32x32x16 bf16 MFMAs: acc[o][b] = weight operand o x token operand b (32 tokens each)
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int o = 0; o < 2; ++o)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[o][b][r] = 0.f;
+  // operand lanes: row (or token) lane % 32 of the operand, K half lane / 32
+  const int r32 = lane & 31, kh = lane >> 5, th = (lane >> 4) & 1;
 
   // software pipeline: the global loads of chunk kc + 1 (token tile rows and this wave's
   // two weight tiles) are in flight while the MFMAs of chunk kc run
@@ -566,35 +571,43 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
       for (int i = 0; i < 4; ++i) ws[2 * wave + d][i][lane] = dq[d][i];
     __syncthreads();
     if (kc + 1 < KC) load_chunk(kc + 1);
+    // MFMA step (p, i) covers the 8 K values 32 (2p + half) + 8i .. + 7 of each lane half:
+    // both operands use the same K order, which is all a dot product needs.  A weight lane
+    // (row r32, half kh) finds them in tile row r32 % 16 of tile wt + r32 / 16, K group
+    // 2p + kh: lane slot r32 % 16 + 16 (2p + kh) of the decoded tile.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x8 A[4], B[4];
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) A[j] = as_bf16x8(ws[wt[j]][i][lane]);
+      for (int i = 0; i < 4; ++i) {
+        uint4 A[2], B[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        B[t] = as_bf16x8(*(const uint4*)&xs[wm * 64 + t * 16 + n][32 * g + 8 * i]);
+        for (int o = 0; o < 2; ++o) A[o] = ws[wt[o] + th][i][(lane & 15) + 16 * (2 * p + kh)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int b = 0; b < 2; ++b)
+          B[b] = *(const uint4*)&xs[wm * 64 + b * 32 + r32][32 * (2 * p + kh) + 8 * i];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], B[t], acc[j][t], 0, 0, 0);
-    }
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[o][b] = mfma_bf16_32(A[o], B[b], acc[o][b]);
+      }
   }
 
+  // lane L holds token r32 of each token operand and, in registers 4q .. 4q + 3, weight
+  // rows 8q + 4 kh .. + 3 of each weight operand
   if (MODE == 0) {
     const float tsg = blob_tscale(blob, 0), tsu = blob_tscale(blob, 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = wm * 64 + t * 16 + n;
+    for (int b = 0; b < 2; ++b) {
+      const int row = wm * 64 + b * 32 + r32;
       if (row < nrows) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int f = fb * 64 + wn * 32 + j * 16 + 4 * g;
+        for (int q = 0; q < 4; ++q) {
+          const int f = fb * 64 + wn * 32 + 8 * q + 4 * kh;
           uint16_t hv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            hv[r] = f32_to_bf16_rne(silu_f32(acc[j][t][r] * tsg) * (acc[j + 2][t][r] * tsu));
+            hv[r] = f32_to_bf16_rne(silu_f32(acc[0][b][4 * q + r] * tsg) *
+                                    (acc[1][b][4 * q + r] * tsu));
           *(uint2*)(a.hperm + (uint64_t)(row0 + row) * a.I + f) =
               make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
                          (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
@@ -604,16 +617,18 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
   } else {
     const float tsd = blob_tscale(blob, 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = wm * 64 + t * 16 + n;
+    for (int b = 0; b < 2; ++b) {
+      const int row = wm * 64 + b * 32 + r32;
       if (row < nrows) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int f = fb * kGemmN + wn * 64 + j * 16 + 4 * g;
-          *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + f) =
-              make_float4(acc[j][t][0] * tsd, acc[j][t][1] * tsd, acc[j][t][2] * tsd,
-                          acc[j][t][3] * tsd);
-        }
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int f = fb * kGemmN + wn * 64 + o * 32 + 8 * q + 4 * kh;
+            *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + f) =
+                make_float4(acc[o][b][4 * q] * tsd, acc[o][b][4 * q + 1] * tsd,
+                            acc[o][b][4 * q + 2] * tsd, acc[o][b][4 * q + 3] * tsd);
+          }
       }
     }
   }
