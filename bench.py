@@ -81,6 +81,21 @@ def measured_traffic(key, kind):
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
+def read_reference(ctx, achieved):
+    """The same box's plain HBM read bandwidth (2 GiB streamed, far above the 256 MB Infinity
+    Cache) and the kernel's achieved bandwidth as a fraction of it."""
+    import torch
+
+    from mxfp4_expert_layer_amd import ft
+
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    v = ft.probe_hbm_read(ctx, buf, nbytes, reps=10)
+    del buf
+    return {"measured_read_GBps": v, "frac_of_measured_read": achieved / v if v > 0 else None}
+
+
 def cpu_baseline(cfg, x_batches, seconds):
     """Time the float64 oracle (as it stands) on decode steps of the same workload."""
     import numpy as np
@@ -217,7 +232,8 @@ def bench_decode(args, wl):
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"k_gateup@{args.workload}-T{T}", "decode"),
                      "kernel": "k_gateup", "kernel_us": gate_us, "timing": prof_mode,
-                     "bytes_per_launch": n_exp * gu_bytes_expert},
+                     "bytes_per_launch": n_exp * gu_bytes_expert,
+                     **read_reference(ctx, achieved)},
         "layer": {"algorithmic_bytes_per_step": step_bytes,
                   "GBps_per_step": step_bytes / step_s / 1e9,
                   "hbm_frac_per_step": step_bytes / step_s / 1e9 / HBM_PEAK_GBS,
@@ -500,7 +516,7 @@ def bench_prefill(args, wl):
                 "kernel": "k_s1_gemm<0> (gate/up + SwiGLU + MXFP4 quantise of h)",
                 "kernel_us": gu_us, "bytes_per_launch": by_gu, "flops_per_launch": fl_gu,
                 "fp4_mfma_tflops": gu_tf, "fp4_mfma_frac": gu_tf / FP4_PEAK_TFLOPS,
-                "timing": "dispatch-events"}
+                "timing": "dispatch-events", **read_reference(ctx, gbs)}
     else:
         roof = {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,

@@ -225,6 +225,15 @@ FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
  * layer and used by decode.
  */
 FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh);
+/*
+ * HBM read-bandwidth probe: a plain streaming read of `bytes` (>= 1 MiB, a multiple of 16) of
+ * device memory at buf, launched reps + 1 times (the first untimed) with 32 workgroups per
+ * compute unit; *GBps = bytes * reps / the timed span.  A buffer well above the 256 MB
+ * Infinity Cache measures HBM.  The reference against which kernels' achieved bandwidth is
+ * also quoted.  Blocks.  FT_EINVAL for bad arguments.
+ */
+FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t bytes, int reps,
+                             double* GBps);
 /* Override Bp and Bh (bytes/s, both > 0). */
 FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh);
 /* Force q for every later decode call (q >= 0, clamped to m), or restore the rule (q < 0). */

