@@ -546,3 +546,26 @@ def test_disk_tier_matches_oracle(ctx, tmp_path, fmt):
         f.close()
     assert reads > n_ram, reads          # the tier was refilled from disk
     log(f"[gpu] disk tier {fmt}: {reads} blob reads over 24 calls")
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_decode_more_than_256_experts(ctx, T):
+    """E = 300 (> 256): the top-k paths for wide expert sets (16 logits per lane), resident
+    decode at T = 1, 3 and 8 and ft_route against the oracle."""
+    cfg = synth.small_config("wide300", seed=301, H=256, I=128, E=300, k=8, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 16)
+    L = layer_for(ctx, "wide300", cfg=cfg, max_tokens=16)
+    OL = L.oracle_layer()
+    x = synth.gen_tokens(cfg, T, batch=31 + T)
+    idx, w = run_route(ctx, L, x)
+    ref = moe.moe_forward(OL, x)
+    check_routing(idx, w, ref)
+    check_output(run_decode(ctx, L, x), ref["y"], f"E=300 T={T}")
+
+
+def test_miss_path_more_than_256_experts(ctx):
+    """The one-launch miss-path routing with 16 logits per lane (E = 300), tables bit-exact."""
+    cfg = synth.small_config("wide300m", seed=302, H=256, I=128, E=300, k=8, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 16, zipf_c=0.9)
+    L = layer_for(ctx, "wide300m", cfg=cfg, resident=False, n_slots=20, max_tokens=2)
+    _miss_sequence(ctx, L, steps=12, bp=1.0, bh=2.5, check_every=3, T=2)

@@ -124,6 +124,7 @@ SMALL = [
     ("pf_nv_b", synth.NVFP4, 1024, 384, 37, 5, 777),
     ("pf_mx_a", synth.MXFP4, 768, 512, 20, 4, 513),
     ("pf_nv_one", synth.NVFP4, 256, 128, 6, 2, 1),
+    ("pf_mx_wide", synth.MXFP4, 256, 128, 300, 8, 200),   # E > 256: two router expert groups
 ]
 
 
