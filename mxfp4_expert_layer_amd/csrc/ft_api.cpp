@@ -640,7 +640,8 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   }
   ra.counter = l->route_counter;
   ra.flag_host = (uint32_t*)dev_of(l->route_flag_h);
-  ra.seq = ++l->route_seq;
+  if (++l->route_seq == 0) ++l->route_seq;   // 0 is the flag's initial value
+  ra.seq = l->route_seq;
   HIP_TRY((hipError_t)ftk_route_small(&ra, st));
   HIP_TRY(hipEventRecord(l->ev_route, st));
   HIP_TRY(wait_route(l->route_flag_h, ra.seq, l->ev_route));

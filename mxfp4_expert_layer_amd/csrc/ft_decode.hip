@@ -271,6 +271,10 @@ struct ListLds {
 __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int k, int n_shared,
                                            const int32_t* e2s, ListLds& L) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // this thread's four experts' slots, loaded first so the load overlaps the steps below
+  int slot4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) slot4[i] = e2s[min(tid * 4 + i, E - 1)];
   for (int e = tid; e < E; e += 256) L.tokmask[e] = 0u;
   __syncthreads();
   if (tid < T * k) atomicOr(&L.tokmask[tk.idx[tid / k][tid % k]], 1u << (tid / k));
@@ -281,16 +285,18 @@ __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int 
     const int ee = tid * 4 + i;
     has[i] = ee < E ? (L.tokmask[ee] != 0u) : 0;
   }
-  const int mine = has[0] + has[1] + has[2] + has[3];
-  int incl = mine;
+  // experts of lower lanes in this wave: one ballot per position
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int excl = 0, wtot = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int nb = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += nb;
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t b = __ballot(has[i]);
+    excl += __popcll(b & below);
+    wtot += __popcll(b);
   }
-  if (lane == 63) L.wave_tot[wave] = incl;
+  if (lane == 0) L.wave_tot[wave] = wtot;
   __syncthreads();
-  int base = incl - mine;
+  int base = excl;
   for (int w2 = 0; w2 < wave; ++w2) base += L.wave_tot[w2];
   const int n_routed = L.wave_tot[0] + L.wave_tot[1] + L.wave_tot[2] + L.wave_tot[3];
 #pragma unroll
@@ -299,7 +305,7 @@ __device__ __forceinline__ void build_list(const TopkLds& tk, int T, int E, int 
     if (has[i]) {
       L.pos[ee] = base;
       L.expert[base] = ee;
-      L.slot[base] = e2s[ee];
+      L.slot[base] = slot4[i];
       L.ntok[base] = __popc(L.tokmask[ee]);
       ++base;
     }
