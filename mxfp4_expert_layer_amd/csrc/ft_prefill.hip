@@ -569,8 +569,9 @@ __global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
     for (int d = 0; d < 2; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ws[2 * wave + d][i][lane] = dq[d][i];
-    __syncthreads();
+    // the registers are in LDS now: the next chunk's loads go out before the barrier
     if (kc + 1 < KC) load_chunk(kc + 1);
+    __syncthreads();
     // MFMA step (p, i) covers the 8 K values 32 (2p + half) + 8i .. + 7 of each lane half:
     // both operands use the same K order, which is all a dot product needs.  A weight lane
     // (row r32, half kh) finds them in tile row r32 % 16 of tile wt + r32 / 16, K group
