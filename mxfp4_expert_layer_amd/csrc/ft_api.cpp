@@ -1094,6 +1094,23 @@ extern "C" FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t b
   return FT_OK;
 }
 
+extern "C" FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us) {
+  if (threads < 1 || threads > 256 || jobs < 0 || pause_us < 0)
+    return fail(FT_EINVAL, "ft_debug_pool_stress: bad argument");
+  ThreadPool pool(threads);
+  std::vector<std::atomic<int>> hits((size_t)threads);
+  for (int j = 0; j < jobs; ++j) {
+    for (auto& h : hits) h.store(0);
+    pool.run([&](int i, int n) {
+      if (n == threads && i >= 0 && i < n) hits[(size_t)i].fetch_add(1);
+    });
+    for (auto& h : hits)
+      if (h.load() != 1) return fail(FT_ESTATE, "ft_debug_pool_stress: a worker missed or repeated a job");
+    if (pause_us) std::this_thread::sleep_for(std::chrono::microseconds(pause_us));
+  }
+  return FT_OK;
+}
+
 // ---- kernel timing ------------------------------------------------------------------------
 extern "C" FT_API int ft_profile_begin(ft_layer* layer, int n) {
   if (!layer || n < 0 || n > 1000000) return fail(FT_EINVAL, "ft_profile_begin: bad argument");

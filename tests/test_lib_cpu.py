@@ -252,3 +252,12 @@ def test_host_expert_ffn_mixed_scale_ranges():
     wg, wu, wd = moe.expert_weights(L, ex)
     ref = moe.swiglu_ffn(fp4.bf16_bits_to_f64(x), wg, wu, wd)
     assert moe.rel_l2(y, ref) <= 1e-3
+
+
+@pytest.mark.parametrize("threads,jobs,pause_us", [(8, 400, 0), (8, 40, 1500), (1, 10, 0),
+                                                   (16, 25, 700)])
+def test_host_thread_pool_runs_every_job_once(threads, jobs, pause_us):
+    """The spin-then-sleep pool: back-to-back jobs (workers spinning) and jobs after pauses
+    longer than the spin (workers asleep, woken by the next job) each run every index once;
+    a lost wake-up would hang here (the test has a timeout)."""
+    ft.check(ft.lib.ft_debug_pool_stress(threads, jobs, pause_us))
