@@ -219,10 +219,11 @@ FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
 
 /*
  * Startup probes: Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
- * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.
- * Needs host_blobs, or a disk tier not yet used by a decode call (the probe then reads
- * experts 0 and 1 into its first host-memory slots).  Blocks.  The values are stored in the
- * layer and used by decode.
+ * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.  The
+ * repetitions cycle over up to 8 distinct blobs, more than a host cache holds, as decode
+ * reads them.  Needs host_blobs, or a disk tier not yet used by a decode call (the probe then
+ * reads experts 0..7 into its first host-memory slots).  Blocks.  The values are stored in
+ * the layer and used by decode.
  */
 FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh);
 /*

@@ -1006,21 +1006,29 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   if (!ctx || !layer) return fail(FT_EINVAL, "ft_measure_bandwidth: null argument");
   const ft_layer_desc& d = layer->d;
   HIP_TRY(hipSetDevice(ctx->device));
-  // probe sources: two host blobs, from host_blobs or read into the first slots of a disk
-  // tier that no decode call has used yet
-  const uint8_t* srcs[2];
+  // probe sources: up to 8 distinct host blobs (more bytes than a host's last-level cache
+  // holds, so the host FFN reads DRAM as it does in decode), from host_blobs or read into the
+  // first slots of a disk tier that no decode call has used yet
+  constexpr int kProbeBlobs = 8;
+  const uint8_t* srcs[kProbeBlobs];
+  int nsrc = 0;
   if (d.host_blobs) {
-    for (int i = 0; i < 2; ++i)
-      srcs[i] = (const uint8_t*)d.host_blobs + (uint64_t)(i % d.E) * d.blob_stride;
+    nsrc = std::min(kProbeBlobs, d.E);
+    for (int i = 0; i < nsrc; ++i)
+      srcs[i] = (const uint8_t*)d.host_blobs + (uint64_t)i * d.blob_stride;
   } else if (layer->ftw) {
     for (int32_t e : layer->ram_lru.s2e)
       if (e >= 0) return fail(FT_ESTATE, "ft_measure_bandwidth: the disk tier is already in use");
-    int32_t ids[2] = {0, d.E > 1 ? 1 : 0};
-    uint8_t* dst[2] = {layer->ram, layer->ram + (layer->n_ram > 1 ? d.blob_stride : 0)};
-    const int rc = ftw_read(ctx->pool.get(), layer->ftw, ids, layer->n_ram > 1 ? 2 : 1, dst, 0);
+    nsrc = std::min(kProbeBlobs, std::min(layer->n_ram, d.E));
+    int32_t ids[kProbeBlobs];
+    uint8_t* dst[kProbeBlobs];
+    for (int i = 0; i < nsrc; ++i) {
+      ids[i] = i;
+      dst[i] = layer->ram + (uint64_t)i * d.blob_stride;
+    }
+    const int rc = ftw_read(ctx->pool.get(), layer->ftw, ids, nsrc, dst, 1u << 20);
     if (rc) return rc;
-    srcs[0] = dst[0];
-    srcs[1] = dst[1];
+    for (int i = 0; i < nsrc; ++i) srcs[i] = dst[i];
   } else {
     return fail(FT_ESTATE, "ft_measure_bandwidth: the layer has neither host_blobs nor a disk tier");
   }
@@ -1034,7 +1042,7 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   std::vector<double> bps;
   const int reps = env_int("FT_PROBE_REPS", 7);
   for (int r = 0; r < reps + 1; ++r) {
-    const uint8_t* src = srcs[r % 2];
+    const uint8_t* src = srcs[r % nsrc];
     hipEventRecord(a, ctx->copy_stream);
     hipMemcpyAsync(tmp, src, bytes, hipMemcpyHostToDevice, ctx->copy_stream);
     hipEventRecord(b, ctx->copy_stream);
@@ -1050,7 +1058,7 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   std::vector<uint16_t> x(d.H, 0x3f80);  // ones
   std::vector<float> y(d.H);
   for (int r = 0; r < reps + 1; ++r) {
-    const uint8_t* src = srcs[(r + 1) % 2];
+    const uint8_t* src = srcs[(r + 1) % nsrc];
     auto t0 = clk::now();
     int rc = host_expert_ffn(ctx->pool.get(), layer->L, src, x.data(), 1, y.data());
     if (rc) return rc;
