@@ -536,7 +536,11 @@ def bench_prefill(args, wl):
                   "fp4_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / FP4_PEAK_TFLOPS,
                   "bf16_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / BF16_PEAK_TFLOPS,
                   "down_kernel_us": dn_us,
-                  "down_TFLOPs": fl_dn / (dn_us * 1e-6) / 1e12},
+                  "down_TFLOPs": fl_dn / (dn_us * 1e-6) / 1e12,
+                  # algorithmic FLOPs over the two grouped GEMMs' summed kernel time
+                  "grouped_gemm_TFLOPs": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12,
+                  "grouped_gemm_peak_frac": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12
+                  / (FP4_PEAK_TFLOPS if s1 else BF16_PEAK_TFLOPS)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
