@@ -113,21 +113,31 @@ def cpu_baseline(cfg, x_batches, seconds):
         for e in np.unique(idx):
             OL.expert(int(e))
         todo.append(xb)
-    t0 = time.perf_counter()
-    tokens = 0
-    while True:
-        xb = todo[n % len(todo)]
-        moe.moe_forward(OL, xb)
-        tokens += xb.shape[0]
-        n += 1
-        if time.perf_counter() - t0 >= seconds or n >= 4096:
-            break
-    dt = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+
+    def timed(budget):
+        t0 = time.perf_counter()
+        tokens = steps = 0
+        while True:
+            xb = todo[steps % len(todo)]
+            moe.moe_forward(OL, xb)
+            tokens += xb.shape[0]
+            steps += 1
+            if time.perf_counter() - t0 >= budget or steps >= 4096:
+                break
+        return tokens, steps, time.perf_counter() - t0
+
+    tokens, n, dt = timed(seconds)
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    # the same oracle on one thread (a third of the time budget)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t1, n1, dt1 = timed(seconds / 3)
     return {"value": tokens / dt, "unit": "tokens/s", "cores": max(blas) if blas else 1,
             "kind": "oracle",
             "sample": f"{n} steps of {x_batches[0].shape[0]} token(s) ({tokens} tokens) of the "
-                      f"same workload, float64 numpy oracle, {dt:.1f} s"}
+                      f"same workload, float64 numpy oracle, {dt:.1f} s",
+            "single_thread": {"value": t1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} steps ({t1} tokens), {dt1:.1f} s"}}
 
 
 def bench_decode(args, wl):
