@@ -569,3 +569,12 @@ def test_miss_path_more_than_256_experts(ctx):
                              code_dist="normal", router_sigma=1 / 16, zipf_c=0.9)
     L = layer_for(ctx, "wide300m", cfg=cfg, resident=False, n_slots=20, max_tokens=2)
     _miss_sequence(ctx, L, steps=12, bp=1.0, bh=2.5, check_every=3, T=2)
+
+
+def test_miss_path_sixteen_tokens(ctx):
+    """The miss path at its largest call (T = 16): the one-launch routing with 16 token rows,
+    long work lists, host experts with up to 16 token columns; tables bit-exact each call."""
+    cfg = synth.small_config("miss16", seed=87, H=384, I=256, E=24, k=4, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 20, zipf_c=0.6)
+    L = layer_for(ctx, "miss16", cfg=cfg, resident=False, n_slots=10, max_tokens=16)
+    _miss_sequence(ctx, L, steps=10, bp=1.0, bh=2.0, check_every=2, T=16)
