@@ -244,7 +244,6 @@ extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
     hipStreamSynchronize(ctx->copy_stream);
     hipStreamDestroy(ctx->copy_stream);
   }
-
   delete ctx;
   return FT_OK;
 }
@@ -1036,24 +1035,26 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   void* tmp = nullptr;
   if (hipMalloc(&tmp, bytes) != hipSuccess)
     return fail(FT_ENOMEM, "ft_measure_bandwidth: probe buffer allocation failed");
-  hipEvent_t a, b;
-  HIP_TRY(hipEventCreate(&a));
-  HIP_TRY(hipEventCreate(&b));
+  hipEvent_t a = nullptr, b = nullptr;
   std::vector<double> bps;
   const int reps = env_int("FT_PROBE_REPS", 7);
-  for (int r = 0; r < reps + 1; ++r) {
+  hipError_t he = hipEventCreate(&a);
+  if (he == hipSuccess) he = hipEventCreate(&b);
+  for (int r = 0; r < reps + 1 && he == hipSuccess; ++r) {
     const uint8_t* src = srcs[r % nsrc];
-    hipEventRecord(a, ctx->copy_stream);
-    hipMemcpyAsync(tmp, src, bytes, hipMemcpyHostToDevice, ctx->copy_stream);
-    hipEventRecord(b, ctx->copy_stream);
-    hipEventSynchronize(b);
+    he = hipEventRecord(a, ctx->copy_stream);
+    if (he == hipSuccess) he = hipMemcpyAsync(tmp, src, bytes, hipMemcpyHostToDevice, ctx->copy_stream);
+    if (he == hipSuccess) he = hipEventRecord(b, ctx->copy_stream);
+    if (he == hipSuccess) he = hipEventSynchronize(b);
     float ms = 0.f;
-    hipEventElapsedTime(&ms, a, b);
-    if (r > 0 && ms > 0.f) bps.push_back((double)bytes / (ms * 1e-3));
+    if (he == hipSuccess) he = hipEventElapsedTime(&ms, a, b);
+    if (he == hipSuccess && r > 0 && ms > 0.f) bps.push_back((double)bytes / (ms * 1e-3));
   }
-  hipEventDestroy(a);
-  hipEventDestroy(b);
-  hipFree(tmp);
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  (void)hipFree(tmp);
+  if (he != hipSuccess)
+    return fail(FT_EHIP, std::string("ft_measure_bandwidth: ") + hipGetErrorString(he));
   std::vector<double> bhs;
   std::vector<uint16_t> x(d.H, 0x3f80);  // ones
   std::vector<float> y(d.H);
