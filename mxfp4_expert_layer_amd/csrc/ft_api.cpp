@@ -590,7 +590,7 @@ static int host_tier_step(ft_ctx* ctx, ft_layer* l, const std::vector<int>& need
   HIP_TRY(hipEventSynchronize(l->ev_copy));
   const auto t0 = clk::now();
   // 1 MiB requests spread over the host threads: a whole-blob request is one queue entry,
-  // and small requests pay per-request costs (measured on the box: 1 MiB direct reads move
+  // and small requests pay per-request costs (measured on an MI355X host: 1 MiB direct reads move
   // 7.1 GB/s, 64 KiB 4.8 GB/s, 4 KiB 0.7 GB/s)
   const int rc = ftw_read(ctx->pool.get(), l->ftw, ids.data(), (int)ids.size(), dst.data(),
                           1u << 20);

@@ -62,7 +62,7 @@ extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix,
 
 // HBM read-bandwidth probe: every lane streams 16-byte loads over the buffer (grid-stride,
 // eight loads in flight) and folds them into one word, so nothing is dead code.  A sweep on
-// the box (1K-16K workgroups, 4-16 loads in flight) peaked at 32 workgroups per compute unit
+// an MI355X (1K-16K workgroups, 4-16 loads in flight) peaked at 32 workgroups per compute unit
 // and eight loads: 5.8 TB/s.
 __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, uint64_t n16,
                                                     uint32_t* __restrict__ sink) {
