@@ -82,7 +82,7 @@ def measured_traffic(key, kind):
 
 
 def read_reference(ctx, achieved):
-    """The same box's plain HBM read bandwidth (2 GiB streamed, far above the 256 MB Infinity
+    """This machine's plain HBM read bandwidth (2 GiB streamed, far above the 256 MB Infinity
     Cache) and the kernel's achieved bandwidth as a fraction of it."""
     import torch
 
