@@ -261,3 +261,34 @@ def test_host_thread_pool_runs_every_job_once(threads, jobs, pause_us):
     longer than the spin (workers asleep, woken by the next job) each run every index once;
     a lost wake-up would hang here (the test has a timeout)."""
     ft.check(ft.lib.ft_debug_pool_stress(threads, jobs, pause_us))
+
+
+def test_null_arguments_return_einval():
+    """Every entry point that takes an object rejects a null one with FT_EINVAL (and touches
+    no GPU doing so)."""
+    L = ft.lib
+    calls = [
+        lambda: L.ft_set_prefetch(None, None, 0),
+        lambda: L.ft_set_miss_policy(None, 0, 0.0),
+        lambda: L.ft_set_bandwidth(None, 1.0, 1.0),
+        lambda: L.ft_force_q(None, 0),
+        lambda: L.ft_layer_set_disk_tier(None, None, None, 0),
+        lambda: L.ft_debug_host_tier(None, None, None),
+        lambda: L.ft_debug_tables(None, None, None),
+        lambda: L.ft_residual_bf16(None, None, None, 1.0, 1, None, None),
+        lambda: L.ft_probe_hbm_read(None, None, 1 << 20, 1, None),
+        lambda: L.ft_ftw_open(None, 0, None),
+        lambda: L.ft_ftw_get_info(None, None),
+        lambda: L.ft_ftw_read(None, None, None, 1, None, 0, 0, None),
+        lambda: L.ft_ftw_write(None, 0, 256, 128, 1, 0, None, 0),
+        lambda: L.ft_moe_decode(None, None, None, 1, None, None, None),
+        lambda: L.ft_route(None, None, None, 1, None, None, None),
+        lambda: L.ft_layer_create(None, None, None),
+        lambda: L.ft_measure_bandwidth(None, None, None, None),
+        lambda: L.ft_debug_pool_stress(0, 1, 0),
+    ]
+    for i, c in enumerate(calls):
+        assert c() == ft.FT_EINVAL, i
+    # destroying nothing is a no-op
+    assert L.ft_layer_destroy(None) == ft.FT_OK and L.ft_ctx_destroy(None) == ft.FT_OK
+    assert L.ft_ftw_close(None) == ft.FT_OK
