@@ -83,7 +83,8 @@ def measured_traffic(key, kind):
 
 def read_reference(ctx, achieved):
     """This machine's plain HBM read bandwidth (2 GiB streamed, far above the 256 MB Infinity
-    Cache) and the kernel's achieved bandwidth as a fraction of it."""
+    Cache; the faster of the library probe's register-load and LDS-copy forms) and the
+    kernel's achieved bandwidth as a fraction of it."""
     import torch
 
     from mxfp4_expert_layer_amd import ft

@@ -228,10 +228,12 @@ FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
 FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh);
 /*
  * HBM read-bandwidth probe: a plain streaming read of `bytes` (>= 1 MiB, a multiple of 16) of
- * device memory at buf, launched reps + 1 times (the first untimed) with 32 workgroups per
- * compute unit; *GBps = bytes * reps / the timed span.  A buffer well above the 256 MB
- * Infinity Cache measures HBM.  The reference against which kernels' achieved bandwidth is
- * also quoted.  Blocks.  FT_EINVAL for bad arguments.
+ * device memory at buf in two forms, each launched reps + 1 times (the first untimed):
+ * 16-byte register loads by 32 workgroups per compute unit, and direct global -> LDS copies
+ * of 1 KB blocks by one workgroup per compute unit.  *GBps = bytes * reps / the timed span
+ * of the faster form.  A buffer well above the 256 MB Infinity Cache measures HBM.  The
+ * reference against which kernels' achieved bandwidth is also quoted.  Blocks.  FT_EINVAL
+ * for bad arguments.
  */
 FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t bytes, int reps,
                              double* GBps);

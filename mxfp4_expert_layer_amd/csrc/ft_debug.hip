@@ -60,10 +60,10 @@ extern "C" int ftk_dequant(const uint8_t* blob, const BlobLayout* L, int matrix,
   return (int)hipGetLastError();
 }
 
-// HBM read-bandwidth probe: every lane streams 16-byte loads over the buffer (grid-stride,
-// eight loads in flight) and folds them into one word, so nothing is dead code.  A sweep on
-// an MI355X (1K-16K workgroups, 4-16 loads in flight) peaked at 32 workgroups per compute unit
-// and eight loads: 5.8 TB/s.
+// HBM read-bandwidth probes.  k_read_probe: every lane streams 16-byte loads over the buffer
+// (grid-stride, eight loads in flight) and folds them into one word, so nothing is dead code; a
+// sweep on an MI355X (1K-16K workgroups, 4-16 loads in flight) peaked at 32 workgroups per
+// compute unit and eight loads: 5.8 TB/s.
 __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, uint64_t n16,
                                                     uint32_t* __restrict__ sink) {
   const uint64_t stride = (uint64_t)gridDim.x * 256;
@@ -83,9 +83,38 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   if (acc == 0x9e3779b9u) atomicXor(&sink[blockIdx.x], acc);   // practically never taken
 }
 
+// k_read_probe_lds: one workgroup per compute unit (its 128 KB of LDS keeps a second one off)
+// whose waves copy 1 KB blocks of the buffer (grid-stride over waves) into LDS with the direct
+// global -> LDS load, up to 33 blocks in flight per wave and no register holding data.  On an
+// MI355X this reaches 6.4-6.5 TB/s where the register loads above stop at 5.8 (more workgroups
+// per CU lower both).  The tail below 1 KB is read by plain loads of workgroup 0.
+__global__ __launch_bounds__(256) void k_read_probe_lds(const uint8_t* __restrict__ p,
+                                                        uint64_t bytes, uint32_t* __restrict__ sink) {
+  __shared__ uint4 ring[8192];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t n1k = bytes >> 10, nw = (uint64_t)gridDim.x * 4;
+  uint64_t i = (uint64_t)blockIdx.x * 4 + wave;
+  for (int k = 0; i < n1k; i += nw, ++k) {
+    dma16(p + i * 1024 + lane * 16, &ring[(wave * 32 + (k & 31)) * 64]);
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(32));
+  }
+  __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
+  uint32_t acc = 0;
+  if (blockIdx.x == 0)
+    for (uint64_t o = (n1k << 10) + 16 * threadIdx.x; o + 16 <= bytes; o += 16 * 256) {
+      const uint4 a = *(const uint4*)(p + o);
+      acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+  if (acc == 0x9e3779b9u) atomicXor(&sink[blockIdx.x], acc);   // practically never taken
+}
+
 extern "C" int ftk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int grid,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
-                     sink);
+                              int lds_form, hipStream_t st) {
+  if (lds_form)
+    hipLaunchKernelGGL(k_read_probe_lds, dim3(grid), dim3(256), 0, st, (const uint8_t*)buf, bytes,
+                       sink);
+  else
+    hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
+                       sink);
   return (int)hipGetLastError();
 }

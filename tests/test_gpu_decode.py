@@ -578,3 +578,16 @@ def test_miss_path_sixteen_tokens(ctx):
                              code_dist="normal", router_sigma=1 / 20, zipf_c=0.6)
     L = layer_for(ctx, "miss16", cfg=cfg, resident=False, n_slots=10, max_tokens=16)
     _miss_sequence(ctx, L, steps=10, bp=1.0, bh=2.0, check_every=2, T=16)
+
+
+@pytest.mark.parametrize("nbytes", [(1 << 20), (1 << 20) + 16, (3 << 20) + 1008])
+def test_hbm_read_probe(ctx, nbytes):
+    """The read probe over buffers that are and are not whole 1 KB blocks (the LDS form reads
+    the tail with register loads): a finite positive rate, and bad sizes are refused."""
+    log(f"[gpu] read probe over {nbytes} bytes")
+    buf = torch.ones((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+    v = ft.probe_hbm_read(ctx, buf, nbytes, reps=2)
+    torch.cuda.synchronize()
+    assert np.isfinite(v) and v > 0
+    with pytest.raises(ft.FtError):
+        ft.probe_hbm_read(ctx, buf, nbytes - 8, reps=1)
