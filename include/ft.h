@@ -28,7 +28,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is enqueued on it
  *     asynchronously unless stated otherwise; outputs are valid after the stream syncs.
  *   - bf16 values are passed as uint16_t bit patterns.
- *   - Calls on one layer must be serialised by the caller.
+ *   - Calls on one layer must be serialised by the caller.  An all-resident layer's calls
+ *     also share its device scratch: issue them on one stream, or synchronise between calls
+ *     made on different streams.  (A call that takes the miss path waits for the previous
+ *     call's device work itself.)
  */
 #ifndef FT_H
 #define FT_H

@@ -606,6 +606,10 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   ft_decode_stats S{};
   if (!l->ftw && !d.host_blobs)
     return fail(FT_ESTATE, "ft_moe_decode: the layer has neither host_blobs nor a disk tier");
+  // checked before anything runs, so a refused call leaves the pool untouched
+  if (l->bp <= 0.0 || l->bh <= 0.0)
+    return fail(FT_ESTATE, "ft_moe_decode: Bp/Bh unknown; call ft_measure_bandwidth or "
+                           "ft_set_bandwidth first");
   auto t0 = clk::now();
   // routing in one launch, written straight into the mapped pinned staging: the layer's own
   // and, for a linked next layer, that layer's router on the same input (the prediction)
@@ -641,6 +645,9 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   ra.flag_host = (uint32_t*)dev_of(l->route_flag_h);
   if (++l->route_seq == 0) ++l->route_seq;   // 0 is the flag's initial value
   ra.seq = l->route_seq;
+  // the previous call's device work (perhaps on another stream) still reads this layer's
+  // pinned staging, which the host rewrites once this routing is back
+  HIP_TRY(hipStreamWaitEvent(st, l->ev_done, 0));
   HIP_TRY((hipError_t)ftk_route_small(&ra, st));
   HIP_TRY(hipEventRecord(l->ev_route, st));
   HIP_TRY(wait_route(l->route_flag_h, ra.seq, l->ev_route));
@@ -676,9 +683,6 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
   const int m = (int)misses.size();
   int q = 0;
   double qstar = 0.0;
-  if (l->bp <= 0.0 || l->bh <= 0.0)
-    return fail(FT_ESTATE, "ft_moe_decode: Bp/Bh unknown; call ft_measure_bandwidth or "
-                           "ft_set_bandwidth first");
   // the previous call's streamed copies have finished by now (its kernels waited for them
   // before the routing of this call ran): their copy time gives an observation of Bp
   if (l->pend_copy_bytes > 0 && hipEventQuery(l->ev_cp1) == hipSuccess) {

@@ -591,3 +591,27 @@ def test_hbm_read_probe(ctx, nbytes):
     assert np.isfinite(v) and v > 0
     with pytest.raises(ft.FtError):
         ft.probe_hbm_read(ctx, buf, nbytes - 8, reps=1)
+
+
+def test_miss_path_alternating_streams(ctx):
+    """Miss-path calls on one layer alternate between two streams with no host wait between
+    them: each call orders its device work after the previous call's (which still reads the
+    layer's pinned staging), so every output matches the oracle."""
+    cfg = synth.small_config("missstreams", seed=91, H=384, I=256, E=16, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 20, zipf_c=0.7)
+    L = layer_for(ctx, "missstreams", cfg=cfg, resident=False, n_slots=5, max_tokens=2)
+    OL = L.oracle_layer()
+    ft.set_bandwidth(L.handle, 1.0, 2.5)
+    ft.force_q(L.handle, -1)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    xs = [synth.gen_tokens(cfg, 2, batch=300 + s) for s in range(12)]
+    xd = [to_dev(x) for x in xs]
+    ys = [torch.empty((2, cfg.H), dtype=torch.float32, device="cuda") for _ in xs]
+    torch.cuda.synchronize()
+    for s in range(len(xs)):
+        ft.moe_decode(ctx, L.handle, xd[s], 2, ys[s], streams[s % 2].cuda_stream, None)
+    torch.cuda.synchronize()
+    for s, x in enumerate(xs):
+        _, _, _, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+        assert np.all(gap >= 1e-6), "near-tie; choose another seed"
+        check_output(ys[s].cpu().numpy(), moe.moe_forward(OL, x)["y"], f"alternating step {s}")
