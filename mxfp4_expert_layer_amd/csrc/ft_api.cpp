@@ -159,13 +159,13 @@ static bool dims_ok(int format, int H, int I) {
          I % kTileK == 0;
 }
 
-extern "C" FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes) {
+extern "C" FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes) try {
   if (!bytes || !dims_ok(format, H, I))
     return fail(FT_EINVAL, "ft_blob_bytes: format must be FT_MXFP4/FT_NVFP4 and H, I positive "
                            "multiples of 128");
   *bytes = blob_layout(format, H, I).bytes;
   return FT_OK;
-}
+} FT_CATCH("ft_blob_bytes")
 
 static void pack_matrix(int fmt, int R, int K, const uint8_t* codes, const uint8_t* scales,
                         uint8_t* dst_codes, uint8_t* dst_scales) {
@@ -194,7 +194,7 @@ static void pack_matrix(int fmt, int R, int K, const uint8_t* codes, const uint8
 extern "C" FT_API int ft_pack_expert(int format, int H, int I, const uint8_t* gc,
                                      const uint8_t* gs, const uint8_t* uc, const uint8_t* us,
                                      const uint8_t* dc, const uint8_t* ds,
-                                     const float* tensor_scales, void* blob) {
+                                     const float* tensor_scales, void* blob) try {
   if (!dims_ok(format, H, I)) return fail(FT_EINVAL, "ft_pack_expert: bad format or sizes");
   if (!gc || !gs || !uc || !us || !dc || !ds || !blob)
     return fail(FT_EINVAL, "ft_pack_expert: null pointer");
@@ -217,10 +217,10 @@ extern "C" FT_API int ft_pack_expert(int format, int H, int I, const uint8_t* gc
   pack_matrix(format, I, H, uc, us, b + L.off[2], b + L.off[3]);
   pack_matrix(format, H, I, dc, ds, b + L.off[4], b + L.off[5]);
   return FT_OK;
-}
+} FT_CATCH("ft_pack_expert")
 
 // ---- context ----------------------------------------------------------------------------------
-extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) {
+extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) try {
   if (!out) return fail(FT_EINVAL, "ft_ctx_create: out is null");
   int n = 0;
   HIP_TRY(hipGetDeviceCount(&n));
@@ -235,9 +235,9 @@ extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) {
   c->pool.reset(new ThreadPool(std::max(1, nt)));
   *out = c.release();
   return FT_OK;
-}
+} FT_CATCH("ft_ctx_create")
 
-extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
+extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) try {
   if (!ctx) return FT_OK;
   if (ctx->copy_stream) {
     hipSetDevice(ctx->device);
@@ -246,7 +246,7 @@ extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) {
   }
   delete ctx;
   return FT_OK;
-}
+} FT_CATCH("ft_ctx_destroy")
 
 // ---- layer ------------------------------------------------------------------------------------
 template <class T>
@@ -273,7 +273,7 @@ static void free_layer(ft_layer* l) {
   delete l;
 }
 
-extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** out) {
+extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** out) try {
   if (!ctx || !desc || !out) return fail(FT_EINVAL, "ft_layer_create: null argument");
   const ft_layer_desc& d = *desc;
   if (!dims_ok(d.format, d.H, d.I)) return fail(FT_EINVAL, "ft_layer_create: bad format or H/I");
@@ -399,9 +399,9 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipEventRecord(l->ev_copy, nullptr));
   *out = l.release();
   return FT_OK;
-}
+} FT_CATCH("ft_layer_create")
 
-extern "C" FT_API int ft_layer_destroy(ft_layer* layer) {
+extern "C" FT_API int ft_layer_destroy(ft_layer* layer) try {
   if (!layer) return FT_OK;
   hipSetDevice(layer->ctx->device);
   hipDeviceSynchronize();
@@ -413,7 +413,7 @@ extern "C" FT_API int ft_layer_destroy(ft_layer* layer) {
   if (layer->next && layer->next->prev == layer) layer->next->prev = nullptr;
   free_layer(layer);
   return FT_OK;
-}
+} FT_CATCH("ft_layer_destroy")
 
 // ---- routing / decode ---------------------------------------------------------------------
 static int check_call(const ft_ctx* ctx, const ft_layer* layer, const void* x, int T,
@@ -426,7 +426,7 @@ static int check_call(const ft_ctx* ctx, const ft_layer* layer, const void* x, i
 }
 
 extern "C" FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_t* x, int T,
-                               int32_t* idx, float* w, void* stream) {
+                               int32_t* idx, float* w, void* stream) try {
   int rc = check_call(ctx, layer, x, T, "ft_route");
   if (rc) return rc;
   if (!idx || !w) return fail(FT_EINVAL, "ft_route: idx/w null");
@@ -437,7 +437,7 @@ extern "C" FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_
   HIP_TRY((hipError_t)ftk_topk(layer->logits, T, d.E, d.k, idx, w, nullptr, nullptr, nullptr,
                                nullptr, d.H, st));
   return FT_OK;
-}
+} FT_CATCH("ft_route")
 
 static DecodeLaunch launch_args(ft_layer* l, const uint16_t* x, int T, int route, WorkItem* items,
                                 int* n_items, int max_items) {
@@ -848,7 +848,7 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
 }
 
 extern "C" FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
-                                    float* y, ft_decode_stats* stats, void* stream) {
+                                    float* y, ft_decode_stats* stats, void* stream) try {
   int rc = check_call(ctx, layer, x, T, "ft_moe_decode");
   if (rc) return rc;
   if (!y) return fail(FT_EINVAL, "ft_moe_decode: y null");
@@ -865,26 +865,26 @@ extern "C" FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t
     return decode_resident(layer, x, T, y, st);
   }
   return decode_miss_path(ctx, layer, x, T, y, stats, st);
-}
+} FT_CATCH("ft_moe_decode")
 
 // ---- split rule and probes ----------------------------------------------------------------
-extern "C" FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar) {
+extern "C" FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar) try {
   return qstar_split(m, Bp, Bh, q, qstar);
-}
+} FT_CATCH("ft_qstar_split")
 
-extern "C" FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh) {
+extern "C" FT_API int ft_set_bandwidth(ft_layer* layer, double Bp, double Bh) try {
   if (!layer || !(Bp > 0.0) || !(Bh > 0.0))
     return fail(FT_EINVAL, "ft_set_bandwidth: need a layer and Bp, Bh > 0");
   layer->bp = Bp;
   layer->bh = Bh;
   return FT_OK;
-}
+} FT_CATCH("ft_set_bandwidth")
 
-extern "C" FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q) {
+extern "C" FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q) try {
   return qstar_makespan(m, Bp, Bh, q);
-}
+} FT_CATCH("ft_qstar_split_makespan")
 
-extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha) {
+extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha) try {
   if (!layer) return fail(FT_EINVAL, "ft_set_miss_policy: null layer");
   if (rule != FT_SPLIT_ROUND && rule != FT_SPLIT_MAKESPAN)
     return fail(FT_EINVAL, "ft_set_miss_policy: unknown split rule");
@@ -893,9 +893,9 @@ extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha
   layer->split_rule = rule;
   layer->alpha = alpha;
   return FT_OK;
-}
+} FT_CATCH("ft_set_miss_policy")
 
-extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth) {
+extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth) try {
   if (!layer) return fail(FT_EINVAL, "ft_set_prefetch: null layer");
   if (depth < 0) return fail(FT_EINVAL, "ft_set_prefetch: depth must be >= 0");
   auto unlink = [&]() {
@@ -940,19 +940,19 @@ extern "C" FT_API int ft_set_prefetch(ft_layer* layer, ft_layer* next, int depth
   next->prev = layer;
   layer->pf_depth = depth;
   return FT_OK;
-}
+} FT_CATCH("ft_set_prefetch")
 
 extern "C" FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const float* y, float scale,
-                                       int64_t n, uint16_t* out, void* stream) {
+                                       int64_t n, uint16_t* out, void* stream) try {
   if (!ctx || n < 0) return fail(FT_EINVAL, "ft_residual_bf16: null context or n < 0");
   if (n == 0) return FT_OK;
   if (!x || !y || !out) return fail(FT_EINVAL, "ft_residual_bf16: null array");
   HIP_TRY(hipSetDevice(ctx->device));
   HIP_TRY((hipError_t)ftk_residual(x, y, scale, n, out, (hipStream_t)stream));
   return FT_OK;
-}
+} FT_CATCH("ft_residual_bf16")
 
-extern "C" FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* ram, int n_ram) {
+extern "C" FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* ram, int n_ram) try {
   if (!layer) return fail(FT_EINVAL, "ft_layer_set_disk_tier: null layer");
   if (layer->all_resident) return fail(FT_EINVAL, "ft_layer_set_disk_tier: the layer is resident");
   if (layer->next || layer->prev)
@@ -984,28 +984,28 @@ extern "C" FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* r
   layer->n_ram = n_ram;
   layer->ram_lru.init(d.E, n_ram, false);
   return FT_OK;
-}
+} FT_CATCH("ft_layer_set_disk_tier")
 
-extern "C" FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e) {
+extern "C" FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e) try {
   if (!layer || !e2r || !r2e) return fail(FT_EINVAL, "ft_debug_host_tier: null argument");
   if (!layer->ftw) return fail(FT_ESTATE, "ft_debug_host_tier: the layer has no disk tier");
   std::copy(layer->ram_lru.e2s.begin(), layer->ram_lru.e2s.end(), e2r);
   std::copy(layer->ram_lru.s2e.begin(), layer->ram_lru.s2e.end(), r2e);
   return FT_OK;
-}
+} FT_CATCH("ft_debug_host_tier")
 
-extern "C" FT_API int ft_force_q(ft_layer* layer, int q) {
+extern "C" FT_API int ft_force_q(ft_layer* layer, int q) try {
   if (!layer) return fail(FT_EINVAL, "ft_force_q: null layer");
   layer->force_q = q < 0 ? -1 : q;
   return FT_OK;
-}
+} FT_CATCH("ft_force_q")
 
 static double median(std::vector<double> v) {
   std::sort(v.begin(), v.end());
   return v.empty() ? 0.0 : v[v.size() / 2];
 }
 
-extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh) {
+extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double* Bp, double* Bh) try {
   if (!ctx || !layer) return fail(FT_EINVAL, "ft_measure_bandwidth: null argument");
   const ft_layer_desc& d = layer->d;
   HIP_TRY(hipSetDevice(ctx->device));
@@ -1075,10 +1075,10 @@ extern "C" FT_API int ft_measure_bandwidth(ft_ctx* ctx, ft_layer* layer, double*
   if (Bp) *Bp = layer->bp;
   if (Bh) *Bh = layer->bh;
   return FT_OK;
-}
+} FT_CATCH("ft_measure_bandwidth")
 
 extern "C" FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t bytes, int reps,
-                                        double* GBps) {
+                                        double* GBps) try {
   if (!ctx || !buf || !GBps || reps < 1 || bytes < (1u << 20) || bytes % 16)
     return fail(FT_EINVAL, "ft_probe_hbm_read: bad argument");
   HIP_TRY(hipSetDevice(ctx->device));
@@ -1112,9 +1112,9 @@ extern "C" FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t b
   if (e != hipSuccess) return fail(FT_EHIP, std::string("ft_probe_hbm_read: ") + hipGetErrorString(e));
   *GBps = best;
   return FT_OK;
-}
+} FT_CATCH("ft_probe_hbm_read")
 
-extern "C" FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us) {
+extern "C" FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us) try {
   if (threads < 1 || threads > 256 || jobs < 0 || pause_us < 0)
     return fail(FT_EINVAL, "ft_debug_pool_stress: bad argument");
   ThreadPool pool(threads);
@@ -1129,10 +1129,10 @@ extern "C" FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us) 
     if (pause_us) std::this_thread::sleep_for(std::chrono::microseconds(pause_us));
   }
   return FT_OK;
-}
+} FT_CATCH("ft_debug_pool_stress")
 
 // ---- kernel timing ------------------------------------------------------------------------
-extern "C" FT_API int ft_profile_begin(ft_layer* layer, int n) {
+extern "C" FT_API int ft_profile_begin(ft_layer* layer, int n) try {
   if (!layer || n < 0 || n > 1000000) return fail(FT_EINVAL, "ft_profile_begin: bad argument");
   HIP_TRY(hipSetDevice(layer->ctx->device));
   const size_t need = (size_t)n * 4;
@@ -1144,10 +1144,10 @@ extern "C" FT_API int ft_profile_begin(ft_layer* layer, int n) {
   layer->prof_n = n;
   layer->prof_i = 0;
   return FT_OK;
-}
+} FT_CATCH("ft_profile_begin")
 
 extern "C" FT_API int ft_profile_end(ft_layer* layer, double* gateup_us, double* down_us,
-                                     int* n_recorded) {
+                                     int* n_recorded) try {
   if (!layer) return fail(FT_EINVAL, "ft_profile_end: null layer");
   HIP_TRY(hipSetDevice(layer->ctx->device));
   double a = 0.0, b = 0.0;
@@ -1166,11 +1166,11 @@ extern "C" FT_API int ft_profile_end(ft_layer* layer, double* gateup_us, double*
   if (n_recorded) *n_recorded = n;
   layer->prof_n = layer->prof_i = 0;
   return FT_OK;
-}
+} FT_CATCH("ft_profile_end")
 
 // ---- test hooks ---------------------------------------------------------------------------
 extern "C" FT_API int ft_debug_dequant(const ft_layer* layer, int slot, int matrix, float* out,
-                                       void* stream) {
+                                       void* stream) try {
   if (!layer || !out || matrix < 0 || matrix > 2)
     return fail(FT_EINVAL, "ft_debug_dequant: bad argument");
   const ft_layer_desc& d = layer->d;
@@ -1192,24 +1192,24 @@ extern "C" FT_API int ft_debug_dequant(const ft_layer* layer, int slot, int matr
   }
   HIP_TRY((hipError_t)ftk_dequant(blob, &layer->L, matrix, ts, out, (hipStream_t)stream));
   return FT_OK;
-}
+} FT_CATCH("ft_debug_dequant")
 
-extern "C" FT_API int ft_debug_tables(const ft_layer* layer, int32_t* e2s, int32_t* s2e) {
+extern "C" FT_API int ft_debug_tables(const ft_layer* layer, int32_t* e2s, int32_t* s2e) try {
   if (!layer || !e2s || !s2e) return fail(FT_EINVAL, "ft_debug_tables: null argument");
   HIP_TRY(hipSetDevice(layer->ctx->device));
   HIP_TRY(hipDeviceSynchronize());
   HIP_TRY(hipMemcpy(e2s, layer->e2s_dev, (size_t)layer->d.E * 4, hipMemcpyDeviceToHost));
   HIP_TRY(hipMemcpy(s2e, layer->s2e_dev, (size_t)layer->d.n_slots * 4, hipMemcpyDeviceToHost));
   return FT_OK;
-}
+} FT_CATCH("ft_debug_tables")
 
 extern "C" FT_API int ft_host_expert_ffn(ft_ctx* ctx, int format, int H, int I, const void* blob,
-                                         const uint16_t* x, int T, float* y) {
+                                         const uint16_t* x, int T, float* y) try {
   if (!dims_ok(format, H, I) || !blob || !x || !y || T < 1)
     return fail(FT_EINVAL, "ft_host_expert_ffn: bad argument");
   return host_expert_ffn(ctx ? ctx->pool.get() : nullptr, blob_layout(format, H, I),
                          (const uint8_t*)blob, x, T, y);
-}
+} FT_CATCH("ft_host_expert_ffn")
 
 // ---- prefill ------------------------------------------------------------------------------
 // Workspace layout of one prefill call (every region 256-byte aligned); returns the bytes.
@@ -1295,17 +1295,17 @@ static int prefill_check(const ft_layer* layer, int T, int mode, const char* who
 }
 
 extern "C" FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T, int mode,
-                                                    size_t* bytes) {
+                                                    size_t* bytes) try {
   int rc = prefill_check(layer, T, mode, "ft_moe_prefill_workspace_size");
   if (rc) return rc;
   if (!bytes) return fail(FT_EINVAL, "ft_moe_prefill_workspace_size: bytes is null");
   *bytes = prefill_carve(layer, T, mode, nullptr, nullptr);
   return FT_OK;
-}
+} FT_CATCH("ft_moe_prefill_workspace_size")
 
 extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
                                      float* y, int mode, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     void* stream) try {
   int rc = prefill_check(layer, T, mode, "ft_moe_prefill");
   if (rc) return rc;
   if (!ctx || !x || !y || !ws) return fail(FT_EINVAL, "ft_moe_prefill: null argument");
@@ -1333,11 +1333,11 @@ extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_
   a.y = y;
   HIP_TRY((hipError_t)ftk_prefill(&a, (hipStream_t)stream, prof_events(layer)));
   return FT_OK;
-}
+} FT_CATCH("ft_moe_prefill")
 
 extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
                                             int32_t* counts, int32_t* offsets, int32_t* pos,
-                                            void* stream) {
+                                            void* stream) try {
   if (!layer || !ws || !counts || !offsets || !pos || T < 1)
     return fail(FT_EINVAL, "ft_debug_prefill_perm: bad argument");
   PrefillLaunch a{};
@@ -1349,10 +1349,10 @@ extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* w
   HIP_TRY(hipMemcpyAsync(offsets, a.offsets, (size_t)(d.E + 1) * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(pos, a.pos, (size_t)T * d.k * 4, hipMemcpyDeviceToDevice, st));
   return FT_OK;
-}
+} FT_CATCH("ft_debug_prefill_perm")
 
 extern "C" FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* ws, int T,
-                                             int32_t* idx, float* w, void* stream) {
+                                             int32_t* idx, float* w, void* stream) try {
   if (!layer || !ws || !idx || !w || T < 1)
     return fail(FT_EINVAL, "ft_debug_prefill_route: bad argument");
   PrefillLaunch a{};
@@ -1363,11 +1363,11 @@ extern "C" FT_API int ft_debug_prefill_route(const ft_layer* layer, const void* 
   HIP_TRY(hipMemcpyAsync(idx, a.idx, n, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(w, a.w, n, hipMemcpyDeviceToDevice, st));
   return FT_OK;
-}
+} FT_CATCH("ft_debug_prefill_route")
 
 extern "C" FT_API int ft_debug_prefill_quant(const ft_layer* layer, const void* ws, int T,
                                              int which, uint8_t* codes, uint8_t* scales,
-                                             void* stream) {
+                                             void* stream) try {
   if (!layer || !ws || !codes || !scales || T < 1 || (which != 0 && which != 1))
     return fail(FT_EINVAL, "ft_debug_prefill_quant: bad argument");
   PrefillLaunch a{};
@@ -1385,10 +1385,10 @@ extern "C" FT_API int ft_debug_prefill_quant(const ft_layer* layer, const void* 
     HIP_TRY((hipError_t)ftk_untile_h(&a, codes, scales, st));
   }
   return FT_OK;
-}
+} FT_CATCH("ft_debug_prefill_quant")
 
 extern "C" FT_API int ft_debug_prefill_weights(const ft_layer* layer, int e, void* out,
-                                               void* stream) {
+                                               void* stream) try {
   if (!layer || !out || e < 0 || e >= layer->d.E)
     return fail(FT_EINVAL, "ft_debug_prefill_weights: bad argument");
   if (!layer->mx_pool) return fail(FT_ESTATE, "ft_debug_prefill_weights: no MXFP4 weights");
@@ -1397,4 +1397,4 @@ extern "C" FT_API int ft_debug_prefill_weights(const ft_layer* layer, int e, voi
                          blob_layout(FT_MXFP4, layer->d.H, layer->d.I).bytes,
                          hipMemcpyDeviceToDevice, (hipStream_t)stream));
   return FT_OK;
-}
+} FT_CATCH("ft_debug_prefill_weights")

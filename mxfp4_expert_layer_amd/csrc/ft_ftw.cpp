@@ -83,7 +83,7 @@ void ftw_dims(const ft_ftw* f, int* fmt, int* H, int* I, int* E, int* n_shared) 
 }  // namespace ft
 
 extern "C" FT_API int ft_ftw_write(const char* path, int format, int H, int I, int E,
-                                   int n_shared, const void* blobs, uint64_t src_stride) {
+                                   int n_shared, const void* blobs, uint64_t src_stride) try {
   if (!path || !blobs || !dims_valid(format, H, I) || E < 1 || n_shared < 0)
     return fail(FT_EINVAL, "ft_ftw_write: bad argument");
   const BlobLayout L = blob_layout(format, H, I);
@@ -118,9 +118,9 @@ extern "C" FT_API int ft_ftw_write(const char* path, int format, int H, int I, i
   errno = saved;
   if (!ok) return io_fail("ft_ftw_write: write failed for", path);
   return FT_OK;
-}
+} FT_CATCH("ft_ftw_write")
 
-extern "C" FT_API int ft_ftw_open(const char* path, int flags, ft_ftw** out) {
+extern "C" FT_API int ft_ftw_open(const char* path, int flags, ft_ftw** out) try {
   if (!path || !out || (flags & ~(FT_FTW_DIRECT | FT_FTW_STAGED)))
     return fail(FT_EINVAL, "ft_ftw_open: bad argument");
   int fd = -1, direct = 0;
@@ -172,9 +172,9 @@ extern "C" FT_API int ft_ftw_open(const char* path, int flags, ft_ftw** out) {
   f->h = h;
   *out = f;
   return FT_OK;
-}
+} FT_CATCH("ft_ftw_open")
 
-extern "C" FT_API int ft_ftw_get_info(const ft_ftw* f, ft_ftw_info* info) {
+extern "C" FT_API int ft_ftw_get_info(const ft_ftw* f, ft_ftw_info* info) try {
   if (!f || !info) return fail(FT_EINVAL, "ft_ftw_get_info: null argument");
   info->format = f->h.fmt;
   info->H = f->h.H;
@@ -187,14 +187,14 @@ extern "C" FT_API int ft_ftw_get_info(const ft_ftw* f, ft_ftw_info* info) {
   info->blob_bytes = f->h.blob_bytes;
   info->file_bytes = f->h.file_bytes;
   return FT_OK;
-}
+} FT_CATCH("ft_ftw_get_info")
 
-extern "C" FT_API int ft_ftw_close(ft_ftw* f) {
+extern "C" FT_API int ft_ftw_close(ft_ftw* f) try {
   if (!f) return FT_OK;
   if (f->fd >= 0) close(f->fd);
   delete f;
   return FT_OK;
-}
+} FT_CATCH("ft_ftw_close")
 
 namespace ft {
 int ftw_read(ThreadPool* pool, ft_ftw* f, const int32_t* ids, int n, uint8_t* const* dst,
@@ -265,7 +265,7 @@ int ftw_read(ThreadPool* pool, ft_ftw* f, const int32_t* ids, int n, uint8_t* co
 }  // namespace ft
 
 extern "C" FT_API int ft_ftw_read(ft_ctx* ctx, ft_ftw* f, const int32_t* ids, int n, void* dst,
-                                  uint64_t dst_stride, uint64_t chunk, double* seconds) {
+                                  uint64_t dst_stride, uint64_t chunk, double* seconds) try {
   if (!f || n < 0 || (n > 0 && (!ids || !dst))) return fail(FT_EINVAL, "ft_ftw_read: bad argument");
   if (dst_stride < f->h.blob_bytes && n > 1) return fail(FT_EINVAL, "ft_ftw_read: dst_stride below the blob size");
   if (f->direct && dst_stride % kAlign) return fail(FT_EINVAL, "ft_ftw_read: O_DIRECT needs a dst_stride multiple of 4096");
@@ -276,4 +276,4 @@ extern "C" FT_API int ft_ftw_read(ft_ctx* ctx, ft_ftw* f, const int32_t* ids, in
   if (seconds)
     *seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   return rc;
-}
+} FT_CATCH("ft_ftw_read")

@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <new>
+#include <system_error>
 
 namespace ft {
 
@@ -17,6 +19,20 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
   return code;
+}
+
+int caught(const char* who) {
+  try {
+    throw;
+  } catch (const std::bad_alloc&) {
+    return fail(FT_ENOMEM, std::string(who) + ": out of host memory");
+  } catch (const std::system_error& e) {
+    return fail(FT_ENOMEM, std::string(who) + ": " + e.what());
+  } catch (const std::exception& e) {
+    return fail(FT_ESTATE, std::string(who) + ": " + e.what());
+  } catch (...) {
+    return fail(FT_ESTATE, std::string(who) + ": unknown exception");
+  }
 }
 
 }  // namespace ft

@@ -16,6 +16,12 @@ namespace ft {
 // thread-local last error
 void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
+// The handler of an entry point's function-try-block: no C++ exception crosses the C ABI.
+// Running out of host memory or threads gives FT_ENOMEM, any other exception FT_ESTATE, each
+// with a message naming the entry point.
+int caught(const char* who);
+#define FT_CATCH(who) \
+  catch (...) { return ft::caught(who); }
 
 // Fixed set of worker threads; run(fn) calls fn(i, n) for i in [0, n) on the workers and the
 // calling thread (i = n - 1) and returns when all have finished.  Jobs are short (one expert's
