@@ -373,11 +373,15 @@ FT_API int ft_ftw_read(ft_ctx* ctx, ft_ftw* f, const int32_t* ids, int n, void* 
  */
 FT_API int ft_layer_set_disk_tier(ft_layer* layer, ft_ftw* f, void* ram, int n_ram);
 /* Test hook: the host-memory tier's tables, expert -> slot [E] and slot -> expert [n_ram]. */
+FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e);
 /* Test hook (host only): run `jobs` jobs on a fresh pool of `threads` threads, pausing
  * pause_us between them (a pause past the workers' spin makes them sleep and be woken), and
  * check every job ran on every index exactly once.  FT_ESTATE if one did not. */
 FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us);
-FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e);
+/* Test hook (host only) of the no-throw rule: kind 0 returns FT_OK; kind 1 throws
+ * std::bad_alloc, 2 std::runtime_error, 3 std::system_error inside an entry point, which
+ * returns FT_ENOMEM, FT_ESTATE and FT_ENOMEM for them.  FT_EINVAL for another kind. */
+FT_API int ft_debug_throw(int kind);
 
 FT_API const char* ft_last_error(void);
 

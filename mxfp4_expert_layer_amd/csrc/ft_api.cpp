@@ -2,6 +2,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <system_error>
+#include <stdexcept>
 #include <chrono>
 #include <cmath>
 #include <cstdlib>
@@ -1113,6 +1115,15 @@ extern "C" FT_API int ft_probe_hbm_read(ft_ctx* ctx, const void* buf, uint64_t b
   *GBps = best;
   return FT_OK;
 } FT_CATCH("ft_probe_hbm_read")
+
+extern "C" FT_API int ft_debug_throw(int kind) try {
+  if (kind == 1) throw std::bad_alloc();
+  if (kind == 2) throw std::runtime_error("planted exception");
+  if (kind == 3)
+    throw std::system_error(std::make_error_code(std::errc::resource_unavailable_try_again));
+  if (kind != 0) return fail(FT_EINVAL, "ft_debug_throw: kind must be 0..3");
+  return FT_OK;
+} FT_CATCH("ft_debug_throw")
 
 extern "C" FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us) try {
   if (threads < 1 || threads > 256 || jobs < 0 || pause_us < 0)

@@ -84,6 +84,7 @@ _sig = {
     "ft_set_miss_policy": [_vp, _i, _d],
     "ft_set_prefetch": [_vp, _vp, _i],
     "ft_debug_pool_stress": [_i, _i, _i],
+    "ft_debug_throw": [_i],
     "ft_probe_hbm_read": [_vp, _vp, _u64, _i, C.POINTER(_d)],
     "ft_ftw_write": [C.c_char_p, _i, _i, _i, _i, _i, _vp, _u64],
     "ft_ftw_open": [C.c_char_p, _i, C.POINTER(_vp)],

@@ -292,3 +292,19 @@ def test_null_arguments_return_einval():
     # destroying nothing is a no-op
     assert L.ft_layer_destroy(None) == ft.FT_OK and L.ft_ctx_destroy(None) == ft.FT_OK
     assert L.ft_ftw_close(None) == ft.FT_OK
+
+
+@pytest.mark.parametrize("kind,code,text", [(0, "FT_OK", None), (1, "FT_ENOMEM", "out of host memory"),
+                                            (2, "FT_ESTATE", "planted exception"),
+                                            (3, "FT_ENOMEM", None), (7, "FT_EINVAL", "kind must be")])
+def test_exceptions_do_not_cross_the_abi(kind, code, text):
+    """An exception thrown inside an entry point comes back as a status code with a message
+    naming the entry point (bad_alloc and system_error: FT_ENOMEM; others: FT_ESTATE)."""
+    code = getattr(ft, code)
+    rc = ft.lib.ft_debug_throw(kind)
+    assert rc == code
+    if code:
+        msg = ft.lib.ft_last_error().decode()
+        assert msg.startswith("ft_debug_throw"), msg
+        if text:
+            assert text in msg, msg
