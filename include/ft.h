@@ -133,8 +133,14 @@ FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft_layer** ou
 FT_API int ft_layer_destroy(ft_layer* layer);
 
 /*
- * Routing (top-k softmax).  x: device bf16 [T][H]; idx: device int32 [T][k] (rank order);
- * w: device fp32 [T][k].  1 <= T <= max_tokens.  Asynchronous on `stream`.
+ * Routing (top-k softmax; smzdm explainer a825qpgl, section 二: each MoE layer's gate
+ * activates a few of its experts per token, 6 of 256 in the DeepSeek-V4-Flash layer, and the
+ * chosen experts' outputs are later merged by these routing weights).  logits = x W_r^T + b
+ * in fp32; idx = the k largest logits in rank order (descending, ties to the lower index);
+ * w = softmax over those k logits (the full softmax over E renormalised over the kept k is the
+ * same number).  x: device bf16 [T][H]; idx: device int32 [T][k]; w: device fp32 [T][k].
+ * 1 <= T <= max_tokens.  FT_EINVAL for a null pointer or T out of range.  Asynchronous on
+ * `stream`.
  */
 FT_API int ft_route(ft_ctx* ctx, const ft_layer* layer, const uint16_t* x, int T,
                     int32_t* idx, float* w, void* stream);
@@ -221,7 +227,10 @@ enum { FT_SPLIT_ROUND = 0, FT_SPLIT_MAKESPAN = 1 };
 FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
 
 /*
- * Startup probes: Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
+ * Startup probes of the split rule's two bandwidths (smzdm explainer a825qpgl, section 二: q*
+ * is computed from measured bandwidths, Bp the measured PCIe transfer rate and Bh the CPU
+ * side's effective memory bandwidth):
+ * Bp = median bytes/s of a pinned hipMemcpyAsync of one expert blob to the
  * device; Bh = median bytes/s of the host expert FFN over one blob on the host threads.  The
  * repetitions cycle over up to 8 distinct blobs, more than a host cache holds, as decode
  * reads them.  Needs host_blobs, or a disk tier not yet used by a decode call (the probe then
@@ -301,7 +310,7 @@ FT_API int ft_residual_bf16(ft_ctx* ctx, const uint16_t* x, const float* y, floa
                             int64_t n, uint16_t* out, void* stream);
 
 /*
- * FTW expert files (smzdm explainer a825qpgl, section 三: every tensor 4096-aligned, so a
+ * FTW expert files (lowalt.boxinlu2.cn article, section 三: every tensor 4096-aligned, so a
  * blob moves from disk in a few large direct reads instead of many fragmented ones).
  * Layout: bytes [0, 4096) hold the header (magic "FTW1", version 1, format, H, I, E,
  * n_shared, blob bytes, blob stride, data offset, file bytes; little-endian); blob i sits at

@@ -1,4 +1,4 @@
-// FTW expert files: the blob store on disk (smzdm explainer a825qpgl, section 三: every tensor
+// FTW expert files: the blob store on disk (lowalt.boxinlu2.cn article, section 三: every tensor
 // 4096-aligned, so an expert moves from disk in a few large direct reads).  The file is a
 // 4096-byte header page followed by the packed blobs at one stride; blobs are stored exactly
 // as ft_pack_expert lays them out, so a read lands them ready for the slot pool and the host

@@ -180,17 +180,20 @@ static void gemv_tiles(const BlobLayout& L, const uint8_t* codes, const uint8_t*
 // scaled by the block's E8M0 scale (the scale is added to the exponent field of the nonzero
 // entries), and vdpbf16ps accumulates the products with the bf16 activations into 16 fp32
 // lanes per row.  acc[row] sums for rows rt*16 .. rt*16+15.  The table trick is exact when
-// every scaled E2M1 value is a normal bf16 number: scale codes 2..253 (0.5 * 2^-125 ..
-// 6 * 2^126).  A row tile with any other scale code (including the NaN code 255) goes to the
-// scalar path, which follows the format definition for every code (xs: x as fp32).
-// Whether the KC * 64 E8M0 codes of one row tile all lie in 2..253.
+// every scaled E2M1 value is a normal bf16 number.  Adding s - 127 to the exponent field
+// keeps 0.5 (field 126) at or above 1 for s >= 2 and 6.0 (field 129) at or below 254 for
+// s <= 252, so the scale codes taken here are 2..252 (0.5 * 2^-125 .. 6 * 2^125); at 253 the
+// entries of 4 and 6 would land on the infinity/NaN field.  A row tile with any other scale
+// code (including the NaN code 255) goes to the scalar path, which follows the format
+// definition for every code (xs: x as fp32).
+// Whether the KC * 64 E8M0 codes of one row tile all lie in 2..252.
 __attribute__((target("avx512f,avx512bw")))
 static bool mx_scale_row_in_range(const uint8_t* s, int KC) {
   __mmask64 bad = 0;
   for (int kc = 0; kc < KC; ++kc) {
     const __m512i v = _mm512_loadu_si512((const void*)(s + 64 * kc));
     bad |= _mm512_cmp_epu8_mask(v, _mm512_set1_epi8(2), _MM_CMPINT_LT) |
-           _mm512_cmp_epu8_mask(v, _mm512_set1_epi8((char)253), _MM_CMPINT_NLE);
+           _mm512_cmp_epu8_mask(v, _mm512_set1_epi8((char)252), _MM_CMPINT_NLE);
   }
   return bad == 0;
 }

@@ -101,8 +101,9 @@ def _allcodes_layer(ctx):
 
 
 def test_dequant_every_code_normal_scales(ctx):
-    """Every byte of E2M1 code pairs under every E8M0 scale whose products are normal fp32
-    and bf16 numbers (codes 2..253)."""
+    """Every byte of E2M1 code pairs under E8M0 scale codes 2..253.  Up to 252 every product
+    is a normal fp32 number; at 253 the products of +-4 and +-6 (2^128 and 1.5 * 2^128)
+    exceed the fp32 range and must be +-inf on both sides."""
     L, ex = _allcodes_layer(ctx)
     got = _dequant(L, 0, 0)
     exp = _expected(L, ex, 0, "mxfp4")

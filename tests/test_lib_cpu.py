@@ -254,6 +254,39 @@ def test_host_expert_ffn_mixed_scale_ranges():
     assert moe.rel_l2(y, ref) <= 1e-3
 
 
+def test_host_expert_ffn_scale_code_253(monkeypatch):
+    """E8M0 code 253 (2^126) with codes 6 and -4 in the block: 6 * 2^126 and 4 * 2^126 are past
+    the bf16 and fp32 range, so the AVX-512 table path must not take that row tile.  One gate
+    block of row 7 holds +6 and -4 at the two elements where x is 2^-126 (a normal bf16), so
+    the block adds exactly 6 - 4 = 2 to that row's dot product; the vectorised path (on CPUs
+    with AVX-512 BF16), the scalar path and the oracle must agree, with every output finite."""
+    cfg = synth.small_config(seed=10, H=256, I=128, code_dist="normal")
+    ex = synth.gen_expert(cfg, 5)
+    ex.gate_codes = ex.gate_codes.copy()
+    ex.gate_scales = ex.gate_scales.copy()
+    ex.gate_codes[7, 32:48] = 0
+    ex.gate_codes[7, 32] = 0x7 | (0xE << 4)       # elements 64, 65: +6, -4
+    ex.gate_scales[7, 2] = 253                     # block 2 = elements 64..95
+    blob = ft.pack_expert("mxfp4", cfg.H, cfg.I, ex)
+    x = synth.gen_tokens(cfg, 2)
+    x[:, 64:66] = synth.f32_to_bf16_bits(np.full(2, 2.0 ** -126, np.float32))
+    ys = []
+    for scalar in ("0", "1"):
+        monkeypatch.setenv("FT_HOST_SCALAR", scalar)
+        ys.append(ft.host_expert_ffn("mxfp4", cfg.H, cfg.I, blob, x))
+
+    class _L:
+        pass
+    L = _L()
+    L.cfg = cfg
+    wg, wu, wd = moe.expert_weights(L, ex)
+    ref = moe.swiglu_ffn(fp4.bf16_bits_to_f64(x), wg, wu, wd)
+    for y in ys:
+        assert np.all(np.isfinite(y))
+        assert moe.rel_l2(y, ref) <= 1e-3
+    assert moe.rel_l2(ys[0], ys[1]) <= 1e-5
+
+
 @pytest.mark.parametrize("threads,jobs,pause_us", [(8, 400, 0), (8, 40, 1500), (1, 10, 0),
                                                    (16, 25, 700)])
 def test_host_thread_pool_runs_every_job_once(threads, jobs, pause_us):
