@@ -2,22 +2,32 @@
 """Benchmark of the FP4 MoE expert layer on one MI355X (prints one JSON line).
 
 Workloads (seeded synthetic layers, no trained weights exist for these shapes):
-  decode-35b-a3b   hidden 2048, 256 experts, top-8, intermediate 512, MXFP4   (default)
+  decode-35b-a3b   hidden 2048, 256 experts, top-8, intermediate 512, MXFP4
   decode-35b-a3b-nvfp4  the same layer with NVFP4 experts (E4M3 per 16, tensor scale 1/64)
   decode-284b      hidden 4096, 256 experts + 1 shared, top-6, intermediate 2048, MXFP4
   miss-path-284b   the 284B-class layer with a 48-slot pool, q* split of misses
                    (--layers N chains N such layers, --prefetch D adds cross-layer prefetch)
   prefill-753b     4096 tokens through hidden 6144, 160 experts, top-8, intermediate 2048,
                    NVFP4 (exact bf16-MFMA grouped GEMMs)
-A step is one ft_moe_decode call of T tokens (routing, gate/up + SwiGLU, down, combine).
+  headline         (default) prefill-753b as the line's value and roofline, plus the same
+                   layer in the scaled-FP4 mode and decode-284b at 1, 4 and 16 tokens per
+                   step as extra keys
+A decode step is one ft_moe_decode call of T tokens (routing, gate/up + SwiGLU, down,
+combine); a prefill step is one ft_moe_prefill call of 4096 tokens.
 Decode steps are captured in a HIP graph and replayed; inputs are resident in HBM; the
 layer is replicated to several device copies (different addresses) so repeated steps are
 not served from the 256 MB Infinity Cache.
 
-roofline: the gate/up kernel reads two thirds of the expert bytes and dominates; its
-algorithmic bytes per launch = distinct experts of the call x 2*I*H*(1/2 + 1/B) bytes
-(codes + one scale byte per block of B = 32 (MXFP4) or 16 (NVFP4)), divided by its mean
-duration from start/stop events that its dispatches record.  peak = 8 TB/s (MI355X HBM3E).
+roofline (the dominant kernel, its duration from start/stop events that its own dispatches
+record on the call's stream):
+  prefill, exact mode: the gate/up grouped GEMM, bound by the bf16 MFMA; achieved =
+    2 * (T*k) * 2*I*H flop per launch / its mean duration, peak 2.5 PFLOP/s;
+  prefill, scaled-FP4 mode: the gate/up grouped GEMM, bound by HBM (its arithmetic intensity
+    is below the FP4 ridge); achieved = its algorithmic bytes per launch / duration, peak
+    8 TB/s, with its FP4 MFMA rate against 10.1 PFLOP/s alongside;
+  decode: the gate/up kernel, which reads two thirds of the expert bytes; achieved =
+    distinct experts of the call x 2*I*H*(1/2 + 1/B) bytes (codes + one scale byte per block
+    of B = 32 (MXFP4) or 16 (NVFP4)) / duration, peak 8 TB/s (MI355X HBM3E).
 cpu_baseline: the float64 oracle on a bounded sample of the same steps (host cores).
 """
 from __future__ import annotations
@@ -97,6 +107,24 @@ def read_reference(ctx, achieved):
     return {"measured_read_GBps": v, "frac_of_measured_read": achieved / v if v > 0 else None}
 
 
+def host_info():
+    """nproc (CPUs this process may run on), the machine's logical CPU count and its model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"nproc": nproc, "logical_cpus": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(cfg, x_batches, seconds):
     """Time the float64 oracle (as it stands) on decode steps of the same workload."""
     import numpy as np
@@ -134,28 +162,29 @@ def cpu_baseline(cfg, x_batches, seconds):
     with threadpool_limits(limits=1, user_api="blas"):
         t1, n1, dt1 = timed(seconds / 3)
     return {"value": tokens / dt, "unit": "tokens/s", "cores": max(blas) if blas else 1,
-            "kind": "oracle",
+            "kind": "oracle", **host_info(),
             "sample": f"{n} steps of {x_batches[0].shape[0]} token(s) ({tokens} tokens) of the "
                       f"same workload, float64 numpy oracle, {dt:.1f} s",
             "single_thread": {"value": t1 / dt1, "unit": "tokens/s", "cores": 1,
                               "sample": f"{n1} steps ({t1} tokens), {dt1:.1f} s"}}
 
 
-def bench_decode(args, wl):
+def decode_layer(ctx, cfg, copies, max_tokens):
+    from mxfp4_expert_layer_amd.layer import GpuLayer
+
+    log(f"[bench] building {copies} device copies of {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I})")
+    return GpuLayer(ctx, cfg, resident=True, max_tokens=max_tokens, copies=copies, threads=16)
+
+
+def decode_run(ctx, L, cfg, T, K, W, copies, tag):
+    """K timed decode steps of T tokens (graph replay, after W eager warm-up steps and one
+    untimed replay of every captured graph), the gate/up and down kernels' event-timed
+    durations over an eager pass of 64 steps, and the algorithmic bytes behind them."""
     import numpy as np
     import torch
 
     from mxfp4_expert_layer_amd import ft, synth
-    from mxfp4_expert_layer_amd.layer import GpuLayer
 
-    cfg = synth.CONFIGS[wl["cfg"]]
-    T = args.tokens or wl["T"]
-    copies = args.copies or wl["copies"]
-    K = args.steps if args.steps is not None else wl["steps"]
-    W = args.warmup if args.warmup is not None else wl["warmup"]
-    ctx = ft.Context(0)
-    log(f"[bench] building {copies} device copies of {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I})")
-    L = GpuLayer(ctx, cfg, resident=True, max_tokens=max(T, 1), copies=copies, threads=16)
     NB = 16
     xh = [synth.gen_tokens(cfg, T, batch=1000 + b) for b in range(NB)]
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xh]
@@ -171,7 +200,6 @@ def bench_decode(args, wl):
     torch.cuda.synchronize()
 
     G = 64
-    graphs = []
 
     def capture(n):
         g = torch.cuda.CUDAGraph()
@@ -182,6 +210,10 @@ def bench_decode(args, wl):
 
     full = capture(G) if K >= G else None
     rest = capture(K % G) if K % G else None
+    # one untimed replay of each graph: its first launch uploads it
+    for g in (full, rest):
+        if g is not None:
+            g.replay()
     torch.cuda.synchronize()
     reps = K // G
     t0 = time.perf_counter()
@@ -191,7 +223,7 @@ def bench_decode(args, wl):
         rest.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    log(f"[bench] timed {K} steps in {dt * 1e3:.2f} ms")
+    log(f"[bench] {tag}: timed {K} steps in {dt * 1e3:.2f} ms")
 
     # dominant kernel: start/stop events recorded by the gate/up dispatches themselves, over
     # an eager pass of the same steps (events cannot be timed inside a captured graph).  The
@@ -204,7 +236,6 @@ def bench_decode(args, wl):
         for i in range(G):
             step(i, stream)
     torch.cuda.synchronize()
-    prof_mode = "dispatch-events"
     gu, dn, nrec = [], [], 0
     for h in L.handles:
         a, b, n = ft.profile_end(h)
@@ -231,10 +262,28 @@ def bench_decode(args, wl):
     achieved = n_exp * gu_bytes_expert / (gate_us * 1e-6) / 1e9
     step_bytes = n_exp * (gu_bytes_expert + dn_bytes_expert) + router_bytes
     step_s = dt / K
+    return dict(tokens_per_s=T * K / dt, steps=K, ms_per_step=step_s * 1e3, xh=xh,
+                gate_us=gate_us, down_us=down_us, n_exp=n_exp, achieved=achieved,
+                gu_bytes=n_exp * gu_bytes_expert, step_bytes=step_bytes,
+                layer_GBps=step_bytes / step_s / 1e9)
+
+
+def bench_decode(args, wl):
+    from mxfp4_expert_layer_amd import ft, synth
+
+    cfg = synth.CONFIGS[wl["cfg"]]
+    T = args.tokens or wl["T"]
+    copies = args.copies or wl["copies"]
+    K = args.steps if args.steps is not None else wl["steps"]
+    W = args.warmup if args.warmup is not None else wl["warmup"]
+    ctx = ft.Context(0)
+    L = decode_layer(ctx, cfg, copies, max(T, 1))
+    r = decode_run(ctx, L, cfg, T, K, W, copies, f"{args.workload}-T{T}")
+    achieved = r["achieved"]
     res = {
-        "metric": METRIC, "value": T * K / dt, "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}-T{T}", "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "shared_experts": cfg.n_shared,
                    "tokens_per_step": T, "weights": cfg.fmt, "layer_copies": copies,
@@ -242,20 +291,39 @@ def bench_decode(args, wl):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"k_gateup@{args.workload}-T{T}", "decode"),
-                     "kernel": "k_gateup", "kernel_us": gate_us, "timing": prof_mode,
-                     "bytes_per_launch": n_exp * gu_bytes_expert,
-                     **read_reference(ctx, achieved)},
-        "layer": {"algorithmic_bytes_per_step": step_bytes,
-                  "GBps_per_step": step_bytes / step_s / 1e9,
-                  "hbm_frac_per_step": step_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-                  "down_kernel_us": down_us, "distinct_experts_per_step": n_exp},
+                     "kernel": "k_gateup", "kernel_us": r["gate_us"], "timing": "dispatch-events",
+                     "bytes_per_launch": r["gu_bytes"], **read_reference(ctx, achieved)},
+        "layer": {"algorithmic_bytes_per_step": r["step_bytes"],
+                  "GBps_per_step": r["layer_GBps"],
+                  "hbm_frac_per_step": r["layer_GBps"] / HBM_PEAK_GBS,
+                  "down_kernel_us": r["down_us"], "distinct_experts_per_step": r["n_exp"]},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(cfg, xh, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, r["xh"], args.cpu_seconds)
     L.close()
     ctx.close()
     return res
+
+
+def decode_sweep(ctx, cfg_name, Ts, copies, K=1024, W=64):
+    """The decode layer of one class at several token counts: tokens/s and the gate/up
+    kernel's and the whole step's fraction of the 8 TB/s HBM peak, per T."""
+    from mxfp4_expert_layer_amd import synth
+
+    cfg = synth.CONFIGS[cfg_name]
+    L = decode_layer(ctx, cfg, copies, max(Ts))
+    out = {}
+    for T in Ts:
+        r = decode_run(ctx, L, cfg, T, K, W, copies, f"{cfg.name}-T{T}")
+        out[f"T{T}"] = {"tokens_per_s": r["tokens_per_s"], "us_per_step": r["ms_per_step"] * 1e3,
+                        "gateup_us": r["gate_us"], "down_us": r["down_us"],
+                        "gateup_GBps": r["achieved"],
+                        "gateup_hbm_frac": r["achieved"] / HBM_PEAK_GBS,
+                        "layer_hbm_frac": r["layer_GBps"] / HBM_PEAK_GBS,
+                        "distinct_experts": r["n_exp"], "steps": K}
+    L.close()
+    return out
 
 
 def bench_miss_path(args, wl):
@@ -441,53 +509,47 @@ def disk_tier_setup(args, ctx, Ls, cfg):
 
 
 def cpu_baseline_prefill(cfg, x, seconds, mode="exact"):
-    """The float64 oracle on a sample of the prefill tokens (experts drawn beforehand).  The
-    "mxfp4" mode requantises every selected expert's weights, so its sample is one token with
-    the experts evaluated on 16 threads."""
+    """The float64 oracle on a sample of the prefill tokens (experts drawn beforehand): the
+    sample's distinct experts are evaluated on `threads` host threads (one per expert at a
+    time, numpy's BLAS held to one thread each, so `cores` is the threads used).  The "mxfp4"
+    mode requantises every selected expert's weights, so its sample is one token."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from mxfp4_expert_layer_amd import synth
     from oracle import fp4, moe
 
+    info = host_info()
+    threads = max(1, min(16, info["nproc"] or 1))
     OL = synth.gen_layer(cfg, experts=None)
-    n_tok = 2 if mode == "exact" else 1
-    threads = 1 if mode == "exact" else 16
+    n_tok = 4 if mode == "exact" else 1
     xs = x[:n_tok]
     idx, _, _, _ = moe.route(fp4.bf16_bits_to_f64(xs), OL.router_w, OL.router_b, cfg.k)
     for e in np.unique(idx):
         OL.expert(int(e))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        moe.moe_forward(OL, xs, mode=mode, threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds or reps >= 3:
-            break
-    dt = time.perf_counter() - t0
-    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
-    return {"value": reps * n_tok / dt, "unit": "tokens/s", "cores": max(cores, threads),
-            "kind": "oracle",
-            "sample": f"{reps} x {n_tok} of the 4096 prefill tokens (float64 numpy oracle, "
-                      f"mode {mode}, {dt:.1f} s)"}
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            moe.moe_forward(OL, xs, mode=mode, threads=threads)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds or reps >= 8:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": reps * n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            **info,
+            "sample": f"{reps} x {n_tok} of the 4096 prefill tokens ({len(np.unique(idx))} "
+                      f"experts; float64 numpy oracle, mode {mode}, {dt:.1f} s)"}
 
 
-def bench_prefill(args, wl):
+def prefill_run(ctx, L, cfg, T, K, W, s1, workload):
+    """K timed ft_moe_prefill calls of T tokens (after W untimed ones) in one mode, then the
+    two grouped GEMMs' event-timed durations over K more calls."""
     import numpy as np
     import torch
 
     from mxfp4_expert_layer_amd import ft, synth
-    from mxfp4_expert_layer_amd.layer import GpuLayer
 
-    cfg = synth.CONFIGS[wl["cfg"]]
-    T = args.tokens or wl["T"]
-    K = args.steps if args.steps is not None else wl["steps"]
-    W = args.warmup if args.warmup is not None else wl["warmup"]
-    ctx = ft.Context(0)
-    s1 = wl.get("mode") == "mxfp4"
-    log(f"[bench] building {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I}, {cfg.fmt})")
-    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16, prefill_mxfp4=s1)
     xh = [synth.gen_tokens(cfg, T, batch=b) for b in range(2)]
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xh]
     y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
@@ -503,17 +565,19 @@ def bench_prefill(args, wl):
         ft.moe_prefill(ctx, L.handle, xs[i % 2], T, y, mode, ws, nbytes, s)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    log(f"[bench] timed {K} prefill steps in {dt * 1e3:.1f} ms")
+    log(f"[bench] {workload}: timed {K} prefill steps in {dt * 1e3:.1f} ms")
     ft.profile_begin(L.handle, K)
     for i in range(K):
         ft.moe_prefill(ctx, L.handle, xs[i % 2], T, y, mode, ws, nbytes, s)
     torch.cuda.synchronize()
     gu_us, dn_us, nrec = ft.profile_end(L.handle)
+    del ws
     pairs = T * cfg.k
     fl_gu = 2.0 * pairs * 2 * cfg.I * cfg.H
     fl_dn = 2.0 * pairs * cfg.H * cfg.I
     step_s = dt / K
     gu_tf = fl_gu / (gu_us * 1e-6) / 1e12
+    peak = FP4_PEAK_TFLOPS if s1 else BF16_PEAK_TFLOPS
     if s1:
         # algorithmic bytes of k_s1_gemm<0>: the gate and up MXFP4 weights of every expert
         # (17/32 byte per weight: code nibble + E8M0 byte per 32), the quantised tokens once,
@@ -523,41 +587,113 @@ def bench_prefill(args, wl):
         gbs = by_gu / (gu_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS,
-                "traffic": measured_traffic(f"k_s1_gemm<0>@{args.workload}", "prefill"),
+                "traffic": measured_traffic(f"k_s1_gemm<0>@{workload}", "prefill"),
                 "kernel": "k_s1_gemm<0> (gate/up + SwiGLU + MXFP4 quantise of h)",
                 "kernel_us": gu_us, "bytes_per_launch": by_gu, "flops_per_launch": fl_gu,
                 "fp4_mfma_tflops": gu_tf, "fp4_mfma_frac": gu_tf / FP4_PEAK_TFLOPS,
-                "timing": "dispatch-events", **read_reference(ctx, gbs)}
+                "timing": "dispatch-events"}
     else:
         roof = {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,
-                "traffic": measured_traffic(f"k_ggemm<0>@{args.workload}", "prefill"),
+                "traffic": measured_traffic(f"k_ggemm<0>@{workload}", "prefill"),
                 "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
                 "flops_per_launch": fl_gu, "timing": "dispatch-events"}
+    layer = {"flops_per_step": fl_gu + fl_dn,
+             "TFLOPs_per_step": (fl_gu + fl_dn) / step_s / 1e12,
+             "fp4_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / FP4_PEAK_TFLOPS,
+             "bf16_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / BF16_PEAK_TFLOPS,
+             "down_kernel_us": dn_us,
+             "down_TFLOPs": fl_dn / (dn_us * 1e-6) / 1e12,
+             # algorithmic FLOPs over the two grouped GEMMs' summed kernel time
+             "grouped_gemm_TFLOPs": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12,
+             "grouped_gemm_peak_frac": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12 / peak,
+             "peak_TFLOPs": peak}
+    return dict(tokens_per_s=T * K / dt, ms_per_step=step_s * 1e3, roofline=roof, layer=layer,
+                xh=xh)
+
+
+def prefill_config(cfg, T, workload, s1):
+    return {"workload": workload, "tokens": T, "hidden": cfg.H, "intermediate": cfg.I,
+            "experts": cfg.E, "top_k": cfg.k, "weights": cfg.fmt,
+            "mode": "mxfp4-scaled-fp4-mfma" if s1 else "exact-bf16-mfma"}
+
+
+def bench_prefill(args, wl):
+    from mxfp4_expert_layer_amd import ft, synth
+    from mxfp4_expert_layer_amd.layer import GpuLayer
+
+    cfg = synth.CONFIGS[wl["cfg"]]
+    T = args.tokens or wl["T"]
+    K = args.steps if args.steps is not None else wl["steps"]
+    W = args.warmup if args.warmup is not None else wl["warmup"]
+    ctx = ft.Context(0)
+    s1 = wl.get("mode") == "mxfp4"
+    log(f"[bench] building {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I}, {cfg.fmt})")
+    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16, prefill_mxfp4=s1)
+    r = prefill_run(ctx, L, cfg, T, K, W, s1, args.workload)
+    roof = r["roofline"]
+    if s1:
+        roof.update(read_reference(ctx, roof["achieved"]))
     res = {
-        "metric": METRIC, "value": T * K / dt, "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4" if s1 else "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "hidden": cfg.H,
-                   "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k, "weights": cfg.fmt,
-                   "mode": "mxfp4-scaled-fp4-mfma" if s1 else "exact-bf16-mfma"},
-        "roofline": roof,
-        "layer": {"flops_per_step": fl_gu + fl_dn,
-                  "TFLOPs_per_step": (fl_gu + fl_dn) / step_s / 1e12,
-                  "fp4_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / FP4_PEAK_TFLOPS,
-                  "bf16_peak_frac": (fl_gu + fl_dn) / step_s / 1e12 / BF16_PEAK_TFLOPS,
-                  "down_kernel_us": dn_us,
-                  "down_TFLOPs": fl_dn / (dn_us * 1e-6) / 1e12,
-                  # algorithmic FLOPs over the two grouped GEMMs' summed kernel time
-                  "grouped_gemm_TFLOPs": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12,
-                  "grouped_gemm_peak_frac": (fl_gu + fl_dn) / ((gu_us + dn_us) * 1e-6) / 1e12
-                  / (FP4_PEAK_TFLOPS if s1 else BF16_PEAK_TFLOPS)},
+        "config": prefill_config(cfg, T, args.workload, s1),
+        "roofline": roof, "layer": r["layer"],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline_prefill(cfg, xh[0], args.cpu_seconds,
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, r["xh"][0], args.cpu_seconds,
                                                    "mxfp4" if s1 else "exact")
     L.close()
+    ctx.close()
+    return res
+
+
+def bench_headline(args):
+    """The default line: the 753B-class prefill of 4096 tokens in the exact mode (bf16
+    activations, bf16 MFMA) is `value`, with its gate/up grouped GEMM as the roofline kernel.
+    The same run adds the scaled-FP4 mode of that layer (tokens/s, its gate/up kernel's HBM
+    and FP4 MFMA fractions, both grouped GEMMs' FP4 fraction) and the 284B-class decode at 1,
+    4 and 16 tokens per step (tokens/s and HBM fractions), as extra keys."""
+    from mxfp4_expert_layer_amd import ft, synth
+    from mxfp4_expert_layer_amd.layer import GpuLayer
+
+    wl = WORKLOADS["prefill-753b"]
+    cfg = synth.CONFIGS[wl["cfg"]]
+    T = wl["T"]
+    K = args.steps if args.steps is not None else wl["steps"]
+    W = args.warmup if args.warmup is not None else wl["warmup"]
+    ctx = ft.Context(0)
+    log(f"[bench] building {cfg.name} (E={cfg.E}, H={cfg.H}, I={cfg.I}, {cfg.fmt}) with its "
+        f"MXFP4 transcode")
+    L = GpuLayer(ctx, cfg, resident=True, max_tokens=1, threads=16, prefill_mxfp4=True)
+    r0 = prefill_run(ctx, L, cfg, T, K, W, False, "prefill-753b")
+    r1 = prefill_run(ctx, L, cfg, T, K, W, True, "prefill-753b-mxfp4")
+    L.close()
+    del L
+    ref = read_reference(ctx, r1["roofline"]["achieved"])
+    r1["roofline"].update(ref)
+    Ts = (1, 4, 16)
+    dec = decode_sweep(ctx, "cfg3", Ts, copies=4)
+    for v in dec.values():
+        v["gateup_frac_of_measured_read"] = v["gateup_GBps"] / ref["measured_read_GBps"]
+    res = {
+        "metric": METRIC, "value": r0["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": r0["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": prefill_config(cfg, T, "prefill-753b-T4096", False),
+        "roofline": r0["roofline"], "layer": r0["layer"],
+        "prefill_mxfp4": {"tokens_per_s": r1["tokens_per_s"], "ms_per_step": r1["ms_per_step"],
+                          "dtype": "mxfp4", "roofline": r1["roofline"], "layer": r1["layer"]},
+        "decode_284b": {"config": {"hidden": 4096, "intermediate": 2048, "experts": 256,
+                                   "top_k": 6, "shared_experts": 1, "weights": "mxfp4",
+                                   "layer_copies": 4, "graph_replay": True},
+                        "measured_read_GBps": ref["measured_read_GBps"], **dec},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, r0["xh"][0], args.cpu_seconds, "exact")
     ctx.close()
     return res
 
@@ -586,7 +722,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode-35b-a3b", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="headline", choices=["headline"] + sorted(WORKLOADS))
     ap.add_argument("--tokens", type=int, default=None, help="decode tokens per step")
     ap.add_argument("--copies", type=int, default=None, help="device copies of the layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -617,6 +753,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         print(json.dumps(copy_probe(args)), flush=True)
+        return
+    if args.workload == "headline":
+        print(json.dumps(bench_headline(args)), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if args.workload == "miss-path-284b":

@@ -85,13 +85,16 @@ def swiglu_ffn(xs: np.ndarray, wg, wu, wd, h_quant=None) -> np.ndarray:
 
 
 def expert_outputs(layer, x: np.ndarray, idx: np.ndarray, mode: str = "exact",
-                   threads: int = 1):
+                   threads: int = 1, weights_fn=None):
     """Per-(t, j) expert outputs y_{t,j} [T][k][H] and shared outputs [T][n_shared][H].
 
     Each selected (token, expert) pair is evaluated by the definition above; tokens sharing
     an expert are evaluated together with one matmul (a library primitive), which changes
     nothing but the order of independent rows.  threads > 1 evaluates distinct experts
-    concurrently (each writes only its own rows)."""
+    concurrently (each writes only its own rows).  weights_fn(e), when given, supplies routed
+    expert e's weights after the mode's weight transform (the caller computes the same values,
+    e.g. to check them against another implementation on the way); it is called once per
+    expert, from the worker threads."""
     cfg = layer.cfg
     T, k = idx.shape
     ys = np.zeros((T, k, cfg.H))
@@ -100,7 +103,10 @@ def expert_outputs(layer, x: np.ndarray, idx: np.ndarray, mode: str = "exact",
 
     def one(e):
         tt, jj = np.nonzero(idx == e)
-        wg, wu, wd = wq(expert_weights(layer, layer.expert(int(e))))
+        if weights_fn is not None:
+            wg, wu, wd = weights_fn(int(e))
+        else:
+            wg, wu, wd = wq(expert_weights(layer, layer.expert(int(e))))
         ys[tt, jj] = swiglu_ffn(xq[tt], wg, wu, wd, hq)
 
     experts = [int(e) for e in np.unique(idx)]
@@ -123,12 +129,14 @@ def combine(w: np.ndarray, ys: np.ndarray, sh: np.ndarray) -> np.ndarray:
     return np.einsum("tj,tjh->th", w, ys) + sh.sum(axis=1)
 
 
-def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact", threads: int = 1):
+def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact", threads: int = 1,
+                weights_fn=None):
     """The whole layer on bf16 tokens x_bits (uint16 [T][H]).
 
     ``idx`` overrides the routing choice (its weights are then recomputed from the oracle's
     own logits), which the tests use when a near-tie makes two index sets valid.
     mode "exact" is the bf16-activation layer; "mxfp4" is the S1 variant (see ``mxq``).
+    ``weights_fn``: see ``expert_outputs``.
     Returns dict(y, idx, w, logits, gap)."""
     cfg = layer.cfg
     x = fp4.bf16_bits_to_f64(x_bits)
@@ -139,7 +147,7 @@ def moe_forward(layer, x_bits: np.ndarray, idx=None, mode: str = "exact", thread
         p = np.exp(sel - sel.max(axis=1, keepdims=True))
         r_w = p / p.sum(axis=1, keepdims=True)
         r_idx = idx
-    ys, sh = expert_outputs(layer, x, r_idx, mode, threads)
+    ys, sh = expert_outputs(layer, x, r_idx, mode, threads, weights_fn)
     y = combine(r_w, ys, sh)
     return dict(y=y, idx=r_idx, w=r_w, logits=logits, gap=gap, ys=ys, shared=sh)
 

@@ -21,7 +21,7 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_workloads_and_options():
     r = _run("--help")
     assert r.returncode == 0
-    for w in ("decode-35b-a3b", "decode-35b-a3b-nvfp4", "decode-284b", "miss-path-284b",
+    for w in ("headline", "decode-35b-a3b", "decode-35b-a3b-nvfp4", "decode-284b", "miss-path-284b",
               "prefill-753b", "prefill-753b-mxfp4"):
         assert w in r.stdout
     for opt in ("--layers", "--prefetch", "--residual-scale", "--disk-dir", "--ram-slots",

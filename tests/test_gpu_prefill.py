@@ -89,7 +89,7 @@ def prefill_weights(L, e):
     return tiled.matrices(blob, "mxfp4", cfg.H, cfg.I)
 
 
-def check_s1_weights(L, OL, e, threads=1):
+def check_s1_weights(L, OL, e, threads=1, got=None):
     """The expert's MXFP4 weights against the oracle's requantisation of its exact weights:
     codes and scales bit-exact for a transcoded NVFP4 expert, values for an MXFP4 pool blob
     (requantising keeps an MXFP4 block's values but may re-express its codes).  Returns the
@@ -98,7 +98,8 @@ def check_s1_weights(L, OL, e, threads=1):
     ws = moe.expert_weights(OL, OL.expert(e))
     with ThreadPoolExecutor(max_workers=max(1, threads)) as pool:
         qs = list(pool.map(mxq.quantize, ws))
-    got = prefill_weights(L, e)
+    if got is None:
+        got = prefill_weights(L, e)
     out = []
     for m, ((c, s), (gc, gs)) in enumerate(zip(qs, got)):
         if L.cfg.fmt == synth.NVFP4:
@@ -188,9 +189,34 @@ def test_prefill_rejects_bad_calls(ctx):
         bare.close()
 
 
+def cfg5_sample(idx, E, n=256, seed=0):
+    """A seeded sample of n tokens that routes to every expert: for each expert the last token
+    routed to it (its row is the last row of the expert's last row block, in every block size
+    the grouped GEMMs use), then first tokens of experts, then random tokens."""
+    rng = np.random.default_rng(seed)
+    T = idx.shape[0]
+    last, first = [], []
+    for e in range(E):
+        tt = np.nonzero((idx == e).any(axis=1))[0]
+        if len(tt):
+            last.append(int(tt[-1]))
+            first.append(int(tt[0]))
+    pick = set(last)
+    for t in rng.permutation(first):
+        if len(pick) >= n:
+            break
+        pick.add(int(t))
+    while len(pick) < n:
+        pick.add(int(rng.integers(0, T)))
+    sample = np.array(sorted(pick))
+    assert set(np.unique(idx[sample])) == set(np.unique(idx))
+    return sample
+
+
 def test_prefill_753b_layer(ctx):
     """The 753B-class NVFP4 layer at T = 4096: routing and the full permutation checked
-    exactly, outputs checked on sampled tokens (the oracle evaluates those tokens only)."""
+    exactly; outputs checked on a seeded sample of 256 tokens that routes to all 160 experts,
+    including each expert's last row (the oracle evaluates those tokens only)."""
     cfg = synth.CONFIGS["cfg5"]
     L = layer_for(ctx, "cfg5", cfg, threads=16)
     T = 4096
@@ -203,9 +229,10 @@ def test_prefill_753b_layer(ctx):
     r_idx, r_w, logits, gap = moe.route(xr, OL.router_w, OL.router_b, cfg.k)
     check_routing(idx, w, dict(idx=r_idx, w=r_w, logits=logits, gap=gap))
     _check_perm(idx, counts, offsets, pos, cfg.E)
-    assert counts.sum() == T * cfg.k
-    sample = np.array([0, 1377, 2900, T - 1])
-    ref = moe.moe_forward(OL, x[sample], idx=idx[sample])
+    assert counts.sum() == T * cfg.k and np.all(counts > 0)
+    sample = cfg5_sample(idx, cfg.E)
+    log(f"[gpu] oracle on {len(sample)} sampled tokens ({len(np.unique(idx[sample]))} experts)")
+    ref = moe.moe_forward(OL, x[sample], idx=idx[sample], threads=16)
     check_output(y[sample], ref["y"], "753b-class sampled tokens")
     assert np.all(np.isfinite(y))
 
@@ -304,8 +331,13 @@ def test_prefill_mxfp4_is_deterministic(ctx):
 
 def test_prefill_mxfp4_753b_layer(ctx):
     """The 753B-class NVFP4 layer at T = 4096 in the scaled-FP4 mode: routing, permutation and
-    all quantised tokens exact; one expert's transcoded weights bit-exact and its quantised h
-    rows checked; one sampled token's output against the oracle's "mxfp4" mode."""
+    all quantised tokens exact; all 160 transcoded experts bit-exact (codes and scales); the
+    quantised h rows and the outputs of a seeded 256-token sample that routes to every expert
+    (each expert's last row included) against the oracle's "mxfp4" mode.  Each expert's
+    weights are requantised by the oracle once: the transcode check and the oracle's forward
+    pass use the same values."""
+    import threading
+
     cfg = synth.CONFIGS["cfg5"]
     L = layer_for(ctx, "cfg5", cfg, threads=16)
     T = 4096
@@ -320,15 +352,31 @@ def test_prefill_mxfp4_753b_layer(ctx):
     _check_perm(idx, counts, offsets, pos, cfg.E)
     xc, xs = prefill_quant(L, ws, T, 0)
     check_mx_quant(xc, xs, xr, "tokens", exact=True)
-    t_s = 2049
-    e = int(idx[t_s, 0])
-    log(f"[gpu] checking transcoded expert {e} and its h rows")
-    wg, wu, _ = check_s1_weights(L, OL, e, threads=3)
     hc, hs = prefill_quant(L, ws, T, 1)
-    tt, jj = np.nonzero(idx == e)
-    xq = mxq.quantize_dequant(xr[tt])
-    nd = check_mx_quant(hc[pos[tt, jj]], hs[pos[tt, jj]], moe.swiglu_hidden(xq, wg, wu), "h")
-    log(f"[gpu] 753b h: {len(tt)} rows, {nd} boundary decisions; oracle output of token {t_s}")
-    ref = moe.moe_forward(OL, x[[t_s]], idx=idx[[t_s]], mode="mxfp4", threads=16)
-    check_output(y[[t_s]], ref["y"], "753b-class mxfp4 sampled token")
+    sample = cfg5_sample(idx, cfg.E, seed=1)
+    xq = mxq.quantize_dequant(xr[sample])
+    # the GPU's MXFP4 blobs of all experts, read before the oracle's worker threads start
+    blobs = {e: prefill_weights(L, e) for e in range(cfg.E)}
+    lock = threading.Lock()
+    done, ndiff = [], [0]
+
+    def weights_fn(e):
+        deq = check_s1_weights(L, OL, e, got=blobs.pop(e))
+        # h of the sampled rows routed to e, from the oracle's own quantised operands
+        tt, jj = np.nonzero(idx[sample] == e)
+        nd = check_mx_quant(hc[pos[sample[tt], jj]], hs[pos[sample[tt], jj]],
+                            moe.swiglu_hidden(xq[tt], deq[0], deq[1]), f"h of {e}")
+        with lock:
+            done.append(e)
+            ndiff[0] += nd
+            if len(done) % 32 == 0:
+                log(f"[gpu] 753b mxfp4: {len(done)} experts checked")
+        return tuple(deq)
+
+    log(f"[gpu] oracle on {len(sample)} sampled tokens, all {cfg.E} experts requantised")
+    ref = moe.moe_forward(OL, x[sample], idx=idx[sample], mode="mxfp4", threads=16,
+                          weights_fn=weights_fn)
+    assert sorted(done) == list(range(cfg.E))
+    log(f"[gpu] 753b mxfp4: {ndiff[0]} h decisions at fp32/fp64 boundaries")
+    check_output(y[sample], ref["y"], "753b-class mxfp4 sampled tokens")
     assert np.all(np.isfinite(y))

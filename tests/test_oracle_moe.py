@@ -298,3 +298,26 @@ def test_mxfp4_mode_hand_layer_catches_plausible_mistakes(monkeypatch):
         monkeypatch.setattr(moe, "mode_ops", lambda mode, ops=ops: ops)
         y = moe.moe_forward(L, x, mode="mxfp4")["y"]
         assert not np.array_equal(y[0, :2], good), name
+
+
+@pytest.mark.parametrize("mode", ["exact", "mxfp4"])
+def test_weights_fn_with_the_modes_own_weights_changes_nothing(mode):
+    """moe_forward's weights_fn hook (a caller supplying each expert's transformed weights)
+    gives the same y as the default path when it supplies what the mode computes, and is
+    called once per routed expert; supplying other weights changes y."""
+    from oracle import mxq
+    L = _tiny(41, E=5, k=2, H=64, I=32, fmt=synth.NVFP4, nv_tensor_scale=0.25)
+    x = synth.gen_tokens(L.cfg, 6, batch=2)
+    ref = moe.moe_forward(L, x, mode=mode)
+    _, _, wq = moe.mode_ops(mode)
+    calls = []
+
+    def fn(e):
+        calls.append(e)
+        return wq(moe.expert_weights(L, L.expert(e)))
+    got = moe.moe_forward(L, x, mode=mode, weights_fn=fn)
+    assert np.array_equal(got["y"], ref["y"])
+    assert sorted(calls) == sorted(set(int(e) for e in np.unique(ref["idx"])))
+    other = moe.moe_forward(L, x, mode=mode, weights_fn=lambda e: tuple(
+        2.0 * w for w in wq(moe.expert_weights(L, L.expert(e)))))
+    assert not np.array_equal(other["y"], ref["y"])
