@@ -33,6 +33,15 @@ class FtError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libft.so not found at {LIB_PATH}: build it with "
                       "`python -m mxfp4_expert_layer_amd.build` (no fallback path exists)")
+# torch carries its own HIP runtime under the same soname (libamdhip64.so.7) as the ROCm one
+# libft is linked against, and a process holds one copy of a soname: whichever loads first
+# serves both.  torch's own HIP libraries need the runtime they were built with, so torch is
+# loaded first and libft binds to that same runtime (the buffers and streams it is handed
+# come from it).
+try:
+    import torch  # noqa: F401
+except ImportError:   # a process without torch uses the ROCm runtime libft is linked against
+    pass
 lib = C.CDLL(LIB_PATH)
 
 
