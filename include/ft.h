@@ -210,6 +210,23 @@ FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T
                           int mode, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ft_moe_prefill without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops or harnesses that forbid allocation).  The same
+ * kernels run with their workspace in a static device array of
+ * FT_PREFILL_STATIC_SCRATCH_BYTES that the library's code object holds on every GPU it runs on
+ * until the process ends; the call itself allocates nothing.  The caller still passes x
+ * (device bf16 [T][H]) and y (device fp32 [T][H]); results and errors are those of
+ * ft_moe_prefill, plus FT_EINVAL when the call's workspace
+ * (ft_moe_prefill_workspace_size(layer, T, mode)) exceeds the static array.  Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents: calls that overlap
+ * on one GPU (on different streams, or from different contexts or threads) race and must be
+ * serialised by the caller.  Asynchronous on `stream`.
+ */
+#define FT_PREFILL_STATIC_SCRATCH_BYTES (64u << 20)
+FT_API int ft_moe_prefill_noalloc(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
+                                  float* y, int mode, void* stream);
+
+/*
  * The split rule (smzdm explainer a825qpgl, section 二; lowalt.boxinlu2.cn article,
  * section 二): qstar = m * Bp / Bh; q = floor(qstar + 1/2) clamped to [0, m] (Bh <= Bp
  * gives m).  FT_EINVAL if m < 0, Bp <= 0 or Bh <= 0.  Pure host function.

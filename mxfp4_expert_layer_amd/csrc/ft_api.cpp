@@ -39,6 +39,7 @@ extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes,
 extern "C" int ftk_prefill(const PrefillLaunch* a, hipStream_t st, const hipEvent_t* ev);
 extern "C" int ftk_nv_to_mx(const uint8_t* src, uint8_t* dst, const BlobLayout* S,
                             const BlobLayout* D, hipStream_t st);
+extern "C" int ftk_static_scratch(int device, void** addr, size_t* bytes);
 extern "C" int ftk_untile_h(const PrefillLaunch* a, uint8_t* codes, uint8_t* scales,
                             hipStream_t st);
 
@@ -67,6 +68,10 @@ struct ft_ctx {
   int device = 0;
   hipStream_t copy_stream = nullptr;
   std::unique_ptr<ThreadPool> pool;
+  // device address and size of the library's static scratch on this device
+  // (ft_moe_prefill_noalloc), looked up once per device at context creation
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
 };
 
 namespace ft {
@@ -231,6 +236,7 @@ extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) try {
   std::unique_ptr<ft_ctx> c(new (std::nothrow) ft_ctx);
   if (!c) return fail(FT_ENOMEM, "ft_ctx_create: out of host memory");
   c->device = device;
+  HIP_TRY((hipError_t)ftk_static_scratch(device, &c->scratch, &c->scratch_bytes));
   HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
   const int hw = (int)std::thread::hardware_concurrency();
   const int nt = env_int("FT_HOST_THREADS", std::max(1, std::min(16, hw)));
@@ -1314,16 +1320,9 @@ extern "C" FT_API int ft_moe_prefill_workspace_size(const ft_layer* layer, int T
   return FT_OK;
 } FT_CATCH("ft_moe_prefill_workspace_size")
 
-extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
-                                     float* y, int mode, void* ws, size_t ws_bytes,
-                                     void* stream) try {
-  int rc = prefill_check(layer, T, mode, "ft_moe_prefill");
-  if (rc) return rc;
-  if (!ctx || !x || !y || !ws) return fail(FT_EINVAL, "ft_moe_prefill: null argument");
-  if (layer->ctx != ctx) return fail(FT_EINVAL, "ft_moe_prefill: layer of another context");
-  if ((uintptr_t)ws % 256) return fail(FT_EINVAL, "ft_moe_prefill: ws must be 256-byte aligned");
-  const size_t need = prefill_carve(layer, T, mode, nullptr, nullptr);
-  if (ws_bytes < need) return fail(FT_EINVAL, "ft_moe_prefill: workspace too small");
+// One prefill call's launches over the workspace ws (checked by the caller).
+static int prefill_launch(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T, float* y,
+                          int mode, void* ws, void* stream) {
   const ft_layer_desc& d = layer->d;
   HIP_TRY(hipSetDevice(ctx->device));
   PrefillLaunch a{};
@@ -1344,7 +1343,37 @@ extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_
   a.y = y;
   HIP_TRY((hipError_t)ftk_prefill(&a, (hipStream_t)stream, prof_events(layer)));
   return FT_OK;
+}
+
+extern "C" FT_API int ft_moe_prefill(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
+                                     float* y, int mode, void* ws, size_t ws_bytes,
+                                     void* stream) try {
+  int rc = prefill_check(layer, T, mode, "ft_moe_prefill");
+  if (rc) return rc;
+  if (!ctx || !x || !y || !ws) return fail(FT_EINVAL, "ft_moe_prefill: null argument");
+  if (layer->ctx != ctx) return fail(FT_EINVAL, "ft_moe_prefill: layer of another context");
+  if ((uintptr_t)ws % 256) return fail(FT_EINVAL, "ft_moe_prefill: ws must be 256-byte aligned");
+  const size_t need = prefill_carve(layer, T, mode, nullptr, nullptr);
+  if (ws_bytes < need) return fail(FT_EINVAL, "ft_moe_prefill: workspace too small");
+  return prefill_launch(ctx, layer, x, T, y, mode, ws, stream);
 } FT_CATCH("ft_moe_prefill")
+
+// The workspace is the static scratch looked up at ft_ctx_create: nothing is allocated here.
+extern "C" FT_API int ft_moe_prefill_noalloc(ft_ctx* ctx, ft_layer* layer, const uint16_t* x,
+                                             int T, float* y, int mode, void* stream) try {
+  int rc = prefill_check(layer, T, mode, "ft_moe_prefill_noalloc");
+  if (rc) return rc;
+  if (!ctx || !x || !y) return fail(FT_EINVAL, "ft_moe_prefill_noalloc: null argument");
+  if (layer->ctx != ctx)
+    return fail(FT_EINVAL, "ft_moe_prefill_noalloc: layer of another context");
+  if (!ctx->scratch) return fail(FT_ESTATE, "ft_moe_prefill_noalloc: no static scratch");
+  const size_t need = prefill_carve(layer, T, mode, nullptr, nullptr);
+  if (need > ctx->scratch_bytes)
+    return fail(FT_EINVAL, "ft_moe_prefill_noalloc: T = " + std::to_string(T) + " needs " +
+                               std::to_string(need) + " workspace bytes, more than the " +
+                               std::to_string(ctx->scratch_bytes) + " of the static scratch");
+  return prefill_launch(ctx, layer, x, T, y, mode, ctx->scratch, stream);
+} FT_CATCH("ft_moe_prefill_noalloc")
 
 extern "C" FT_API int ft_debug_prefill_perm(const ft_layer* layer, const void* ws, int T,
                                             int32_t* counts, int32_t* offsets, int32_t* pos,

@@ -85,6 +85,7 @@ _sig = {
     "ft_moe_decode": [_vp, _vp, _vp, _i, _vp, C.POINTER(DecodeStats), _vp],
     "ft_moe_prefill_workspace_size": [_vp, _i, _i, C.POINTER(C.c_size_t)],
     "ft_moe_prefill": [_vp, _vp, _vp, _i, _vp, _i, _vp, C.c_size_t, _vp],
+    "ft_moe_prefill_noalloc": [_vp, _vp, _vp, _i, _vp, _i, _vp],
     "ft_qstar_split": [_i, _d, _d, C.POINTER(_i), C.POINTER(_d)],
     "ft_measure_bandwidth": [_vp, _vp, C.POINTER(_d), C.POINTER(_d)],
     "ft_set_bandwidth": [_vp, _d, _d],
@@ -222,6 +223,14 @@ def moe_prefill_workspace_size(layer_h, T, mode) -> int:
 def moe_prefill(ctx, layer_h, x, T, y, mode, ws, ws_bytes, stream=None):
     check(lib.ft_moe_prefill(ctx.handle, layer_h, _ptr(x), T, _ptr(y), mode, _ptr(ws), ws_bytes,
                              stream))
+
+
+# bytes of the library's static device scratch behind ft_moe_prefill_noalloc
+PREFILL_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_prefill_noalloc(ctx, layer_h, x, T, y, mode, stream=None):
+    check(lib.ft_moe_prefill_noalloc(ctx.handle, layer_h, _ptr(x), T, _ptr(y), mode, stream))
 
 
 def measure_bandwidth(ctx, layer_h):
