@@ -1,6 +1,8 @@
 """Build libft.so in-tree: HIP kernels for gfx950 with hipcc, host runtime with g++.
 
 Usage: python -m mxfp4_expert_layer_amd.build   (or call build()).  Always recompiles.
+       python -m mxfp4_expert_layer_amd.build --sanitize address|thread   (host runtime under
+       ASan + UBSan or TSan, for the CPU tests; see build_sanitized).
 """
 from __future__ import annotations
 
@@ -60,5 +62,53 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+SANITIZERS = {
+    # kind -> g++ flags of the host runtime (the HIP objects are the ordinary ones)
+    "address": ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"],
+    "thread": ["-fsanitize=thread"],
+}
+
+
+def sanitizer_runtime(kind: str) -> str:
+    """The shared sanitizer runtime a process must preload to load the sanitized library."""
+    name = {"address": "libasan.so", "thread": "libtsan.so"}[kind]
+    return subprocess.run(["g++", f"-print-file-name={name}"], stdout=subprocess.PIPE,
+                          text=True, check=True).stdout.strip()
+
+
+def build_sanitized(kind: str) -> str:
+    """libft_<kind>.so: the host runtime (thread pool, LRU, host FFN, FTW files, C ABI) built
+    by g++ with AddressSanitizer + UndefinedBehaviorSanitizer ("address") or ThreadSanitizer
+    ("thread"), linked with the ordinary gfx950 kernel objects (sanitizers apply to host code
+    only).  Load it with FT_LIB and the runtime from sanitizer_runtime() preloaded."""
+    if kind not in SANITIZERS:
+        raise ValueError(f"unknown sanitizer {kind!r}")
+    os.makedirs(BUILD, exist_ok=True)
+    hip_objs = []
+    jobs = []
+    for s in HIP_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        hip_objs.append(o)
+        if not os.path.exists(o):
+            jobs.append([f"{ROCM}/bin/hipcc", *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+    objs = []
+    flags = [f for f in CXX_FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer",
+                                                    *SANITIZERS[kind]]
+    for s in CXX_SOURCES:
+        o = os.path.join(BUILD, f"{s}.{kind}.o")
+        objs.append(o)
+        jobs.append(["g++", *flags, "-c", os.path.join(CSRC, s), "-o", o])
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        list(ex.map(_run, jobs))
+    out = os.path.join(HERE, f"libft_{kind}.so")
+    _run(["g++", "-shared", "-o", out + ".tmp", *objs, *hip_objs, *SANITIZERS[kind], "-pthread",
+          f"-L{ROCM}/lib", f"-Wl,-rpath,{ROCM}/lib", "-lamdhip64"])
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(sys.argv[sys.argv.index("--sanitize") + 1]))
+    else:
+        print(build(verbose="-v" in sys.argv))

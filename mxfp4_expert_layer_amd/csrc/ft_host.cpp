@@ -232,7 +232,10 @@ static void gemv_tiles_mx_avx512(const BlobLayout& L, const uint8_t* codes,
           const __m512i bytes = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)(c + 16 * l)));
           const __m512i idx = _mm512_or_si512(_mm512_and_si512(bytes, m15),
                                               _mm512_slli_epi32(_mm512_srli_epi32(bytes, 4), 16));
-          const __m512i shift = _mm512_set1_epi16((short)((int)sc[l] - 127) << 7);
+          // (s - 127) << 7 as a 16-bit two's-complement pattern (unsigned arithmetic: a left
+          // shift of a negative value is undefined)
+          const __m512i shift =
+              _mm512_set1_epi16((short)(uint16_t)(((uint32_t)sc[l] - 127u) << 7));
           const __m512i table = _mm512_mask_add_epi16(base, nonzero, base, shift);
           const __m512bh w = (__m512bh)_mm512_permutexvar_epi16(idx, table);
           acc[l & 15] = _mm512_dpbf16_ps(acc[l & 15], w, xv[l >> 4]);

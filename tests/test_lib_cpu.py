@@ -94,8 +94,9 @@ def test_host_expert_ffn_matches_oracle(fmt, T, scalar, monkeypatch):
 
 def test_bad_arguments_return_einval():
     with pytest.raises(ft.FtError) as e:
-        ft.host_expert_ffn("mxfp4", 256, 128, np.zeros(16, np.uint8), np.zeros((1, 256), np.uint16))
-    assert e.value.code == ft.FT_EINVAL          # blob header mismatch
+        ft.host_expert_ffn("mxfp4", 256, 128, np.zeros(ft.blob_bytes("mxfp4", 256, 128), np.uint8),
+                           np.zeros((1, 256), np.uint16))
+    assert e.value.code == ft.FT_EINVAL          # a whole blob whose header is not one
     with pytest.raises(ft.FtError) as e:
         ft.pack_expert("mxfp4", 250, 128, synth.gen_expert(synth.small_config(H=256, I=128), 0))
     assert e.value.code == ft.FT_EINVAL
