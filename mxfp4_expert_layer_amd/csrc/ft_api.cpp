@@ -1252,6 +1252,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* tb_off = take((size_t)(d.E + 1) * 4);
   uint8_t* pos = take(pairs * 4);
   uint8_t* perm_tok = take(pairs * 4);
+  uint8_t* perm_w = take(pairs * 4);
   const bool mx = mode == FT_PREFILL_MXFP4;
   uint8_t* hperm = mx ? nullptr : take(pairs * d.I * 2);
   uint8_t* xq = mx ? take((size_t)T * d.H / 2) : nullptr;
@@ -1263,9 +1264,10 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* xts = mx ? take(prows * d.H / 32) : nullptr;
   uint8_t* ht = mx ? take(prows * d.I / 2) : nullptr;
   uint8_t* hts = mx ? take(prows * d.I / 32) : nullptr;
-  uint8_t* yperm = take(pairs * d.H * (mx ? 3 : 4));   // S1: 24-bit floats
-  // MXFP4 mode: the expert of each kS1Rows-row token block (at most pairs / kS1Rows + E)
-  uint8_t* blk_e = mx ? take(((pairs + kS1Rows - 1) / kS1Rows + d.E) * 4) : nullptr;
+  uint8_t* yperm = mx ? take(pairs * d.H * 3) : nullptr;   // S1: 24-bit floats
+  // the expert of each token block (at most pairs / rows + E blocks of `rows` rows)
+  const size_t brows = mx ? kS1Rows : kGemmM;
+  uint8_t* blk_e = take(((pairs + brows - 1) / brows + d.E) * 4);
   uint8_t* tile_e = mx ? take(prows / 16 * 4) : nullptr;   // expert of each 16-row tile row
   if (a) {
     a->logits = (float*)logits;
@@ -1279,6 +1281,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     a->tb_off = (int32_t*)tb_off;
     a->pos = (int32_t*)pos;
     a->perm_tok = (int32_t*)perm_tok;
+    a->perm_w = (float*)perm_w;
     a->hperm = (uint16_t*)hperm;
     a->xq = xq;
     a->xqs = xqs;

@@ -122,8 +122,7 @@ struct RouteSmall {
 
 // Prefill of T tokens through an all-resident layer (slot e = expert e).
 constexpr int kPermBlock = 256;   // tokens per permutation block (one mask word per 32)
-constexpr int kGemmM = 128;       // tokens per grouped-GEMM block
-constexpr int kGemmN = 128;       // weight rows per grouped-GEMM block
+constexpr int kGemmM = 256;       // token rows per exact-mode grouped-GEMM block
 constexpr int kS1Rows = 256;      // token rows per scaled-FP4 grouped-GEMM block
 
 // Prefill router: 128 tokens per workgroup, up to 6 tiles of 32 experts per workgroup, and the
@@ -172,10 +171,11 @@ struct PrefillLaunch {
   int32_t* offsets;             // [E+1]
   int32_t* base;                // [T/256][E]
   int32_t* tb_off;              // [E+1] prefix of mrows-row token blocks per expert
-  int32_t* blk_e;               // MXFP4 mode: [T*k/mrows + E] expert of each token block
+  int32_t* blk_e;               // [T*k/mrows + E] expert of each token block
   int32_t* tile_e;              // MXFP4 mode: [P/16] expert of each padded 16-row tile row
   int32_t* pos;                 // [T][k]
-  int32_t* perm_tok;            // [T*k]
+  int32_t* perm_tok;            // [T*k] token of each permuted row
+  float* perm_w;                // [T*k] routing weight of each permuted row
   uint16_t* hperm;              // [T*k][I] bf16 (exact mode)
   uint8_t* xq;                  // MXFP4 mode: quantised x, codes [T][H/2]
   uint8_t* xqs;                 //   and E8M0 scales [T][H/32]
@@ -188,7 +188,7 @@ struct PrefillLaunch {
   uint8_t* xts;                 //   scales [P/16][H/128][64 B]
   uint8_t* ht;                  // quantised h rows: codes [P/16][I/128][1 KB]
   uint8_t* hts;                 //   scales [P/16][I/128][64 B]
-  float* Yperm;                 // [T*k][H] fp32; MXFP4 mode: 24-bit floats, 4 in 12 bytes
+  float* Yperm;                 // MXFP4 mode: [T*k][H] 24-bit floats, 4 in 12 bytes
   float* y;                     // [T][H]
 };
 

@@ -11,16 +11,18 @@
 //   k_topk_many       logits = sum of the partials in order + b; per-token top-k + softmax
 //                     (the decode routine, 16 tokens a workgroup).
 //   k_perm_masks      per 256-token block: a token bitmask per expert (LDS atomics).
-//   k_perm_scan       counts, offsets (exclusive scan), per-block bases, 128-row block map.
+//   k_perm_scan       counts, offsets (exclusive scan), per-block bases, the row-block map.
 //   k_perm_place      pos[t][j] = base + (tokens below t in the block's mask); the row of
 //                     every pair, expert ascending then token ascending (stable).
-//   k_ggemm<0>        per (expert, 128-token block, 64 gate + 64 up features): G, U on the
-//                     32x32x16 bf16 MFMA with NVFP4 weights decoded to bf16 in LDS (E2M1 x E4M3 has at
-//                     most 6 significant bits, so the decode is exact; the fp32 tensor scale
-//                     is applied in the epilogue), h = bf16(silu(ts_g G) * (ts_u U)).
-//   k_ggemm<1>        per (expert, token block, 128 rows of W_d): Y_perm = ts_d (W_d h).
-//   k_unpermute       y[t] = sum_j w[t][j] Y_perm[pos[t][j]].
-// The scaled-FP4 mode replaces the two GEMMs (both operands FP4):
+//   k_zero            y = 0 (the down GEMM adds into it).
+//   k_xgemm<0>        per (expert, 256-row block, 128 gate + 128 up features): G, U on the
+//                     32x32x16 bf16 MFMA with the FP4 weights decoded to bf16 in registers
+//                     (E2M1 x E4M3 has at most 6 significant bits, so the decode is exact; the
+//                     fp32 tensor scale is applied in the epilogue), h = bf16(silu(ts_g G) *
+//                     (ts_u U)).
+//   k_xgemm<1>        per (expert, 256-row block, 256 rows of W_d): y[t] += w ts_d (W_d h) for
+//                     each row's token t and routing weight w (the combine, as atomic adds).
+// The scaled-FP4 mode replaces the two GEMMs (both operands FP4) and combines separately:
 //   k_quant_x         x -> MXFP4 per 32 along H (OCP MX rule), once per token.
 //   k_tile_xq         the quantised rows, in permuted order with every expert padded to a
 //                     multiple of 16 rows, into the tile format of the GEMM operand.
@@ -28,12 +30,14 @@
 //                     32x32x64 scaled-FP4 MFMA; h = silu(G) * U quantised to MXFP4 per 32
 //                     features in the epilogue.
 //   k_s1_gemm<1>      per (expert, row block, 256 rows of W_d): Y_perm = W_d h.
+//   k_unpermute       y[t] = sum_j w[t][j] Y_perm[pos[t][j]].
 // and its NVFP4 weights come from k_nv_to_mx, run once when the layer is created.
 // Workgroups of one kernel never wait on each other.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ft_device.h"
 
@@ -404,62 +408,7 @@ __global__ __launch_bounds__(256) void k_perm_place(PrefillLaunch a) {
     const int p = a.base[(uint64_t)b * a.E + e] + r;
     a.pos[(uint64_t)t * a.k + j] = p;
     a.perm_tok[p] = t;
-  }
-}
-
-// ---- grouped GEMM (S0: exact bf16 operands) ------------------------------------------------
-// Two E2M1 codes (byte B of w) times a non-power-of-two scale s -> packed bf16 pair.  The
-// scaled convert uses only the exponent of its scale, so it runs with 1.0 and the fp32
-// product (exact) is truncated to bf16 (exact: at most 6 significant bits).
-template <int B>
-__device__ __forceinline__ uint32_t nv_pair_c(uint32_t w, float s) {
-  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
-  return (__float_as_uint(f[0] * s) >> 16) | (__float_as_uint(f[1] * s) & 0xffff0000u);
-}
-__device__ __forceinline__ uint32_t nv_pair(uint32_t w, float s, int b) {
-  return b == 0 ? nv_pair_c<0>(w, s) : b == 1 ? nv_pair_c<1>(w, s) : b == 2 ? nv_pair_c<2>(w, s)
-                                                                             : nv_pair_c<3>(w, s);
-}
-
-// Decode one 16-row x 128-K weight tile lane (16 code bytes + its scales) into four 16 B
-// MFMA operands (k-steps i = 0..3, eight K values each).
-__device__ __forceinline__ void decode_tile_lane(int fmt, const uint8_t* codes, const uint8_t* scales,
-                                                 uint64_t tile, int lane, uint4 out[4]) {
-  const uint4 c = ((const uint4*)codes)[tile * 64 + lane];
-  const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
-  if (fmt == FT_MXFP4) {
-    const float s = e8m0_f32(scales[tile * 64 + lane]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(uint4, fp4x8_bf16(wv[i], s));
-  } else {
-    // E2M1 -> fp32 (exact), times the E4M3 block scale (exact: <= 6 significant bits), then
-    // the top half of each fp32 is the bf16 value
-    const float s0 = e4m3_f32(scales[tile * 128 + 2 * lane]);
-    const float s1 = e4m3_f32(scales[tile * 128 + 2 * lane + 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = i < 2 ? s0 : s1;
-      out[i] = make_uint4(nv_pair(wv[i], s, 0), nv_pair(wv[i], s, 1), nv_pair(wv[i], s, 2),
-                          nv_pair(wv[i], s, 3));
-    }
-  }
-}
-
-__device__ __forceinline__ void decode_tile_regs(int fmt, uint4 c, uint32_t sc0, uint32_t sc1,
-                                                 uint4 out[4]) {
-  const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
-  if (fmt == FT_MXFP4) {
-    const float s = e8m0_f32(sc0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(uint4, fp4x8_bf16(wv[i], s));
-  } else {
-    const float s0 = e4m3_f32(sc0), s1 = e4m3_f32(sc1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = i < 2 ? s0 : s1;
-      out[i] = make_uint4(nv_pair(wv[i], s, 0), nv_pair(wv[i], s, 1), nv_pair(wv[i], s, 2),
-                          nv_pair(wv[i], s, 3));
-    }
+    a.perm_w[p] = a.w[(uint64_t)t * a.k + j];
   }
 }
 
@@ -467,172 +416,233 @@ __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
   return ((const BlobHeader*)blob)->tensor_scale[m];
 }
 
-// MODE 0: gate/up + SwiGLU -> hperm; MODE 1: down -> Yperm.  NB feature blocks.
-// Block (token block g, feature block fb) sits on XCD g % 8 (workgroup ids go round-robin
-// over the 8 XCDs), so all feature blocks of one token block share that XCD's L2 for x.
-template <int MODE>
-__global__ __launch_bounds__(256) void k_ggemm(PrefillLaunch a, int NB) {
-  constexpr int XS = kTileK + 8;               // LDS row stride of the token tile (bf16)
-  __shared__ uint16_t xs[kGemmM][XS];          // 34 KB
-  __shared__ uint4 ws[8][4][64];               // 32 KB: [weight tile][k-step][lane]
-  __shared__ int s_e;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int Lb = blockIdx.x, xcd = Lb & 7, jj = Lb >> 3;
-  const int gblk = xcd + 8 * (jj / NB), fb = jj % NB;
-  const int G = a.tb_off[a.E];
-  if (gblk >= G) return;
-  if (tid == 0) {  // expert of this token block: tb_off[e] <= gblk < tb_off[e + 1]
-    int lo = 0, hi = a.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.tb_off[mid] <= gblk) lo = mid; else hi = mid - 1;
-    }
-    s_e = lo;
-  }
-  __syncthreads();
-  const int e = s_e;
-  const int row0 = a.offsets[e] + (gblk - a.tb_off[e]) * kGemmM;
-  const int nrows = min(kGemmM, a.offsets[e + 1] - row0);
+// ---- grouped GEMM, exact mode: weights decoded in registers, tokens through LDS -----------
+// A workgroup owns one block of up to 256 permuted rows of one expert and one feature block:
+//   MODE 0 (gate/up + SwiGLU): 128 features, i.e. 128 gate rows and the same 128 up rows;
+//   MODE 1 (down + combine):   256 rows of W_d (outputs).
+// Each of the four waves owns 64 weight rows as two 32-row operands (MODE 0: operand o holds
+// gate rows f .. f + 15 in lanes 0..15 and the up rows of the same features in lanes 16..31,
+// so one lane holds a feature's gate and up sums; MODE 1: two 16-row tiles of W_d) and all
+// 256 rows as eight 32-row token operands, on the 32x32x16 bf16 MFMA with fp32 accumulators.
+// The K axis runs in chunks of 64.  Per chunk, each wave copies global -> LDS (the direct
+// form of the vector load, which lands every lane's 16 bytes in lane order) its weight
+// operands' code slots and scale dwords, and two of the eight token operands for the four
+// 16-K steps, all in MFMA operand order, so the reads are one conflict-free 16-byte LDS read
+// per lane.  Three LDS stages keep two chunks of copies in flight while one is multiplied.
+// A weight lane (row r, K half h) reads the tile slot r % 16 + 16 (2 c + h) of chunk half c:
+// 32 K values, of which step ks takes values 8 ks .. 8 ks + 7; the token lane (row t, half h)
+// supplies the same K (64 chunk + 32 h + 8 ks + i), since a dot product needs both operands in
+// the same K order and no other.  The weights are decoded to bf16 in registers (exact: an
+// E2M1 value times an E8M0 scale, or times an E4M3 scale, has at most 6 significant bits).
+// MODE 1 uses the token operand as the MFMA's A and the weights as B, so a result register
+// holds 32 consecutive outputs of one row across a lane half: the routing-weighted combine
+// is then a coalesced fp32 atomic add of w x ts_d x y into y[token] (y zeroed first), and no
+// per-pair output is stored.  Blocks (token block g, feature block fb) sit on XCD g % 8, so
+// the feature blocks of one token block share that XCD's L2 for the token rows.
+constexpr int kXRows = 256;
+constexpr int kXCopies = 12;   // copies per wave per chunk: 8 token, 2 code, 2 scale
+
+template <int MODE, int FMT>
+__global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
+  // stage s: token operands [ks 4][j 8][64 lanes] (tk), then in wk the weight code slots
+  // [wave 4][o 2][64 lanes] followed by the weight scale dwords [wave 4][o 2][64 lanes] (one
+  // array per kind and stage: six copy targets, few enough for the compiler to keep apart)
+  __shared__ uint4 tk0[2048], tk1[2048], tk2[2048];
+  __shared__ uint4 wk0[640], wk1[640], wk2[640];
+  __shared__ int s_tok[kXRows];
+  __shared__ float s_w[kXRows];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Lb = blockIdx.x, jj = Lb >> 3;
+  const int gblk = (Lb & 7) + 8 * (jj / NB), fb = jj % NB;
+  if (gblk >= a.tb_off[a.E]) return;
+  const int e = a.blk_e[gblk];
+  const int row0 = a.offsets[e] + (gblk - a.tb_off[e]) * kXRows;
+  const int nrows = min(kXRows, a.offsets[e + 1] - row0);
+  const int nj = (nrows + 31) >> 5;
   const int K = MODE == 0 ? a.H : a.I;
   const int KC = K / kTileK;
+  const int nrt = (MODE == 0 ? a.I : a.H) / kTileRows;
   const uint8_t* blob = a.pool + (uint64_t)e * a.stride;
-  const int fmt = a.L.fmt;
-  const int wm = wave >> 1, wn = wave & 1;
-  // staging role: row r of the token tile, half h2 (64 K values)
-  const int sr = tid >> 1, sh = tid & 1;
-  // rows past the expert's last token re-read its last row (always valid) and are zeroed
-  const bool srow = sr < nrows;
-  const int rr = row0 + min(sr, nrows - 1);
-  const uint16_t* src = MODE == 0 ? a.x + (uint64_t)a.perm_tok[rr] * a.H
-                                  : a.hperm + (uint64_t)rr * a.I;
-  // weight tiles this wave decodes: q = 2*wave, 2*wave + 1 of the block's 8
-  const uint8_t* wc[2];
-  const uint8_t* wsc[2];
-  uint64_t wrow[2];
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // copy sources.  Weight operand o of this wave, lane (r32, h): tile rt of matrix m,
+  // slot (r32 % 16) + 16 h of chunk 0 (chunk ch adds (ch / 2) tiles and 32 (ch % 2) slots)
+  const uint8_t* wsrc[2];
+  const uint8_t* ssrc[2];
 #pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const int q = 2 * wave + d;
+  for (int o = 0; o < 2; ++o) {
     int m, rt;
-    if (MODE == 0) { m = q < 4 ? 0 : 1; rt = fb * 4 + (q & 3); }
-    else { m = 2; rt = fb * 8 + q; }
-    wc[d] = blob + a.L.off[2 * m];
-    wsc[d] = blob + a.L.off[2 * m + 1];
-    wrow[d] = (uint64_t)rt * KC;
+    if (MODE == 0) { m = r32 >> 4; rt = fb * 8 + 2 * wave + o; }
+    else { m = 2; rt = min(fb * 16 + 4 * wave + 2 * o + (r32 >> 4), nrt - 1); }
+    const int slot = (r32 & 15) + 16 * h;
+    wsrc[o] = blob + a.L.off[2 * m] + ((uint64_t)rt * KC * 64 + slot) * 16;
+    const uint64_t sb = FMT == FT_MXFP4 ? (uint64_t)rt * KC * 64 + slot
+                                        : (uint64_t)rt * KC * 128 + 2 * slot;
+    ssrc[o] = blob + a.L.off[2 * m + 1] + (sb & ~(uint64_t)3);
   }
-  // the wave's two 32-row weight operands, each a pair of 16-row tiles of the block tile
-  // (gate/up: 32 gate rows and the same 32 up rows; down: 64 rows of W_d)
-  int wt[2];
+  // token rows j = 2 wave, 2 wave + 1 of this lane (rows past the block re-read its last row;
+  // their results are never used)
+  const uint16_t* tsrc[2];
 #pragma unroll
-  for (int o = 0; o < 2; ++o) wt[o] = MODE == 0 ? (o == 0 ? 2 * wn : 4 + 2 * wn) : 4 * wn + 2 * o;
-
-  // 32x32x16 bf16 MFMAs: acc[o][b] = weight operand o x token operand b (32 tokens each)
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int o = 0; o < 2; ++o)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[o][b][r] = 0.f;
-  // operand lanes: row (or token) lane % 32 of the operand, K half lane / 32
-  const int r32 = lane & 31, kh = lane >> 5, th = (lane >> 4) & 1;
-
-  // software pipeline: the global loads of chunk kc + 1 (token tile rows and this wave's
-  // two weight tiles) are in flight while the MFMAs of chunk kc run
-  uint4 xv[8], cw[2];
-  uint32_t sc[2][2];
-  auto load_chunk = [&](int kc) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = *(const uint4*)(src + kc * kTileK + sh * 64 + 8 * i);
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const uint64_t tile = wrow[d] + kc;
-      cw[d] = ((const uint4*)wc[d])[tile * 64 + lane];
-      if (fmt == FT_MXFP4) {
-        sc[d][0] = wsc[d][tile * 64 + lane];
-        sc[d][1] = 0u;
-      } else {
-        sc[d][0] = wsc[d][tile * 128 + 2 * lane];
-        sc[d][1] = wsc[d][tile * 128 + 2 * lane + 1];
-      }
+  for (int q = 0; q < 2; ++q) {
+    const int tl = min(32 * (2 * wave + q) + r32, nrows - 1);
+    tsrc[q] = MODE == 0 ? a.x + (uint64_t)a.perm_tok[row0 + tl] * a.H + 32 * h
+                        : a.hperm + (uint64_t)(row0 + tl) * a.I + 32 * h;
+  }
+  if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
+    const float tsd = blob_tscale(blob, 2);
+    for (int i = tid; i < nrows; i += 256) {
+      s_tok[i] = a.perm_tok[row0 + i];
+      s_w[i] = a.perm_w[row0 + i] * tsd;
     }
-  };
-  load_chunk(0);
-  for (int kc = 0; kc < KC; ++kc) {
-    uint4 dq[2][4];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) decode_tile_regs(fmt, cw[d], sc[d][0], sc[d][1], dq[d]);
-    __syncthreads();  // the previous chunk's MFMAs are done with the LDS tiles
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *(uint4*)&xs[sr][sh * 64 + 8 * i] = srow ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ws[2 * wave + d][i][lane] = dq[d][i];
-    // the registers are in LDS now: the next chunk's loads go out before the barrier
-    if (kc + 1 < KC) load_chunk(kc + 1);
-    __syncthreads();
-    // MFMA step (p, i) covers the 8 K values 32 (2p + half) + 8i .. + 7 of each lane half:
-    // both operands use the same K order, which is all a dot product needs.  A weight lane
-    // (row r32, half kh) finds them in tile row r32 % 16 of tile wt + r32 / 16, K group
-    // 2p + kh: lane slot r32 % 16 + 16 (2p + kh) of the decoded tile.
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 A[2], B[2];
-#pragma unroll
-        for (int o = 0; o < 2; ++o) A[o] = ws[wt[o] + th][i][(lane & 15) + 16 * (2 * p + kh)];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          B[b] = *(const uint4*)&xs[wm * 64 + b * 32 + r32][32 * (2 * p + kh) + 8 * i];
-#pragma unroll
-        for (int o = 0; o < 2; ++o)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[o][b] = mfma_bf16_32(A[o], B[b], acc[o][b]);
-      }
   }
+  // The main loop and epilogue with NJ (= ceil(rows / 32)) token operands, a compile-time
+  // count so that every step is straight-line code.  The LDS arrays are named directly (they
+  // are static, not captured), which lets the compiler see that the reads of one stage do not
+  // wait on the copies into another.
+  auto block = [&](auto njc) {
+    constexpr int NJ = decltype(njc)::value;
+    const int NC = K / 64;
 
-  // lane L holds token r32 of each token operand and, in registers 4q .. 4q + 3, weight
-  // rows 8q + 4 kh .. + 3 of each weight operand
-  if (MODE == 0) {
-    const float tsg = blob_tscale(blob, 0), tsu = blob_tscale(blob, 1);
+#define FT_X_ISSUE(ch_, TK_, WK_)                                                          \
+    do {                                                                                     \
+      const int c_ = min((ch_), NC - 1);                                                     \
+      const uint64_t wo_ = (uint64_t)(c_ >> 1) * 1024 + (c_ & 1) * 512;                      \
+      const uint64_t so_ = FMT == FT_MXFP4 ? (uint64_t)(c_ >> 1) * 64 + (c_ & 1) * 32        \
+                                           : (uint64_t)(c_ >> 1) * 128 + (c_ & 1) * 64;      \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                     \
+        dma16(wsrc[o_] + wo_, &WK_[(wave * 2 + o_) * 64]);                                   \
+        dma4(ssrc[o_] + so_, (uint32_t*)&WK_[512] + (wave * 2 + o_) * 64);                   \
+      }                                                                                      \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                    \
+        _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_)                                     \
+          dma16(tsrc[q_] + c_ * 64 + 8 * ks_, &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);         \
+    } while (0)
+
+    f32x16 acc[2][NJ];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int row = wm * 64 + b * 32 + r32;
-      if (row < nrows) {
+    for (int o = 0; o < 2; ++o)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = fb * 64 + wn * 32 + 8 * q + 4 * kh;
-          uint16_t hv[4];
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            hv[r] = f32_to_bf16_rne(silu_f32(acc[0][b][4 * q + r] * tsg) *
-                                    (acc[1][b][4 * q + r] * tsu));
-          *(uint2*)(a.hperm + (uint64_t)(row0 + row) * a.I + f) =
-              make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
-                         (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+        for (int r = 0; r < 16; ++r) acc[o][j][r] = 0.f;
+
+    // one chunk: its copies have landed for this wave (count wait) and, after the barrier, for
+    // every wave, and every wave is done with the stage the next issue refills
+#define FT_X_STEP(ch_, TK_, WK_, TKN_, WKN_)                                               \
+    do {                                                                                     \
+      __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies) & ~(15 << 8));                           \
+      asm volatile("" ::: "memory");                                                         \
+      __builtin_amdgcn_s_barrier();                                                          \
+      asm volatile("" ::: "memory");                                                         \
+      FT_X_ISSUE((ch_) + 2, TKN_, WKN_);                                               \
+      uint4 A_[2][4];                                                                        \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                     \
+        const uint4 cw_ = WK_[(wave * 2 + o_) * 64 + lane];                                  \
+        const uint32_t sw_ = ((const uint32_t*)&WK_[512])[(wave * 2 + o_) * 64 + lane];     \
+        const uint32_t w_[4] = {cw_.x, cw_.y, cw_.z, cw_.w};                                 \
+        if (FMT == FT_MXFP4) {                                                               \
+          const float s_ = e8m0_f32((sw_ >> (8 * (lane & 3))) & 0xffu);                      \
+          _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                \
+            A_[o_][ks_] = __builtin_bit_cast(uint4, fp4x8_bf16(w_[ks_], s_));                \
+        } else {                                                                             \
+          const uint32_t p_ = (sw_ >> (16 * (lane & 1))) & 0xffffu;                          \
+          const float s0_ = e4m3_f32_fast(p_ & 0xffu), s1_ = e4m3_f32_fast(p_ >> 8);         \
+          _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                \
+            A_[o_][ks_] = __builtin_bit_cast(uint4, fp4x8_bf16_mul(w_[ks_], ks_ < 2 ? s0_ : s1_)); \
+        }                                                                                    \
+      }                                                                                      \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_) {                                  \
+        uint4 B_[NJ];                                                                        \
+        _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                    \
+          B_[j_] = TK_[(ks_ * 8 + j_) * 64 + lane];                                          \
+        _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                    \
+          _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_)                                   \
+            acc[o_][j_] = MODE == 0 ? mfma_bf16_32(A_[o_][ks_], B_[j_], acc[o_][j_])         \
+                                    : mfma_bf16_32(B_[j_], A_[o_][ks_], acc[o_][j_]);        \
+      }                                                                                      \
+    } while (0)
+
+    FT_X_ISSUE(0, tk0, wk0);
+    FT_X_ISSUE(1, tk1, wk1);
+    // whole rounds of three chunks with no branch inside (a branch there makes the compiler
+    // wait for every copy in flight before the next LDS read), then the remaining one or two
+    int ch = 0;
+    for (; ch + 3 <= NC; ch += 3) {
+      FT_X_STEP(ch, tk0, wk0, tk2, wk2);
+      FT_X_STEP(ch + 1, tk1, wk1, tk0, wk0);
+      FT_X_STEP(ch + 2, tk2, wk2, tk1, wk1);
+    }
+    if (ch < NC) FT_X_STEP(ch, tk0, wk0, tk2, wk2);
+    if (ch + 1 < NC) FT_X_STEP(ch + 1, tk1, wk1, tk0, wk0);
+    // the trailing copies (clamped re-reads) land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
+#undef FT_X_STEP
+#undef FT_X_ISSUE
+
+    if (MODE == 0) {
+      // lane (r32, h) holds token row 32 j + r32 and, in registers 8 (r / 4) + 4 h + r % 4 for
+      // r < 8, gate features f0 + 8 (r / 4) + 4 h + r % 4 of operand o, with the up sums of the
+      // same features in registers r + 8
+      const float tsg = blob_tscale(blob, 0), tsu = blob_tscale(blob, 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int tl = 32 * j + r32;
+        if (tl < nrows) {
+#pragma unroll
+          for (int o = 0; o < 2; ++o) {
+            const int f0 = fb * 128 + wave * 32 + 16 * o + 4 * h;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              uint16_t hv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                hv[r] = f32_to_bf16_rne(silu_f32(acc[o][j][4 * q + r] * tsg) *
+                                        (acc[o][j][8 + 4 * q + r] * tsu));
+              *(uint2*)(a.hperm + (uint64_t)(row0 + tl) * a.I + f0 + 8 * q) =
+                  make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
+                             (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+            }
+          }
+        }
+      }
+    } else {
+      // lane (r32, h) holds output fb * 256 + 64 wave + 32 o + r32 of token rows
+      // 32 j + 8 (r / 4) + 4 h + r % 4 in register r
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int out = fb * 256 + wave * 64 + 32 * o + r32;
+        if (out < a.H) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int tl = 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+              if (tl < nrows)
+                unsafeAtomicAdd(a.y + (uint64_t)s_tok[tl] * a.H + out, s_w[tl] * acc[o][j][r]);
+            }
+          }
         }
       }
     }
-  } else {
-    const float tsd = blob_tscale(blob, 2);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int row = wm * 64 + b * 32 + r32;
-      if (row < nrows) {
-#pragma unroll
-        for (int o = 0; o < 2; ++o)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = fb * kGemmN + wn * 64 + o * 32 + 8 * q + 4 * kh;
-            *(float4*)(a.Yperm + (uint64_t)(row0 + row) * a.H + f) =
-                make_float4(acc[o][b][4 * q] * tsd, acc[o][b][4 * q + 1] * tsd,
-                            acc[o][b][4 * q + 2] * tsd, acc[o][b][4 * q + 3] * tsd);
-          }
-      }
-    }
+  };
+#define FT_X_BLOCK(N)                                                                       \
+  case N:                                                                                  \
+    block(std::integral_constant<int, N>{});                                               \
+    break
+  switch (nj) {
+    FT_X_BLOCK(1); FT_X_BLOCK(2); FT_X_BLOCK(3); FT_X_BLOCK(4);
+    FT_X_BLOCK(5); FT_X_BLOCK(6); FT_X_BLOCK(7); default: FT_X_BLOCK(8);
   }
+#undef FT_X_BLOCK
+}
+
+// y = 0 before the down GEMM's atomic combine (a kernel, not a memset node, so that the call
+// can be captured into a graph).
+__global__ __launch_bounds__(256) void k_zero(float* __restrict__ y, uint64_t n4) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) ((float4*)y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ---- scaled-FP4 mode (both MFMA operands FP4) ------------------------------------------------
@@ -1293,7 +1303,6 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   const int g8 = (gmax + 7) / 8 * 8;
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-  const int nb0 = a.I / 64, nb1 = a.H / kGemmN;
   if (a.mode == FT_PREFILL_MXFP4) {
     const int sb0 = a.I / 128, sb1 = (a.H + 255) / 256;   // feature blocks
     // The branch-free main loop needs the chunk count to be a multiple of the stage count.
@@ -1306,18 +1315,22 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     if ((a.I / kTileK) % kS1Stages == 0)
       FT_PLAUNCH((k_s1_gemm<1, true>), dim3(std::min(g8 * sb1, slots)), e2, e3, a, sb1);
     else FT_PLAUNCH((k_s1_gemm<1, false>), dim3(g8 * sb1), e2, e3, a, sb1);
+    const dim3 ug((a.H / 4 + 255) / 256, a.T);
+    if (a.k <= 8) hipLaunchKernelGGL((k_unpermute<8, true>), ug, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_unpermute<FT_MAX_TOPK, true>), ug, dim3(256), 0, st, a);
   } else {
-    FT_PLAUNCH(k_ggemm<0>, dim3(g8 * nb0), e0, e1, a, nb0);
-    FT_PLAUNCH(k_ggemm<1>, dim3(g8 * nb1), e2, e3, a, nb1);
-  }
-  const dim3 ug((a.H / 4 + 255) / 256, a.T);
-  const bool f24 = a.mode == FT_PREFILL_MXFP4;
-  if (a.k <= 8) {
-    if (f24) hipLaunchKernelGGL((k_unpermute<8, true>), ug, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_unpermute<8, false>), ug, dim3(256), 0, st, a);
-  } else {
-    if (f24) hipLaunchKernelGGL((k_unpermute<FT_MAX_TOPK, true>), ug, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_unpermute<FT_MAX_TOPK, false>), ug, dim3(256), 0, st, a);
+    // exact mode: gate/up + SwiGLU into h, then down with the combine folded into its
+    // epilogue (atomic adds into y, zeroed first)
+    const uint64_t n4 = (uint64_t)a.T * a.H / 4;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a.y, n4);
+    const int nb0 = a.I / 128, nb1 = (a.H + 255) / 256;
+    if (a.L.fmt == FT_MXFP4) {
+      FT_PLAUNCH((k_xgemm<0, FT_MXFP4>), dim3(g8 * nb0), e0, e1, a, nb0);
+      FT_PLAUNCH((k_xgemm<1, FT_MXFP4>), dim3(g8 * nb1), e2, e3, a, nb1);
+    } else {
+      FT_PLAUNCH((k_xgemm<0, FT_NVFP4>), dim3(g8 * nb0), e0, e1, a, nb0);
+      FT_PLAUNCH((k_xgemm<1, FT_NVFP4>), dim3(g8 * nb1), e2, e3, a, nb1);
+    }
   }
   return (int)hipGetLastError();
 }

@@ -147,15 +147,23 @@ def test_prefill_matches_oracle(ctx, name, fmt, H, I, E, k, T):
     check_output(y, ref["y"], name)
 
 
-def test_prefill_is_deterministic(ctx):
+def test_prefill_repeat_agrees(ctx):
+    """The exact mode combines the k expert outputs of a token by fp32 atomic adds into y, so
+    the summation order (and only that) may differ between calls: two calls agree to a few
+    fp32 roundings of k = 5 terms (2^-24 each, relative to the largest output), and every
+    intermediate (routing, permutation) is identical."""
     name, fmt, H, I, E, k, T = SMALL[1]
     cfg = synth.small_config(name, seed=H + E, H=H, I=I, E=E, k=k, fmt=fmt, code_dist="normal",
                              router_sigma=0.5 / np.sqrt(H), nv_tensor_scale=1 / 64)
     L = layer_for(ctx, name, cfg)
     x = synth.gen_tokens(cfg, T, batch=9)
-    a, _ = run_prefill(ctx, L, x)
-    b, _ = run_prefill(ctx, L, x)
-    assert np.array_equal(a, b)
+    a, wsa = run_prefill(ctx, L, x)
+    sa = prefill_state(L, wsa, T)
+    b, wsb = run_prefill(ctx, L, x)
+    sb = prefill_state(L, wsb, T)
+    for u, v in zip(sa, sb):
+        assert np.array_equal(u, v)
+    assert np.max(np.abs(a - b)) <= k * 2.0 ** -22 * np.max(np.abs(a))
 
 
 def test_prefill_rejects_bad_calls(ctx):
