@@ -528,57 +528,147 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[o][j][r] = 0.f;
 
-    // one chunk: its copies have landed for this wave (count wait) and, after the barrier, for
-    // every wave, and every wave is done with the stage the next issue refills
-#define FT_X_STEP(ch_, TK_, WK_, TKN_, WKN_)                                               \
-    do {                                                                                     \
-      __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies) & ~(15 << 8));                           \
-      asm volatile("" ::: "memory");                                                         \
-      __builtin_amdgcn_s_barrier();                                                          \
-      asm volatile("" ::: "memory");                                                         \
-      FT_X_ISSUE((ch_) + 2, TKN_, WKN_);                                               \
-      uint4 A_[2][4];                                                                        \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                     \
-        const uint4 cw_ = WK_[(wave * 2 + o_) * 64 + lane];                                  \
-        const uint32_t sw_ = ((const uint32_t*)&WK_[512])[(wave * 2 + o_) * 64 + lane];     \
-        const uint32_t w_[4] = {cw_.x, cw_.y, cw_.z, cw_.w};                                 \
-        if (FMT == FT_MXFP4) {                                                               \
-          const float s_ = e8m0_f32((sw_ >> (8 * (lane & 3))) & 0xffu);                      \
-          _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                \
-            A_[o_][ks_] = __builtin_bit_cast(uint4, fp4x8_bf16(w_[ks_], s_));                \
-        } else {                                                                             \
-          const uint32_t p_ = (sw_ >> (16 * (lane & 1))) & 0xffffu;                          \
-          const float s0_ = e4m3_f32_fast(p_ & 0xffu), s1_ = e4m3_f32_fast(p_ >> 8);         \
-          _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                \
-            A_[o_][ks_] = __builtin_bit_cast(uint4, fp4x8_bf16_mul(w_[ks_], ks_ < 2 ? s0_ : s1_)); \
-        }                                                                                    \
-      }                                                                                      \
-      _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_) {                                  \
-        uint4 B_[NJ];                                                                        \
-        _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                    \
-          B_[j_] = TK_[(ks_ * 8 + j_) * 64 + lane];                                          \
-        _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                    \
-          _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_)                                   \
-            acc[o_][j_] = MODE == 0 ? mfma_bf16_32(A_[o_][ks_], B_[j_], acc[o_][j_])         \
-                                    : mfma_bf16_32(B_[j_], A_[o_][ks_], acc[o_][j_]);        \
-      }                                                                                      \
+    // Software pipeline over the four 16-K steps of a chunk: while the MFMAs of step ks run,
+    // the token operands of step ks + 1 are read from LDS and its weights decoded.  Between
+    // steps 2 and 3 every wave's reads of the chunk are done, so after a count wait and a
+    // barrier that stage is refilled with the chunk three ahead; step 3's MFMAs then cover the
+    // reads and decode of the next chunk's first step.  Scheduling groups fix the interleave
+    // (1 MFMA, 1 LDS read, 1 MFMA, up to 4 VALU), which the compiler would otherwise undo.
+    uint4 cw[2], Bc[NJ], Bn[NJ], Ac[2], An[2];
+    float s0[2], s1[2];
+#define FT_X_READW(WK_, CW_, SW_)                                                           \
+    do {                                                                                    \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
+        CW_[o_] = WK_[(wave * 2 + o_) * 64 + lane];                                         \
+        SW_[o_] = ((const uint32_t*)&WK_[512])[(wave * 2 + o_) * 64 + lane];               \
+      }                                                                                     \
+    } while (0)
+#define FT_X_SCALES(SW_, S0_, S1_)                                                          \
+    do {                                                                                    \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
+        if (FMT == FT_MXFP4) {                                                              \
+          S0_[o_] = S1_[o_] = e8m0_f32((SW_[o_] >> (8 * (lane & 3))) & 0xffu);              \
+        } else {                                                                            \
+          const uint32_t p_ = (SW_[o_] >> (16 * (lane & 1))) & 0xffffu;                     \
+          S0_[o_] = e4m3_f32_fast(p_ & 0xffu);                                              \
+          S1_[o_] = e4m3_f32_fast(p_ >> 8);                                                 \
+        }                                                                                   \
+      }                                                                                     \
+    } while (0)
+#define FT_X_DEC(KS_, CW_, S0_, S1_, A_)                                                    \
+    do {                                                                                    \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
+        const uint32_t w_ = (KS_) == 0 ? CW_[o_].x : (KS_) == 1 ? CW_[o_].y                 \
+                          : (KS_) == 2 ? CW_[o_].z : CW_[o_].w;                             \
+        A_[o_] = FMT == FT_MXFP4                                                            \
+                     ? __builtin_bit_cast(uint4, fp4x8_bf16(w_, S0_[o_]))                   \
+                     : __builtin_bit_cast(uint4, fp4x8_bf16_mul(w_, (KS_) < 2 ? S0_[o_]     \
+                                                                           : S1_[o_]));     \
+      }                                                                                     \
+    } while (0)
+#define FT_X_READB(TK_, KS_, B_)                                                            \
+    _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) B_[j_] = TK_[((KS_) * 8 + j_) * 64 + lane]
+#define FT_X_MMA()                                                                          \
+    _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                       \
+      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_)                                      \
+        acc[o_][j_] = MODE == 0 ? mfma_bf16_32(Ac[o_], Bc[j_], acc[o_][j_])                 \
+                                : mfma_bf16_32(Bc[j_], Ac[o_], acc[o_][j_])
+#define FT_X_SCHED(NR_, NV_)                                                                \
+    do {                                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < NJ; ++i_) {                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR_), 0);                              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x002, (NV_), 0);                              \
+      }                                                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+    } while (0)
+#define FT_X_NEXT()                                                                         \
+    do {                                                                                    \
+      _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) Bc[j_] = Bn[j_];                    \
+      Ac[0] = An[0];                                                                        \
+      Ac[1] = An[1];                                                                        \
+    } while (0)
+    // one chunk, read from stage (TK_, WK_); (TKN_, WKN_) holds the next chunk.  A wave reads
+    // only its own weight slots, so it may read the next chunk's weights (in step 2) after
+    // its own count wait; the token operands are shared, so they wait for the barrier.
+#define FT_X_CHUNK(ch_, TK_, WK_, TKN_, WKN_)                                               \
+    do {                                                                                    \
+      FT_X_READB(TK_, 1, Bn);                                                               \
+      FT_X_DEC(1, cw, s0, s1, An);                                                          \
+      FT_X_MMA();                                                                           \
+      FT_X_SCHED(1, 4);                                                                     \
+      FT_X_NEXT();                                                                          \
+      /* this wave's copies of the next chunk have landed: its weights can be read */       \
+      __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies));                                       \
+      asm volatile("" ::: "memory");                                                        \
+      uint4 cwn_[2];                                                                        \
+      uint32_t swn_[2];                                                                     \
+      float s0n_[2], s1n_[2];                                                               \
+      FT_X_READB(TK_, 2, Bn);                                                               \
+      FT_X_READW(WKN_, cwn_, swn_);                                                         \
+      FT_X_DEC(2, cw, s0, s1, An);                                                          \
+      FT_X_MMA();                                                                           \
+      FT_X_SCHED(2, 4);                                                                     \
+      FT_X_NEXT();                                                                          \
+      FT_X_READB(TK_, 3, Bn);                                                               \
+      FT_X_SCALES(swn_, s0n_, s1n_);                                                        \
+      FT_X_DEC(3, cw, s0, s1, An);                                                          \
+      FT_X_MMA();                                                                           \
+      FT_X_SCHED(1, 10);                                                                    \
+      FT_X_NEXT();                                                                          \
+      /* this wave's reads of the stage are done (LDS count 0); after the barrier, every */ \
+      /* wave's are, and every wave's copies of the next chunk have landed */               \
+      __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies) & ~(15 << 8));                          \
+      asm volatile("" ::: "memory");                                                        \
+      __builtin_amdgcn_s_barrier();                                                         \
+      asm volatile("" ::: "memory");                                                        \
+      FT_X_ISSUE((ch_) + 3, TK_, WK_);                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      FT_X_READB(TKN_, 0, Bn);                                                              \
+      FT_X_DEC(0, cwn_, s0n_, s1n_, An);                                                    \
+      FT_X_MMA();                                                                           \
+      FT_X_SCHED(1, 4);                                                                     \
+      FT_X_NEXT();                                                                          \
+      cw[0] = cwn_[0]; cw[1] = cwn_[1];                                                     \
+      s0[0] = s0n_[0]; s0[1] = s0n_[1];                                                     \
+      s1[0] = s1n_[0]; s1[1] = s1n_[1];                                                     \
     } while (0)
 
     FT_X_ISSUE(0, tk0, wk0);
     FT_X_ISSUE(1, tk1, wk1);
+    __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies) & ~(15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    FT_X_ISSUE(2, tk2, wk2);
+    {
+      uint32_t sw0[2];
+      FT_X_READW(wk0, cw, sw0);
+      FT_X_SCALES(sw0, s0, s1);
+    }
+    FT_X_READB(tk0, 0, Bc);
+    FT_X_DEC(0, cw, s0, s1, Ac);
     // whole rounds of three chunks with no branch inside (a branch there makes the compiler
     // wait for every copy in flight before the next LDS read), then the remaining one or two
     int ch = 0;
     for (; ch + 3 <= NC; ch += 3) {
-      FT_X_STEP(ch, tk0, wk0, tk2, wk2);
-      FT_X_STEP(ch + 1, tk1, wk1, tk0, wk0);
-      FT_X_STEP(ch + 2, tk2, wk2, tk1, wk1);
+      FT_X_CHUNK(ch, tk0, wk0, tk1, wk1);
+      FT_X_CHUNK(ch + 1, tk1, wk1, tk2, wk2);
+      FT_X_CHUNK(ch + 2, tk2, wk2, tk0, wk0);
     }
-    if (ch < NC) FT_X_STEP(ch, tk0, wk0, tk2, wk2);
-    if (ch + 1 < NC) FT_X_STEP(ch + 1, tk1, wk1, tk0, wk0);
+    if (ch < NC) FT_X_CHUNK(ch, tk0, wk0, tk1, wk1);
+    if (ch + 1 < NC) FT_X_CHUNK(ch + 1, tk1, wk1, tk2, wk2);
+#undef FT_X_CHUNK
+#undef FT_X_NEXT
+#undef FT_X_SCHED
+#undef FT_X_MMA
+#undef FT_X_READB
+#undef FT_X_DEC
+#undef FT_X_SCALES
+#undef FT_X_READW
     // the trailing copies (clamped re-reads) land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(FT_VMCNT(0));
-#undef FT_X_STEP
 #undef FT_X_ISSUE
 
     if (MODE == 0) {
