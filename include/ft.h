@@ -99,6 +99,19 @@ FT_API int ft_pack_expert(int format, int H, int I,
 FT_API int ft_ctx_create(int device, ft_ctx** out);
 FT_API int ft_ctx_destroy(ft_ctx* ctx);
 
+/*
+ * Host placement of a context.  The host experts read the pinned blob store and the streamed
+ * copies cross PCIe from it, with the CPU side's memory bandwidth setting Bh (smzdm explainer
+ * a825qpgl, section 二: the CPU side's effective memory bandwidth; mubeitech explainer: the
+ * CPU computes in host memory without crossing PCIe).  ft_ctx_create therefore binds the
+ * pool's worker threads to the CPUs of the GPU's NUMA node (read from sysfs through the GPU's
+ * PCI bus id) that the process may run on, unless FT_HOST_AFFINITY=0.  *node is that node
+ * (-1 when the platform reports none), *pinned_cpus the CPUs the workers are bound to (0: not
+ * bound).  A caller places the pinned blob store on the same node by allocating it from a
+ * thread bound to those CPUs (the pages land on the allocating thread's node).
+ */
+FT_API int ft_ctx_numa(const ft_ctx* ctx, int* node, int* pinned_cpus);
+
 typedef struct ft_layer_desc {
   int32_t H, I, E, k, n_shared;
   int32_t format;             /* FT_MXFP4 or FT_NVFP4 */
@@ -404,6 +417,9 @@ FT_API int ft_debug_host_tier(const ft_layer* layer, int32_t* e2r, int32_t* r2e)
  * pause_us between them (a pause past the workers' spin makes them sleep and be woken), and
  * check every job ran on every index exactly once.  FT_ESTATE if one did not. */
 FT_API int ft_debug_pool_stress(int threads, int jobs, int pause_us);
+/* Test hook (host only): the CPUs of a Linux cpulist string ("0-3,8,10-11"), ascending as
+ * written; *n = their count (0 for a malformed list), the first cap written to cpus. */
+FT_API int ft_debug_parse_cpulist(const char* text, int32_t* cpus, int cap, int* n);
 /* Test hook (host only) of the no-throw rule: kind 0 returns FT_OK; kind 1 throws
  * std::bad_alloc, 2 std::runtime_error, 3 std::system_error inside an entry point, which
  * returns FT_ENOMEM, FT_ESTATE and FT_ENOMEM for them.  FT_EINVAL for another kind. */

@@ -100,7 +100,7 @@ def build_sanitized(kind: str) -> str:
         jobs.append(["g++", *flags, "-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(max_workers=4) as ex:
         list(ex.map(_run, jobs))
-    out = os.path.join(HERE, f"libft_{kind}.so")
+    out = os.path.join(BUILD, f"libft_{kind}.so")
     _run(["g++", "-shared", "-o", out + ".tmp", *objs, *hip_objs, *SANITIZERS[kind], "-pthread",
           f"-L{ROCM}/lib", f"-Wl,-rpath,{ROCM}/lib", "-lamdhip64"])
     os.replace(out + ".tmp", out)

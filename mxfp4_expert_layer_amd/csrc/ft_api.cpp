@@ -72,6 +72,10 @@ struct ft_ctx {
   // (ft_moe_prefill_noalloc), looked up once per device at context creation
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
+  // host placement: the GPU's NUMA node (-1 if the platform reports none) and the CPUs of
+  // that node the pool's workers are bound to (0: not bound)
+  int numa_node = -1;
+  int pinned_cpus = 0;
 };
 
 namespace ft {
@@ -241,9 +245,35 @@ extern "C" FT_API int ft_ctx_create(int device, ft_ctx** out) try {
   const int hw = (int)std::thread::hardware_concurrency();
   const int nt = env_int("FT_HOST_THREADS", std::max(1, std::min(16, hw)));
   c->pool.reset(new ThreadPool(std::max(1, nt)));
+  // the host experts read pinned host memory and the copies cross PCIe from it: keep the
+  // pool's workers on the GPU's NUMA node (FT_HOST_AFFINITY=0 leaves them unbound)
+  char bus[64] = {0};
+  if (hipDeviceGetPCIBusId(bus, (int)sizeof(bus), device) == hipSuccess) {
+    c->numa_node = pci_numa_node(bus);
+    if (env_int("FT_HOST_AFFINITY", 1) != 0) {
+      const std::vector<int> cpus = numa_node_cpus(c->numa_node);
+      if (!cpus.empty() && c->pool->pin(cpus) > 0) c->pinned_cpus = (int)cpus.size();
+    }
+  }
   *out = c.release();
   return FT_OK;
 } FT_CATCH("ft_ctx_create")
+
+extern "C" FT_API int ft_ctx_numa(const ft_ctx* ctx, int* node, int* pinned_cpus) try {
+  if (!ctx || !node || !pinned_cpus) return fail(FT_EINVAL, "ft_ctx_numa: null argument");
+  *node = ctx->numa_node;
+  *pinned_cpus = ctx->pinned_cpus;
+  return FT_OK;
+} FT_CATCH("ft_ctx_numa")
+
+extern "C" FT_API int ft_debug_parse_cpulist(const char* text, int32_t* cpus, int cap,
+                                             int* n) try {
+  if (!text || !n || (cap > 0 && !cpus)) return fail(FT_EINVAL, "ft_debug_parse_cpulist: null");
+  const std::vector<int> v = parse_cpulist(text);
+  *n = (int)v.size();
+  for (int i = 0; i < (int)v.size() && i < cap; ++i) cpus[i] = v[i];
+  return FT_OK;
+} FT_CATCH("ft_debug_parse_cpulist")
 
 extern "C" FT_API int ft_ctx_destroy(ft_ctx* ctx) try {
   if (!ctx) return FT_OK;

@@ -10,6 +10,12 @@
 #include <cstring>
 #include <new>
 #include <system_error>
+#include <cctype>
+#include <fstream>
+#include <string>
+
+#include <pthread.h>
+#include <sched.h>
 
 namespace ft {
 
@@ -79,6 +85,68 @@ void ThreadPool::worker(int id) {
     (*job_)(id, n_);
     pending_.fetch_sub(1, std::memory_order_release);
   }
+}
+
+int ThreadPool::pin(const std::vector<int>& cpus) {
+  if (cpus.empty()) return 0;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  for (int c : cpus)
+    if (c >= 0 && c < CPU_SETSIZE) CPU_SET(c, &set);
+  int n = 0;
+  for (auto& t : threads_)
+    if (pthread_setaffinity_np(t.native_handle(), sizeof(set), &set) == 0) ++n;
+  return n;
+}
+
+std::vector<int> parse_cpulist(const char* text) {
+  std::vector<int> out;
+  const char* p = text;
+  while (p && *p) {
+    while (*p == ',' || *p == ' ' || *p == '\n') ++p;
+    if (!*p) break;
+    char* end = nullptr;
+    const long a = std::strtol(p, &end, 10);
+    if (end == p || a < 0) return {};
+    long b = a;
+    p = end;
+    if (*p == '-') {
+      b = std::strtol(p + 1, &end, 10);
+      if (end == p + 1 || b < a) return {};
+      p = end;
+    }
+    for (long c = a; c <= b && c < 1 << 16; ++c) out.push_back((int)c);
+    if (*p && *p != ',' && *p != '\n' && *p != ' ') return {};
+  }
+  return out;
+}
+
+static std::string read_text(const std::string& path) {
+  std::ifstream f(path);
+  std::string s;
+  if (f) std::getline(f, s);
+  return s;
+}
+
+int pci_numa_node(const char* pci_bus_id) {
+  std::string id(pci_bus_id ? pci_bus_id : "");
+  for (auto& c : id) c = (char)std::tolower((unsigned char)c);
+  const std::string v = read_text("/sys/bus/pci/devices/" + id + "/numa_node");
+  if (v.empty()) return -1;
+  return std::atoi(v.c_str());
+}
+
+std::vector<int> numa_node_cpus(int node) {
+  if (node < 0) return {};
+  const std::string v =
+      read_text("/sys/devices/system/node/node" + std::to_string(node) + "/cpulist");
+  std::vector<int> cpus = parse_cpulist(v.c_str()), out;
+  cpu_set_t allowed;
+  CPU_ZERO(&allowed);
+  if (sched_getaffinity(0, sizeof(allowed), &allowed) != 0) return {};
+  for (int c : cpus)
+    if (c < CPU_SETSIZE && CPU_ISSET(c, &allowed)) out.push_back(c);
+  return out;
 }
 
 void ThreadPool::run(const std::function<void(int, int)>& fn) {

@@ -34,6 +34,9 @@ class ThreadPool {
   ~ThreadPool();
   int size() const { return n_; }
   void run(const std::function<void(int, int)>& fn);
+  // Bind every worker thread to the given CPUs (the calling thread, which takes a share of
+  // every job, is left alone).  Returns the workers bound.
+  int pin(const std::vector<int>& cpus);
 
  private:
   void worker(int id);
@@ -47,6 +50,13 @@ class ThreadPool {
   std::atomic<int> sleepers_{0};
   std::atomic<bool> stop_{false};
 };
+
+// Host placement: the NUMA node of a PCI device ("0000:75:00.0"; -1 when the platform
+// reports none), the CPUs of a node that this process may run on, and the Linux cpulist
+// format ("0-3,8,10-11") they are read in.
+int pci_numa_node(const char* pci_bus_id);
+std::vector<int> numa_node_cpus(int node);
+std::vector<int> parse_cpulist(const char* text);
 
 // SwiGLU FFN of one expert blob on host cores: y[t] = W_d bf16(silu(W_g x_t) * (W_u x_t)),
 // fp32 accumulation, x as bf16 bits [T][H], y fp32 [T][H].  pool may be null.

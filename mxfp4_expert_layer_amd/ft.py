@@ -79,6 +79,8 @@ _sig = {
     "ft_pack_expert": [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "ft_ctx_create": [_i, C.POINTER(_vp)],
     "ft_ctx_destroy": [_vp],
+    "ft_ctx_numa": [_vp, C.POINTER(_i), C.POINTER(_i)],
+    "ft_debug_parse_cpulist": [C.c_char_p, _vp, _i, C.POINTER(_i)],
     "ft_layer_create": [_vp, C.POINTER(LayerDesc), C.POINTER(_vp)],
     "ft_layer_destroy": [_vp],
     "ft_route": [_vp, _vp, _vp, _i, _vp, _vp, _vp],
@@ -231,6 +233,20 @@ PREFILL_STATIC_SCRATCH_BYTES = 64 << 20
 
 def moe_prefill_noalloc(ctx, layer_h, x, T, y, mode, stream=None):
     check(lib.ft_moe_prefill_noalloc(ctx.handle, layer_h, _ptr(x), T, _ptr(y), mode, stream))
+
+
+def ctx_numa(ctx):
+    """(NUMA node of the context's GPU or -1, CPUs its host threads are bound to or 0)."""
+    node, n = C.c_int(), C.c_int()
+    check(lib.ft_ctx_numa(ctx.handle, C.byref(node), C.byref(n)))
+    return node.value, n.value
+
+
+def debug_parse_cpulist(text: str):
+    n = C.c_int()
+    buf = (C.c_int32 * 4096)()
+    check(lib.ft_debug_parse_cpulist(text.encode(), buf, 4096, C.byref(n)))
+    return list(buf[:min(n.value, 4096)])
 
 
 def measure_bandwidth(ctx, layer_h):

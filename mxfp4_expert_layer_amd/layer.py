@@ -7,12 +7,44 @@ router tensors, shared-expert blobs and (for a partial pool) the pinned host blo
 """
 from __future__ import annotations
 
+import contextlib
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
 from . import ft, synth
+
+
+def node_cpus(node: int):
+    """CPUs of a NUMA node that this process may run on (empty when unknown)."""
+    if node < 0:
+        return set()
+    try:
+        with open(f"/sys/devices/system/node/node{node}/cpulist") as fh:
+            cpus = set(ft.debug_parse_cpulist(fh.read().strip()))
+    except OSError:
+        return set()
+    return cpus & os.sched_getaffinity(0)
+
+
+@contextlib.contextmanager
+def on_gpu_node(ctx):
+    """Run the block on the CPUs of the GPU's NUMA node, so that host memory allocated in it
+    (pinned pages land on the allocating thread's node) sits next to the GPU and to the
+    library's host threads, which the context binds there."""
+    node, _ = ft.ctx_numa(ctx)
+    cpus = node_cpus(node)
+    old = os.sched_getaffinity(0)
+    if not cpus or cpus == old:
+        yield
+        return
+    os.sched_setaffinity(0, cpus)
+    try:
+        yield
+    finally:
+        os.sched_setaffinity(0, old)
 
 
 def _pack_all(cfg, ids, dst: np.ndarray, stride: int, threads: int, shared=False,
@@ -50,10 +82,16 @@ class GpuLayer:
             # share another layer's pinned blob store (same expert bytes, e.g. for timing)
             assert not resident and host_store.numel() == E * self.stride and host_store.is_pinned()
             host = host_store
-        else:
-            host = torch.empty(E * self.stride, dtype=torch.uint8, pin_memory=not resident)
+        elif resident:
+            host = torch.empty(E * self.stride, dtype=torch.uint8)
             _pack_all(cfg, list(range(E)), host.numpy(), self.stride, threads,
                       override=self.override)
+        else:
+            # the pinned blob store the miss path streams and computes from: on the GPU's node
+            with on_gpu_node(ctx):
+                host = torch.empty(E * self.stride, dtype=torch.uint8, pin_memory=True)
+                _pack_all(cfg, list(range(E)), host.numpy(), self.stride, threads,
+                          override=self.override)
         if resident:
             self.pools = [host.to(device)]
             for _ in range(1, copies):

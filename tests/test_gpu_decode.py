@@ -331,6 +331,62 @@ def test_miss_path_adaptive_bandwidths(ctx, rule):
     log(f"[gpu] adaptive rule {rule}: final Bp {prev.bp / 1e9:.2f} GB/s, Bh {prev.bh / 1e9:.2f} GB/s")
 
 
+def test_measure_bandwidth_feeds_the_split(ctx):
+    """The startup probes: Bp (pinned H2D copies of expert blobs) and Bh (the host expert FFN
+    over blobs) come back finite and positive, the next decode calls report exactly those
+    values and split their misses by them (q = round(m Bp / Bh)), and the slot tables follow
+    the oracle's pool driven by the measured pair."""
+    cfg = synth.small_config("missmeas", seed=83, H=512, I=256, E=16, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 22, zipf_c=0.7)
+    L = layer_for(ctx, "missmeas", cfg=cfg, resident=False, n_slots=5, max_tokens=2)
+    bp, bh = ft.measure_bandwidth(ctx, L.handle)
+    log(f"[gpu] measured Bp {bp / 1e9:.2f} GB/s, Bh {bh / 1e9:.2f} GB/s")
+    assert np.isfinite(bp) and np.isfinite(bh) and bp > 0 and bh > 0
+    assert 1e8 < bp < 1e12 and 1e8 < bh < 1e13
+    ft.force_q(L.handle, -1)
+    OL = L.oracle_layer()
+    pool = policy.LruPool(cfg.E, L.n_slots)
+    for s in range(6):
+        x = synth.gen_tokens(cfg, 2, batch=500 + s)
+        st = ft.DecodeStats()
+        y = run_decode(ctx, L, x, st)
+        assert (st.bp, st.bh) == (bp, bh)
+        q, qstar = ft.qstar_split(st.n_miss, bp, bh)
+        assert st.q == q and st.qstar == pytest.approx(qstar, rel=1e-12)
+        r_idx, r_w, _, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+        assert np.all(gap >= 1e-6)
+        res = pool.step(r_idx, r_w, bp, bh)
+        e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+        assert np.array_equal(e2s, res.e2s) and np.array_equal(s2e, res.s2e), s
+        if s % 2 == 0:
+            check_output(y, moe.moe_forward(OL, x)["y"], f"measured split step {s}")
+
+
+def test_context_binds_host_threads_to_the_gpu_node(ctx):
+    """ft_ctx_create binds the host pool's workers to the CPUs of the GPU's NUMA node: when it
+    reports a binding, that many workers run with exactly that node's CPU list."""
+    import os
+    from mxfp4_expert_layer_amd.layer import node_cpus
+    node, pinned = ft.ctx_numa(ctx)
+    log(f"[gpu] GPU NUMA node {node}, host threads bound to {pinned} CPUs")
+    assert node >= -1 and pinned >= 0
+    if pinned == 0:
+        assert not node_cpus(node) or os.environ.get("FT_HOST_AFFINITY") == "0"
+        return
+    cpus = node_cpus(node)
+    assert len(cpus) == pinned
+    bound = 0
+    for tid in os.listdir("/proc/self/task"):
+        try:
+            with open(f"/proc/self/task/{tid}/status") as fh:
+                line = [ln for ln in fh if ln.startswith("Cpus_allowed_list")][0]
+        except (OSError, IndexError):
+            continue
+        if set(ft.debug_parse_cpulist(line.split(":", 1)[1].strip())) == cpus:
+            bound += 1
+    assert bound >= 1
+
+
 def test_miss_path_284b_layer(ctx):
     """The 284B-class layer with a 48-slot pool: 64 warm-up and 64 timed single tokens with the
     slot tables checked after every step and the outputs every 8th step."""

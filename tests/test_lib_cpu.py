@@ -342,3 +342,13 @@ def test_exceptions_do_not_cross_the_abi(kind, code, text):
         assert msg.startswith("ft_debug_throw"), msg
         if text:
             assert text in msg, msg
+
+
+def test_cpulist_parser():
+    """The Linux cpulist format the context reads a NUMA node's CPUs in: ranges and single
+    CPUs, in order; a malformed list gives no CPUs."""
+    assert ft.debug_parse_cpulist("0-3,8,10-11") == [0, 1, 2, 3, 8, 10, 11]
+    assert ft.debug_parse_cpulist("5\n") == [5]
+    assert ft.debug_parse_cpulist("0-1, 4") == [0, 1, 4]
+    for bad in ("", "a-b", "4-2", "1-", "3x"):
+        assert ft.debug_parse_cpulist(bad) == []
