@@ -70,6 +70,24 @@ def qstar_makespan(m: int, Bp: float, Bh: float) -> int:
     return int(np.argmin(cost))
 
 
+def qstar_load(m: int, g0: int, Bp: float, Bh: float, blob: float, t_gpu: float) -> int:
+    """Variant with the GPU's load (mubeitech explainer: the balancing watches the PCIe
+    bandwidth, the CPU's compute and the GPU's load, so that the two sides finish at the same
+    moment).  The integer q in [0, m] minimising max(T_gpu(q), T_host(q)), lowest q on ties:
+      T_gpu(q)  = max(g0 t_gpu, q blob / Bp) + q t_gpu: the GPU runs the g0 experts it holds
+                  while the q copies stream, then the q streamed experts, t_gpu seconds each;
+      T_host(q) = (m - q) blob / (Bh - Bp): the host experts, the copies taking Bp of the
+                  host's memory bandwidth.
+    Bh <= Bp gives m; t_gpu = 0 is the makespan variant."""
+    if m < 0 or g0 < 0 or not (Bp > 0) or not (Bh > 0) or not (blob > 0) or not (t_gpu >= 0):
+        raise ValueError("need m, g0 >= 0, Bp, Bh, blob > 0, t_gpu >= 0")
+    if Bh <= Bp:
+        return m
+    cost = [max(max(g0 * t_gpu, q * blob / Bp) + q * t_gpu, (m - q) * blob / (Bh - Bp))
+            for q in range(m + 1)]
+    return int(np.argmin(cost))
+
+
 def order_misses(misses, weight):
     """Misses sorted by descending total routing weight, ties to the lower expert id."""
     return sorted(misses, key=lambda e: (-weight[e], e))
@@ -145,6 +163,8 @@ class LruPool:
             q = max(0, min(m, q_override))
         elif rule == "makespan":
             q = qstar_makespan(m, Bp, Bh)
+        elif rule == "load":
+            raise ValueError("the load rule needs g0, blob and t_gpu: pass q_override")
         else:
             q = qstar_split(m, Bp, Bh)[0]
         streamed, host, evicted = [], [], []

@@ -256,3 +256,39 @@ def test_permutation_matches_stable_sort(T, k, E):
         assert pos[t, j] == p
         e = idx[t, j]
         assert offsets[e] <= p < offsets[e + 1]
+
+
+def test_load_rule_hand_worked():
+    """blob = 1, Bp = 1, Bh = 3 (a copy takes 1, a host expert 1/2), m = 6 misses, g0 = 4
+    experts already on the GPU.
+    t_gpu = 1/4: q = 0: max(1, 0) + 0 = 1 vs 3 -> 3; q = 1: max(1, 1) + 1/4 vs 5/2 -> 5/2;
+      q = 2: max(1, 2) + 1/2 vs 2 -> 5/2; q = 3: 3 + 3/4 vs 3/2 -> 15/4: the tie of q = 1 and
+      q = 2 goes to q = 1 (the makespan variant, with no GPU term, picks 2: max(2, 2)).
+    t_gpu = 1 (a busy GPU): q = 0: max(4, 0) vs 3 -> 4; q = 1: max(4, 1) + 1 -> 5: q = 0."""
+    assert policy.qstar_load(6, 4, 1.0, 3.0, 1.0, 0.25) == 1
+    assert policy.qstar_makespan(6, 1.0, 3.0) == 2
+    assert policy.qstar_load(6, 4, 1.0, 3.0, 1.0, 1.0) == 0
+    assert policy.qstar_load(0, 4, 1.0, 3.0, 1.0, 1.0) == 0
+    assert policy.qstar_load(5, 0, 2.0, 1.5, 1.0, 0.1) == 5          # Bh <= Bp: every miss streams
+
+
+def test_load_rule_without_gpu_term_is_the_makespan_variant():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        m, g0 = int(rng.integers(0, 20)), int(rng.integers(0, 12))
+        Bp, Bh = float(rng.uniform(1, 60)), float(rng.uniform(1, 250))
+        assert policy.qstar_load(m, g0, Bp, Bh, 13.4, 0.0) == policy.qstar_makespan(m, Bp, Bh)
+
+
+def test_load_rule_never_streams_more_than_the_makespan_variant():
+    """A GPU term only lengthens the GPU side, so the balance point cannot move toward more
+    copies; and a heavier GPU term never streams more."""
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        m, g0 = int(rng.integers(0, 20)), int(rng.integers(0, 12))
+        Bp, Bh = float(rng.uniform(1, 60)), float(rng.uniform(1, 250))
+        t1 = float(rng.uniform(0, 0.5))
+        t2 = t1 + float(rng.uniform(0, 0.5))
+        q1 = policy.qstar_load(m, g0, Bp, Bh, 13.4, t1)
+        assert q1 <= policy.qstar_makespan(m, Bp, Bh)
+        assert policy.qstar_load(m, g0, Bp, Bh, 13.4, t2) <= q1
