@@ -183,6 +183,10 @@ typedef struct ft_decode_stats {
      disk, and the wall time of those reads */
   int32_t n_disk;
   double disk_us;
+  /* GPU load (FT_SPLIT_LOAD): the previous call's GPU time for its hit and shared experts in
+     microseconds (0 if none was timed) and the per-expert GPU time this call's split used,
+     in seconds */
+  double gpu_us_obs, t_gpu;
 } ft_decode_stats;
 
 /*
@@ -253,8 +257,22 @@ FT_API int ft_qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
  * max(q / Bp, (m - q) / (Bh - Bp)), lowest q on ties; Bh <= Bp gives m.  FT_EINVAL as
  * ft_qstar_split.  Pure host function.
  */
-enum { FT_SPLIT_ROUND = 0, FT_SPLIT_MAKESPAN = 1 };
+enum { FT_SPLIT_ROUND = 0, FT_SPLIT_MAKESPAN = 1, FT_SPLIT_LOAD = 2 };
 FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* q);
+
+/*
+ * The split's load variant (mubeitech explainer: the balancing watches the PCIe bandwidth, the
+ * CPU's compute and the GPU's load, so that the two sides finish at the same moment): with g0
+ * experts the GPU computes anyway (hits and shared experts), blob bytes per expert and t_gpu
+ * seconds of GPU time per expert, the integer q in [0, m] minimising
+ *   max( max(g0 t_gpu, q blob / Bp) + q t_gpu,  (m - q) blob / (Bh - Bp) )
+ * (the GPU runs its g0 experts while the q copies stream and then the q streamed ones; the
+ * host runs the rest with the bandwidth the copies leave), lowest q on ties; Bh <= Bp gives m;
+ * t_gpu = 0 is the makespan variant.  FT_EINVAL for m < 0, g0 < 0, Bp, Bh or blob <= 0, or
+ * t_gpu negative or not finite.  Pure host function.
+ */
+FT_API int ft_qstar_split_load(int m, int g0, double Bp, double Bh, double blob, double t_gpu,
+                               int* q);
 
 /*
  * Startup probes of the split rule's two bandwidths (smzdm explainer a825qpgl, section 二: q*
@@ -287,7 +305,11 @@ FT_API int ft_force_q(ft_layer* layer, int q);
 /*
  * Miss-path policy of a layer (the pages let q* follow the hardware as it runs: smzdm
  * explainer a825qpgl, section 二; lowalt.boxinlu2.cn article, section 二).
- *   rule: FT_SPLIT_ROUND (default: q = round(q*)) or FT_SPLIT_MAKESPAN.
+ *   rule: FT_SPLIT_ROUND (default: q = round(q*)), FT_SPLIT_MAKESPAN or FT_SPLIT_LOAD (see
+ *     ft_qstar_split_load; t_gpu is measured on every call of the layer: the GPU time of its
+ *     hit and shared experts' kernels, from events around them, per expert, read at the next
+ *     call; the estimate moves toward each observation by alpha, or takes it when alpha is 0;
+ *     until a first observation t_gpu is 0).
  *   alpha in [0, 1]: 0 (default) keeps Bp and Bh as measured or set.  alpha > 0 re-measures
  *     them during decode and moves each estimate toward its observation by alpha
  *     (est += alpha (obs - est)), before the next call's split:

@@ -125,6 +125,9 @@ struct ft_layer {
   hipEvent_t ev_copy = nullptr;
   hipEvent_t ev_route = nullptr;
   hipEvent_t ev_cp0 = nullptr, ev_cp1 = nullptr;   // timing events around streamed copies
+  hipEvent_t ev_g0 = nullptr, ev_g1 = nullptr;     // around the hit experts' kernels
+  int pend_gpu_items = 0;        // experts of the last call timed by ev_g0/ev_g1
+  double t_gpu = 0.0;            // GPU seconds per expert (FT_SPLIT_LOAD)
   // policy state
   LruState lru;
   double bp = 0.0, bh = 0.0;
@@ -301,6 +304,8 @@ static void free_layer(ft_layer* l) {
   if (l->ev_route) hipEventDestroy(l->ev_route);
   if (l->ev_cp0) hipEventDestroy(l->ev_cp0);
   if (l->ev_cp1) hipEventDestroy(l->ev_cp1);
+  if (l->ev_g0) hipEventDestroy(l->ev_g0);
+  if (l->ev_g1) hipEventDestroy(l->ev_g1);
   if (l->ev_done) hipEventDestroy(l->ev_done);
   if (l->ev_pref) hipEventDestroy(l->ev_pref);
   if (l->pf_dev) hipFree(l->pf_dev);
@@ -431,6 +436,8 @@ extern "C" FT_API int ft_layer_create(ft_ctx* ctx, const ft_layer_desc* desc, ft
   HIP_TRY(hipEventCreateWithFlags(&l->ev_route, hipEventDisableTiming));
   HIP_TRY(hipEventCreate(&l->ev_cp0));
   HIP_TRY(hipEventCreate(&l->ev_cp1));
+  HIP_TRY(hipEventCreate(&l->ev_g0));
+  HIP_TRY(hipEventCreate(&l->ev_g1));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_done, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&l->ev_pref, hipEventDisableTiming));
   HIP_TRY(hipEventRecord(l->ev_done, nullptr));
@@ -730,12 +737,29 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
     l->pend_copy_bytes = 0;
     if (l->alpha > 0.0) l->bp = bandwidth_update(l->bp, S.bp_obs, l->alpha);
   }
+  // the previous call's hit experts have run by now too: their GPU time per expert is an
+  // observation of the GPU's load
+  if (l->pend_gpu_items > 0 && hipEventQuery(l->ev_g1) == hipSuccess) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, l->ev_g0, l->ev_g1) == hipSuccess && ms > 0.f) {
+      S.gpu_us_obs = ms * 1e3;
+      const double obs = ms * 1e-3 / l->pend_gpu_items;
+      l->t_gpu = (l->alpha > 0.0 && l->t_gpu > 0.0) ? bandwidth_update(l->t_gpu, obs, l->alpha)
+                                                     : obs;
+    }
+    l->pend_gpu_items = 0;
+  }
   int rc = qstar_split(m, l->bp, l->bh, &q, &qstar);
   if (rc) return rc;
   if (l->split_rule == FT_SPLIT_MAKESPAN) {
     rc = qstar_makespan(m, l->bp, l->bh, &q);
     if (rc) return rc;
+  } else if (l->split_rule == FT_SPLIT_LOAD) {
+    rc = qstar_load(m, (int)hits.size() + d.n_shared, l->bp, l->bh, (double)l->L.bytes,
+                    l->t_gpu, &q);
+    if (rc) return rc;
   }
+  S.t_gpu = l->t_gpu;
   if (l->force_q >= 0) q = std::min(m, l->force_q);
   std::vector<int> streamed, host;
   for (int n = 0; n < m; ++n) {
@@ -835,7 +859,13 @@ static int decode_miss_path(ft_ctx* ctx, ft_layer* l, const uint16_t* x, int T, 
       a.fuse_combine = 1;
       a.y = y;
     }
+    const bool timed = l->split_rule == FT_SPLIT_LOAD;
+    if (timed) HIP_TRY(hipEventRecord(l->ev_g0, st));
     HIP_TRY((hipError_t)ftk_decode_experts(&a, st, nullptr));
+    if (timed) {
+      HIP_TRY(hipEventRecord(l->ev_g1, st));
+      l->pend_gpu_items = n0;
+    }
   }
   if (n1 > 0) {
     HIP_TRY(hipStreamWaitEvent(st, l->ev_copy, 0));
@@ -922,9 +952,14 @@ extern "C" FT_API int ft_qstar_split_makespan(int m, double Bp, double Bh, int* 
   return qstar_makespan(m, Bp, Bh, q);
 } FT_CATCH("ft_qstar_split_makespan")
 
+extern "C" FT_API int ft_qstar_split_load(int m, int g0, double Bp, double Bh, double blob,
+                                          double t_gpu, int* q) try {
+  return qstar_load(m, g0, Bp, Bh, blob, t_gpu, q);
+} FT_CATCH("ft_qstar_split_load")
+
 extern "C" FT_API int ft_set_miss_policy(ft_layer* layer, int rule, double alpha) try {
   if (!layer) return fail(FT_EINVAL, "ft_set_miss_policy: null layer");
-  if (rule != FT_SPLIT_ROUND && rule != FT_SPLIT_MAKESPAN)
+  if (rule != FT_SPLIT_ROUND && rule != FT_SPLIT_MAKESPAN && rule != FT_SPLIT_LOAD)
     return fail(FT_EINVAL, "ft_set_miss_policy: unknown split rule");
   if (!(alpha >= 0.0 && alpha <= 1.0))
     return fail(FT_EINVAL, "ft_set_miss_policy: alpha must be in [0, 1]");

@@ -430,6 +430,25 @@ int qstar_makespan(int m, double Bp, double Bh, int* q) {
   return FT_OK;
 }
 
+int qstar_load(int m, int g0, double Bp, double Bh, double blob, double t_gpu, int* q) {
+  if (m < 0 || g0 < 0 || !(Bp > 0.0) || !(Bh > 0.0) || !(blob > 0.0) || !(t_gpu >= 0.0) ||
+      !std::isfinite(t_gpu))
+    return fail(FT_EINVAL, "ft_qstar_split_load: need m, g0 >= 0, Bp, Bh, blob > 0 and a "
+                           "finite t_gpu >= 0");
+  int best = m;
+  if (Bh > Bp) {
+    double best_t = 0.0;
+    for (int c = 0; c <= m; ++c) {
+      const double gpu = std::max(g0 * t_gpu, c * blob / Bp) + c * t_gpu;
+      const double host = (m - c) * blob / (Bh - Bp);
+      const double t = std::max(gpu, host);
+      if (c == 0 || t < best_t) { best = c; best_t = t; }
+    }
+  }
+  if (q) *q = best;
+  return FT_OK;
+}
+
 double bandwidth_update(double est, double obs, double alpha) {
   if (!(obs > 0.0) || !std::isfinite(obs)) return est;
   return est + alpha * (obs - est);

@@ -68,6 +68,9 @@ int qstar_split(int m, double Bp, double Bh, int* q, double* qstar);
 // Its makespan variant: the integer q in [0, m] minimising max(q / Bp, (m - q) / (Bh - Bp)),
 // lowest q on ties; Bh <= Bp gives m.
 int qstar_makespan(int m, double Bp, double Bh, int* q);
+// The load variant: the q in [0, m] minimising max(max(g0 t_gpu, q blob / Bp) + q t_gpu,
+// (m - q) blob / (Bh - Bp)), lowest q on ties; Bh <= Bp gives m.
+int qstar_load(int m, int g0, double Bp, double Bh, double blob, double t_gpu, int* q);
 // One step of the running estimate of a bandwidth: est + alpha (obs - est); observations
 // that are not positive and finite leave it unchanged.
 double bandwidth_update(double est, double obs, double alpha);

@@ -19,7 +19,7 @@ FT_FTW_DIRECT, FT_FTW_STAGED = 1, 2
 FT_MXFP4, FT_NVFP4 = 0, 1
 FT_PREFILL_EXACT, FT_PREFILL_MXFP4 = 0, 1
 FT_LAYER_PREFILL_MXFP4 = 1
-FT_SPLIT_ROUND, FT_SPLIT_MAKESPAN = 0, 1
+FT_SPLIT_ROUND, FT_SPLIT_MAKESPAN, FT_SPLIT_LOAD = 0, 1, 2
 MAX_DECODE_TOKENS = 16
 FORMATS = {"mxfp4": FT_MXFP4, "nvfp4": FT_NVFP4}
 
@@ -61,7 +61,8 @@ class DecodeStats(C.Structure):
                 ("bp", C.c_double), ("bh", C.c_double), ("host_us", C.c_double),
                 ("wait_us", C.c_double), ("bp_obs", C.c_double), ("bh_obs", C.c_double),
                 ("n_prefetched", C.c_int32), ("n_prefetch_hits", C.c_int32),
-                ("n_disk", C.c_int32), ("disk_us", C.c_double)]
+                ("n_disk", C.c_int32), ("disk_us", C.c_double),
+                ("gpu_us_obs", C.c_double), ("t_gpu", C.c_double)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -93,6 +94,7 @@ _sig = {
     "ft_set_bandwidth": [_vp, _d, _d],
     "ft_force_q": [_vp, _i],
     "ft_qstar_split_makespan": [_i, _d, _d, C.POINTER(_i)],
+    "ft_qstar_split_load": [_i, _i, _d, _d, _d, _d, C.POINTER(_i)],
     "ft_set_miss_policy": [_vp, _i, _d],
     "ft_set_prefetch": [_vp, _vp, _i],
     "ft_debug_pool_stress": [_i, _i, _i],
@@ -261,6 +263,12 @@ def set_bandwidth(layer_h, Bp, Bh):
 
 def force_q(layer_h, q):
     check(lib.ft_force_q(layer_h, q))
+
+
+def qstar_split_load(m: int, g0: int, Bp: float, Bh: float, blob: float, t_gpu: float) -> int:
+    q = C.c_int()
+    check(lib.ft_qstar_split_load(m, g0, Bp, Bh, blob, t_gpu, C.byref(q)))
+    return q.value
 
 
 def qstar_split_makespan(m: int, Bp: float, Bh: float) -> int:

@@ -331,6 +331,50 @@ def test_miss_path_adaptive_bandwidths(ctx, rule):
     log(f"[gpu] adaptive rule {rule}: final Bp {prev.bp / 1e9:.2f} GB/s, Bh {prev.bh / 1e9:.2f} GB/s")
 
 
+def test_miss_path_load_rule(ctx):
+    """The split's load variant: every call times its hit experts' kernels, the next call
+    reports that GPU time and the per-expert estimate it split with, and its q is the load
+    rule's for the call's m, hits (+ shared), Bp, Bh and that estimate; the oracle's pool,
+    given each call's q, keeps the slot tables bit-exact, and outputs match the oracle."""
+    cfg = synth.small_config("missload", seed=85, H=512, I=256, E=16, k=3, n_shared=1,
+                             code_dist="normal", router_sigma=1 / 22, zipf_c=0.7)
+    L = layer_for(ctx, "missload", cfg=cfg, resident=False, n_slots=6, max_tokens=2)
+    # bandwidths in a ratio where a GPU term of a few microseconds per expert moves q
+    bp, bh = 2.0e9, 5.0e9
+    ft.set_bandwidth(L.handle, bp, bh)
+    ft.force_q(L.handle, -1)
+    ft.set_miss_policy(L.handle, ft.FT_SPLIT_LOAD, 0.0)
+    OL = L.oracle_layer()
+    pool = policy.LruPool(cfg.E, L.n_slots)
+    seen, prev_hits = 0, None
+    try:
+        for s in range(20):
+            x = synth.gen_tokens(cfg, 2, batch=700 + s)
+            st = ft.DecodeStats()
+            y = run_decode(ctx, L, x, st)
+            if prev_hits:
+                assert st.gpu_us_obs > 0, s
+                assert st.t_gpu == pytest.approx(st.gpu_us_obs * 1e-6 / prev_hits, rel=1e-6), s
+                seen += 1
+            g0 = st.n_hits + cfg.n_shared
+            assert st.q == ft.qstar_split_load(st.n_miss, g0, st.bp, st.bh, float(L.stride),
+                                               st.t_gpu)
+            assert st.q == policy.qstar_load(st.n_miss, g0, st.bp, st.bh, float(L.stride),
+                                             st.t_gpu)
+            r_idx, r_w, _, gap = moe.route(fp4.bf16_bits_to_f64(x), OL.router_w, OL.router_b, cfg.k)
+            assert np.all(gap >= 1e-6)
+            res = pool.step(r_idx, r_w, bp, bh, q_override=st.q)
+            e2s, s2e = ft.debug_tables(L.handle, cfg.E, L.n_slots)
+            assert np.array_equal(e2s, res.e2s) and np.array_equal(s2e, res.s2e), s
+            if s % 3 == 0:
+                check_output(y, moe.moe_forward(OL, x)["y"], f"load rule step {s}")
+            prev_hits = st.n_hits + cfg.n_shared
+        log(f"[gpu] load rule: t_gpu {st.t_gpu * 1e6:.2f} us per expert")
+    finally:
+        ft.set_miss_policy(L.handle, ft.FT_SPLIT_ROUND, 0.0)
+    assert seen > 0
+
+
 def test_measure_bandwidth_feeds_the_split(ctx):
     """The startup probes: Bp (pinned H2D copies of expert blobs) and Bh (the host expert FFN
     over blobs) come back finite and positive, the next decode calls report exactly those

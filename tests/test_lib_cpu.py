@@ -137,6 +137,25 @@ def test_makespan_split_matches_oracle():
         assert e.value.code == ft.FT_EINVAL
 
 
+def test_load_split_matches_oracle():
+    """The library's load variant against the oracle's over random (m, g0, Bp, Bh, t_gpu),
+    including no GPU term and a busy GPU, and its argument checks."""
+    rng = np.random.default_rng(4)
+    blob = 13369344.0
+    for i in range(600):
+        m, g0 = int(rng.integers(0, 17)), int(rng.integers(0, 12))
+        Bp, Bh = float(rng.uniform(1e9, 60e9)), float(rng.uniform(1e9, 250e9))
+        t = 0.0 if i % 5 == 0 else float(rng.uniform(0, 5e-4))
+        assert ft.qstar_split_load(m, g0, Bp, Bh, blob, t) == policy.qstar_load(m, g0, Bp, Bh, blob, t), \
+            (m, g0, Bp, Bh, t)
+    for bad in ((-1, 0, 1.0, 1.0, 1.0, 0.0), (1, -1, 1.0, 1.0, 1.0, 0.0), (1, 0, 0.0, 1.0, 1.0, 0.0),
+                (1, 0, 1.0, 1.0, 0.0, 0.0), (1, 0, 1.0, 1.0, 1.0, -1.0),
+                (1, 0, 1.0, 1.0, 1.0, float("inf"))):
+        with pytest.raises(ft.FtError) as e:
+            ft.qstar_split_load(*bad)
+        assert e.value.code == ft.FT_EINVAL
+
+
 def _aligned(nbytes):
     """A 4096-aligned uint8 view of nbytes (O_DIRECT destinations)."""
     raw = np.zeros(nbytes + 4096, dtype=np.uint8)
