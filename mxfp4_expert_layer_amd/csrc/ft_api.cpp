@@ -1319,12 +1319,15 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   uint8_t* perm_tok = take(pairs * 4);
   uint8_t* perm_w = take(pairs * 4);
   const bool mx = mode == FT_PREFILL_MXFP4;
-  uint8_t* hperm = mx ? nullptr : take(pairs * d.I * 2);
   uint8_t* xq = mx ? take((size_t)T * d.H / 2) : nullptr;
   uint8_t* xqs = mx ? take((size_t)T * d.H / 32) : nullptr;
-  // tiled operands: padded permuted rows (at most T*k + 15 E), 16 per tile row
-  const size_t prows = mx ? (pairs + 15 * (size_t)d.E + 15) / 16 * 16 : 0;
-  uint8_t* poff = mx ? take((size_t)(d.E + 1) * 4) : nullptr;
+  // tiled operands: permuted rows, each expert's padded to a multiple of pad (at most
+  // T*k + (pad - 1) E rows, rounded up to pad)
+  const size_t pad = mx ? 16 : 32;
+  const size_t prows = (pairs + (pad - 1) * (size_t)d.E + pad - 1) / pad * pad;
+  uint8_t* poff = take((size_t)(d.E + 1) * 4);
+  uint8_t* xtb = mx ? nullptr : take(prows * d.H * 2);
+  uint8_t* htb = mx ? nullptr : take(prows * d.I * 2);
   uint8_t* xt = mx ? take(prows * d.H / 2) : nullptr;
   uint8_t* xts = mx ? take(prows * d.H / 32) : nullptr;
   uint8_t* ht = mx ? take(prows * d.I / 2) : nullptr;
@@ -1333,7 +1336,7 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
   // the expert of each token block (at most pairs / rows + E blocks of `rows` rows)
   const size_t brows = mx ? kS1Rows : kGemmM;
   uint8_t* blk_e = take(((pairs + brows - 1) / brows + d.E) * 4);
-  uint8_t* tile_e = mx ? take(prows / 16 * 4) : nullptr;   // expert of each 16-row tile row
+  uint8_t* tile_e = take(prows / pad * 4);   // expert of each padded row group
   if (a) {
     a->logits = (float*)logits;
     a->idx = (int32_t*)idx;
@@ -1347,7 +1350,9 @@ static size_t prefill_carve(const ft_layer* l, int T, int mode, uint8_t* base,
     a->pos = (int32_t*)pos;
     a->perm_tok = (int32_t*)perm_tok;
     a->perm_w = (float*)perm_w;
-    a->hperm = (uint16_t*)hperm;
+    a->xtb = (uint16_t*)xtb;
+    a->htb = (uint16_t*)htb;
+    a->pad_rows = (int)pad;
     a->xq = xq;
     a->xqs = xqs;
     a->poff = (int32_t*)poff;

@@ -158,6 +158,8 @@ struct PrefillLaunch {
   BlobLayout L;
   int mode;                     // FT_PREFILL_EXACT or FT_PREFILL_MXFP4
   int mrows;                    // token rows per grouped-GEMM block (kGemmM or kS1Rows)
+  int pad_rows;                 // every expert's permuted rows padded to a multiple of this in
+                                // the token-operand tiles (16: scaled-FP4 mode; 32: exact mode)
   const uint8_t* mxpool;        // FT_PREFILL_MXFP4: MXFP4 blob of expert e at e * mxstride
   uint64_t mxstride;
   BlobLayout ML;                // layout of those blobs
@@ -172,11 +174,16 @@ struct PrefillLaunch {
   int32_t* base;                // [T/256][E]
   int32_t* tb_off;              // [E+1] prefix of mrows-row token blocks per expert
   int32_t* blk_e;               // [T*k/mrows + E] expert of each token block
-  int32_t* tile_e;              // MXFP4 mode: [P/16] expert of each padded 16-row tile row
+  int32_t* tile_e;              // [P/pad_rows] expert of each padded row group
   int32_t* pos;                 // [T][k]
   int32_t* perm_tok;            // [T*k] token of each permuted row
   float* perm_w;                // [T*k] routing weight of each permuted row
-  uint16_t* hperm;              // [T*k][I] bf16 (exact mode)
+  // exact mode: the GEMMs' token operands as bf16 tiles of 32 padded rows x 16 K in the
+  // operand order of the 32x32x16 MFMA, 1 KB each: tile (row group g, 64-K chunk c, step s)
+  // at ((g * K/64 + c) * 4 + s) * 1 KB, lane (t, h) holding row 32 g + t, K 64 c + 32 h + 8 s
+  // .. + 7; expert e's rows start at padded row poff[e]
+  uint16_t* xtb;                // x rows, K = H (padding rows zero)
+  uint16_t* htb;                // h rows, K = I (padding rows unspecified)
   uint8_t* xq;                  // MXFP4 mode: quantised x, codes [T][H/2]
   uint8_t* xqs;                 //   and E8M0 scales [T][H/32]
   // MXFP4 mode: the grouped GEMMs' token operands in the blob's tile format (16 rows x 128 K

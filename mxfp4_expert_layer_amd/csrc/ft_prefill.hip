@@ -14,6 +14,8 @@
 //   k_perm_scan       counts, offsets (exclusive scan), per-block bases, the row-block map.
 //   k_perm_place      pos[t][j] = base + (tokens below t in the block's mask); the row of
 //                     every pair, expert ascending then token ascending (stable).
+//   k_tile_x          the permuted x rows, each expert's padded to a multiple of 32, into
+//                     the token tiles of the gate/up GEMM (MFMA operand order).
 //   k_zero            y = 0 (the down GEMM adds into it).
 //   k_xgemm<0>        per (expert, 256-row block, 128 gate + 128 up features): G, U on the
 //                     32x32x16 bf16 MFMA with the FP4 weights decoded to bf16 in registers
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     blk[i] = (cnt[i] + a.mrows - 1) / a.mrows;
-    pad[i] = (cnt[i] + 15) & ~15;
+    pad[i] = (cnt[i] + a.pad_rows - 1) / a.pad_rows * a.pad_rows;
   }
   // exclusive scans over experts (pairs, row blocks and, in the MXFP4 mode, 16-padded rows),
   // four experts per thread
@@ -372,8 +374,8 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
         out[e] = base;
         if (pass == 1 && a.blk_e)   // the expert of every row block
           for (int j = 0; j < v[i]; ++j) a.blk_e[base + j] = e;
-        if (pass == 2 && a.tile_e)  // the expert of every padded 16-row tile row
-          for (int j = 0; j < v[i] / 16; ++j) a.tile_e[base / 16 + j] = e;
+        if (pass == 2 && a.tile_e)  // the expert of every padded row group
+          for (int j = 0; j < v[i] / a.pad_rows; ++j) a.tile_e[base / a.pad_rows + j] = e;
         if (pass == 0) {
           a.counts[e] = cnt[i];
           int run = base;
@@ -481,14 +483,15 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
                                         : (uint64_t)rt * KC * 128 + 2 * slot;
     ssrc[o] = blob + a.L.off[2 * m + 1] + (sb & ~(uint64_t)3);
   }
-  // token rows j = 2 wave, 2 wave + 1 of this lane (rows past the block re-read its last row;
-  // their results are never used)
-  const uint16_t* tsrc[2];
+  // this wave's token operands j = 2 wave, 2 wave + 1: row groups of the tiled operand (a
+  // group past the block re-reads the block's last group; its results are never used)
+  const int prow0 = a.poff[e] + (gblk - a.tb_off[e]) * kXRows;   // padded row of the block
+  const uint8_t* tsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int tl = min(32 * (2 * wave + q) + r32, nrows - 1);
-    tsrc[q] = MODE == 0 ? a.x + (uint64_t)a.perm_tok[row0 + tl] * a.H + 32 * h
-                        : a.hperm + (uint64_t)(row0 + tl) * a.I + 32 * h;
+    const int g = (prow0 >> 5) + min(2 * wave + q, nj - 1);
+    tsrc[q] = (const uint8_t*)(MODE == 0 ? a.xtb : a.htb) + (uint64_t)g * (K / 64) * 4096 +
+              16 * lane;
   }
   if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
     const float tsd = blob_tscale(blob, 2);
@@ -517,7 +520,8 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
       }                                                                                      \
       _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                    \
         _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_)                                     \
-          dma16(tsrc[q_] + c_ * 64 + 8 * ks_, &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);         \
+          dma16(tsrc[q_] + ((uint64_t)c_ * 4 + ks_) * 1024,                                  \
+                &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);                                       \
     } while (0)
 
     f32x16 acc[2][NJ];
@@ -676,21 +680,29 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
       // r < 8, gate features f0 + 8 (r / 4) + 4 h + r % 4 of operand o, with the up sums of the
       // same features in registers r + 8
       const float tsg = blob_tscale(blob, 0), tsu = blob_tscale(blob, 1);
+      // into the down GEMM's token tiles: feature f = 64 c + 32 h' + 8 s + i of padded row
+      // 32 g + t sits in tile (g, c, s), lane t + 32 h', element i; a lane's four consecutive
+      // features are one 8-byte piece
+      const int NCI = a.I / 64;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int tl = 32 * j + r32;
         if (tl < nrows) {
+          const int prow = prow0 + tl, g = prow >> 5, t = prow & 31;
 #pragma unroll
           for (int o = 0; o < 2; ++o) {
-            const int f0 = fb * 128 + wave * 32 + 16 * o + 4 * h;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
+              const int f = fb * 128 + wave * 32 + 16 * o + 8 * q + 4 * h;
               uint16_t hv[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 hv[r] = f32_to_bf16_rne(silu_f32(acc[o][j][4 * q + r] * tsg) *
                                         (acc[o][j][8 + 4 * q + r] * tsu));
-              *(uint2*)(a.hperm + (uint64_t)(row0 + tl) * a.I + f0 + 8 * q) =
+              const int c = f >> 6, kk = f & 63;
+              const uint64_t slot = (((uint64_t)g * NCI + c) * 4 + ((kk >> 3) & 3)) * 64 + t +
+                                    32 * (kk >> 5);
+              *(uint2*)(a.htb + slot * 8 + (kk & 7)) =
                   make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
                              (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
             }
@@ -726,6 +738,38 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
     FT_X_BLOCK(5); FT_X_BLOCK(6); FT_X_BLOCK(7); default: FT_X_BLOCK(8);
   }
 #undef FT_X_BLOCK
+}
+
+// Exact mode: the permuted x rows into the gate/up GEMM's token tiles (xtb).  One workgroup
+// per 32-row group of padded permuted rows (its expert from the group map k_perm_scan wrote)
+// and 8 chunks of 64 K: thread (t, p) reads 16 bytes, K 64 c + 8 p .. + 7 of the group's row t
+// (eight threads read a row's 128-byte chunk contiguously) and writes them to tile
+// (g, c, p % 4), lane t + 32 (p / 4); padding rows get zeros.  The grid covers the largest
+// padded row count.
+constexpr int kTileXChunks = 8;
+__global__ __launch_bounds__(256) void k_tile_x(PrefillLaunch a) {
+  const int g = blockIdx.x;
+  if (g >= (a.poff[a.E] >> 5)) return;
+  const int NC = a.H / 64;
+  const int t = threadIdx.x >> 3, p = threadIdx.x & 7;
+  const int e = a.tile_e[g];
+  const int r = 32 * g + t - a.poff[e];
+  const bool valid = r < a.counts[e];
+  const uint16_t* xr =
+      a.x + (uint64_t)a.perm_tok[a.offsets[e] + min(r, a.counts[e] - 1)] * a.H + 8 * p;
+  const int c0 = blockIdx.y * kTileXChunks;
+  uint4 v[kTileXChunks];
+#pragma unroll
+  for (int u = 0; u < kTileXChunks; ++u)
+    v[u] = *(const uint4*)(xr + (uint64_t)min(c0 + u, NC - 1) * 64);
+#pragma unroll
+  for (int u = 0; u < kTileXChunks; ++u) {
+    const int c = c0 + u;
+    if (c < NC) {
+      const uint64_t slot = (((uint64_t)g * NC + c) * 4 + (p & 3)) * 64 + t + 32 * (p >> 2);
+      *(uint4*)(a.xtb + slot * 8) = valid ? v[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
 }
 
 // y = 0 before the down GEMM's atomic combine (a kernel, not a memset node, so that the call
@@ -1387,6 +1431,11 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     // tiles of the padded permuted tokens: at most T*k + 15 E rows
     const unsigned maxtrows = (unsigned)((a.T * a.k + 15 * a.E + 15) / 16);
     hipLaunchKernelGGL(k_tile_xq, dim3(maxtrows), dim3(256), 0, st, a);
+  } else {
+    // at most T*k + 31 E padded rows, 32 per group
+    const unsigned groups = (unsigned)((a.T * a.k + 31 * a.E + 31) / 32);
+    const unsigned cg = (unsigned)((a.H / 64 + kTileXChunks - 1) / kTileXChunks);
+    hipLaunchKernelGGL(k_tile_x, dim3(groups, cg), dim3(256), 0, st, a);
   }
   // upper bound on mrows-row token blocks: sum_e ceil(c_e / mrows) <= T*k/mrows + E
   const int gmax = (a.T * a.k + a.mrows - 1) / a.mrows + a.E;
