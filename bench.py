@@ -361,7 +361,8 @@ def bench_miss_path(args, wl):
     disk = None
     if args.disk_dir is not None:
         disk = disk_tier_setup(args, ctx, Ls, cfg)
-    rule = ft.FT_SPLIT_MAKESPAN if args.split == "makespan" else ft.FT_SPLIT_ROUND
+    rule = {"round": ft.FT_SPLIT_ROUND, "makespan": ft.FT_SPLIT_MAKESPAN,
+            "load": ft.FT_SPLIT_LOAD}[args.split]
     for li, L in enumerate(Ls):
         ft.set_bandwidth(L.handle, bp, bh)
         ft.set_miss_policy(L.handle, rule, args.adaptive)
@@ -437,6 +438,7 @@ def bench_miss_path(args, wl):
                       "mean_host_us": host_us / calls, "mean_wait_us": wait_us / calls,
                       "split_rule": args.split, "adaptive_alpha": args.adaptive,
                       "final_Bp_GBps": st.bp / 1e9, "final_Bh_GBps": st.bh / 1e9,
+                      "final_t_gpu_us": st.t_gpu * 1e6 if args.split == "load" else None,
                       "median_Bp_obs_GBps": float(np.median(bp_obs)) / 1e9 if bp_obs else None,
                       "median_Bh_obs_GBps": float(np.median(bh_obs)) / 1e9 if bh_obs else None},
         "roofline": None,
@@ -595,8 +597,8 @@ def prefill_run(ctx, L, cfg, T, K, W, s1, workload):
     else:
         roof = {"bound": "mfma", "achieved": gu_tf, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": gu_tf / BF16_PEAK_TFLOPS,
-                "traffic": measured_traffic(f"k_ggemm<0>@{workload}", "prefill"),
-                "kernel": "k_ggemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
+                "traffic": measured_traffic(f"k_xgemm<0>@{workload}", "prefill"),
+                "kernel": "k_xgemm<0> (gate/up + SwiGLU)", "kernel_us": gu_us,
                 "flops_per_launch": fl_gu, "timing": "dispatch-events"}
     layer = {"flops_per_step": fl_gu + fl_dn,
              "TFLOPs_per_step": (fl_gu + fl_dn) / step_s / 1e12,
@@ -729,8 +731,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--zipf-c", type=float, default=None,
                     help="miss path: router bias strength c of b_e = -c ln(rank_e)")
-    ap.add_argument("--split", choices=["round", "makespan"], default="round",
-                    help="miss path: split rule (round(q*) or the makespan variant)")
+    ap.add_argument("--split", choices=["round", "makespan", "load"], default="round",
+                    help="miss path: split rule (round(q*), the makespan variant, or the "
+                         "variant that also balances the GPU's measured load)")
     ap.add_argument("--adaptive", type=float, default=0.0,
                     help="miss path: running-average weight for re-measuring Bp, Bh (0: fixed)")
     ap.add_argument("--layers", type=int, default=1,
