@@ -543,7 +543,7 @@ __device__ __forceinline__ void tile_gemv(const uint8_t* const* codes, const uin
 // work list is read from memory (miss path); EPL < 0: the list is built from the routed
 // indices a previous k_topk wrote.  Workgroup 0 publishes the list for k_down.
 template <int KSPLIT, int UNR, int EPL, int FMT>
-__global__ __launch_bounds__(256) void k_gateup(DecodeLaunch a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup(DecodeLaunch a) {
   constexpr int RPW = 4 / KSPLIT;
   __shared__ TopkLds tk;
   __shared__ ListLds ls;
@@ -905,7 +905,7 @@ static void launch_gateup(const DecodeLaunch& a, hipStream_t st, hipEvent_t e0, 
   const int KC = a.H / kTileK, RT = a.I / kTileRows;
 #define FT_GATEUP(KS_, RPW_)                                                                \
   do {                                                                                      \
-    auto* k_ = k_gateup<KS_, 4, EPL, FMT>;                                                  \
+    auto* k_ = k_gateup<KS_, 2, EPL, FMT>;                                                  \
     const int cap_ = resident_workgroups((const void*)k_);                                  \
     FT_LAUNCH(k_, dim3(grid_for(a.max_items * ((RT + (RPW_) - 1) / (RPW_)), cap_)), e0, e1, a); \
   } while (0)
