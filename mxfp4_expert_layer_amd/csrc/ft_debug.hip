@@ -33,8 +33,8 @@ __global__ __launch_bounds__(64) void k_dequant_nv(const uint8_t* codes, const u
   const int row = rt * kTileRows + (lane & 15);
   const int k0 = kc * kTileK + 32 * (lane >> 4);
   const uint4 c = ((const uint4*)codes)[(uint64_t)tile * 64 + lane];
-  const float s0 = e4m3_f32(scales[(uint64_t)tile * 128 + 2 * lane]);
-  const float s1 = e4m3_f32(scales[(uint64_t)tile * 128 + 2 * lane + 1]);
+  const float s0 = e4m3_f32_fast(scales[(uint64_t)tile * 128 + 2 * lane]);
+  const float s1 = e4m3_f32_fast(scales[(uint64_t)tile * 128 + 2 * lane + 1]);
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   for (int q = 0; q < 32; ++q) {
     const uint32_t code = (w[q >> 3] >> (4 * (q & 7))) & 15;

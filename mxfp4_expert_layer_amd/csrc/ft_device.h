@@ -22,6 +22,17 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
 }
+// The same copies through a buffer resource: the address is the resource's base + voff (per
+// lane) + soff (wave-uniform); a lane whose offset lies past the resource's size reads zeros.
+constexpr int kBufFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 word 3)
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                       void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 field layout)
 #define FT_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
@@ -123,11 +134,14 @@ __device__ __forceinline__ float e2m1_f32(uint32_t c) {
 }
 // The same E4M3 decode by bit assembly: a normal code's fp32 exponent field is e + 120 with
 // its 3 mantissa bits on top of the fp32 mantissa; a subnormal is m x 2^-9.
+// The magnitude bits eeeemmm placed at fp32 bit 20 read as 2^(e - 127) (1 + m/8) for e > 0 and
+// as the fp32 subnormal m 2^-129 for e = 0; one multiply by 2^120 turns both into the E4M3
+// value (2^(e - 7) (1 + m/8), or m 2^-9), exactly.  No branch and no select but the NaN code's.
+// Needs fp32 denormal inputs kept (the kernels' default float mode, which does not flush).
 __device__ __forceinline__ float e4m3_f32_fast(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  if ((c & 0x7fu) == 0x7fu) v = __uint_as_float(0x7fc00000u);
-  return (c & 0x80u) ? -v : v;
+  const float mag = __uint_as_float((c & 0x7fu) << 20) * 0x1p120f;
+  const float v = (c & 0x7fu) == 0x7fu ? __uint_as_float(0x7fc00000u) : mag;
+  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
 }
 __device__ __forceinline__ float e4m3_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15, m = c & 7;

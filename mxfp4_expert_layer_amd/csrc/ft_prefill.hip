@@ -442,10 +442,11 @@ __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
 // per-pair output is stored.  Blocks (token block g, feature block fb) sit on XCD g % 8, so
 // the feature blocks of one token block share that XCD's L2 for the token rows.
 constexpr int kXRows = 256;
+constexpr int kXThreads = 256;
 constexpr int kXCopies = 12;   // copies per wave per chunk: 8 token, 2 code, 2 scale
 
 template <int MODE, int FMT>
-__global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
+__global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   // stage s: token operands [ks 4][j 8][64 lanes] (tk), then in wk the weight code slots
   // [wave 4][o 2][64 lanes] followed by the weight scale dwords [wave 4][o 2][64 lanes] (one
   // array per kind and stage: six copy targets, few enough for the compiler to keep apart)
@@ -468,31 +469,40 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
   const uint8_t* blob = a.pool + (uint64_t)e * a.stride;
   const int h = lane >> 5, r32 = lane & 31;
 
-  // copy sources.  Weight operand o of this wave, lane (r32, h): tile rt of matrix m,
-  // slot (r32 % 16) + 16 h of chunk 0 (chunk ch adds (ch / 2) tiles and 32 (ch % 2) slots)
-  const uint8_t* wsrc[2];
-  const uint8_t* ssrc[2];
+  // copy sources: buffer resources over the weight codes, the weight scales and the block's
+  // token tiles, a fixed lane offset per copy in a vector register and the chunk's offset in
+  // a scalar one, so a chunk step is scalar arithmetic.  Weight operand o of this wave, lane
+  // (r32, h): tile rt of matrix m, slot (r32 % 16) + 16 h of chunk 0 (chunk ch adds (ch / 2)
+  // tiles and 32 (ch % 2) slots).  MODE 0 reads gate (lanes 0..15) and up (16..31) rows, so
+  // the code resource starts at the gate codes and spans to the end of the blob.
+  const int m0 = MODE == 0 ? 0 : 2;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(blob + a.L.off[2 * m0]), (short)0, (int)(a.L.bytes - a.L.off[2 * m0]), kBufFlags);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(blob + a.L.off[2 * m0 + 1]), (short)0, (int)(a.L.bytes - a.L.off[2 * m0 + 1]),
+      kBufFlags);
+  uint32_t wvo[2], svo[2];
 #pragma unroll
   for (int o = 0; o < 2; ++o) {
     int m, rt;
     if (MODE == 0) { m = r32 >> 4; rt = fb * 8 + 2 * wave + o; }
     else { m = 2; rt = min(fb * 16 + 4 * wave + 2 * o + (r32 >> 4), nrt - 1); }
     const int slot = (r32 & 15) + 16 * h;
-    wsrc[o] = blob + a.L.off[2 * m] + ((uint64_t)rt * KC * 64 + slot) * 16;
+    wvo[o] = (uint32_t)(a.L.off[2 * m] - a.L.off[2 * m0] + ((uint64_t)rt * KC * 64 + slot) * 16);
     const uint64_t sb = FMT == FT_MXFP4 ? (uint64_t)rt * KC * 64 + slot
                                         : (uint64_t)rt * KC * 128 + 2 * slot;
-    ssrc[o] = blob + a.L.off[2 * m + 1] + (sb & ~(uint64_t)3);
+    svo[o] = (uint32_t)(a.L.off[2 * m + 1] - a.L.off[2 * m0 + 1] + (sb & ~(uint64_t)3));
   }
   // this wave's token operands j = 2 wave, 2 wave + 1: row groups of the tiled operand (a
   // group past the block re-reads the block's last group; its results are never used)
   const int prow0 = a.poff[e] + (gblk - a.tb_off[e]) * kXRows;   // padded row of the block
-  const uint8_t* tsrc[2];
+  const uint32_t gbytes = (uint32_t)(K / 64) * 4096;              // one row group's tiles
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)(MODE == 0 ? a.xtb : a.htb) + (uint64_t)(prow0 >> 5) * gbytes),
+      (short)0, (int)(nj * gbytes), kBufFlags);
+  uint32_t tvo[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int g = (prow0 >> 5) + min(2 * wave + q, nj - 1);
-    tsrc[q] = (const uint8_t*)(MODE == 0 ? a.xtb : a.htb) + (uint64_t)g * (K / 64) * 4096 +
-              16 * lane;
-  }
+  for (int q = 0; q < 2; ++q) tvo[q] = (uint32_t)min(2 * wave + q, nj - 1) * gbytes + 16 * lane;
   if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
     const float tsd = blob_tscale(blob, 2);
     for (int i = tid; i < nrows; i += 256) {
@@ -511,17 +521,17 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
 #define FT_X_ISSUE(ch_, TK_, WK_)                                                          \
     do {                                                                                     \
       const int c_ = min((ch_), NC - 1);                                                     \
-      const uint64_t wo_ = (uint64_t)(c_ >> 1) * 1024 + (c_ & 1) * 512;                      \
-      const uint64_t so_ = FMT == FT_MXFP4 ? (uint64_t)(c_ >> 1) * 64 + (c_ & 1) * 32        \
-                                           : (uint64_t)(c_ >> 1) * 128 + (c_ & 1) * 64;      \
+      const uint32_t wo_ = (c_ >> 1) * 1024 + (c_ & 1) * 512;                                \
+      const uint32_t so_ = FMT == FT_MXFP4 ? (c_ >> 1) * 64 + (c_ & 1) * 32                  \
+                                           : (c_ >> 1) * 128 + (c_ & 1) * 64;                \
       _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                     \
-        dma16(wsrc[o_] + wo_, &WK_[(wave * 2 + o_) * 64]);                                   \
-        dma4(ssrc[o_] + so_, (uint32_t*)&WK_[512] + (wave * 2 + o_) * 64);                   \
+        bdma16(wres, wvo[o_], wo_, &WK_[(wave * 2 + o_) * 64]);                              \
+        bdma4(sres, svo[o_], so_, (uint32_t*)&WK_[512] + (wave * 2 + o_) * 64);              \
       }                                                                                      \
       _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                    \
         _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_)                                     \
-          dma16(tsrc[q_] + ((uint64_t)c_ * 4 + ks_) * 1024,                                  \
-                &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);                                       \
+          bdma16(tres, tvo[q_], (uint32_t)(c_ * 4 + ks_) * 1024,                             \
+                 &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);                                      \
     } while (0)
 
     f32x16 acc[2][NJ];
@@ -582,8 +592,10 @@ __global__ __launch_bounds__(256) void k_xgemm(PrefillLaunch a, int NB) {
       _Pragma("unroll") for (int i_ = 0; i_ < NJ; ++i_) {                                   \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
         __builtin_amdgcn_sched_group_barrier(0x100, (NR_), 0);                              \
+      }                                                                                     \
+      _Pragma("unroll") for (int i_ = 0; i_ < NJ; ++i_) {                                   \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
-        __builtin_amdgcn_sched_group_barrier(0x002, (NV_), 0);                              \
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * (NV_), 0);                          \
       }                                                                                     \
       __builtin_amdgcn_sched_barrier(0);                                                    \
     } while (0)
@@ -1372,12 +1384,13 @@ extern "C" int ftk_split_router(const float* wr, int E, int H, uint16_t* planes,
   return (int)hipGetLastError();
 }
 
-#define FT_PLAUNCH(kern, grid, evs, eve, ...)                                              \
+#define FT_PLAUNCH_NT(kern, grid, nt, evs, eve, ...)                                       \
   do {                                                                                     \
     auto* kfn_ = kern;                                                                     \
-    if (evs) hipExtLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, evs, eve, 0, __VA_ARGS__); \
-    else hipLaunchKernelGGL(kfn_, grid, dim3(256), 0, st, __VA_ARGS__);                    \
+    if (evs) hipExtLaunchKernelGGL(kfn_, grid, dim3(nt), 0, st, evs, eve, 0, __VA_ARGS__);  \
+    else hipLaunchKernelGGL(kfn_, grid, dim3(nt), 0, st, __VA_ARGS__);                     \
   } while (0)
+#define FT_PLAUNCH(kern, grid, evs, eve, ...) FT_PLAUNCH_NT(kern, grid, 256, evs, eve, __VA_ARGS__)
 
 // ev: null or 4 events (gate/up start, stop, down start, stop).
 // Workgroups of a persistent S1 kernel: the device's resident count, rounded down to a
@@ -1464,11 +1477,11 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     hipLaunchKernelGGL(k_zero, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a.y, n4);
     const int nb0 = a.I / 128, nb1 = (a.H + 255) / 256;
     if (a.L.fmt == FT_MXFP4) {
-      FT_PLAUNCH((k_xgemm<0, FT_MXFP4>), dim3(g8 * nb0), e0, e1, a, nb0);
-      FT_PLAUNCH((k_xgemm<1, FT_MXFP4>), dim3(g8 * nb1), e2, e3, a, nb1);
+      FT_PLAUNCH_NT((k_xgemm<0, FT_MXFP4>), dim3(g8 * nb0), kXThreads, e0, e1, a, nb0);
+      FT_PLAUNCH_NT((k_xgemm<1, FT_MXFP4>), dim3(g8 * nb1), kXThreads, e2, e3, a, nb1);
     } else {
-      FT_PLAUNCH((k_xgemm<0, FT_NVFP4>), dim3(g8 * nb0), e0, e1, a, nb0);
-      FT_PLAUNCH((k_xgemm<1, FT_NVFP4>), dim3(g8 * nb1), e2, e3, a, nb1);
+      FT_PLAUNCH_NT((k_xgemm<0, FT_NVFP4>), dim3(g8 * nb0), kXThreads, e0, e1, a, nb0);
+      FT_PLAUNCH_NT((k_xgemm<1, FT_NVFP4>), dim3(g8 * nb1), kXThreads, e2, e3, a, nb1);
     }
   }
   return (int)hipGetLastError();

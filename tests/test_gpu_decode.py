@@ -135,6 +135,19 @@ def test_dequant_nvfp4_bit_exact(ctx):
             assert _same(_dequant(L, slot, m), _expected(L, OL.expert(slot), m, "nvfp4"))
 
 
+def test_dequant_nvfp4_every_scale_code(ctx):
+    """Every E4M3 scale code, subnormals (0x01..0x07), negative codes and the NaN codes 0x7f
+    and 0xff included, under every E2M1 code pair: the kernels' scale decode is bit-exact."""
+    cfg = synth.small_config("nvallscales", seed=9, H=256, I=256, E=2, k=1, fmt=synth.NVFP4,
+                             nv_tensor_scale=1 / 64)
+    ex = synth.gen_expert(cfg, 0)
+    rows, nb = cfg.I, cfg.H // 2
+    ex.gate_codes = ((np.arange(rows)[:, None] * nb + np.arange(nb)[None, :]) % 256).astype(np.uint8)
+    ex.gate_scales = (np.arange(rows * cfg.H // 16) % 256).astype(np.uint8).reshape(rows, -1)
+    L = layer_for(ctx, "nvallscales", cfg=cfg, max_tokens=1, experts={0: ex})
+    assert _same(_dequant(L, 0, 0), _expected(L, ex, 0, "nvfp4"))
+
+
 # ---- A1: routing ------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8), ("cfg3", 1), ("cfg3", 16)])
