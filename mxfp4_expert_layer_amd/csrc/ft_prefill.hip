@@ -422,15 +422,17 @@ __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
 // A workgroup owns one block of up to 256 permuted rows of one expert and one feature block:
 //   MODE 0 (gate/up + SwiGLU): 128 features, i.e. 128 gate rows and the same 128 up rows;
 //   MODE 1 (down + combine):   256 rows of W_d (outputs).
-// Each of the four waves owns 64 weight rows as two 32-row operands (MODE 0: operand o holds
-// gate rows f .. f + 15 in lanes 0..15 and the up rows of the same features in lanes 16..31,
-// so one lane holds a feature's gate and up sums; MODE 1: two 16-row tiles of W_d) and all
-// 256 rows as eight 32-row token operands, on the 32x32x16 bf16 MFMA with fp32 accumulators.
-// The K axis runs in chunks of 64.  Per chunk, each wave copies global -> LDS (the direct
-// form of the vector load, which lands every lane's 16 bytes in lane order) its weight
-// operands' code slots and scale dwords, and two of the eight token operands for the four
-// 16-K steps, all in MFMA operand order, so the reads are one conflict-free 16-byte LDS read
-// per lane.  Three LDS stages keep two chunks of copies in flight while one is multiplied.
+// Eight waves, two per SIMD: wave w owns one 32-row weight operand (MODE 0: gate rows of 16
+// features in lanes 0..15 and the up rows of the same features in lanes 16..31, so one lane
+// holds a feature's gate and up sums; MODE 1: two 16-row tiles of W_d) and multiplies it by
+// all of the block's 32-row token operands on the 32x32x16 bf16 MFMA with fp32 accumulators.
+// Each weight is decoded once per block, and the second wave on a SIMD issues while the
+// first waits; the token operands are read from LDS by every wave (the LDS has the bandwidth).
+// The K axis runs in chunks of 64.  Per chunk the waves copy global -> LDS (buffer loads
+// that land every lane's 16 bytes in lane order) their weight operands' code slots and scale
+// dwords and four of the 32 token tiles (8 operands x 4 steps), all in MFMA operand order, so
+// the reads are one conflict-free 16-byte LDS read per lane.  Three LDS stages keep two
+// chunks of copies in flight while one is multiplied.
 // A weight lane (row r, K half h) reads the tile slot r % 16 + 16 (2 c + h) of chunk half c:
 // 32 K values, of which step ks takes values 8 ks .. 8 ks + 7; the token lane (row t, half h)
 // supplies the same K (64 chunk + 32 h + 8 ks + i), since a dot product needs both operands in
@@ -442,13 +444,16 @@ __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
 // per-pair output is stored.  Blocks (token block g, feature block fb) sit on XCD g % 8, so
 // the feature blocks of one token block share that XCD's L2 for the token rows.
 constexpr int kXRows = 256;
-constexpr int kXThreads = 256;
-constexpr int kXCopies = 12;   // copies per wave per chunk: 8 token, 2 code, 2 scale
+constexpr int kXWaves = 8;                    // waves per workgroup
+constexpr int kXThreads = 64 * kXWaves;
+constexpr int kXOps = 8 / kXWaves;            // 32-row weight operands per wave
+constexpr int kXTok = 32 / kXWaves;           // token tiles each wave copies per chunk
+constexpr int kXCopies = kXTok + 2 * kXOps;   // copies per wave per chunk (tokens, codes, scales)
 
 template <int MODE, int FMT>
 __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   // stage s: token operands [ks 4][j 8][64 lanes] (tk), then in wk the weight code slots
-  // [wave 4][o 2][64 lanes] followed by the weight scale dwords [wave 4][o 2][64 lanes] (one
+  // [operand 8][64 lanes] followed by the weight scale dwords [operand 8][64 lanes] (one
   // array per kind and stage: six copy targets, few enough for the compiler to keep apart)
   __shared__ uint4 tk0[2048], tk1[2048], tk2[2048];
   __shared__ uint4 wk0[640], wk1[640], wk2[640];
@@ -481,28 +486,33 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(blob + a.L.off[2 * m0 + 1]), (short)0, (int)(a.L.bytes - a.L.off[2 * m0 + 1]),
       kBufFlags);
-  uint32_t wvo[2], svo[2];
+  uint32_t wvo[kXOps], svo[kXOps];
 #pragma unroll
-  for (int o = 0; o < 2; ++o) {
+  for (int o = 0; o < kXOps; ++o) {
+    const int go = wave * kXOps + o;   // the workgroup's operand index, 0..7
     int m, rt;
-    if (MODE == 0) { m = r32 >> 4; rt = fb * 8 + 2 * wave + o; }
-    else { m = 2; rt = min(fb * 16 + 4 * wave + 2 * o + (r32 >> 4), nrt - 1); }
+    if (MODE == 0) { m = r32 >> 4; rt = fb * 8 + go; }
+    else { m = 2; rt = min(fb * 16 + 2 * go + (r32 >> 4), nrt - 1); }
     const int slot = (r32 & 15) + 16 * h;
     wvo[o] = (uint32_t)(a.L.off[2 * m] - a.L.off[2 * m0] + ((uint64_t)rt * KC * 64 + slot) * 16);
     const uint64_t sb = FMT == FT_MXFP4 ? (uint64_t)rt * KC * 64 + slot
                                         : (uint64_t)rt * KC * 128 + 2 * slot;
     svo[o] = (uint32_t)(a.L.off[2 * m + 1] - a.L.off[2 * m0 + 1] + (sb & ~(uint64_t)3));
   }
-  // this wave's token operands j = 2 wave, 2 wave + 1: row groups of the tiled operand (a
-  // group past the block re-reads the block's last group; its results are never used)
+  // this wave's token copies: tiles (step ks, operand j) with ks * 8 + j in
+  // [kXTok wave, kXTok (wave + 1)), each from a row group of the tiled operand (a group past
+  // the block re-reads the block's last group; its results are never used)
   const int prow0 = a.poff[e] + (gblk - a.tb_off[e]) * kXRows;   // padded row of the block
   const uint32_t gbytes = (uint32_t)(K / 64) * 4096;              // one row group's tiles
   const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint8_t*)(MODE == 0 ? a.xtb : a.htb) + (uint64_t)(prow0 >> 5) * gbytes),
       (short)0, (int)(nj * gbytes), kBufFlags);
-  uint32_t tvo[2];
+  uint32_t tvo[kXTok];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) tvo[q] = (uint32_t)min(2 * wave + q, nj - 1) * gbytes + 16 * lane;
+  for (int q = 0; q < kXTok; ++q) {
+    const int tile = kXTok * wave + q, ks = tile >> 3, j = tile & 7;
+    tvo[q] = (uint32_t)min(j, nj - 1) * gbytes + ks * 1024 + 16 * lane;
+  }
   if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
     const float tsd = blob_tscale(blob, 2);
     for (int i = tid; i < nrows; i += 256) {
@@ -524,19 +534,17 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       const uint32_t wo_ = (c_ >> 1) * 1024 + (c_ & 1) * 512;                                \
       const uint32_t so_ = FMT == FT_MXFP4 ? (c_ >> 1) * 64 + (c_ & 1) * 32                  \
                                            : (c_ >> 1) * 128 + (c_ & 1) * 64;                \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                     \
-        bdma16(wres, wvo[o_], wo_, &WK_[(wave * 2 + o_) * 64]);                              \
-        bdma4(sres, svo[o_], so_, (uint32_t*)&WK_[512] + (wave * 2 + o_) * 64);              \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                 \
+        bdma16(wres, wvo[o_], wo_, &WK_[(wave * kXOps + o_) * 64]);                          \
+        bdma4(sres, svo[o_], so_, (uint32_t*)&WK_[512] + (wave * kXOps + o_) * 64);          \
       }                                                                                      \
-      _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                    \
-        _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_)                                     \
-          bdma16(tres, tvo[q_], (uint32_t)(c_ * 4 + ks_) * 1024,                             \
-                 &TK_[(ks_ * 8 + 2 * wave + q_) * 64]);                                      \
+      _Pragma("unroll") for (int q_ = 0; q_ < kXTok; ++q_)                                   \
+        bdma16(tres, tvo[q_], (uint32_t)c_ * 4096, &TK_[(kXTok * wave + q_) * 64]);          \
     } while (0)
 
-    f32x16 acc[2][NJ];
+    f32x16 acc[kXOps][NJ];
 #pragma unroll
-    for (int o = 0; o < 2; ++o)
+    for (int o = 0; o < kXOps; ++o)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -546,20 +554,22 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
     // the token operands of step ks + 1 are read from LDS and its weights decoded.  Between
     // steps 2 and 3 every wave's reads of the chunk are done, so after a count wait and a
     // barrier that stage is refilled with the chunk three ahead; step 3's MFMAs then cover the
-    // reads and decode of the next chunk's first step.  Scheduling groups fix the interleave
-    // (1 MFMA, 1 LDS read, 1 MFMA, up to 4 VALU), which the compiler would otherwise undo.
-    uint4 cw[2], Bc[NJ], Bn[NJ], Ac[2], An[2];
-    float s0[2], s1[2];
+    // reads and decode of the next chunk's first step.  Scheduling groups fix the interleave,
+    // which the compiler would otherwise undo: the LDS reads go out one or two per MFMA in
+    // the first half of a step (so they land before the next step needs them), the decode
+    // VALU work between the MFMAs of the second half.
+    uint4 cw[kXOps], Bc[NJ], Bn[NJ], Ac[kXOps], An[kXOps];
+    float s0[kXOps], s1[kXOps];
 #define FT_X_READW(WK_, CW_, SW_)                                                           \
     do {                                                                                    \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
-        CW_[o_] = WK_[(wave * 2 + o_) * 64 + lane];                                         \
-        SW_[o_] = ((const uint32_t*)&WK_[512])[(wave * 2 + o_) * 64 + lane];               \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                \
+        CW_[o_] = WK_[(wave * kXOps + o_) * 64 + lane];                                     \
+        SW_[o_] = ((const uint32_t*)&WK_[512])[(wave * kXOps + o_) * 64 + lane];           \
       }                                                                                     \
     } while (0)
 #define FT_X_SCALES(SW_, S0_, S1_)                                                          \
     do {                                                                                    \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                \
         if (FMT == FT_MXFP4) {                                                              \
           S0_[o_] = S1_[o_] = e8m0_f32((SW_[o_] >> (8 * (lane & 3))) & 0xffu);              \
         } else {                                                                            \
@@ -571,7 +581,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
     } while (0)
 #define FT_X_DEC(KS_, CW_, S0_, S1_, A_)                                                    \
     do {                                                                                    \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_) {                                    \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                \
         const uint32_t w_ = (KS_) == 0 ? CW_[o_].x : (KS_) == 1 ? CW_[o_].y                 \
                           : (KS_) == 2 ? CW_[o_].z : CW_[o_].w;                             \
         A_[o_] = FMT == FT_MXFP4                                                            \
@@ -584,16 +594,16 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
     _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) B_[j_] = TK_[((KS_) * 8 + j_) * 64 + lane]
 #define FT_X_MMA()                                                                          \
     _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                       \
-      _Pragma("unroll") for (int o_ = 0; o_ < 2; ++o_)                                      \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_)                                  \
         acc[o_][j_] = MODE == 0 ? mfma_bf16_32(Ac[o_], Bc[j_], acc[o_][j_])                 \
                                 : mfma_bf16_32(Bc[j_], Ac[o_], acc[o_][j_])
 #define FT_X_SCHED(NR_, NV_)                                                                \
     do {                                                                                    \
-      _Pragma("unroll") for (int i_ = 0; i_ < NJ; ++i_) {                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < NJ * kXOps / 2; ++i_) {                       \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
-        __builtin_amdgcn_sched_group_barrier(0x100, (NR_), 0);                              \
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR_) * 2 / kXOps, 0);                  \
       }                                                                                     \
-      _Pragma("unroll") for (int i_ = 0; i_ < NJ; ++i_) {                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < NJ * kXOps / 2; ++i_) {                       \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
         __builtin_amdgcn_sched_group_barrier(0x002, 2 * (NV_), 0);                          \
       }                                                                                     \
@@ -602,8 +612,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
 #define FT_X_NEXT()                                                                         \
     do {                                                                                    \
       _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) Bc[j_] = Bn[j_];                    \
-      Ac[0] = An[0];                                                                        \
-      Ac[1] = An[1];                                                                        \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) Ac[o_] = An[o_];                 \
     } while (0)
     // one chunk, read from stage (TK_, WK_); (TKN_, WKN_) holds the next chunk.  A wave reads
     // only its own weight slots, so it may read the next chunk's weights (in step 2) after
@@ -618,9 +627,9 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       /* this wave's copies of the next chunk have landed: its weights can be read */       \
       __builtin_amdgcn_s_waitcnt(FT_VMCNT(kXCopies));                                       \
       asm volatile("" ::: "memory");                                                        \
-      uint4 cwn_[2];                                                                        \
-      uint32_t swn_[2];                                                                     \
-      float s0n_[2], s1n_[2];                                                               \
+      uint4 cwn_[kXOps];                                                                    \
+      uint32_t swn_[kXOps];                                                                 \
+      float s0n_[kXOps], s1n_[kXOps];                                                       \
       FT_X_READB(TK_, 2, Bn);                                                               \
       FT_X_READW(WKN_, cwn_, swn_);                                                         \
       FT_X_DEC(2, cw, s0, s1, An);                                                          \
@@ -646,9 +655,9 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       FT_X_MMA();                                                                           \
       FT_X_SCHED(1, 4);                                                                     \
       FT_X_NEXT();                                                                          \
-      cw[0] = cwn_[0]; cw[1] = cwn_[1];                                                     \
-      s0[0] = s0n_[0]; s0[1] = s0n_[1];                                                     \
-      s1[0] = s1n_[0]; s1[1] = s1n_[1];                                                     \
+      _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                \
+        cw[o_] = cwn_[o_]; s0[o_] = s0n_[o_]; s1[o_] = s1n_[o_];                            \
+      }                                                                                     \
     } while (0)
 
     FT_X_ISSUE(0, tk0, wk0);
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
     asm volatile("" ::: "memory");
     FT_X_ISSUE(2, tk2, wk2);
     {
-      uint32_t sw0[2];
+      uint32_t sw0[kXOps];
       FT_X_READW(wk0, cw, sw0);
       FT_X_SCALES(sw0, s0, s1);
     }
@@ -702,10 +711,10 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
         if (tl < nrows) {
           const int prow = prow0 + tl, g = prow >> 5, t = prow & 31;
 #pragma unroll
-          for (int o = 0; o < 2; ++o) {
+          for (int o = 0; o < kXOps; ++o) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-              const int f = fb * 128 + wave * 32 + 16 * o + 8 * q + 4 * h;
+              const int f = fb * 128 + (wave * kXOps + o) * 16 + 8 * q + 4 * h;
               uint16_t hv[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r)
@@ -725,8 +734,8 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       // lane (r32, h) holds output fb * 256 + 64 wave + 32 o + r32 of token rows
       // 32 j + 8 (r / 4) + 4 h + r % 4 in register r
 #pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        const int out = fb * 256 + wave * 64 + 32 * o + r32;
+      for (int o = 0; o < kXOps; ++o) {
+        const int out = fb * 256 + (wave * kXOps + o) * 32 + r32;
         if (out < a.H) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
