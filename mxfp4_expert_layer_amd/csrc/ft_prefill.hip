@@ -731,7 +731,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
         }
       }
     } else {
-      // lane (r32, h) holds output fb * 256 + 64 wave + 32 o + r32 of token rows
+      // lane (r32, h) holds output fb * 256 + 32 (wave kXOps + o) + r32 of token rows
       // 32 j + 8 (r / 4) + 4 h + r % 4 in register r
 #pragma unroll
       for (int o = 0; o < kXOps; ++o) {
