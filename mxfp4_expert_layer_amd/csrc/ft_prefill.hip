@@ -443,19 +443,20 @@ __device__ __forceinline__ float blob_tscale(const uint8_t* blob, int m) {
 // is then a coalesced fp32 atomic add of w x ts_d x y into y[token] (y zeroed first), and no
 // per-pair output is stored.  Blocks (token block g, feature block fb) sit on XCD g % 8, so
 // the feature blocks of one token block share that XCD's L2 for the token rows.
-constexpr int kXRows = 256;
+constexpr int kXRows = kGemmM;                // token rows per block
+constexpr int kXJ = kXRows / 32;              // 32-row token operands per block
 constexpr int kXWaves = 8;                    // waves per workgroup
 constexpr int kXThreads = 64 * kXWaves;
 constexpr int kXOps = 8 / kXWaves;            // 32-row weight operands per wave
-constexpr int kXTok = 32 / kXWaves;           // token tiles each wave copies per chunk
+constexpr int kXTok = 4 * kXJ / kXWaves;      // token tiles each wave copies per chunk
 constexpr int kXCopies = kXTok + 2 * kXOps;   // copies per wave per chunk (tokens, codes, scales)
 
 template <int MODE, int FMT>
 __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
-  // stage s: token operands [ks 4][j 8][64 lanes] (tk), then in wk the weight code slots
+  // stage s: token operands [ks 4][j kXJ][64 lanes] (tk), then in wk the weight code slots
   // [operand 8][64 lanes] followed by the weight scale dwords [operand 8][64 lanes] (one
   // array per kind and stage: six copy targets, few enough for the compiler to keep apart)
-  __shared__ uint4 tk0[2048], tk1[2048], tk2[2048];
+  __shared__ uint4 tk0[4 * kXJ * 64], tk1[4 * kXJ * 64], tk2[4 * kXJ * 64];
   __shared__ uint4 wk0[640], wk1[640], wk2[640];
   __shared__ int s_tok[kXRows];
   __shared__ float s_w[kXRows];
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
                                         : (uint64_t)rt * KC * 128 + 2 * slot;
     svo[o] = (uint32_t)(a.L.off[2 * m + 1] - a.L.off[2 * m0 + 1] + (sb & ~(uint64_t)3));
   }
-  // this wave's token copies: tiles (step ks, operand j) with ks * 8 + j in
+  // this wave's token copies: tiles (step ks, operand j) with ks * kXJ + j in
   // [kXTok wave, kXTok (wave + 1)), each from a row group of the tiled operand (a group past
   // the block re-reads the block's last group; its results are never used)
   const int prow0 = a.poff[e] + (gblk - a.tb_off[e]) * kXRows;   // padded row of the block
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   uint32_t tvo[kXTok];
 #pragma unroll
   for (int q = 0; q < kXTok; ++q) {
-    const int tile = kXTok * wave + q, ks = tile >> 3, j = tile & 7;
+    const int tile = kXTok * wave + q, ks = tile / kXJ, j = tile % kXJ;
     tvo[q] = (uint32_t)min(j, nj - 1) * gbytes + ks * 1024 + 16 * lane;
   }
   if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       }                                                                                     \
     } while (0)
 #define FT_X_READB(TK_, KS_, B_)                                                            \
-    _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) B_[j_] = TK_[((KS_) * 8 + j_) * 64 + lane]
+    _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) B_[j_] = TK_[((KS_) * kXJ + j_) * 64 + lane]
 #define FT_X_MMA()                                                                          \
     _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_)                                       \
       _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_)                                  \
@@ -754,9 +755,16 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   case N:                                                                                  \
     block(std::integral_constant<int, N>{});                                               \
     break
-  switch (nj) {
-    FT_X_BLOCK(1); FT_X_BLOCK(2); FT_X_BLOCK(3); FT_X_BLOCK(4);
-    FT_X_BLOCK(5); FT_X_BLOCK(6); FT_X_BLOCK(7); default: FT_X_BLOCK(8);
+  if constexpr (kXJ == 8) {
+    switch (nj) {
+      FT_X_BLOCK(1); FT_X_BLOCK(2); FT_X_BLOCK(3); FT_X_BLOCK(4);
+      FT_X_BLOCK(5); FT_X_BLOCK(6); FT_X_BLOCK(7); default: FT_X_BLOCK(8);
+    }
+  } else {
+    static_assert(kXJ == 4, "blocks of 128 or 256 rows");
+    switch (nj) {
+      FT_X_BLOCK(1); FT_X_BLOCK(2); FT_X_BLOCK(3); default: FT_X_BLOCK(4);
+    }
   }
 #undef FT_X_BLOCK
 }

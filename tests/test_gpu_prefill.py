@@ -126,6 +126,8 @@ SMALL = [
     ("pf_mx_a", synth.MXFP4, 768, 512, 20, 4, 513),
     ("pf_nv_one", synth.NVFP4, 256, 128, 6, 2, 1),
     ("pf_mx_wide", synth.MXFP4, 256, 128, 300, 8, 200),   # E > 256: two router expert groups
+    # about 370 rows per expert: every expert spans two 256-row blocks, the second partial
+    ("pf_nv_deep", synth.NVFP4, 256, 128, 6, 2, 1100),
 ]
 
 
@@ -142,6 +144,8 @@ def test_prefill_matches_oracle(ctx, name, fmt, H, I, E, k, T):
     ref = moe.moe_forward(OL, x)
     ties = check_routing(idx, w, ref)
     _check_perm(idx, counts, offsets, pos, E)
+    if name == "pf_nv_deep":
+        assert int(np.asarray(counts).min()) > 256, counts   # every expert has a second block
     if ties:
         ref = moe.moe_forward(OL, x, idx=idx)
     check_output(y, ref["y"], name)
