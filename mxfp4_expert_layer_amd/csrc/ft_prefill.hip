@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
   }
   if (MODE == 1) {   // visible to the epilogue through the main loop's barriers
     const float tsd = blob_tscale(blob, 2);
-    for (int i = tid; i < nrows; i += 256) {
+    for (int i = tid; i < nrows; i += kXThreads) {
       s_tok[i] = a.perm_tok[row0 + i];
       s_w[i] = a.perm_w[row0 + i] * tsd;
     }
