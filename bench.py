@@ -46,12 +46,12 @@ METRIC = "MoE-layer decode tok/s + HBM GB/s % peak; prefill tok/s + FP4 MFMA %"
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
-    "decode-35b-a3b": dict(cfg="cfg2", T=1, copies=8, steps=2048, warmup=128),
-    "decode-35b-a3b-nvfp4": dict(cfg="cfg2nv", T=1, copies=8, steps=2048, warmup=128),
-    "decode-284b": dict(cfg="cfg3", T=1, copies=4, steps=2048, warmup=128),
-    "miss-path-284b": dict(cfg="cfg4", T=1, copies=1, steps=64, warmup=64),
-    "prefill-753b": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3),
-    "prefill-753b-mxfp4": dict(cfg="cfg5", T=4096, copies=1, steps=20, warmup=3, mode="mxfp4"),
+    "decode-35b-a3b": dict(cfg="35b-a3b", T=1, copies=8, steps=2048, warmup=128),
+    "decode-35b-a3b-nvfp4": dict(cfg="35b-a3b-nvfp4", T=1, copies=8, steps=2048, warmup=128),
+    "decode-284b": dict(cfg="284b", T=1, copies=4, steps=2048, warmup=128),
+    "miss-path-284b": dict(cfg="284b-miss-path", T=1, copies=1, steps=64, warmup=64),
+    "prefill-753b": dict(cfg="753b", T=4096, copies=1, steps=20, warmup=3),
+    "prefill-753b-mxfp4": dict(cfg="753b", T=4096, copies=1, steps=20, warmup=3, mode="mxfp4"),
 }
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
@@ -677,7 +677,7 @@ def bench_headline(args):
     ref = read_reference(ctx, r1["roofline"]["achieved"])
     r1["roofline"].update(ref)
     Ts = (1, 4, 16)
-    dec = decode_sweep(ctx, "cfg3", Ts, copies=4)
+    dec = decode_sweep(ctx, "284b", Ts, copies=4)
     for v in dec.values():
         v["gateup_frac_of_measured_read"] = v["gateup_GBps"] / ref["measured_read_GBps"]
     res = {

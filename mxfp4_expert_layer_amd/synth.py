@@ -66,28 +66,32 @@ class LayerConfig:
 # The five workloads (sizes from the pages' model classes; distributions are this build's
 # synthetic stand-ins).  E8M0 exponent e maps to code e + 127.
 CONFIGS = {
-    "cfg1": LayerConfig("tiny-decode", 1001, H=256, I=128, E=8, k=2, n_shared=0, fmt=MXFP4,
-                        n_slots=8, router_sigma=0.02, code_dist="uniform",
-                        scale_lo=127 - 8, scale_hi=127 - 4, batches=(4,)),
-    "cfg2": LayerConfig("35b-a3b-decode", 1002, H=2048, I=512, E=256, k=8, n_shared=0, fmt=MXFP4,
-                        n_slots=256, router_sigma=1.0 / math.sqrt(2048),
-                        scale_lo=127 - 7, scale_hi=127 - 3, batches=(1, 8)),
-    "cfg3": LayerConfig("284b-decode", 1003, H=4096, I=2048, E=256, k=6, n_shared=1, fmt=MXFP4,
-                        n_slots=256, router_sigma=1.0 / math.sqrt(4096), zipf_c=1.1,
-                        scale_lo=127 - 8, scale_hi=127 - 3, batches=(1, 4, 16)),
-    "cfg4": LayerConfig("284b-miss-path", 1004, H=4096, I=2048, E=256, k=6, n_shared=1, fmt=MXFP4,
-                        n_slots=48, router_sigma=1.0 / math.sqrt(4096), zipf_c=1.1,
-                        scale_lo=127 - 8, scale_hi=127 - 3, batches=(1,)),
+    "tiny": LayerConfig(
+        "tiny-decode", 1001, H=256, I=128, E=8, k=2, n_shared=0, fmt=MXFP4, n_slots=8,
+        router_sigma=0.02, code_dist="uniform", scale_lo=127 - 8, scale_hi=127 - 4,
+        batches=(4,)),
+    "35b-a3b": LayerConfig(
+        "35b-a3b-decode", 1002, H=2048, I=512, E=256, k=8, n_shared=0, fmt=MXFP4, n_slots=256,
+        router_sigma=1.0 / math.sqrt(2048), scale_lo=127 - 7, scale_hi=127 - 3,
+        batches=(1, 8)),
+    "284b": LayerConfig(
+        "284b-decode", 1003, H=4096, I=2048, E=256, k=6, n_shared=1, fmt=MXFP4, n_slots=256,
+        router_sigma=1.0 / math.sqrt(4096), zipf_c=1.1, scale_lo=127 - 8, scale_hi=127 - 3,
+        batches=(1, 4, 16)),
+    "284b-miss-path": LayerConfig(
+        "284b-miss-path", 1004, H=4096, I=2048, E=256, k=6, n_shared=1, fmt=MXFP4, n_slots=48,
+        router_sigma=1.0 / math.sqrt(4096), zipf_c=1.1, scale_lo=127 - 8, scale_hi=127 - 3,
+        batches=(1,)),
     # NVFP4 scales: the 49 E4M3 codes 0x08..0x38 (values 2^-6 .. 2^0), tensor scale 1/64.
     # The 35B-A3B class with NVFP4 experts (the format of the pages' laptop decode result).
-    "cfg2nv": LayerConfig("35b-a3b-decode-nvfp4", 1006, H=2048, I=512, E=256, k=8, n_shared=0,
-                          fmt=NVFP4, n_slots=256, router_sigma=1.0 / math.sqrt(2048),
-                          scale_lo=0x08, scale_hi=0x38, nv_tensor_scale=1.0 / 64.0,
-                          batches=(1, 8)),
-    "cfg5": LayerConfig("753b-prefill", 1005, H=6144, I=2048, E=160, k=8, n_shared=0, fmt=NVFP4,
-                        n_slots=160, router_sigma=0.5 / math.sqrt(6144),
-                        scale_lo=0x08, scale_hi=0x38, nv_tensor_scale=1.0 / 64.0,
-                        batches=(4096,)),
+    "35b-a3b-nvfp4": LayerConfig(
+        "35b-a3b-decode-nvfp4", 1006, H=2048, I=512, E=256, k=8, n_shared=0, fmt=NVFP4,
+        n_slots=256, router_sigma=1.0 / math.sqrt(2048), scale_lo=0x08, scale_hi=0x38,
+        nv_tensor_scale=1.0 / 64.0, batches=(1, 8)),
+    "753b": LayerConfig(
+        "753b-prefill", 1005, H=6144, I=2048, E=160, k=8, n_shared=0, fmt=NVFP4, n_slots=160,
+        router_sigma=0.5 / math.sqrt(6144), scale_lo=0x08, scale_hi=0x38,
+        nv_tensor_scale=1.0 / 64.0, batches=(4096,)),
 }
 
 

@@ -84,7 +84,7 @@ def _same(a, b):
 
 
 def test_dequant_bit_exact_tiny_workload(ctx):
-    L = layer_for(ctx, "cfg1", max_tokens=16)
+    L = layer_for(ctx, "tiny", max_tokens=16)
     OL = L.oracle_layer()
     for slot in range(L.cfg.E):
         for m in range(3):
@@ -150,7 +150,8 @@ def test_dequant_nvfp4_every_scale_code(ctx):
 
 # ---- A1: routing ------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8), ("cfg3", 1), ("cfg3", 16)])
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("35b-a3b", 1), ("35b-a3b", 8), ("284b", 1),
+                                    ("284b", 16)])
 def test_route_matches_oracle(ctx, name, T):
     L = layer_for(ctx, name, max_tokens=16)
     OL = L.oracle_layer()
@@ -195,9 +196,9 @@ def _decode_and_check(ctx, L, T, batch):
     return check_output(y, ref["y"], f"{L.cfg.name} T={T}")
 
 
-@pytest.mark.parametrize("name,T", [("cfg1", 4), ("cfg2", 1), ("cfg2", 8),
-                                    ("cfg3", 1), ("cfg3", 4), ("cfg3", 16),
-                                    ("cfg2nv", 1), ("cfg2nv", 8)])
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("35b-a3b", 1), ("35b-a3b", 8),
+                                    ("284b", 1), ("284b", 4), ("284b", 16),
+                                    ("35b-a3b-nvfp4", 1), ("35b-a3b-nvfp4", 8)])
 def test_decode_matches_oracle(ctx, name, T):
     L = layer_for(ctx, name, max_tokens=16)
     err = _decode_and_check(ctx, L, T, batch=100 + T)
@@ -228,7 +229,7 @@ def test_decode_nvfp4_shapes(ctx, H, I, E, k, ns, T, ts):
 
 
 def test_decode_is_deterministic(ctx):
-    L = layer_for(ctx, "cfg2", max_tokens=16)
+    L = layer_for(ctx, "35b-a3b", max_tokens=16)
     x = synth.gen_tokens(L.cfg, 8, batch=3)
     a = run_decode(ctx, L, x)
     b = run_decode(ctx, L, x)
@@ -236,7 +237,7 @@ def test_decode_is_deterministic(ctx):
 
 
 def test_decode_rejects_bad_token_count(ctx):
-    L = layer_for(ctx, "cfg1_T4", cfg=synth.CONFIGS["cfg1"], max_tokens=4)
+    L = layer_for(ctx, "tiny_T4", cfg=synth.CONFIGS["tiny"], max_tokens=4)
     x = synth.gen_tokens(L.cfg, 5)
     with pytest.raises(ft.FtError) as e:
         run_decode(ctx, L, x)
@@ -447,9 +448,9 @@ def test_context_binds_host_threads_to_the_gpu_node(ctx):
 def test_miss_path_284b_layer(ctx):
     """The 284B-class layer with a 48-slot pool: 64 warm-up and 64 timed single tokens with the
     slot tables checked after every step and the outputs every 8th step."""
-    L = layer_for(ctx, "cfg4", resident=False, n_slots=48, max_tokens=1)
+    L = layer_for(ctx, "284b-miss-path", resident=False, n_slots=48, max_tokens=1)
     rate = _miss_sequence(ctx, L, steps=128, bp=50e9, bh=120e9, check_every=16, T=1)
-    log(f"[gpu] cfg4 hit rate over 128 steps: {rate:.3f}")
+    log(f"[gpu] 284b-miss-path hit rate over 128 steps: {rate:.3f}")
 
 
 def _bf16_rne_bits(f32):

@@ -201,7 +201,7 @@ def test_prefill_rejects_bad_calls(ctx):
         bare.close()
 
 
-def cfg5_sample(idx, E, n=256, seed=0):
+def expert_cover_sample(idx, E, n=256, seed=0):
     """A seeded sample of n tokens that routes to every expert: for each expert the last token
     routed to it (its row is the last row of the expert's last row block, in every block size
     the grouped GEMMs use), then first tokens of experts, then random tokens."""
@@ -229,8 +229,8 @@ def test_prefill_753b_layer(ctx):
     """The 753B-class NVFP4 layer at T = 4096: routing and the full permutation checked
     exactly; outputs checked on a seeded sample of 256 tokens that routes to all 160 experts,
     including each expert's last row (the oracle evaluates those tokens only)."""
-    cfg = synth.CONFIGS["cfg5"]
-    L = layer_for(ctx, "cfg5", cfg, threads=16)
+    cfg = synth.CONFIGS["753b"]
+    L = layer_for(ctx, "753b", cfg, threads=16)
     T = 4096
     x = synth.gen_tokens(cfg, T, batch=0)
     log("[gpu] prefill 753b-class T=4096")
@@ -242,7 +242,7 @@ def test_prefill_753b_layer(ctx):
     check_routing(idx, w, dict(idx=r_idx, w=r_w, logits=logits, gap=gap))
     _check_perm(idx, counts, offsets, pos, cfg.E)
     assert counts.sum() == T * cfg.k and np.all(counts > 0)
-    sample = cfg5_sample(idx, cfg.E)
+    sample = expert_cover_sample(idx, cfg.E)
     log(f"[gpu] oracle on {len(sample)} sampled tokens ({len(np.unique(idx[sample]))} experts)")
     ref = moe.moe_forward(OL, x[sample], idx=idx[sample], threads=16)
     check_output(y[sample], ref["y"], "753b-class sampled tokens")
@@ -350,8 +350,8 @@ def test_prefill_mxfp4_753b_layer(ctx):
     pass use the same values."""
     import threading
 
-    cfg = synth.CONFIGS["cfg5"]
-    L = layer_for(ctx, "cfg5", cfg, threads=16)
+    cfg = synth.CONFIGS["753b"]
+    L = layer_for(ctx, "753b", cfg, threads=16)
     T = 4096
     x = synth.gen_tokens(cfg, T, batch=1)
     log("[gpu] prefill mxfp4 753b-class T=4096")
@@ -365,7 +365,7 @@ def test_prefill_mxfp4_753b_layer(ctx):
     xc, xs = prefill_quant(L, ws, T, 0)
     check_mx_quant(xc, xs, xr, "tokens", exact=True)
     hc, hs = prefill_quant(L, ws, T, 1)
-    sample = cfg5_sample(idx, cfg.E, seed=1)
+    sample = expert_cover_sample(idx, cfg.E, seed=1)
     xq = mxq.quantize_dequant(xr[sample])
     # the GPU's MXFP4 blobs of all experts, read before the oracle's worker threads start
     blobs = {e: prefill_weights(L, e) for e in range(cfg.E)}

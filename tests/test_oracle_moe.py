@@ -72,7 +72,7 @@ def test_dense_masked_equality_tiny(seed):
 
 
 def test_dense_masked_equality_tiny_workload():
-    L = synth.gen_layer(synth.CONFIGS["cfg1"], threads=1)
+    L = synth.gen_layer(synth.CONFIGS["tiny"], threads=1)
     x = synth.gen_tokens(L.cfg, 4)
     ys = moe.moe_forward(L, x)["y"]
     yd = moe.dense_masked_forward(L, x)
