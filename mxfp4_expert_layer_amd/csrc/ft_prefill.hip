@@ -1057,33 +1057,40 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
     ptile0_ = (a.poff[e_] >> 4) + ((gblk_) - a.tb_off[e_]) * (kS1Rows / 16);              \
     wvalid_ = MODE == 0 || (fb_) * 16 + wm * 8 < nrt;                                     \
   } while (0)
-  // this wave's copy sources: weight tiles wave + 4i and the scale dwords of tiles
-  // 4 wave .. + 3; token tiles wave + 4i and the scale dwords of rows 64 wave .. + 63 (rows
-  // past the block re-read its last row; MODE 1 row tiles past the matrix are clamped, their
-  // results never stored)
-#define FT_S1_SOURCES(e_, fb_, ntile16_, ptile0_)                                            \
+  // this wave's copy sources, as buffer resources (base and extent) with scalar offsets per
+  // copy, the chunk's offset added to them at issue: weight tiles wave + 4i of the expert's
+  // blob and the scale dwords of tiles 4 wave .. + 3 (a lane offset); token tiles wave + 4i
+  // and the scale dwords of rows 64 wave .. + 63 from resources spanning exactly the block's
+  // tiles (rows past the block re-read its last row; MODE 1 row tiles past the matrix are
+  // clamped, their results never stored).  Only the lane offsets (16 lane and the two scale
+  // offsets) sit in vector registers.
+#define FT_S1_SOURCES(e_, fb_, ntile16_, ptile0_)                                         \
   do {                                                                                    \
-    const uint8_t* blob_ = a.mxpool + (uint64_t)(e_) * a.mxstride;                        \
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)(a.mxpool + (uint64_t)(e_) * a.mxstride), \
+                                             (short)0, (int)a.ML.bytes, kBufFlags);       \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                    \
       const int q_ = wave + 4 * i_;                                                       \
       const int m_ = MODE == 0 ? (q_ < 8 ? 0 : 1) : 2;                                    \
       const int rt_ = min(MODE == 0 ? (fb_) * 8 + (q_ & 7) : (fb_) * 16 + q_, nrt - 1);   \
-      wsrc[i_] = blob_ + a.ML.off[2 * m_] + (uint64_t)rt_ * KC * kTileCodeBytes + lane * 16; \
+      wso[i_] = __builtin_amdgcn_readfirstlane(                                           \
+          (uint32_t)(a.ML.off[2 * m_] + (uint64_t)rt_ * KC * kTileCodeBytes));            \
     }                                                                                     \
     {                                                                                     \
       const int q_ = 4 * wave + (lane >> 4);                                              \
       const int m_ = MODE == 0 ? (q_ < 8 ? 0 : 1) : 2;                                    \
       const int rt_ = min(MODE == 0 ? (fb_) * 8 + (q_ & 7) : (fb_) * 16 + q_, nrt - 1);   \
-      wssrc = blob_ + a.ML.off[2 * m_ + 1] + (uint64_t)rt_ * KC * 64 + 4 * (lane & 15);   \
+      wsv = (uint32_t)(a.ML.off[2 * m_ + 1] + (uint64_t)rt_ * KC * 64) + 4 * (lane & 15); \
     }                                                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                    \
-      const uint64_t pt_ = (uint64_t)((ptile0_) + min(wave + 4 * i_, (ntile16_) - 1));    \
-      tsrc[i_] = tcodes + pt_ * KC * kTileCodeBytes + lane * 16;                          \
-    }                                                                                     \
-    {                                                                                     \
-      const uint64_t pt_ = (uint64_t)((ptile0_) + min(4 * wave + (lane >> 4), (ntile16_) - 1)); \
-      tssrc = tscales + pt_ * KC * 64 + 4 * (lane & 15);                                  \
-    }                                                                                     \
+    const uint64_t tb_ = (uint64_t)(ptile0_) * KC;                                        \
+    tres = __builtin_amdgcn_make_buffer_rsrc((void*)(tcodes + tb_ * kTileCodeBytes),      \
+                                             (short)0, (ntile16_) * KC * kTileCodeBytes,  \
+                                             kBufFlags);                                  \
+    tsres = __builtin_amdgcn_make_buffer_rsrc((void*)(tscales + tb_ * 64), (short)0,      \
+                                              (ntile16_) * KC * 64, kBufFlags);           \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
+      tso[i_] = __builtin_amdgcn_readfirstlane(                                           \
+          (uint32_t)(min(wave + 4 * i_, (ntile16_) - 1) * KC * kTileCodeBytes));          \
+    tsv = (uint32_t)(min(4 * wave + (lane >> 4), (ntile16_) - 1) * KC * 64) + 4 * (lane & 15); \
   } while (0)
 
   int Lb = blockIdx.x, gblk, fb;
@@ -1092,10 +1099,9 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   int e, row0, nrows, nj, ntile16, ptile0;
   bool wvalid;
   FT_S1_SCALARS(gblk, fb, e, row0, nrows, nj, ntile16, ptile0, wvalid);
-  const uint8_t* wsrc[4];
-  const uint8_t* wssrc;
-  const uint8_t* tsrc[4];
-  const uint8_t* tssrc;
+  __amdgpu_buffer_rsrc_t wres, tres, tsres;
+  uint32_t wso[4], tso[4], wsv, tsv;
+  const uint32_t lo16 = 16 * lane;
   FT_S1_SOURCES(e, fb, ntile16, ptile0);
 
   f32x16 acc[4][4];
@@ -1112,13 +1118,15 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
 
 #define FT_S1_ISSUE(kc_, WC_, TC_, WS_, TS_)                                              \
   do {                                                                                    \
-    const uint64_t c_ = (uint64_t)((kc_) < KC ? (kc_) : (nxt ? (kc_) - KC : KC - 1));    \
+    const uint32_t c_ = (uint32_t)((kc_) < KC ? (kc_) : (nxt ? (kc_) - KC : KC - 1));     \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
-      dma16(wsrc[i_] + c_ * kTileCodeBytes, &WC_[(wave + 4 * i_) * 64]);                  \
-    dma4(wssrc + c_ * 64, &WS_[64 * wave]);                                               \
+      bdma16(wres, lo16, __builtin_amdgcn_readfirstlane(wso[i_] + c_ * kTileCodeBytes),   \
+             &WC_[(wave + 4 * i_) * 64]);                                                 \
+    bdma4(wres, wsv, c_ * 64, &WS_[64 * wave]);                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
-      dma16(tsrc[i_] + c_ * kTileCodeBytes, &TC_[(wave + 4 * i_) * 64]);                  \
-    dma4(tssrc + c_ * 64, &TS_[64 * wave]);                                               \
+      bdma16(tres, lo16, __builtin_amdgcn_readfirstlane(tso[i_] + c_ * kTileCodeBytes),   \
+             &TC_[(wave + 4 * i_) * 64]);                                                 \
+    bdma4(tsres, tsv, c_ * 64, &TS_[64 * wave]);                                          \
   } while (0)
 
   // Operands are double-buffered in registers: step kc reads chunk kc's operands from its
@@ -1214,18 +1222,26 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
         if (nxt)
           FT_S1_SCALARS(n_gblk, n_fb, n_e, n_row0, n_nrows, n_nj, n_ntile16, n_ptile0, n_wvalid);
       }
-      // each phase stays where it is written (scheduling barriers): copies go out first, the
-      // next chunk's operands are read into the other register set, then this chunk's MFMAs
-      // run without waiting on those reads
+      // after the barrier the matrix core starts at once: the first 16 of this chunk's 32
+      // MFMAs each carry one of the wave's copies (the first kS1Copies) and two of its LDS
+      // reads of the next chunk's operands into the other register set (scheduling groups),
+      // so the copy and read issue hides behind the MFMAs instead of preceding them
 #define FT_S1_FAST_STEP(kcn_, WCN_, TCN_, WSN_, TSN_, WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_, \
                         CA_, CB_, CSA_, CSB_)                                               \
       do {                                                                                \
         FT_S1_SYNC();                                                                     \
         FT_S1_ISSUE(kcn_, WCN_, TCN_, WSN_, TSN_);                                        \
-        __builtin_amdgcn_sched_barrier(0);                                                \
         FT_S1_READ(WC_, TC_, WS_, TS_, RA_, RB_, RSA_, RSB_);                             \
-        __builtin_amdgcn_sched_barrier(0);                                                \
         FT_S1_MFMA(CA_, CB_, CSA_, CSB_);                                                 \
+        _Pragma("unroll") for (int g_ = 0; g_ < kS1Copies; ++g_) {                        \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
+        }                                                                                 \
+        _Pragma("unroll") for (int g_ = 0; g_ < 16 - kS1Copies; ++g_) {                   \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                              \
+        }                                                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                \
       } while (0)
       for (int kc = 1; kc <= KC; kc += kS1Stages) {
