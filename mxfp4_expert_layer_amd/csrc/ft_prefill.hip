@@ -769,6 +769,16 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
 #undef FT_X_BLOCK
 }
 
+// Nontemporal stores (the nt bit), for large outputs that the caches cannot keep until their
+// reader, a later kernel, runs: the lines are not retained on the way to memory.  Used where
+// each store instruction fills whole 128-byte lines; Y_perm's stores (24 bytes per row per
+// instruction) ran three times slower with it.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
+}
+
 // Exact mode: the permuted x rows into the gate/up GEMM's token tiles (xtb).  One workgroup
 // per 32-row group of padded permuted rows (its expert from the group map k_perm_scan wrote)
 // and 8 chunks of 64 K: thread (t, p) reads 16 bytes, K 64 c + 8 p .. + 7 of the group's row t
@@ -796,7 +806,7 @@ __global__ __launch_bounds__(256) void k_tile_x(PrefillLaunch a) {
     const int c = c0 + u;
     if (c < NC) {
       const uint64_t slot = (((uint64_t)g * NC + c) * 4 + (p & 3)) * 64 + t + 32 * (p >> 2);
-      *(uint4*)(a.xtb + slot * 8) = valid ? v[u] : make_uint4(0u, 0u, 0u, 0u);
+      st_nt(a.xtb + slot * 8, valid ? v[u] : make_uint4(0u, 0u, 0u, 0u));
     }
   }
 }
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(256) void k_tile_x(PrefillLaunch a) {
 // can be captured into a graph).
 __global__ __launch_bounds__(256) void k_zero(float* __restrict__ y, uint64_t n4) {
   const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) ((float4*)y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < n4) st_nt((uint4*)y + i, make_uint4(0u, 0u, 0u, 0u));
 }
 
 // ---- scaled-FP4 mode (both MFMA operands FP4) ------------------------------------------------
@@ -905,7 +915,7 @@ __global__ __launch_bounds__(256) void k_tile_xq(PrefillLaunch a) {
       const int kc = kc0 + 4 * u;
       if (kc < KC) {
         const uint64_t tile = (uint64_t)trow * KC + kc;
-        *(uint4*)(a.xt + tile * 1024 + l * 16) = valid ? c[u] : make_uint4(0u, 0u, 0u, 0u);
+        st_nt(a.xt + tile * 1024 + l * 16, valid ? c[u] : make_uint4(0u, 0u, 0u, 0u));
         a.xts[tile * 64 + l] = valid ? sc[u] : (uint8_t)0;
       }
     }
@@ -1389,8 +1399,14 @@ __global__ __launch_bounds__(256) void k_unpermute(PrefillLaunch a) {
     const int jc = min(j, a.k - 1);
     const int p = a.pos[(uint64_t)t * a.k + jc];
     wj[j] = a.w[(uint64_t)t * a.k + jc];
-    if (F24) v[j] = unpack_f24x4(*(const uint3*)((const uint8_t*)a.Yperm + ((uint64_t)p * a.H + h) * 3));
-    else v[j] = *(const float4*)(a.Yperm + (uint64_t)p * a.H + h);
+    if (F24) {
+      // read once: nontemporal loads
+      const u32x3 q = __builtin_nontemporal_load(
+          (const u32x3*)((const uint8_t*)a.Yperm + ((uint64_t)p * a.H + h) * 3));
+      v[j] = unpack_f24x4(make_uint3(q.x, q.y, q.z));
+    } else {
+      v[j] = *(const float4*)(a.Yperm + (uint64_t)p * a.H + h);
+    }
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll

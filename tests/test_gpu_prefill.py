@@ -128,6 +128,8 @@ SMALL = [
     ("pf_mx_wide", synth.MXFP4, 256, 128, 300, 8, 200),   # E > 256: two router expert groups
     # about 370 rows per expert: every expert spans two 256-row blocks, the second partial
     ("pf_nv_deep", synth.NVFP4, 256, 128, 6, 2, 1100),
+    # twelve 128-K chunks: three passes of the scaled-FP4 gate/up GEMM's four-step loop
+    ("pf_nv_k12", synth.NVFP4, 1536, 256, 10, 3, 600),
 ]
 
 
