@@ -45,6 +45,14 @@
 
 namespace ft {
 
+// A 16-byte buffer copy into LDS with the nontemporal bit: for weight streams read once per
+// block, so they do not displace the token tiles that other blocks re-read from L2 (measured:
+// the exact-mode down GEMM 925 -> 915 us, the scaled-FP4 down 430 -> 418 us; the scaled-FP4
+// gate/up got slower with it and keeps plain copies).
+__device__ __forceinline__ void bdma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 2);
+}
 
 // ---- router ------------------------------------------------------------------------------
 // planes (bf16, tiled, see PrefillLaunch::wr_planes): w = plane0 + plane1 + plane2 exactly
@@ -536,7 +544,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       const uint32_t so_ = FMT == FT_MXFP4 ? (c_ >> 1) * 64 + (c_ & 1) * 32                  \
                                            : (c_ >> 1) * 128 + (c_ & 1) * 64;                \
       _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                 \
-        bdma16(wres, wvo[o_], wo_, &WK_[(wave * kXOps + o_) * 64]);                          \
+        bdma16_nt(wres, wvo[o_], wo_, &WK_[(wave * kXOps + o_) * 64]);                       \
         bdma4(sres, svo[o_], so_, (uint32_t*)&WK_[512] + (wave * kXOps + o_) * 64);          \
       }                                                                                      \
       _Pragma("unroll") for (int q_ = 0; q_ < kXTok; ++q_)                                   \
@@ -1130,8 +1138,12 @@ __global__ __launch_bounds__(256) void k_s1_gemm(PrefillLaunch a, int NB) {
   do {                                                                                    \
     const uint32_t c_ = (uint32_t)((kc_) < KC ? (kc_) : (nxt ? (kc_) - KC : KC - 1));     \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
-      bdma16(wres, lo16, __builtin_amdgcn_readfirstlane(wso[i_] + c_ * kTileCodeBytes),   \
-             &WC_[(wave + 4 * i_) * 64]);                                                 \
+      if (MODE == 1)                                                                      \
+        bdma16_nt(wres, lo16, __builtin_amdgcn_readfirstlane(wso[i_] + c_ * kTileCodeBytes), \
+                  &WC_[(wave + 4 * i_) * 64]);                                            \
+      else                                                                                \
+        bdma16(wres, lo16, __builtin_amdgcn_readfirstlane(wso[i_] + c_ * kTileCodeBytes), \
+               &WC_[(wave + 4 * i_) * 64]);                                               \
     bdma4(wres, wsv, c_ * 64, &WS_[64 * wave]);                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                      \
       bdma16(tres, lo16, __builtin_amdgcn_readfirstlane(tso[i_] + c_ * kTileCodeBytes),   \
