@@ -618,6 +618,25 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       }                                                                                     \
       __builtin_amdgcn_sched_barrier(0);                                                    \
     } while (0)
+    // the step after the barrier: its first MFMAs also carry the wave's copies of the chunk
+    // three ahead, two each, so the matrix core starts right after the barrier
+#define FT_X_SCHED_COPIES()                                                                 \
+    do {                                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < kXCopies / 2; ++i_) {                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 / kXOps, 0);                          \
+      }                                                                                     \
+      _Pragma("unroll") for (int i_ = kXCopies / 2; i_ < NJ * kXOps / 2; ++i_) {            \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 / kXOps, 0);                          \
+      }                                                                                     \
+      _Pragma("unroll") for (int i_ = 0; i_ < NJ * kXOps / 2; ++i_) {                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);                                  \
+      }                                                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+    } while (0)
 #define FT_X_NEXT()                                                                         \
     do {                                                                                    \
       _Pragma("unroll") for (int j_ = 0; j_ < NJ; ++j_) Bc[j_] = Bn[j_];                    \
@@ -658,11 +677,10 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
       __builtin_amdgcn_s_barrier();                                                         \
       asm volatile("" ::: "memory");                                                        \
       FT_X_ISSUE((ch_) + 3, TK_, WK_);                                                      \
-      __builtin_amdgcn_sched_barrier(0);                                                    \
       FT_X_READB(TKN_, 0, Bn);                                                              \
       FT_X_DEC(0, cwn_, s0n_, s1n_, An);                                                    \
       FT_X_MMA();                                                                           \
-      FT_X_SCHED(1, 4);                                                                     \
+      FT_X_SCHED_COPIES();                                                                  \
       FT_X_NEXT();                                                                          \
       _Pragma("unroll") for (int o_ = 0; o_ < kXOps; ++o_) {                                \
         cw[o_] = cwn_[o_]; s0[o_] = s0n_[o_]; s1[o_] = s1n_[o_];                            \
@@ -696,6 +714,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
 #undef FT_X_CHUNK
 #undef FT_X_NEXT
 #undef FT_X_SCHED
+#undef FT_X_SCHED_COPIES
 #undef FT_X_MMA
 #undef FT_X_READB
 #undef FT_X_DEC
