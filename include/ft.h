@@ -74,7 +74,8 @@ typedef struct ft_layer ft_layer;
  * the three NVFP4 tensor scales.  Blobs are produced by ft_pack_expert.
  */
 
-/* Bytes of one blob (a multiple of 4096).  H and I must be positive multiples of 128. */
+/* Bytes of one blob (a multiple of 4096).  H and I must be positive multiples of 128, and the
+ * blob must stay under 2 GiB (FT_EINVAL otherwise; ft_layer_create applies the same rule). */
 FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes);
 
 /*

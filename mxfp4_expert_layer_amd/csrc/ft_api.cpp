@@ -168,15 +168,17 @@ static const hipEvent_t* prof_events(ft_layer* l) {
 }
 
 // ---- blobs ------------------------------------------------------------------------------------
+// H, I multiples of 128, and one blob under 2 GiB: the GEMM kernels address a blob through
+// buffer resources, whose extent and offsets are 32-bit.
 static bool dims_ok(int format, int H, int I) {
   return (format == FT_MXFP4 || format == FT_NVFP4) && H > 0 && I > 0 && H % kTileK == 0 &&
-         I % kTileK == 0;
+         I % kTileK == 0 && blob_layout(format, H, I).bytes < (1ull << 31);
 }
 
 extern "C" FT_API int ft_blob_bytes(int format, int H, int I, uint64_t* bytes) try {
   if (!bytes || !dims_ok(format, H, I))
     return fail(FT_EINVAL, "ft_blob_bytes: format must be FT_MXFP4/FT_NVFP4 and H, I positive "
-                           "multiples of 128");
+                           "multiples of 128 with a blob under 2 GiB");
   *bytes = blob_layout(format, H, I).bytes;
   return FT_OK;
 } FT_CATCH("ft_blob_bytes")

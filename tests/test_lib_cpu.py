@@ -44,6 +44,11 @@ def test_blob_bytes_and_alignment():
     assert ft.blob_bytes("mxfp4", 2048, 512) % 4096 == 0
     with pytest.raises(ft.FtError):
         ft.blob_bytes("mxfp4", 100, 128)
+    # the largest square NVFP4 expert under 2 GiB, and the next size up
+    # (3 matrices x 9/16 B per weight: 35584^2 is 2,136,752,128 B, 35712^2 is 2,152,161,280 B)
+    assert ft.blob_bytes("nvfp4", 35584, 35584) == 2_136_752_128
+    with pytest.raises(ft.FtError):
+        ft.blob_bytes("nvfp4", 35712, 35712)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
