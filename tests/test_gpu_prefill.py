@@ -130,6 +130,8 @@ SMALL = [
     ("pf_nv_deep", synth.NVFP4, 256, 128, 6, 2, 1100),
     # twelve 128-K chunks: three passes of the scaled-FP4 gate/up GEMM's four-step loop
     ("pf_nv_k12", synth.NVFP4, 1536, 256, 10, 3, 600),
+    # one expert takes every token: three row blocks of 256, 256 and 1 rows
+    ("pf_mx_e1", synth.MXFP4, 256, 128, 1, 1, 513),
 ]
 
 
