@@ -207,9 +207,11 @@ def test_decode_matches_oracle(ctx, name, T):
 
 @pytest.mark.parametrize("H,I,E,k,ns,T", [(128, 128, 4, 2, 0, 3), (384, 256, 5, 3, 1, 7),
                                           (640, 384, 9, 4, 2, 16), (1152, 640, 17, 5, 1, 11),
-                                          (256, 1152, 6, 1, 0, 2), (512, 2176, 3, 3, 1, 5)])
+                                          (256, 1152, 6, 1, 0, 2), (512, 2176, 3, 3, 1, 5),
+                                          (256, 128, 40, 16, 1, 16), (128, 128, 16, 16, 0, 1)])
 def test_decode_ragged_shapes(ctx, H, I, E, k, ns, T):
-    """K chunk counts that do not divide the wave split, odd row-tile counts, shared experts."""
+    """K chunk counts that do not divide the wave split, odd row-tile counts, shared experts;
+    the largest k (16), with sixteen tokens, and with k = E (every expert selected)."""
     cfg = synth.small_config(f"rag{H}_{I}", seed=H + I, H=H, I=I, E=E, k=k, n_shared=ns,
                              code_dist="normal", router_sigma=1 / np.sqrt(H))
     L = layer_for(ctx, cfg.name, cfg=cfg, max_tokens=16)
