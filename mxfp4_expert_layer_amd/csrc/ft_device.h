@@ -86,9 +86,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
-// silu with the hardware exp and reciprocal (v_exp_f32, v_rcp_f32: a few ulp); used where h
-// is then quantised to FP4, whose rounding decisions it moves only within 1e-6 of their
-// boundaries.
+// silu with the hardware exp and reciprocal (v_exp_f32, v_rcp_f32: a few ulp), for the
+// prefill epilogues, where h is then quantised to FP4 or rounded to bf16: either decision
+// moves only for values within a few fp32 ulp of its boundary.
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }

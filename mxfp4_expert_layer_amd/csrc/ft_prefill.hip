@@ -21,7 +21,7 @@
 //                     32x32x16 bf16 MFMA with the FP4 weights decoded to bf16 in registers
 //                     (E2M1 x E4M3 has at most 6 significant bits, so the decode is exact; the
 //                     fp32 tensor scale is applied in the epilogue), h = bf16(silu(ts_g G) *
-//                     (ts_u U)).
+//                     (ts_u U)), silu on the hardware exp and reciprocal.
 //   k_xgemm<1>        per (expert, 256-row block, 256 rows of W_d): y[t] += w ts_d (W_d h) for
 //                     each row's token t and routing weight w (the combine, as atomic adds).
 // The scaled-FP4 mode replaces the two GEMMs (both operands FP4) and combines separately:
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
               uint16_t hv[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                hv[r] = f32_to_bf16_rne(silu_f32(acc[o][j][4 * q + r] * tsg) *
+                hv[r] = f32_to_bf16_rne(silu_fast(acc[o][j][4 * q + r] * tsg) *
                                         (acc[o][j][8 + 4 * q + r] * tsu));
               const int c = f >> 6, kk = f & 63;
               const uint64_t slot = (((uint64_t)g * NCI + c) * 4 + ((kk >> 3) & 3)) * 64 + t +
