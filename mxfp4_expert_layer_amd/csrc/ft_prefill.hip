@@ -100,6 +100,13 @@ __device__ __forceinline__ f32x16 mfma_bf16_32(const uint4& a, const uint4& b, f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Two fp32 values -> two bf16 rounded to nearest even by one hardware convert (low half
+// first; a NaN stays a NaN).
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2));
+}
+
 // Grid (ceil(T/128), splits, expert groups of up to 6 tiles).  Wave w takes tokens 32 w ..
 // + 31 of the block (the MFMA columns, loaded from x per lane, two chunks ahead); the NT
 // expert tiles x 3 planes x 2 K-steps of each 32-K chunk (one 1 KB operand each) are copied
@@ -743,17 +750,15 @@ __global__ __launch_bounds__(kXThreads) void k_xgemm(PrefillLaunch a, int NB) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int f = fb * 128 + (wave * kXOps + o) * 16 + 8 * q + 4 * h;
-              uint16_t hv[4];
+              float hf[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                hv[r] = f32_to_bf16_rne(silu_fast(acc[o][j][4 * q + r] * tsg) *
-                                        (acc[o][j][8 + 4 * q + r] * tsu));
+                hf[r] = silu_fast(acc[o][j][4 * q + r] * tsg) * (acc[o][j][8 + 4 * q + r] * tsu);
               const int c = f >> 6, kk = f & 63;
               const uint64_t slot = (((uint64_t)g * NCI + c) * 4 + ((kk >> 3) & 3)) * 64 + t +
                                     32 * (kk >> 5);
               *(uint2*)(a.htb + slot * 8 + (kk & 7)) =
-                  make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
-                             (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+                  make_uint2(bf16x2_bits(hf[0], hf[1]), bf16x2_bits(hf[2], hf[3]));
             }
           }
         }
