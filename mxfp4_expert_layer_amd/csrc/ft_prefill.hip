@@ -1037,8 +1037,9 @@ __global__ __launch_bounds__(256) void k_nv_to_mx(const uint8_t* __restrict__ sr
 // 32-row operands) by the 32-token tiles wn, wn + 2, wn + 4, wn + 6 on the 32x32x64 MFMA
 // (fp32 accumulators in the AGPRs); a 32-row operand is two 16-row tiles, read from LDS at
 // the lane slots that hold its K half.  Per 128-K chunk,
-// the weight tiles (16 KB, contiguous in the blob) and the token tiles (16 rows x 64 B
-// gathered per tile) are copied global -> LDS by the DMA form of the vector load, straight
+// the 16 weight tiles (1 KB each, one per 16-row tile of the blob) and the 16 token tiles
+// (1 KB each, 16 rows x 64 B in the tile layout k_tile_xq wrote) are copied global -> LDS by
+// the DMA form of the buffer load, straight
 // into MFMA operand order, so no register holds data in flight: four LDS stages give three
 // chunks of loads in flight while the fourth is multiplied.  Each stage is its own LDS array,
 // which lets the compiler see that reading one stage does not wait on the copies into
