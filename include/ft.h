@@ -208,7 +208,10 @@ FT_API int ft_moe_decode(ft_ctx* ctx, ft_layer* layer, const uint16_t* x, int T,
  * Prefill (large T, all experts resident; smzdm explainer aomxznrn, "FreeToken干的事", item 4:
  * prefill takes its own, compute-bound strategy).  Routing as ft_route; the (token, choice)
  * pairs are sorted by expert (stable), every expert's rows go through one grouped SwiGLU
- * FFN, and y[t] = sum_j w[t][j] * FFN_{idx[t][j]}(x[t]) in rank order.
+ * FFN, and y[t] = sum_j w[t][j] * FFN_{idx[t][j]}(x[t]).  FT_PREFILL_EXACT forms the sum
+ * over j by fp32 atomic adds into y as the down projection's blocks finish, in no fixed
+ * order, so two calls on the same input can differ by fp32 rounding; FT_PREFILL_MXFP4 sums
+ * in rank order and is deterministic.
  *   FT_PREFILL_EXACT: bf16 activations, the exact FP4 weights, bf16 MFMA, fp32 accumulate,
  *     h rounded to bf16 (as decode).
  *   FT_PREFILL_MXFP4: both operands FP4 on the scaled-FP4 MFMA.  x and h are quantised per
