@@ -9,7 +9,7 @@
 //                     3 x 8 significant bits), so the 32x32x16 bf16 MFMA forms exact products
 //                     with fp32 accumulation.
 //   k_topk_many       logits = sum of the partials in order + b; per-token top-k + softmax
-//                     (the decode routine, 16 tokens a workgroup).
+//                     (the decode routine, one token per wave).
 //   k_perm_masks      per 256-token block: a token bitmask per expert (LDS atomics).
 //   k_perm_scan       counts, offsets (exclusive scan), per-block bases, the row-block map.
 //   k_perm_place      pos[t][j] = base + (tokens below t in the block's mask); the row of
@@ -227,16 +227,19 @@ __device__ __forceinline__ uint32_t order_key_p(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Four tokens per workgroup, one per wave, so the waves' partial-logit loads are all in flight
+// together (more workgroups per CU rather than tokens taken one after another by a wave).
+constexpr int kTopkTokens = 4;
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk_many(const float* __restrict__ logits, int splits,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
-  __shared__ float c_val[16][FT_MAX_TOPK];
-  __shared__ int c_idx[16][FT_MAX_TOPK];
+  __shared__ float c_val[kTopkTokens][FT_MAX_TOPK];
+  __shared__ int c_idx[kTopkTokens][FT_MAX_TOPK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tb = blockIdx.x * 16;
-  const int nt = min(16, T - tb);
+  const int tb = blockIdx.x * kTopkTokens;
+  const int nt = min(kTopkTokens, T - tb);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int tl = wave; tl < nt; tl += 4) {
     const int t = tb + tl;
@@ -413,19 +416,47 @@ __global__ __launch_bounds__(256) void k_perm_scan(PrefillLaunch a) {
   }
 }
 
+// One thread per token.  KMAX (>= k) bounds the choices: all of a token's index and weight
+// loads are issued together, then all of its mask-row and base loads (clamped addresses,
+// results past k unused), so the kernel waits on two rounds of loads rather than two per
+// choice.
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_perm_place(PrefillLaunch a) {
   const int b = blockIdx.x, tl = threadIdx.x;
   const int t = b * kPermBlock + tl;
   if (t >= a.T) return;
-  for (int j = 0; j < a.k; ++j) {
-    const int e = a.idx[(uint64_t)t * a.k + j];
-    const uint32_t* m = a.masks + ((uint64_t)b * a.E + e) * 8;
-    int r = __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
-    for (int q = 0; q < (tl >> 5); ++q) r += __popc(m[q]);
-    const int p = a.base[(uint64_t)b * a.E + e] + r;
+  int e[KMAX];
+  float wv[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const uint64_t q = (uint64_t)t * a.k + min(j, a.k - 1);
+    e[j] = a.idx[q];
+    wv[j] = a.w[q];
+  }
+  uint4 m0[KMAX], m1[KMAX];
+  int bs[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const uint64_t row = (uint64_t)b * a.E + e[j];
+    m0[j] = *(const uint4*)(a.masks + row * 8);
+    m1[j] = *(const uint4*)(a.masks + row * 8 + 4);
+    bs[j] = a.base[row];
+  }
+  const int wq = tl >> 5;
+  const uint32_t below = (1u << (tl & 31)) - 1u;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= a.k) break;
+    const uint32_t m[8] = {m0[j].x, m0[j].y, m0[j].z, m0[j].w, m1[j].x, m1[j].y, m1[j].z, m1[j].w};
+    // tokens of this block below t that chose e[j]: whole words below t's word, then the
+    // bits below t in its own word
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r += q < wq ? __popc(m[q]) : (q == wq ? __popc(m[q] & below) : 0);
+    const int p = bs[j] + r;
     a.pos[(uint64_t)t * a.k + j] = p;
     a.perm_tok[p] = t;
-    a.perm_w[p] = a.w[(uint64_t)t * a.k + j];
+    a.perm_w[p] = wv[j];
   }
 }
 
@@ -1512,7 +1543,7 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
     }
 #undef FT_RT_LAUNCH
   }
-  const dim3 tg((a.T + 15) / 16);
+  const dim3 tg((a.T + kTopkTokens - 1) / kTopkTokens);
 #define FT_TK_ARGS a.logits, a.splits, a.router_b, a.T, a.E, a.k, a.idx, a.w
   if (a.E <= 64) hipLaunchKernelGGL(k_topk_many<1>, tg, dim3(256), 0, st, FT_TK_ARGS);
   else if (a.E <= 128) hipLaunchKernelGGL(k_topk_many<2>, tg, dim3(256), 0, st, FT_TK_ARGS);
@@ -1525,7 +1556,8 @@ extern "C" int ftk_prefill(const PrefillLaunch* ap, hipStream_t st, const hipEve
   }
   hipLaunchKernelGGL(k_perm_masks, dim3(nblk), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_perm_place, dim3(nblk), dim3(256), 0, st, a);
+  if (a.k <= 8) hipLaunchKernelGGL(k_perm_place<8>, dim3(nblk), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_perm_place<FT_MAX_TOPK>, dim3(nblk), dim3(256), 0, st, a);
   if (a.mode == FT_PREFILL_MXFP4) {
     // tiles of the padded permuted tokens: at most T*k + 15 E rows
     const unsigned maxtrows = (unsigned)((a.T * a.k + 15 * a.E + 15) / 16);

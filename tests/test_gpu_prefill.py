@@ -132,6 +132,9 @@ SMALL = [
     ("pf_nv_k12", synth.NVFP4, 1536, 256, 10, 3, 600),
     # one expert takes every token: three row blocks of 256, 256 and 1 rows
     ("pf_mx_e1", synth.MXFP4, 256, 128, 1, 1, 513),
+    # sixteen choices per token (the largest k), 303 tokens: a partial last top-k workgroup
+    # and permutation block
+    ("pf_mx_k16", synth.MXFP4, 256, 128, 40, 16, 303),
 ]
 
 
