@@ -208,10 +208,13 @@ def test_decode_matches_oracle(ctx, name, T):
 @pytest.mark.parametrize("H,I,E,k,ns,T", [(128, 128, 4, 2, 0, 3), (384, 256, 5, 3, 1, 7),
                                           (640, 384, 9, 4, 2, 16), (1152, 640, 17, 5, 1, 11),
                                           (256, 1152, 6, 1, 0, 2), (512, 2176, 3, 3, 1, 5),
-                                          (256, 128, 40, 16, 1, 16), (128, 128, 16, 16, 0, 1)])
+                                          (256, 128, 40, 16, 1, 16), (128, 128, 16, 16, 0, 1),
+                                          (256, 1152, 6, 2, 1, 1), (384, 1664, 12, 9, 1, 1)])
 def test_decode_ragged_shapes(ctx, H, I, E, k, ns, T):
     """K chunk counts that do not divide the wave split, odd row-tile counts, shared experts;
-    the largest k (16), with sixteen tokens, and with k = E (every expert selected)."""
+    the largest k (16), with sixteen tokens, and with k = E (every expert selected); one token
+    with 9 and 13 down-projection K chunks (two load batches, the second partly filled) and
+    ten list entries (two per wave of the down kernel)."""
     cfg = synth.small_config(f"rag{H}_{I}", seed=H + I, H=H, I=I, E=E, k=k, n_shared=ns,
                              code_dist="normal", router_sigma=1 / np.sqrt(H))
     L = layer_for(ctx, cfg.name, cfg=cfg, max_tokens=16)
@@ -219,7 +222,8 @@ def test_decode_ragged_shapes(ctx, H, I, E, k, ns, T):
 
 
 @pytest.mark.parametrize("H,I,E,k,ns,T,ts", [(256, 128, 5, 2, 1, 1, 0.7), (384, 640, 7, 3, 1, 5, 1 / 64),
-                                             (1152, 256, 9, 4, 0, 16, 3.0)])
+                                             (1152, 256, 9, 4, 0, 16, 3.0),
+                                             (256, 1408, 9, 4, 1, 1, 0.7)])
 def test_decode_nvfp4_shapes(ctx, H, I, E, k, ns, T, ts):
     """NVFP4 experts (E4M3 scales per 16 over all 256 codes' normal range, a tensor scale that
     is not a power of two in two of the cases), shared experts, ragged chunk counts."""
