@@ -656,8 +656,10 @@ def bench_headline(args):
     """The default line: the 753B-class prefill of 4096 tokens in the exact mode (bf16
     activations, bf16 MFMA) is `value`, with its gate/up grouped GEMM as the roofline kernel.
     The same run adds the scaled-FP4 mode of that layer (tokens/s, its gate/up kernel's HBM
-    and FP4 MFMA fractions, both grouped GEMMs' FP4 fraction) and the 284B-class decode at 1,
-    4 and 16 tokens per step (tokens/s and HBM fractions), as extra keys."""
+    and FP4 MFMA fractions, both grouped GEMMs' FP4 fraction), the 284B-class decode at 1,
+    4 and 16 tokens per step (tokens/s and HBM fractions) and the 284B-class miss path (48 of
+    256 experts in the pool, Zipf c = 0.7 so that the hit rate falls in 60-90%; tokens/s, hit
+    rate, m, q, Bp, Bh), as extra keys."""
     from mxfp4_expert_layer_amd import ft, synth
     from mxfp4_expert_layer_amd.layer import GpuLayer
 
@@ -693,6 +695,14 @@ def bench_headline(args):
                                    "layer_copies": 4, "graph_replay": True},
                         "measured_read_GBps": ref["measured_read_GBps"], **dec},
     }
+    # the miss path on its own protocol (64 untimed then 64 timed single tokens), in a
+    # context of its own
+    margs = argparse.Namespace(**vars(args))
+    margs.workload, margs.zipf_c, margs.steps, margs.warmup = "miss-path-284b", 0.7, None, None
+    mp = bench_miss_path(margs, WORKLOADS["miss-path-284b"])
+    res["miss_path_284b"] = {"tokens_per_s": mp["value"], "ms_per_step": mp["ms_per_step"],
+                             "steps": mp["steps"], "warmup": mp["warmup"],
+                             "config": mp["config"], **mp["miss_path"]}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline_prefill(cfg, r0["xh"][0], args.cpu_seconds, "exact")
