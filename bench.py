@@ -657,7 +657,8 @@ def bench_headline(args):
     activations, bf16 MFMA) is `value`, with its gate/up grouped GEMM as the roofline kernel.
     The same run adds the scaled-FP4 mode of that layer (tokens/s, its gate/up kernel's HBM
     and FP4 MFMA fractions, both grouped GEMMs' FP4 fraction), the 284B-class decode at 1,
-    4 and 16 tokens per step (tokens/s and HBM fractions) and the 284B-class miss path (48 of
+    4 and 16 tokens per step (tokens/s and HBM fractions), the 35B-A3B-class decode at 1 and
+    8 tokens per step in both weight formats, and the 284B-class miss path (48 of
     256 experts in the pool, Zipf c = 0.7 so that the hit rate falls in 60-90%; tokens/s, hit
     rate, m, q, Bp, Bh), as extra keys."""
     from mxfp4_expert_layer_amd import ft, synth
@@ -695,6 +696,15 @@ def bench_headline(args):
                                    "layer_copies": 4, "graph_replay": True},
                         "measured_read_GBps": ref["measured_read_GBps"], **dec},
     }
+    for name, key in (("35b-a3b", "decode_35b_a3b"), ("35b-a3b-nvfp4", "decode_35b_a3b_nvfp4")):
+        c35 = synth.CONFIGS[name]
+        d35 = decode_sweep(ctx, name, (1, 8), copies=8)
+        for v in d35.values():
+            v["gateup_frac_of_measured_read"] = v["gateup_GBps"] / ref["measured_read_GBps"]
+        res[key] = {"config": {"hidden": c35.H, "intermediate": c35.I, "experts": c35.E,
+                               "top_k": c35.k, "shared_experts": c35.n_shared,
+                               "weights": c35.fmt, "layer_copies": 8, "graph_replay": True},
+                    **d35}
     # the miss path on its own protocol (64 untimed then 64 timed single tokens), in a
     # context of its own
     margs = argparse.Namespace(**vars(args))
