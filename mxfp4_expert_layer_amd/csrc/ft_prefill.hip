@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_router_prefill(PrefillLaunch a) {
 }
 
 // ---- top-k for many tokens ------------------------------------------------------------------
-// Same radix select as decode (see ft_decode.hip), 16 tokens per workgroup.
+// Same radix select as decode (see ft_decode.hip), four tokens per workgroup.
 __device__ __forceinline__ uint32_t order_key_p(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
